@@ -1,0 +1,190 @@
+"""Seeded synthetic workloads for the routed-expert MoE FFN.
+
+This module only draws inputs: token activations, router logits and expert
+weights at the expert shapes of the models the HiNa-MoE paper measures
+(arXiv 2610.05123, §7.3 and Table 3), plus the INT8 group quantisation of
+those weights that the INT8 variant takes as input (§8.1).  It holds none of
+the FFN's arithmetic (no routing, gathering, projection or combine); both the
+CPU oracle and the HIP library receive what it returns.
+
+Recipe (all draws are seeded; BF16 values are float32 draws rounded to
+nearest-even by torch's dtype cast):
+  * x [T,H] ~ N(0,1) in BF16, drawn on the CPU.
+  * router logits [T,E] ~ N(0,1) float32, drawn on the CPU, then shaped by
+    the routing recipe:
+      - "uniform": used as drawn;
+      - "forced" : token t may only pick experts 2t mod E and 2t+1 mod E (all
+        other logits set to -inf), so with E = 8 and top-2 every expert gets
+        exactly T/4 tokens;
+      - "zipf"   : ln p_e is added to every logit, p_e proportional to
+        r_e^-s, r a seeded permutation of 1..E (skewed expert popularity).
+  * expert weights ~ N(0, 0.02): W_gate, W_up [E][I][H] and W_down [E][H][I],
+    row-major BF16, drawn expert by expert on the device that will hold them
+    (one seeded torch generator per (tensor, expert)).
+  * INT8 weights: the float32 draws above, quantised symmetrically per group
+    of 128 consecutive K elements of a row: s = max|w| / 127 (float32),
+    q = clamp(round_half_even(w / s), -127, 127); an all-zero group gets
+    s = 0 and q = 0.
+"""
+from dataclasses import dataclass, replace
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+TAG_X, TAG_LOGITS, TAG_WG, TAG_WU, TAG_WD, TAG_ZIPF = range(6)
+WEIGHT_STD = 0.02
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One MoE FFN layer invocation: shapes, routing recipe and seed."""
+    name: str
+    H: int           # hidden size (model dimension)
+    I: int           # expert intermediate size
+    E: int           # number of routed experts
+    k: int           # experts per token (top-k)
+    T: int           # tokens in the decode batch
+    routing: str = "uniform"   # "uniform" | "forced" | "zipf"
+    zipf_s: float = 0.0
+    int8: bool = False
+    group: int = 128
+    seed: int = 0
+
+    def with_tokens(self, T: int) -> "Workload":
+        return replace(self, T=T, name=f"{self.name.split('@')[0]}@T{T}")
+
+
+def _registry() -> Dict[str, Workload]:
+    w = {}
+    w["tiny"] = Workload("tiny", H=256, I=512, E=8, k=2, T=16)
+    for m in (1, 2, 4, 8, 16):
+        w[f"mixtral8x7b_m{m}"] = Workload(f"mixtral8x7b_m{m}", H=4096, I=14336,
+                                          E=8, k=2, T=4 * m, routing="forced")
+        w[f"mixtral8x7b_int8_m{m}"] = Workload(f"mixtral8x7b_int8_m{m}", H=4096,
+                                               I=14336, E=8, k=2, T=4 * m,
+                                               routing="forced", int8=True)
+    w["deepseekv3_t16"] = Workload("deepseekv3_t16", H=7168, I=2048, E=256, k=8, T=16)
+    w["deepseekv3_zipf_t16"] = Workload("deepseekv3_zipf_t16", H=7168, I=2048,
+                                        E=256, k=8, T=16, routing="zipf", zipf_s=1.1)
+    for T in (1, 4, 16):
+        w[f"mixtral8x22b_t{T}"] = Workload(f"mixtral8x22b_t{T}", H=6144, I=16384,
+                                           E=8, k=2, T=T)
+        w[f"qwen3_235b_t{T}"] = Workload(f"qwen3_235b_t{T}", H=4096, I=1536,
+                                         E=128, k=8, T=T)
+    return w
+
+
+WORKLOADS: Dict[str, Workload] = _registry()
+
+
+def seed_for(seed: int, tag: int, index: int = 0) -> int:
+    """Independent 63-bit seed for (workload seed, tensor tag, index)."""
+    st = np.random.SeedSequence([seed, tag, index]).generate_state(1, np.uint64)[0]
+    return int(st) & ((1 << 63) - 1)
+
+
+def _gen(device, seed: int) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def gen_x(wl: Workload) -> torch.Tensor:
+    """Token activations [T, H], BF16, CPU."""
+    g = _gen("cpu", seed_for(wl.seed, TAG_X))
+    return torch.randn(wl.T, wl.H, generator=g, dtype=torch.float32).to(torch.bfloat16)
+
+
+def gen_logits(wl: Workload) -> torch.Tensor:
+    """Router logits [T, E], float32, CPU, shaped by the routing recipe."""
+    g = _gen("cpu", seed_for(wl.seed, TAG_LOGITS))
+    lg = torch.randn(wl.T, wl.E, generator=g, dtype=torch.float32)
+    if wl.routing == "uniform":
+        return lg
+    if wl.routing == "forced":
+        allowed = torch.zeros(wl.T, wl.E, dtype=torch.bool)
+        t = torch.arange(wl.T)
+        allowed[t, (2 * t) % wl.E] = True
+        allowed[t, (2 * t + 1) % wl.E] = True
+        return torch.where(allowed, lg, torch.full_like(lg, float("-inf")))
+    if wl.routing == "zipf":
+        rng = np.random.default_rng(seed_for(wl.seed, TAG_ZIPF))
+        rank = rng.permutation(wl.E) + 1
+        p = rank.astype(np.float64) ** (-wl.zipf_s)
+        logp = np.log(p / p.sum())
+        return (lg.double() + torch.from_numpy(logp)[None, :]).float()
+    raise ValueError(f"unknown routing recipe {wl.routing!r}")
+
+
+def _draw(wl: Workload, tag: int, e: int, N: int, K: int, device) -> torch.Tensor:
+    g = _gen(device, seed_for(wl.seed, tag, e))
+    return torch.randn(N, K, generator=g, device=device, dtype=torch.float32) * WEIGHT_STD
+
+
+def gen_weights(wl: Workload, device="cpu", experts: Optional[list] = None):
+    """BF16 expert weights (W_gate [E,I,H], W_up [E,I,H], W_down [E,H,I]).
+
+    ``experts`` limits the draw to those experts (the others stay zero); by
+    default every expert is drawn.
+    """
+    ex = range(wl.E) if experts is None else experts
+    Wg = torch.zeros(wl.E, wl.I, wl.H, dtype=torch.bfloat16, device=device)
+    Wu = torch.zeros(wl.E, wl.I, wl.H, dtype=torch.bfloat16, device=device)
+    Wd = torch.zeros(wl.E, wl.H, wl.I, dtype=torch.bfloat16, device=device)
+    for e in ex:
+        Wg[e] = _draw(wl, TAG_WG, e, wl.I, wl.H, device).to(torch.bfloat16)
+        Wu[e] = _draw(wl, TAG_WU, e, wl.I, wl.H, device).to(torch.bfloat16)
+        Wd[e] = _draw(wl, TAG_WD, e, wl.H, wl.I, device).to(torch.bfloat16)
+    return Wg, Wu, Wd
+
+
+def quantize_groupwise(w: torch.Tensor, group: int = 128):
+    """Symmetric INT8 per-group quantisation along the last dim of ``w``.
+
+    Returns (q int8 with w's shape, s float32 of shape [..., K/group]).
+    """
+    *lead, K = w.shape
+    assert K % group == 0
+    wg = w.float().reshape(*lead, K // group, group)
+    s = wg.abs().amax(dim=-1) / 127.0
+    safe = torch.where(s > 0, s, torch.ones_like(s))
+    q = torch.round(wg / safe[..., None]).clamp_(-127, 127)
+    q = torch.where((s > 0)[..., None], q, torch.zeros_like(q))
+    return q.to(torch.int8).reshape(*lead, K), s.contiguous()
+
+
+def gen_weights_int8(wl: Workload, device="cpu", experts: Optional[list] = None):
+    """INT8 expert weights with per-group scales:
+    (Qg [E,I,H], Sg [E,I,H/g], Qu, Su, Qd [E,H,I], Sd [E,H,I/g])."""
+    ex = range(wl.E) if experts is None else experts
+    gsz = wl.group
+    Qg = torch.zeros(wl.E, wl.I, wl.H, dtype=torch.int8, device=device)
+    Qu = torch.zeros(wl.E, wl.I, wl.H, dtype=torch.int8, device=device)
+    Qd = torch.zeros(wl.E, wl.H, wl.I, dtype=torch.int8, device=device)
+    Sg = torch.zeros(wl.E, wl.I, wl.H // gsz, dtype=torch.float32, device=device)
+    Su = torch.zeros(wl.E, wl.I, wl.H // gsz, dtype=torch.float32, device=device)
+    Sd = torch.zeros(wl.E, wl.H, wl.I // gsz, dtype=torch.float32, device=device)
+    for e in ex:
+        Qg[e], Sg[e] = quantize_groupwise(_draw(wl, TAG_WG, e, wl.I, wl.H, device), gsz)
+        Qu[e], Su[e] = quantize_groupwise(_draw(wl, TAG_WU, e, wl.I, wl.H, device), gsz)
+        Qd[e], Sd[e] = quantize_groupwise(_draw(wl, TAG_WD, e, wl.H, wl.I, device), gsz)
+    return Qg, Sg, Qu, Su, Qd, Sd
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    """BF16 tensor -> numpy uint16 bit patterns (host copy)."""
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def bits_to_bf16(a: np.ndarray) -> torch.Tensor:
+    """numpy uint16 bit patterns -> BF16 CPU tensor."""
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).view(torch.bfloat16)
+
+
+def weight_bytes_per_expert(wl: Workload) -> int:
+    """Bytes of one expert's three weight matrices (plus scales for INT8)."""
+    n = 3 * wl.H * wl.I
+    if wl.int8:
+        return n + 3 * (wl.H * wl.I // wl.group) * 4
+    return 2 * n
