@@ -1,0 +1,189 @@
+/*
+ * moe_ffn.h -- C ABI of the routed-expert MoE FFN library for MI355X (gfx950).
+ *
+ * The operation is the routed-expert feed-forward layer of Mixture-of-Experts
+ * decoding described in "HiNa-MoE: High-Performance, Non-Intrusive MoE
+ * Inference on CPUs with Matrix Engines" (arXiv 2610.05123):
+ *   - §2.1 / Fig. 2: a gate sends every token to k of E experts (Table 3:
+ *     top-2 for Mixtral, top-8 for DeepSeek-V3 and Qwen3);
+ *   - §4.1 / Fig. 5: the tokens routed to one expert are gathered into a small
+ *     matrix I and the expert computes FFN(I) = SiLU(I*Wgate) (.) (I*Wup) * Wdown
+ *     (FFN equation of §4.1);
+ *   - §4.1 ("transform I, not W"): expert weights stay in their ordinary
+ *     row-major layout; only the small gathered matrix is laid out for the
+ *     matrix unit, and the result is written back row-major;
+ *   - §4.2.1: BF16 operands with FP32 accumulation; §8.1 / Fig. 11: an INT8
+ *     variant with symmetric group-wise weight quantisation.
+ *
+ * Conventions for every entry point:
+ *   - Tensors are plain device pointers in caller-owned memory (e.g. from
+ *     PyTorch).  The library never allocates, frees, repacks or copies weights,
+ *     and keeps no state between calls besides a cached CU count per device and
+ *     the per-thread benchmark hook of moe_ffn_set_stage_events.
+ *   - BF16 values are IEEE bfloat16 bit patterns (uint16).  All arrays are
+ *     dense row-major with the last index contiguous.
+ *   - `stream` is a hipStream_t (NULL = the default stream) of the current HIP
+ *     device; all pointers must be memory of that device.  Work is enqueued
+ *     asynchronously; no entry point synchronises except
+ *     moe_ffn_check_status.
+ *   - Return value: MOE_FFN_OK (0) or a negative MOE_FFN_ERR_* code; on an
+ *     error nothing has been enqueued.  Shape and pointer checks are done on
+ *     the host before any launch.
+ *   - Calls that use distinct workspaces may run concurrently; calls that
+ *     share a workspace must be ordered (same stream).
+ */
+#ifndef MOE_FFN_H
+#define MOE_FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_FFN_OK 0
+#define MOE_FFN_ERR_NULL_ARG (-1)    /* a required pointer is NULL */
+#define MOE_FFN_ERR_BAD_SHAPE (-2)   /* sizes outside the supported range */
+#define MOE_FFN_ERR_MISALIGNED (-3)  /* a tensor pointer is not 16-byte aligned */
+#define MOE_FFN_ERR_ALIAS (-4)       /* out overlaps x (or ids/weights overlap) */
+#define MOE_FFN_ERR_WORKSPACE (-5)   /* workspace NULL or smaller than required */
+#define MOE_FFN_ERR_HIP (-6)         /* a HIP runtime call or launch failed */
+#define MOE_FFN_ERR_BAD_IDS (-7)     /* (device-side) expert ids outside [0, E) */
+
+/* Largest supported expert count (per-expert tables live in on-chip memory). */
+#define MOE_FFN_MAX_EXPERTS 1024
+/* INT8 variant: one FP32 scale per this many consecutive K elements of a row. */
+#define MOE_FFN_INT8_GROUP 128
+
+/*
+ * Workspace layout.  The workspace is caller-owned device memory, at least
+ * total_bytes long and 256-byte aligned; each region starts at the given byte
+ * offset.  Regions (T tokens, k = top_k, S = T*k slots, slot s = t*k + j):
+ *   meta        int32[8]   [0] number of active experts A, [1] number of slots
+ *                          whose expert id was outside [0, E) (those slots
+ *                          contribute nothing to the output)
+ *   counts      int32[E]   tokens routed to each expert
+ *   offsets     int32[E+1] start of each expert's run in sorted_slot
+ *   active      int32[E]   the A experts with counts > 0, ascending
+ *   sorted_slot int32[S]   slots grouped by expert (ascending), ascending
+ *                          slot order within an expert (the gather order)
+ *   h           bf16[S][I] SiLU(gate)*up of each gathered row, in
+ *                          sorted_slot order (row p belongs to slot
+ *                          sorted_slot[p])
+ *   y           f32[S][H]  down-projection output of each slot, slot order
+ * After a forward call the regions hold these values (tests inspect them).
+ */
+typedef struct moe_ffn_ws_layout {
+    size_t total_bytes;
+    size_t meta;
+    size_t counts;
+    size_t offsets;
+    size_t active;
+    size_t sorted_slot;
+    size_t h;
+    size_t y;
+} moe_ffn_ws_layout;
+
+/* Fill *layout for the given sizes.  Pure host computation (no HIP call).
+ * Returns MOE_FFN_ERR_NULL_ARG if layout is NULL, MOE_FFN_ERR_BAD_SHAPE for
+ * T < 0, H or I < 1, E outside [1, MOE_FFN_MAX_EXPERTS], top_k outside [1, E]. */
+int moe_ffn_workspace_layout(int64_t T, int64_t H, int64_t I, int32_t E,
+                             int32_t top_k, moe_ffn_ws_layout* layout);
+
+/* Workspace bytes needed by moe_ffn_forward / moe_ffn_forward_int8 for these
+ * sizes, or 0 if the sizes are invalid. */
+size_t moe_ffn_workspace_bytes(int64_t T, int64_t H, int64_t I, int32_t E,
+                               int32_t top_k);
+
+/*
+ * Top-k router (HiNa-MoE §2.1 / Fig. 2; k from Table 3).
+ *   logits   [T][E] float32, device.
+ *   topk_ids [T][top_k] int32, device, written: for each token the top_k
+ *            experts by descending logit (= descending softmax probability),
+ *            ties broken toward the lower expert id.
+ *   topk_w   [T][top_k] float32, device, written: the softmax probabilities of
+ *            the chosen experts renormalised to sum to one (equal to a softmax
+ *            over the top_k chosen logits).
+ * Each token needs at least top_k finite logits; NaN logits are not supported.
+ * Errors: NULL_ARG, BAD_SHAPE (T < 0, E outside [1, MOE_FFN_MAX_EXPERTS],
+ * top_k outside [1, min(E, 64)]), ALIAS (outputs overlap), HIP.
+ */
+int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t top_k,
+                   int32_t* topk_ids, float* topk_w, void* stream);
+
+/*
+ * Routed-expert FFN layer, BF16 weights (HiNa-MoE §4.1 FFN equation).
+ *   x        [T][H] bf16, device: token activations.
+ *   topk_ids [T][top_k] int32, device: expert of each slot.  Ids outside
+ *            [0, E) drop that slot (it adds nothing) and are counted in the
+ *            workspace meta[1]; read them with moe_ffn_check_status.
+ *   topk_w   [T][top_k] float32, device: routing weight of each slot (any
+ *            values; they need not sum to one).  Duplicate ids in a row each
+ *            count.
+ *   W_gate, W_up [E][I][H] bf16, device: row i of expert e holds the H
+ *            weights producing intermediate feature i (K = H contiguous).
+ *   W_down   [E][H][I] bf16, device: row n produces output feature n.
+ *            Experts that no slot names are never read.
+ *   out      [T][H] bf16, device, fully overwritten:
+ *            out[t] = RNE_bf16( sum_j topk_w[t,j] * y_{t,j} ), FP32 sum over
+ *            ascending j, where y_{t,j} = W_down[e] * h (FP32 accumulation),
+ *            h = RNE_bf16( silu(g) * u ), g = W_gate[e] x_t, u = W_up[e] x_t
+ *            (BF16 products, FP32 accumulation), e = topk_ids[t,j].
+ *   workspace / workspace_bytes: at least moe_ffn_workspace_bytes(...) bytes,
+ *            256-byte aligned, device; contents on entry are ignored.
+ * Sizes: T >= 0 (T = 0 is a no-op), H and I multiples of 32,
+ * 1 <= E <= MOE_FFN_MAX_EXPERTS, 1 <= top_k <= E, T*top_k < 2^31.
+ * Errors: NULL_ARG, BAD_SHAPE, MISALIGNED (x, out, weights not 16-byte
+ * aligned), ALIAS (out overlaps x), WORKSPACE, HIP.
+ */
+int moe_ffn_forward(const void* x, const int32_t* topk_ids, const float* topk_w,
+                    const void* W_gate, const void* W_up, const void* W_down,
+                    void* out, int64_t T, int64_t H, int64_t I, int32_t E,
+                    int32_t top_k, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/*
+ * Routed-expert FFN layer, INT8 weights with group scales (HiNa-MoE §8.1,
+ * Fig. 11: symmetric group-wise INT8; group = MOE_FFN_INT8_GROUP along K).
+ * As moe_ffn_forward, except every weight row r is int8 q[r][K] with one
+ * float32 scale per group of 128: s[r][K/128], and each dot product is
+ *   sum_g s[r][g] * (sum_{c in group g} v_c * q[r][c])   (FP32).
+ *   Q_gate, Q_up [E][I][H] int8 with S_gate, S_up [E][I][H/128] float32;
+ *   Q_down [E][H][I] int8 with S_down [E][H][I/128] float32.
+ * Sizes: H and I multiples of 128.  Scale pointers must be 16-byte aligned.
+ */
+int moe_ffn_forward_int8(const void* x, const int32_t* topk_ids,
+                         const float* topk_w, const int8_t* Q_gate,
+                         const float* S_gate, const int8_t* Q_up,
+                         const float* S_up, const int8_t* Q_down,
+                         const float* S_down, void* out, int64_t T, int64_t H,
+                         int64_t I, int32_t E, int32_t top_k, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Wait for `stream`, then read the workspace meta written by the last forward
+ * call: MOE_FFN_ERR_BAD_IDS if it dropped slots with out-of-range ids,
+ * MOE_FFN_OK otherwise (MOE_FFN_ERR_HIP if the wait or the read fails).  If
+ * n_dropped is not NULL it receives the number of dropped slots. */
+int moe_ffn_check_status(const void* workspace, void* stream, int64_t* n_dropped);
+
+/* Static description of a status code (never NULL). */
+const char* moe_ffn_status_string(int status);
+
+/*
+ * Benchmark hook: per-kernel timing with HIP events.  After this call, the
+ * next forward call made by the calling host thread (either weight format)
+ * records events[i] on its stream right after enqueuing kernel i, for
+ * i < n_events: 0 = gather index (permute), 1 = gate/up, 2 = down,
+ * 3 = combine.  The events are hipEvent_t handles owned by the caller.  The
+ * setting is consumed by that one call; n_events = 0 (or events = NULL)
+ * clears it.  Only the calling thread is affected.  Returns MOE_FFN_OK, or
+ * MOE_FFN_ERR_BAD_SHAPE if n_events is outside [0, 4].
+ */
+int moe_ffn_set_stage_events(void* const* events, int32_t n_events);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FFN_H */

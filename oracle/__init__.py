@@ -41,6 +41,8 @@ def lib() -> ctypes.CDLL:
         if path == _build.LIB and not os.path.exists(path):
             _build.build()
         L = ctypes.CDLL(path)
+        L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_num_threads.argtypes = []
         L.oracle_bf16_to_f32.restype = ctypes.c_float
         L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
         L.oracle_f32_to_bf16.restype = ctypes.c_uint16
@@ -69,6 +71,11 @@ def lib() -> ctypes.CDLL:
             ctypes.c_int32, ctypes.c_int32, _u16p, _f32p, _u16p, _f32p]
         _LIB = L
     return _LIB
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's loops use."""
+    return int(lib().oracle_num_threads())
 
 
 def _ptr(a: np.ndarray, ctype):

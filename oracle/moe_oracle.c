@@ -38,6 +38,7 @@
  *     a row; g = sum_groups s_g * (sum_{c in group} x_c * q_c), in FP32.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -46,6 +47,9 @@
 #define ORACLE_ERR_ARG (-1)
 #define ORACLE_ERR_MISSING_EXPERT (-2)
 #define ORACLE_ERR_NOMEM (-3)
+
+/* Threads the OpenMP loops below will use (reported with CPU timings). */
+int oracle_num_threads(void) { return omp_get_max_threads(); }
 
 /* ---------------------------------------------------------------------- */
 /* BF16 <-> FP32.  BF16 is the upper half of an IEEE binary32 word.        */

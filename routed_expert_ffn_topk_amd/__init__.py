@@ -1,0 +1,202 @@
+"""MI355X-native routed-expert MoE FFN: ctypes binding over libmoe_ffn.so.
+
+The library (HIP kernels for gfx950 behind the C ABI in ``include/moe_ffn.h``)
+implements the routed-expert feed-forward layer of MoE decoding from the
+HiNa-MoE paper (arXiv 2610.05123, §4.1 FFN equation; §2.1 routing; §8.1 INT8
+variant).  This module only marshals torch tensors (device memory) and the
+current HIP stream into those C calls, with the same names; every step of
+the computation runs in the library's kernels.  There is no fallback: if
+``libmoe_ffn.so`` is missing, loading fails with an error.
+"""
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_ffn.so")
+
+MOE_FFN_OK = 0
+MOE_FFN_ERR_NULL_ARG = -1
+MOE_FFN_ERR_BAD_SHAPE = -2
+MOE_FFN_ERR_MISALIGNED = -3
+MOE_FFN_ERR_ALIAS = -4
+MOE_FFN_ERR_WORKSPACE = -5
+MOE_FFN_ERR_HIP = -6
+MOE_FFN_ERR_BAD_IDS = -7
+MOE_FFN_MAX_EXPERTS = 1024
+MOE_FFN_INT8_GROUP = 128
+
+LAYOUT_FIELDS = ("total_bytes", "meta", "counts", "offsets", "active", "sorted_slot", "h", "y")
+
+
+class MoeFfnError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        self.code = code
+        super().__init__(f"{fn} failed: {moe_ffn_status_string(code)} ({code})")
+
+
+class _Layout(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_size_t) for f in LAYOUT_FIELDS]
+
+
+_lib = None
+_c = ctypes
+_i64, _i32, _vp, _sz = _c.c_int64, _c.c_int32, _c.c_void_p, _c.c_size_t
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe_ffn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "routed_expert_ffn_topk_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        L.moe_ffn_workspace_layout.restype = _c.c_int
+        L.moe_ffn_workspace_layout.argtypes = [_i64, _i64, _i64, _i32, _i32, _c.POINTER(_Layout)]
+        L.moe_ffn_workspace_bytes.restype = _sz
+        L.moe_ffn_workspace_bytes.argtypes = [_i64, _i64, _i64, _i32, _i32]
+        L.moe_route_topk.restype = _c.c_int
+        L.moe_route_topk.argtypes = [_vp, _i64, _i32, _i32, _vp, _vp, _vp]
+        L.moe_ffn_forward.restype = _c.c_int
+        L.moe_ffn_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
+                                      _i32, _i32, _vp, _sz, _vp]
+        L.moe_ffn_forward_int8.restype = _c.c_int
+        L.moe_ffn_forward_int8.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                           _i64, _i64, _i64, _i32, _i32, _vp, _sz, _vp]
+        L.moe_ffn_check_status.restype = _c.c_int
+        L.moe_ffn_check_status.argtypes = [_vp, _vp, _c.POINTER(_i64)]
+        L.moe_ffn_status_string.restype = _c.c_char_p
+        L.moe_ffn_status_string.argtypes = [_c.c_int]
+        L.moe_ffn_set_stage_events.restype = _c.c_int
+        L.moe_ffn_set_stage_events.argtypes = [_c.POINTER(_vp), _i32]
+        _lib = L
+    return _lib
+
+
+def moe_ffn_status_string(code: int) -> str:
+    return lib().moe_ffn_status_string(code).decode()
+
+
+def _check(fn: str, code: int):
+    if code != MOE_FFN_OK:
+        raise MoeFfnError(fn, code)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype) -> int:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a device (cuda) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def moe_ffn_workspace_layout(T: int, H: int, I: int, E: int, top_k: int) -> dict:
+    L = _Layout()
+    _check("moe_ffn_workspace_layout", lib().moe_ffn_workspace_layout(T, H, I, E, top_k, _c.byref(L)))
+    return {f: int(getattr(L, f)) for f in LAYOUT_FIELDS}
+
+
+def moe_ffn_workspace_bytes(T: int, H: int, I: int, E: int, top_k: int) -> int:
+    return int(lib().moe_ffn_workspace_bytes(T, H, I, E, top_k))
+
+
+def alloc_workspace(T: int, H: int, I: int, E: int, top_k: int, device=None) -> torch.Tensor:
+    """Device byte buffer large enough for one forward call of these sizes."""
+    n = moe_ffn_workspace_bytes(T, H, I, E, top_k)
+    if n == 0:
+        raise MoeFfnError("moe_ffn_workspace_bytes", MOE_FFN_ERR_BAD_SHAPE)
+    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+
+
+def moe_route_topk(logits: torch.Tensor, top_k: int, topk_ids: Optional[torch.Tensor] = None,
+                   topk_w: Optional[torch.Tensor] = None, stream=None
+                   ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Top-k router on ``logits`` [T, E] float32 -> (ids [T,k] int32, w [T,k] float32)."""
+    T, E = logits.shape
+    if topk_ids is None:
+        topk_ids = torch.empty(T, top_k, dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty(T, top_k, dtype=torch.float32, device=logits.device)
+    _check("moe_route_topk", lib().moe_route_topk(
+        _dev(logits, "logits", torch.float32), T, E, top_k,
+        _dev(topk_ids, "topk_ids", torch.int32), _dev(topk_w, "topk_w", torch.float32),
+        _stream(stream)))
+    return topk_ids, topk_w
+
+
+def moe_ffn_forward(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor,
+                    W_gate: torch.Tensor, W_up: torch.Tensor, W_down: torch.Tensor,
+                    out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """Routed-expert FFN layer with BF16 weights; returns ``out`` [T, H] bf16."""
+    T, H = x.shape
+    E, I, H2 = W_gate.shape
+    top_k = topk_ids.shape[1]
+    if H2 != H or tuple(W_up.shape) != (E, I, H) or tuple(W_down.shape) != (E, H, I):
+        raise ValueError("weight shapes must be W_gate/W_up [E,I,H], W_down [E,H,I]")
+    if out is None:
+        out = torch.empty_like(x)
+    if workspace is None:
+        workspace = alloc_workspace(T, H, I, E, top_k, x.device)
+    _check("moe_ffn_forward", lib().moe_ffn_forward(
+        _dev(x, "x", torch.bfloat16), _dev(topk_ids, "topk_ids", torch.int32),
+        _dev(topk_w, "topk_w", torch.float32), _dev(W_gate, "W_gate", torch.bfloat16),
+        _dev(W_up, "W_up", torch.bfloat16), _dev(W_down, "W_down", torch.bfloat16),
+        _dev(out, "out", torch.bfloat16), T, H, I, E, top_k,
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream)))
+    return out
+
+
+def moe_ffn_forward_int8(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor,
+                         Q_gate: torch.Tensor, S_gate: torch.Tensor, Q_up: torch.Tensor,
+                         S_up: torch.Tensor, Q_down: torch.Tensor, S_down: torch.Tensor,
+                         out: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Routed-expert FFN layer with INT8 group-quantised weights; returns ``out``."""
+    T, H = x.shape
+    E, I, H2 = Q_gate.shape
+    top_k = topk_ids.shape[1]
+    if H2 != H or tuple(Q_down.shape) != (E, H, I):
+        raise ValueError("weight shapes must be Q_gate/Q_up [E,I,H], Q_down [E,H,I]")
+    if out is None:
+        out = torch.empty_like(x)
+    if workspace is None:
+        workspace = alloc_workspace(T, H, I, E, top_k, x.device)
+    _check("moe_ffn_forward_int8", lib().moe_ffn_forward_int8(
+        _dev(x, "x", torch.bfloat16), _dev(topk_ids, "topk_ids", torch.int32),
+        _dev(topk_w, "topk_w", torch.float32), _dev(Q_gate, "Q_gate", torch.int8),
+        _dev(S_gate, "S_gate", torch.float32), _dev(Q_up, "Q_up", torch.int8),
+        _dev(S_up, "S_up", torch.float32), _dev(Q_down, "Q_down", torch.int8),
+        _dev(S_down, "S_down", torch.float32), _dev(out, "out", torch.bfloat16),
+        T, H, I, E, top_k, _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+        _stream(stream)))
+    return out
+
+
+def moe_ffn_check_status(workspace: torch.Tensor, stream=None) -> Tuple[int, int]:
+    """Synchronise ``stream`` and return (status, dropped slots) of the last call."""
+    n = _i64(0)
+    code = lib().moe_ffn_check_status(_dev(workspace, "workspace", torch.uint8),
+                                      _stream(stream), _c.byref(n))
+    return code, int(n.value)
+
+
+def moe_ffn_set_stage_events(events) -> None:
+    """Benchmark hook: the next forward call of this thread records the given
+    HIP events (``torch.cuda.Event`` objects already recorded once, or raw
+    handles) right after its kernels 0..len-1 (permute, gate/up, down,
+    combine).  An empty list clears the setting."""
+    handles = [e.cuda_event if hasattr(e, "cuda_event") else int(e) for e in events]
+    arr = (_vp * max(1, len(handles)))(*handles)
+    _check("moe_ffn_set_stage_events", lib().moe_ffn_set_stage_events(arr, len(handles)))

@@ -1,0 +1,65 @@
+// Host-side launchers of the MoE FFN kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Pointers into the caller's workspace, carved by the C-ABI layer.
+struct Workspace {
+    int32_t* meta;         // [0] active experts, [1] dropped slots
+    int32_t* counts;       // [E]
+    int32_t* offsets;      // [E+1]
+    int32_t* active;       // [E]
+    int32_t* sorted_slot;  // [T*k]
+    uint16_t* h;           // [T*k][I] bf16, sorted order
+    float* y;              // [T*k][H] f32, slot order
+};
+
+// Optional per-kernel timing events (benchmark hook): ev[i] is recorded
+// right after kernel i of a forward call is enqueued, for i < n.
+struct StageEvents {
+    hipEvent_t ev[4];
+    int n;
+    hipError_t mark(int i, hipStream_t stream) const {
+        return i < n ? hipEventRecord(ev[i], stream) : hipSuccess;
+    }
+};
+
+struct FfnShape {
+    int T, H, I, E, k;
+};
+
+// Weights of one layer: BF16 (q = NULL) or INT8 with per-128 group scales.
+struct FfnWeights {
+    const void* gate;
+    const void* up;
+    const void* down;
+    const float* s_gate;  // INT8 only
+    const float* s_up;
+    const float* s_down;
+};
+
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids,
+                             float* w, hipStream_t stream);
+
+hipError_t launch_permute(const int32_t* ids, const FfnShape& s, const Workspace& ws,
+                          hipStream_t stream);
+
+hipError_t launch_ffn_bf16(const uint16_t* x, const int32_t* ids, const float* w,
+                           const FfnWeights& W, uint16_t* out, const FfnShape& s,
+                           const Workspace& ws, int num_cu, const StageEvents& ev,
+                           hipStream_t stream);
+
+hipError_t launch_ffn_int8(const uint16_t* x, const int32_t* ids, const float* w,
+                           const FfnWeights& W, uint16_t* out, const FfnShape& s,
+                           const Workspace& ws, int num_cu, const StageEvents& ev,
+                           hipStream_t stream);
+
+// Weighted combine shared by both weight formats.
+hipError_t launch_combine(const float* y, const int32_t* ids, const float* w,
+                          uint16_t* out, const FfnShape& s, hipStream_t stream);
+
+}  // namespace moe

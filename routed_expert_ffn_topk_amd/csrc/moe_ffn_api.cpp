@@ -1,0 +1,239 @@
+// C ABI of the routed-expert MoE FFN library: argument checks, workspace
+// layout and kernel launches on the caller's stream.  The declarations and
+// their contracts are in include/moe_ffn.h.
+#include "../../include/moe_ffn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+
+#include "launch.hpp"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxDevices = 64;
+
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool shape_ok(int64_t T, int64_t H, int64_t I, int32_t E, int32_t top_k) {
+    if (T < 0 || H < 1 || I < 1) return false;
+    if (E < 1 || E > MOE_FFN_MAX_EXPERTS) return false;
+    if (top_k < 1 || top_k > E) return false;
+    if (T * (int64_t)top_k >= ((int64_t)1 << 31)) return false;
+    if (H >= ((int64_t)1 << 30) || I >= ((int64_t)1 << 30)) return false;
+    return true;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return pa < pb + nb && pb < pa + na;
+}
+
+std::atomic<int> g_num_cu[kMaxDevices];
+
+// Benchmark hook (moe_ffn_set_stage_events): consumed by the next forward
+// call of this thread.
+thread_local moe::StageEvents t_stage_events = {{nullptr, nullptr, nullptr, nullptr}, 0};
+
+moe::StageEvents take_stage_events() {
+    const moe::StageEvents ev = t_stage_events;
+    t_stage_events.n = 0;
+    return ev;
+}
+
+// Compute units of the current device (cached; the persistent grids are
+// sized from it).
+int num_cu(int* out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_FFN_ERR_HIP;
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int cached = g_num_cu[dev].load(std::memory_order_relaxed);
+        if (cached > 0) {
+            *out = cached;
+            return MOE_FFN_OK;
+        }
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+        return MOE_FFN_ERR_HIP;
+    if (dev >= 0 && dev < kMaxDevices) g_num_cu[dev].store(n, std::memory_order_relaxed);
+    *out = n;
+    return MOE_FFN_OK;
+}
+
+moe::Workspace carve(void* base, const moe_ffn_ws_layout& L) {
+    char* b = static_cast<char*>(base);
+    moe::Workspace ws;
+    ws.meta = reinterpret_cast<int32_t*>(b + L.meta);
+    ws.counts = reinterpret_cast<int32_t*>(b + L.counts);
+    ws.offsets = reinterpret_cast<int32_t*>(b + L.offsets);
+    ws.active = reinterpret_cast<int32_t*>(b + L.active);
+    ws.sorted_slot = reinterpret_cast<int32_t*>(b + L.sorted_slot);
+    ws.h = reinterpret_cast<uint16_t*>(b + L.h);
+    ws.y = reinterpret_cast<float*>(b + L.y);
+    return ws;
+}
+
+// Checks common to both weight formats.
+int check_forward(const void* x, const int32_t* ids, const float* w, const void* out,
+                  int64_t T, int64_t H, int64_t I, int32_t E, int32_t top_k,
+                  const void* workspace, size_t workspace_bytes, int64_t k_multiple,
+                  moe_ffn_ws_layout* L) {
+    if (!shape_ok(T, H, I, E, top_k)) return MOE_FFN_ERR_BAD_SHAPE;
+    if (H % k_multiple != 0 || I % k_multiple != 0) return MOE_FFN_ERR_BAD_SHAPE;
+    if (T == 0) return MOE_FFN_OK;
+    if (!x || !ids || !w || !out) return MOE_FFN_ERR_NULL_ARG;
+    if (!workspace) return MOE_FFN_ERR_WORKSPACE;
+    if (!aligned16(x) || !aligned16(out)) return MOE_FFN_ERR_MISALIGNED;
+    if ((reinterpret_cast<uintptr_t>(ids) & 3u) || (reinterpret_cast<uintptr_t>(w) & 3u))
+        return MOE_FFN_ERR_MISALIGNED;
+    const size_t xb = (size_t)T * (size_t)H * 2;
+    if (overlap(x, xb, out, xb)) return MOE_FFN_ERR_ALIAS;
+    const size_t sb = (size_t)T * (size_t)top_k * 4;
+    if (overlap(ids, sb, out, xb) || overlap(w, sb, out, xb)) return MOE_FFN_ERR_ALIAS;
+    if (moe_ffn_workspace_layout(T, H, I, E, top_k, L) != MOE_FFN_OK) return MOE_FFN_ERR_BAD_SHAPE;
+    if (workspace_bytes < L->total_bytes) return MOE_FFN_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return MOE_FFN_ERR_MISALIGNED;
+    if (overlap(workspace, L->total_bytes, out, xb) || overlap(workspace, L->total_bytes, x, xb))
+        return MOE_FFN_ERR_ALIAS;
+    return MOE_FFN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_ffn_workspace_layout(int64_t T, int64_t H, int64_t I, int32_t E, int32_t top_k,
+                             moe_ffn_ws_layout* layout) {
+    if (!layout) return MOE_FFN_ERR_NULL_ARG;
+    if (!shape_ok(T, H, I, E, top_k)) return MOE_FFN_ERR_BAD_SHAPE;
+    const size_t S = (size_t)T * (size_t)top_k;
+    size_t off = 0;
+    layout->meta = off;
+    off += round_up(8 * sizeof(int32_t));
+    layout->counts = off;
+    off += round_up((size_t)E * sizeof(int32_t));
+    layout->offsets = off;
+    off += round_up(((size_t)E + 1) * sizeof(int32_t));
+    layout->active = off;
+    off += round_up((size_t)E * sizeof(int32_t));
+    layout->sorted_slot = off;
+    off += round_up((S ? S : 1) * sizeof(int32_t));
+    layout->h = off;
+    off += round_up(S * (size_t)I * sizeof(uint16_t));
+    layout->y = off;
+    off += round_up(S * (size_t)H * sizeof(float));
+    layout->total_bytes = off;
+    return MOE_FFN_OK;
+}
+
+size_t moe_ffn_workspace_bytes(int64_t T, int64_t H, int64_t I, int32_t E, int32_t top_k) {
+    moe_ffn_ws_layout L;
+    if (moe_ffn_workspace_layout(T, H, I, E, top_k, &L) != MOE_FFN_OK) return 0;
+    return L.total_bytes;
+}
+
+int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t top_k,
+                   int32_t* topk_ids, float* topk_w, void* stream) {
+    if (T < 0 || E < 1 || E > MOE_FFN_MAX_EXPERTS || top_k < 1 || top_k > E || top_k > 64 ||
+        T * (int64_t)top_k >= ((int64_t)1 << 31))
+        return MOE_FFN_ERR_BAD_SHAPE;
+    if (T == 0) return MOE_FFN_OK;
+    if (!logits || !topk_ids || !topk_w) return MOE_FFN_ERR_NULL_ARG;
+    if ((reinterpret_cast<uintptr_t>(logits) | reinterpret_cast<uintptr_t>(topk_ids) |
+         reinterpret_cast<uintptr_t>(topk_w)) & 3u)
+        return MOE_FFN_ERR_MISALIGNED;
+    const size_t sb = (size_t)T * (size_t)top_k * 4;
+    if (overlap(topk_ids, sb, topk_w, sb) || overlap(logits, (size_t)T * E * 4, topk_ids, sb) ||
+        overlap(logits, (size_t)T * E * 4, topk_w, sb))
+        return MOE_FFN_ERR_ALIAS;
+    const hipError_t err = moe::launch_route_topk(logits, (int)T, E, top_k, topk_ids, topk_w,
+                                                  static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? MOE_FFN_OK : MOE_FFN_ERR_HIP;
+}
+
+int moe_ffn_forward(const void* x, const int32_t* topk_ids, const float* topk_w,
+                    const void* W_gate, const void* W_up, const void* W_down, void* out,
+                    int64_t T, int64_t H, int64_t I, int32_t E, int32_t top_k,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+    moe_ffn_ws_layout L;
+    int rc = check_forward(x, topk_ids, topk_w, out, T, H, I, E, top_k, workspace,
+                           workspace_bytes, 32, &L);
+    if (rc != MOE_FFN_OK || T == 0) return rc;
+    if (!W_gate || !W_up || !W_down) return MOE_FFN_ERR_NULL_ARG;
+    if (!aligned16(W_gate) || !aligned16(W_up) || !aligned16(W_down))
+        return MOE_FFN_ERR_MISALIGNED;
+    int ncu = 0;
+    if ((rc = num_cu(&ncu)) != MOE_FFN_OK) return rc;
+    const moe::FfnShape s{(int)T, (int)H, (int)I, E, top_k};
+    const moe::FfnWeights W{W_gate, W_up, W_down, nullptr, nullptr, nullptr};
+    const hipError_t err = moe::launch_ffn_bf16(
+        static_cast<const uint16_t*>(x), topk_ids, topk_w, W, static_cast<uint16_t*>(out), s,
+        carve(workspace, L), ncu, take_stage_events(), static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? MOE_FFN_OK : MOE_FFN_ERR_HIP;
+}
+
+int moe_ffn_forward_int8(const void* x, const int32_t* topk_ids, const float* topk_w,
+                         const int8_t* Q_gate, const float* S_gate, const int8_t* Q_up,
+                         const float* S_up, const int8_t* Q_down, const float* S_down,
+                         void* out, int64_t T, int64_t H, int64_t I, int32_t E,
+                         int32_t top_k, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+    moe_ffn_ws_layout L;
+    int rc = check_forward(x, topk_ids, topk_w, out, T, H, I, E, top_k, workspace,
+                           workspace_bytes, MOE_FFN_INT8_GROUP, &L);
+    if (rc != MOE_FFN_OK || T == 0) return rc;
+    if (!Q_gate || !S_gate || !Q_up || !S_up || !Q_down || !S_down) return MOE_FFN_ERR_NULL_ARG;
+    if (!aligned16(Q_gate) || !aligned16(Q_up) || !aligned16(Q_down) || !aligned16(S_gate) ||
+        !aligned16(S_up) || !aligned16(S_down))
+        return MOE_FFN_ERR_MISALIGNED;
+    int ncu = 0;
+    if ((rc = num_cu(&ncu)) != MOE_FFN_OK) return rc;
+    const moe::FfnShape s{(int)T, (int)H, (int)I, E, top_k};
+    const moe::FfnWeights W{Q_gate, Q_up, Q_down, S_gate, S_up, S_down};
+    const hipError_t err = moe::launch_ffn_int8(
+        static_cast<const uint16_t*>(x), topk_ids, topk_w, W, static_cast<uint16_t*>(out), s,
+        carve(workspace, L), ncu, take_stage_events(), static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? MOE_FFN_OK : MOE_FFN_ERR_HIP;
+}
+
+int moe_ffn_check_status(const void* workspace, void* stream, int64_t* n_dropped) {
+    if (!workspace) return MOE_FFN_ERR_NULL_ARG;
+    if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess)
+        return MOE_FFN_ERR_HIP;
+    int32_t meta[2] = {0, 0};
+    if (hipMemcpy(meta, workspace, sizeof meta, hipMemcpyDeviceToHost) != hipSuccess)
+        return MOE_FFN_ERR_HIP;
+    if (n_dropped) *n_dropped = meta[1];
+    return meta[1] > 0 ? MOE_FFN_ERR_BAD_IDS : MOE_FFN_OK;
+}
+
+int moe_ffn_set_stage_events(void* const* events, int32_t n_events) {
+    if (n_events < 0 || n_events > 4) return MOE_FFN_ERR_BAD_SHAPE;
+    if (!events) n_events = 0;
+    for (int i = 0; i < n_events; ++i)
+        t_stage_events.ev[i] = static_cast<hipEvent_t>(events[i]);
+    t_stage_events.n = n_events;
+    return MOE_FFN_OK;
+}
+
+const char* moe_ffn_status_string(int status) {
+    switch (status) {
+        case MOE_FFN_OK: return "ok";
+        case MOE_FFN_ERR_NULL_ARG: return "a required pointer is NULL";
+        case MOE_FFN_ERR_BAD_SHAPE: return "sizes outside the supported range";
+        case MOE_FFN_ERR_MISALIGNED: return "a pointer is not suitably aligned";
+        case MOE_FFN_ERR_ALIAS: return "output overlaps an input";
+        case MOE_FFN_ERR_WORKSPACE: return "workspace missing or too small";
+        case MOE_FFN_ERR_HIP: return "HIP runtime error";
+        case MOE_FFN_ERR_BAD_IDS: return "expert ids outside [0, E) were dropped";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,126 @@
+"""C ABI checks that need no GPU: symbols, workspace layout, host-side validation.
+
+Every call here returns before any HIP call (invalid arguments are rejected on
+the host), so fake, never-dereferenced device addresses are safe to pass.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import routed_expert_ffn_topk_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_ffn.h")
+
+A = 0x7f0000000000  # fake, 256-byte aligned device address
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*(moe_[a-z0-9_]+)\s*\(",
+                      text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"moe_ffn_forward", "moe_ffn_forward_int8", "moe_route_topk",
+            "moe_ffn_workspace_bytes", "moe_ffn_workspace_layout", "moe_ffn_check_status",
+            "moe_ffn_status_string"} <= set(names)
+    L = ctypes.CDLL(moe.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for code in range(-7, 1):
+        s = moe.moe_ffn_status_string(code)
+        assert s and s != "unknown status"
+    assert moe.moe_ffn_status_string(-99) == "unknown status"
+
+
+def test_workspace_layout_regions_fit_and_align():
+    T, H, I, E, k = 16, 7168, 2048, 256, 8
+    L = moe.moe_ffn_workspace_layout(T, H, I, E, k)
+    regions = [("meta", 8 * 4), ("counts", E * 4), ("offsets", (E + 1) * 4),
+               ("active", E * 4), ("sorted_slot", T * k * 4), ("h", T * k * I * 2),
+               ("y", T * k * H * 4)]
+    end = 0
+    for name, size in regions:
+        assert L[name] % 256 == 0
+        assert L[name] >= end
+        end = L[name] + size
+    assert L["total_bytes"] >= end and L["total_bytes"] % 256 == 0
+    assert moe.moe_ffn_workspace_bytes(T, H, I, E, k) == L["total_bytes"]
+
+
+@pytest.mark.parametrize("args", [(-1, 64, 64, 8, 2), (4, 0, 64, 8, 2), (4, 64, 64, 0, 1),
+                                  (4, 64, 64, 8, 9), (4, 64, 64, 2000, 2), (4, 64, 64, 8, 0)])
+def test_workspace_bytes_rejects_bad_shapes(args):
+    assert moe.moe_ffn_workspace_bytes(*args) == 0
+    with pytest.raises(moe.MoeFfnError):
+        moe.moe_ffn_workspace_layout(*args)
+
+
+def fwd(**kw):
+    a = dict(x=A, ids=A + 0x100000, w=A + 0x200000, wg=A + 0x1000000, wu=A + 0x2000000,
+             wd=A + 0x3000000, out=A + 0x300000, T=4, H=64, I=96, E=8, k=2,
+             ws=A + 0x4000000, wsb=1 << 30)
+    a.update(kw)
+    return moe.lib().moe_ffn_forward(a["x"], a["ids"], a["w"], a["wg"], a["wu"], a["wd"],
+                                     a["out"], a["T"], a["H"], a["I"], a["E"], a["k"],
+                                     a["ws"], a["wsb"], None)
+
+
+def test_forward_host_validation():
+    assert fwd(T=0) == moe.MOE_FFN_OK                       # empty batch: no-op
+    assert fwd(H=48) == moe.MOE_FFN_ERR_BAD_SHAPE            # H not a multiple of 32
+    assert fwd(I=100) == moe.MOE_FFN_ERR_BAD_SHAPE
+    assert fwd(k=9) == moe.MOE_FFN_ERR_BAD_SHAPE             # top_k > E
+    assert fwd(E=0) == moe.MOE_FFN_ERR_BAD_SHAPE
+    assert fwd(T=-1) == moe.MOE_FFN_ERR_BAD_SHAPE
+    assert fwd(x=None) == moe.MOE_FFN_ERR_NULL_ARG
+    assert fwd(wd=None) == moe.MOE_FFN_ERR_NULL_ARG
+    assert fwd(ws=None) == moe.MOE_FFN_ERR_WORKSPACE
+    assert fwd(wsb=128) == moe.MOE_FFN_ERR_WORKSPACE
+    assert fwd(x=A + 8) == moe.MOE_FFN_ERR_MISALIGNED
+    assert fwd(wg=A + 0x1000000 + 2) == moe.MOE_FFN_ERR_MISALIGNED
+    assert fwd(ws=A + 0x4000000 + 16) == moe.MOE_FFN_ERR_MISALIGNED
+    assert fwd(out=A + 64) == moe.MOE_FFN_ERR_ALIAS          # out overlaps x
+    assert fwd(ws=A + 0x300000 - 256) == moe.MOE_FFN_ERR_ALIAS  # workspace overlaps out
+
+
+def test_forward_int8_requires_group_multiples():
+    L = moe.lib()
+    rc = L.moe_ffn_forward_int8(A, A + 0x100000, A + 0x200000, A + 0x1000000, A + 0x1800000,
+                                A + 0x2000000, A + 0x2800000, A + 0x3000000, A + 0x3800000,
+                                A + 0x300000, 4, 96, 256, 8, 2, A + 0x4000000, 1 << 30, None)
+    assert rc == moe.MOE_FFN_ERR_BAD_SHAPE
+    rc = L.moe_ffn_forward_int8(A, A + 0x100000, A + 0x200000, A + 0x1000000, None,
+                                A + 0x2000000, A + 0x2800000, A + 0x3000000, A + 0x3800000,
+                                A + 0x300000, 4, 128, 256, 8, 2, A + 0x4000000, 1 << 30, None)
+    assert rc == moe.MOE_FFN_ERR_NULL_ARG
+
+
+def test_route_host_validation():
+    L = moe.lib()
+    assert L.moe_route_topk(A, 0, 8, 2, A + 0x1000, A + 0x2000, None) == moe.MOE_FFN_OK
+    assert L.moe_route_topk(A, 4, 8, 9, A + 0x1000, A + 0x2000, None) == moe.MOE_FFN_ERR_BAD_SHAPE
+    assert L.moe_route_topk(A, 4, 2048, 2, A + 0x10000, A + 0x20000, None) == moe.MOE_FFN_ERR_BAD_SHAPE
+    assert L.moe_route_topk(None, 4, 8, 2, A + 0x1000, A + 0x2000, None) == moe.MOE_FFN_ERR_NULL_ARG
+    assert L.moe_route_topk(A, 4, 8, 2, A + 0x1000, A + 0x1010, None) == moe.MOE_FFN_ERR_ALIAS
+    assert L.moe_route_topk(A, 4, 8, 2, A + 0x1001, A + 0x2000, None) == moe.MOE_FFN_ERR_MISALIGNED
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    with pytest.raises((TypeError, moe.MoeFfnError)):
+        moe.moe_ffn_forward(x, torch.zeros(4, 2, dtype=torch.int32), torch.zeros(4, 2),
+                            torch.zeros(8, 96, 64, dtype=torch.bfloat16),
+                            torch.zeros(8, 96, 64, dtype=torch.bfloat16),
+                            torch.zeros(8, 64, 96, dtype=torch.bfloat16),
+                            workspace=torch.zeros(16, dtype=torch.uint8))

@@ -1,0 +1,160 @@
+"""GPU parity of the BF16 routed-expert FFN layer against the oracle.
+
+Small shapes that the oracle finishes in seconds and that still span several
+row tiles, ragged K splits, more than 16 tokens per expert (several token
+tiles), dropped and duplicate ids, and the degenerate cases (one expert,
+one token, an empty batch, zero weights).
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import routed_expert_ffn_topk_amd as moe
+import workloads
+from moe_cases import (TOL_BF16, assert_close, assert_close_scaled, need_gpu, random_case,
+                       read_workspace, say, workload_case)
+
+sys.path.insert(0, os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden"))
+
+pytestmark = pytest.mark.gpu
+
+
+def run(case, ws=None):
+    x, ids, w = case.device_inputs()
+    if ws is None:
+        ws = moe.alloc_workspace(case.T, case.H, case.I, case.E, case.k)
+    out = moe.moe_ffn_forward(x, ids, w, case.Wg, case.Wu, case.Wd, workspace=ws)
+    torch.cuda.synchronize()
+    return workloads.bf16_bits(out), ws
+
+
+def check_h(case, ws, ref_h):
+    """The BF16 intermediate h of every slot: almost all bit-equal to the
+    oracle's, and every element within 1% of max(|ref|, rms(h)) (the FP32
+    summation order of g and u differs, which can move h by one rounding
+    step, or by more when g or u comes out of cancellation)."""
+    r = read_workspace(ws, moe.moe_ffn_workspace_layout(case.T, case.H, case.I, case.E, case.k),
+                       case.T, case.H, case.I, case.E, case.k)
+    n = r["offsets"][case.E]
+    got = np.zeros_like(ref_h)
+    got[r["sorted_slot"][:n]] = r["h"][:n]
+    assert (got == ref_h).mean() >= 0.99
+    assert_close_scaled(got, ref_h, 1e-2, what="h")
+
+
+def test_tiny_workload_matches_oracle_and_golden():
+    need_gpu()
+    import make_golden
+    wl, case = workload_case("tiny", device="cpu")
+    case = type(case)(case.x_bits, case.ids, case.w, case.Wg.cuda(), case.Wu.cuda(),
+                      case.Wd.cuda(), wl.E)
+    say("tiny workload")
+    out, ws = run(case)
+    ref = case.oracle(aux=True)
+    _, _, golden = make_golden.load()
+    assert np.array_equal(ref["out"], golden)
+    assert_close(out, ref["out"], TOL_BF16)
+    # tiny outputs are ~0.02, far below the absolute floor of the bar: also
+    # hold them to 1% of the output scale, and to near bit-equality
+    assert_close_scaled(out, ref["out"], 1e-2)
+    assert (out == ref["out"]).mean() >= 0.95
+    check_h(case, ws, ref["h"])
+
+
+@pytest.mark.parametrize("T,H,I,E,k", [
+    (16, 256, 512, 8, 2),      # several row tiles
+    (5, 96, 160, 4, 2),        # K split 3 / 5 steps: ragged across the four waves
+    (1, 64, 32, 8, 2),         # one token, single row tile
+    (7, 1024, 96, 16, 4),      # long K, unroll remainder
+    (13, 320, 288, 6, 3),
+    (16, 512, 256, 256, 8),    # many experts, most with one token
+    (1, 128, 128, 1, 1),       # single expert
+    (33, 128, 96, 2, 1),       # ~16 tokens per expert, ragged token tile
+])
+def test_bf16_layer_matches_oracle(T, H, I, E, k):
+    need_gpu()
+    case = random_case(T * 100 + H + I + E + k, T, H, I, E, k, std=0.08)
+    say(f"bf16 T={T} H={H} I={I} E={E} k={k}")
+    out, ws = run(case)
+    ref = case.oracle(aux=True)
+    assert_close(out, ref["out"], TOL_BF16)
+    assert_close_scaled(out, ref["out"], 1e-2)
+    check_h(case, ws, ref["h"])
+
+
+@pytest.mark.parametrize("T,E", [(40, 2), (70, 1), (100, 3)])
+def test_bf16_more_than_16_tokens_per_expert(T, E):
+    need_gpu()
+    case = random_case(T + E, T, 128, 96, E, 1, std=0.08)
+    say(f"bf16 >16 tokens/expert T={T} E={E}")
+    out, ws = run(case)
+    ref = case.oracle(aux=True)
+    assert_close(out, ref["out"], TOL_BF16)
+    assert_close_scaled(out, ref["out"], 1e-2)
+    check_h(case, ws, ref["h"])
+
+
+def test_bf16_duplicate_and_dropped_ids():
+    need_gpu()
+    T, E, k = 12, 5, 3
+    rng = np.random.default_rng(5)
+    ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    ids[0] = [2, 2, 2]
+    ids[1] = [-1, 3, 99]
+    ids[2] = [E, E, E]          # every slot dropped: out row must be zero
+    case = random_case(6, T, 96, 64, E, k, std=0.1, ids=ids)
+    say("bf16 duplicate and dropped ids")
+    out, ws = run(case)
+    code, dropped = moe.moe_ffn_check_status(ws)
+    assert code == moe.MOE_FFN_ERR_BAD_IDS and dropped == 5
+    ref = case.oracle()
+    assert_close(out, ref, TOL_BF16)
+    assert np.all(workloads.bits_to_bf16(out[2]).float().numpy() == 0)
+
+
+def test_bf16_empty_batch_is_noop():
+    need_gpu()
+    x = torch.zeros(0, 64, dtype=torch.bfloat16, device="cuda")
+    W = torch.zeros(4, 32, 64, dtype=torch.bfloat16, device="cuda")
+    Wd = torch.zeros(4, 64, 32, dtype=torch.bfloat16, device="cuda")
+    out = moe.moe_ffn_forward(x, torch.zeros(0, 2, dtype=torch.int32, device="cuda"),
+                              torch.zeros(0, 2, device="cuda"), W, W, Wd,
+                              workspace=moe.alloc_workspace(0, 64, 32, 4, 2))
+    assert out.shape == (0, 64)
+
+
+def test_bf16_zero_gate_gives_zero_output():
+    need_gpu()
+    case = random_case(8, 9, 128, 64, 4, 2)
+    case.Wg.zero_()
+    out, _ = run(case)
+    assert np.all(workloads.bits_to_bf16(out).float().numpy() == 0)
+
+
+def test_bf16_deterministic_and_overwrites_out():
+    need_gpu()
+    case = random_case(9, 16, 256, 192, 8, 2)
+    x, ids, w = case.device_inputs()
+    ws = moe.alloc_workspace(case.T, case.H, case.I, case.E, case.k)
+    out1 = torch.full_like(x, 7.0)
+    moe.moe_ffn_forward(x, ids, w, case.Wg, case.Wu, case.Wd, out=out1, workspace=ws)
+    ws.fill_(0xAB)   # stale workspace contents must not matter
+    out2 = torch.full_like(x, -3.0)
+    moe.moe_ffn_forward(x, ids, w, case.Wg, case.Wu, case.Wd, out=out2, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+
+
+def test_bf16_token_permutation_invariance():
+    need_gpu()
+    case = random_case(10, 16, 128, 128, 8, 2)
+    out, _ = run(case)
+    perm = np.random.default_rng(0).permutation(16)
+    case2 = type(case)(case.x_bits[perm], case.ids[perm], case.w[perm], case.Wg, case.Wu,
+                       case.Wd, case.E)
+    out2, _ = run(case2)
+    # the gather order changes, the per-element results do not
+    assert np.array_equal(out[perm], out2)
