@@ -146,6 +146,7 @@ def main():
     # each call (stage 0 permute, 1 gate/up, 2 down, 3 combine)
     names = ("permute", "gateup", "down", "combine")
     dur = {n: [] for n in names}
+    dur_m = {str(b["wl"].T // 4): {n: [] for n in names} for b in batches}
     gu_bytes = []
     for _ in range(max(3, args.steps // 5)):
         for b in batches:
@@ -157,8 +158,12 @@ def main():
             layer(b)
             torch.cuda.synchronize()
             for i, n in enumerate(names):
-                dur[n].append(ev[i].elapsed_time(ev[i + 1]) * 1e3)
+                d = ev[i].elapsed_time(ev[i + 1]) * 1e3
+                dur[n].append(d)
+                dur_m[str(b["wl"].T // 4)][n].append(d)
             gu_bytes.append(gateup_bytes(b["wl"]))
+    for m, d in dur_m.items():
+        per_m[m]["stage_us"] = {n: round(statistics.mean(v), 1) for n, v in d.items()}
     gu_us = statistics.mean(dur["gateup"])
     achieved = statistics.mean(gu_bytes) / (gu_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "kernel": "gateup_bf16", "achieved": round(achieved, 1),

@@ -20,6 +20,15 @@ __device__ __forceinline__ u32x4 load_stream16(const void* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+// Weight load: streaming (non-temporal) or ordinary, chosen per kernel shape.
+template <bool kNonTemporal>
+__device__ __forceinline__ u32x4 load_weight16(const void* p) {
+    if constexpr (kNonTemporal)
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    else
+        return *reinterpret_cast<const u32x4*>(p);
+}
+
 // Ordinary cached 16-byte load (token activations, h rows: reused by many
 // workgroups).
 __device__ __forceinline__ u32x4 load_cached16(const void* p) {
@@ -46,5 +55,32 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 __device__ __forceinline__ float silu(float g) {
     return g / (1.0f + expf(-g));
 }
+
+// Number of XCDs (accelerator dies with private L2) on gfx950; workgroups of
+// a launch are handed to them round-robin by workgroup id.
+constexpr int kXcds = 8;
+
+// Task iteration of a persistent workgroup.  With kXcdSlices each XCD owns a
+// contiguous slice of the task list (tasks are ordered expert-major, so a
+// slice covers few experts and their token rows stay in that XCD's L2); the
+// workgroups of one XCD stride over its slice.  Requires gridDim.x to be a
+// multiple of kXcds.  Otherwise workgroups stride over the whole list.
+template <bool kXcdSlices>
+struct TaskRange {
+    int begin, end, stride;
+    __device__ __forceinline__ explicit TaskRange(int ntask) {
+        if constexpr (kXcdSlices) {
+            const int xcd = blockIdx.x % kXcds;
+            const int per = gridDim.x / kXcds;
+            begin = (int)(((long long)xcd * ntask) / kXcds) + (int)(blockIdx.x / kXcds);
+            end = (int)(((long long)(xcd + 1) * ntask) / kXcds);
+            stride = per;
+        } else {
+            begin = blockIdx.x;
+            end = ntask;
+            stride = gridDim.x;
+        }
+    }
+};
 
 }  // namespace moe
