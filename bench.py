@@ -15,8 +15,10 @@ kernel (gate/up) from per-kernel HIP events, and the CPU oracle timed on a
 bounded sample of the same workload.
 """
 import argparse
+import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -43,6 +45,28 @@ def gateup_bytes(wl) -> int:
     expert plus the token rows (h is scratch and not credited)."""
     active = min(wl.E, wl.T * wl.k)
     return active * 2 * wl.I * wl.H * 2 + wl.T * wl.H * 2
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "expert_gemm_mixtral8x7b_m1-16_hbm_traffic.md")
+KERNEL_SOURCES = ("routed_expert_ffn_topk_amd/csrc/ffn_bf16.hip",
+                  "routed_expert_ffn_topk_amd/csrc/common.hpp")
+
+
+def recorded_traffic():
+    """HBM bytes per gate/up launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE record (scaled by a plain copy of known size), or None when the
+    kernel sources have changed since the counters were taken."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+        digests = "".join(hashlib.sha256(open(os.path.join(ROOT, f), "rb").read()).hexdigest()
+                          for f in KERNEL_SOURCES)
+    except OSError:
+        return None
+    rec = dict(re.findall(r"^(kernel_source_sha256_16|gateup_traffic_bytes_per_launch): (\S+)$",
+                          text, re.M))
+    if rec.get("kernel_source_sha256_16") != hashlib.sha256(digests.encode()).hexdigest()[:16]:
+        return None
+    return int(rec["gateup_traffic_bytes_per_launch"])
 
 
 def cpu_baseline(wl, Wg, Wu, Wd, logits_cpu, x_cpu, reps=3):
@@ -75,7 +99,20 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB, 5 times "
+                         "(calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE), then exit")
     args = ap.parse_args()
+    if args.copy_probe:
+        import torch
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "copies": 5}), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: this build runs the MoE FFN "
               "layer on one GPU only (see the sharding notes in DESIGN.md)", file=sys.stderr)
@@ -166,9 +203,10 @@ def main():
         per_m[m]["stage_us"] = {n: round(statistics.mean(v), 1) for n, v in d.items()}
     gu_us = statistics.mean(dur["gateup"])
     achieved = statistics.mean(gu_bytes) / (gu_us * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "kernel": "gateup_bf16", "achieved": round(achieved, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": None, "avg_us": round(gu_us, 2),
+    roofline = {"bound": "hbm", "kernel": "expert_gemm_kernel (gate/up)",
+                "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
+                "algorithmic_bytes": int(statistics.mean(gu_bytes)), "avg_us": round(gu_us, 2),
                 "stage_us": {n: round(statistics.mean(v), 2) for n, v in dur.items()}}
 
     result = {
