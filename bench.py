@@ -48,7 +48,7 @@ def gateup_bytes(wl) -> int:
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "expert_gemm_mixtral8x7b_m1-16_hbm_traffic.md")
-KERNEL_SOURCES = ("routed_expert_ffn_topk_amd/csrc/ffn_bf16.hip",
+KERNEL_SOURCES = ("routed_expert_ffn_topk_amd/csrc/expert_gemm.hip",
                   "routed_expert_ffn_topk_amd/csrc/common.hpp")
 
 

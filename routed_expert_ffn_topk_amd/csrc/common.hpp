@@ -13,25 +13,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-// 16-byte global load that bypasses cache allocation: expert weights are read
-// exactly once per call, so they should not evict the small, reused operands
-// (token rows, the h intermediate) from L2.
-__device__ __forceinline__ u32x4 load_stream16(const void* p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-}
-
-// Weight load: streaming (non-temporal) or ordinary, chosen per kernel shape.
-template <bool kNonTemporal>
-__device__ __forceinline__ u32x4 load_weight16(const void* p) {
-    if constexpr (kNonTemporal)
-        return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-    else
-        return *reinterpret_cast<const u32x4*>(p);
-}
-
-// Ordinary cached 16-byte load (token activations, h rows: reused by many
-// workgroups).
-__device__ __forceinline__ u32x4 load_cached16(const void* p) {
+// Ordinary 16-byte global load.  Weights are read once per call, but on the
+// row-tile pattern of the kernels cached loads stream HBM faster than
+// non-temporal ones (measured on MI355X), and every weight byte is still
+// fetched from HBM exactly once.
+__device__ __forceinline__ u32x4 load16(const void* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
 
@@ -40,8 +26,9 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
 }
 
 // D(16x16, f32) += A(16x32, bf16) * B(32x16, bf16).  Lane l supplies row
-// (l % 16) of A and column (l % 16) of B, each as 8 consecutive K values of
-// K-group (l / 16); it receives D[4 * (l / 16) + q][l % 16], q = 0..3.
+// (l % 16) of A and column (l % 16) of B, each as 8 K values of K-group
+// (l / 16) (any K order works as long as A and B use the same one); it
+// receives D[4 * (l / 16) + q][l % 16], q = 0..3.
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -59,28 +46,5 @@ __device__ __forceinline__ float silu(float g) {
 // Number of XCDs (accelerator dies with private L2) on gfx950; workgroups of
 // a launch are handed to them round-robin by workgroup id.
 constexpr int kXcds = 8;
-
-// Task iteration of a persistent workgroup.  With kXcdSlices each XCD owns a
-// contiguous slice of the task list (tasks are ordered expert-major, so a
-// slice covers few experts and their token rows stay in that XCD's L2); the
-// workgroups of one XCD stride over its slice.  Requires gridDim.x to be a
-// multiple of kXcds.  Otherwise workgroups stride over the whole list.
-template <bool kXcdSlices>
-struct TaskRange {
-    int begin, end, stride;
-    __device__ __forceinline__ explicit TaskRange(int ntask) {
-        if constexpr (kXcdSlices) {
-            const int xcd = blockIdx.x % kXcds;
-            const int per = gridDim.x / kXcds;
-            begin = (int)(((long long)xcd * ntask) / kXcds) + (int)(blockIdx.x / kXcds);
-            end = (int)(((long long)(xcd + 1) * ntask) / kXcds);
-            stride = per;
-        } else {
-            begin = blockIdx.x;
-            end = ntask;
-            stride = gridDim.x;
-        }
-    }
-};
 
 }  // namespace moe

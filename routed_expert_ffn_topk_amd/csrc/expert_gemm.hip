@@ -1,0 +1,532 @@
+// Routed-expert FFN kernels: the grouped expert product (gate/up with the
+// SiLU*up epilogue, and down), for BF16 and INT8 weights, and the weighted
+// combine.
+//
+// HiNa-MoE §4.1 (FFN equation, Fig. 5): each expert multiplies the small
+// matrix of its gathered tokens by W_gate and W_up, applies SiLU to the gate
+// branch, multiplies the branches elementwise and multiplies by W_down.
+// §4.1 "transform I, not W": the weights are read in their plain row-major
+// layout, which is already the MFMA A-operand layout (one row per lane,
+// consecutive K values per lane); only the small gathered token matrix is
+// rearranged, into the B-operand fragment order, and results are written back
+// row-major.  §4.2.1: BF16 operands, FP32 accumulation; the matrix unit is
+// used for every token count (16-column tiles padded with a real token row),
+// never a vector fallback.  §4.2.2: weights are streamed once, with no reuse.
+// §8.1 / Fig. 11: symmetric group-wise INT8 weights, dequantised in registers.
+//
+// One kernel skeleton serves both projections and both weight formats.  Work
+// unit: a row block (16 output rows of one active expert, all its tokens).
+// The four waves of a workgroup form R row blocks x S K-parts (R * S = 4; S
+// chosen by the host from the problem size so that there are enough waves to
+// keep HBM busy).  Workgroups are persistent: each XCD owns a contiguous slice
+// of the expert-major row-block list, and each workgroup a balanced contiguous
+// range of that slice, walked in rounds of R row blocks of one expert.
+//
+// B operand (the gathered tokens, i.e. the pages' matrix I): the workgroup
+// stages K-slabs of the 16-token tile in LDS, in MFMA fragment order (one
+// 1 KB block per 32-wide K step, direct global->LDS loads, double-buffered),
+// which all its waves share.  Weights stream through registers in batches
+// with the next batch always in flight, also across slab barriers.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;
+constexpr int kSlabBlocks = 16;      // 32-wide K steps per LDS slab buffer (16 KB)
+constexpr int kMinWavesPerCU = 8;    // busy waves per CU that keep HBM streaming
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// Wait until at most N vector-memory loads of this wave are outstanding
+// (loads complete in issue order), leaving LDS and export counters alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// One grouped expert product: for every active expert e and gathered row p
+// of e, out[p][n] = sum_k W[e][n][k] * B[p][k].
+struct ExpertGemm {
+    const uint16_t* b_src;    // B rows: x (gate/up) or the gathered h rows (down)
+    const void* w0;           // W_gate or W_down, [E][N][K] (BF16 or INT8)
+    const void* w1;           // W_up (gate/up only)
+    const float* s0;          // INT8 only: group scales of w0, [E][N][K/128]
+    const float* s1;          // INT8 only: group scales of w1
+    const int32_t* meta;      // [0] = active experts
+    const int32_t* offsets;
+    const int32_t* active;
+    const int32_t* sorted_slot;
+    uint16_t* h;              // gate/up output, row p at p * N
+    float* y;                 // down output, slot s at s * N
+    int b_pitch;              // elements between B rows
+    int N, K;                 // rows per expert matrix, reduction length
+    int top_k;                // gate/up: B row of gathered row p is token sorted_slot[p] / top_k
+};
+
+// ---------------------------------------------------------------------------
+// Weight formats.  A "unit" is the K range one batch entry covers:
+//   BF16: one 32-wide K step = one MFMA per matrix, one LDS block;
+//   INT8: one 128-wide scale group = four MFMAs per matrix, four LDS blocks.
+// ---------------------------------------------------------------------------
+
+struct Bf16Weights {
+    static constexpr int kBlocks = 1;
+    template <int NMAT, int U>
+    struct Batch {
+        u32x4 w[U][NMAT];
+    };
+    // vector-memory load instructions issued by load<NMAT, U>
+    template <int NMAT, int U>
+    static constexpr int loads() { return U * NMAT; }
+    // K offset (elements) of LDS block `sub` of a unit, for K group kg
+    __device__ static int block_offset(int sub, int kg) { return sub * 32 + kg * 8; }
+    __device__ static const void* row_ptr(const void* base, size_t row, int K, int kg) {
+        return static_cast<const uint16_t*>(base) + row * K + kg * 8;
+    }
+    template <int NMAT, int U>
+    __device__ static void load(Batch<NMAT, U>& d, const void* const* a, const float* const*,
+                                int, int u) {
+#pragma unroll
+        for (int i = 0; i < U; ++i)
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m)
+                d.w[i][m] = load16(static_cast<const uint16_t*>(a[m]) + (u + i) * 32);
+    }
+    template <int NMAT, int U>
+    __device__ static void mma(const Batch<NMAT, U>& d, const u32x4 (*blk)[kWave], f32x4* acc) {
+        const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            const u32x4 bq = blk[i][lane];
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m)
+                acc[m] = mfma16x16x32(as_bf16x8(d.w[i][m]), as_bf16x8(bq), acc[m]);
+        }
+    }
+};
+
+// INT8 -> BF16 is exact (|q| <= 127 has at most 7 significant bits).
+__device__ __forceinline__ bf16x8 i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+    bf16x8 r;
+    r[0] = static_cast<__bf16>((float)((int32_t)(lo << 24) >> 24));
+    r[1] = static_cast<__bf16>((float)((int32_t)(lo << 16) >> 24));
+    r[2] = static_cast<__bf16>((float)((int32_t)(lo << 8) >> 24));
+    r[3] = static_cast<__bf16>((float)((int32_t)lo >> 24));
+    r[4] = static_cast<__bf16>((float)((int32_t)(hi << 24) >> 24));
+    r[5] = static_cast<__bf16>((float)((int32_t)(hi << 16) >> 24));
+    r[6] = static_cast<__bf16>((float)((int32_t)(hi << 8) >> 24));
+    r[7] = static_cast<__bf16>((float)((int32_t)hi >> 24));
+    return r;
+}
+
+// INT8 with one FP32 scale per 128 consecutive K of a row.  Each lane loads 16
+// consecutive int8 of its row per 64-wide half group: bytes 0-7 feed one MFMA
+// and bytes 8-15 the next, so within a group LDS block 2c+h holds, for K group
+// kg, the token values at K = 64c + 16kg + 8h .. +8 (the same K the weights
+// use).  The group's FP32 partial tile is scaled by the per-row scale of each
+// of the lane's four output rows (4kg + j) and added to the accumulator:
+//   dot(row, v) = sum_g s[row][g] * (sum_{c in g} v_c * q[row][c]).
+struct Int8Weights {
+    static constexpr int kBlocks = 4;
+    template <int NMAT, int U>
+    struct Batch {
+        u32x4 w[U][NMAT][2];
+        float s[U][NMAT][4];
+    };
+    // two 16-byte weight loads and four scale loads per unit and matrix
+    template <int NMAT, int U>
+    static constexpr int loads() { return U * NMAT * 6; }
+    __device__ static int block_offset(int sub, int kg) {
+        return (sub >> 1) * 64 + kg * 16 + (sub & 1) * 8;
+    }
+    __device__ static const void* row_ptr(const void* base, size_t row, int K, int kg) {
+        return static_cast<const int8_t*>(base) + row * K + kg * 16;
+    }
+    // a[m]: weight row at K offset 16*kg; sc[m]: scale row of output row
+    // 4*kg of the row block; ng: groups per row
+    template <int NMAT, int U>
+    __device__ static void load(Batch<NMAT, U>& d, const void* const* a, const float* const* sc,
+                                int ng, int u) {
+#pragma unroll
+        for (int i = 0; i < U; ++i)
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m) {
+                const int8_t* p = static_cast<const int8_t*>(a[m]) + (size_t)(u + i) * 128;
+                d.w[i][m][0] = load16(p);
+                d.w[i][m][1] = load16(p + 64);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) d.s[i][m][j] = sc[m][(size_t)j * ng + u + i];
+            }
+    }
+    template <int NMAT, int U>
+    __device__ static void mma(const Batch<NMAT, U>& d, const u32x4 (*blk)[kWave], f32x4* acc) {
+        const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m) {
+                f32x4 part = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const u32x4 w = d.w[i][m][c];
+                    part = mfma16x16x32(i8x8_to_bf16x8(w.x, w.y), as_bf16x8(blk[4 * i + 2 * c][lane]),
+                                        part);
+                    part = mfma16x16x32(i8x8_to_bf16x8(w.z, w.w),
+                                        as_bf16x8(blk[4 * i + 2 * c + 1][lane]), part);
+                }
+                acc[m].x += d.s[i][m][0] * part.x;
+                acc[m].y += d.s[i][m][1] * part.y;
+                acc[m].z += d.s[i][m][2] * part.z;
+                acc[m].w += d.s[i][m][3] * part.w;
+            }
+        }
+    }
+};
+
+// Tuning per weight format and projection, measured on MI355X over the
+// Mixtral-8x7B, DeepSeek-V3, Qwen3-235B and Mixtral-8x22B expert shapes at
+// 1-16 tokens per expert: batch length U (units) and resident workgroups per
+// CU (LDS: 32 KB per workgroup).
+template <class Fmt, int NMAT>
+struct GemmTuning;
+template <>
+struct GemmTuning<Bf16Weights, 2> {   // gate/up: two matrices per K step
+    static constexpr int kBlocksPerCU = 4;
+    static constexpr int kBatch = 2;
+};
+template <>
+struct GemmTuning<Bf16Weights, 1> {   // down
+    static constexpr int kBlocksPerCU = 3;
+    static constexpr int kBatch = 8;
+};
+template <>
+struct GemmTuning<Int8Weights, 2> {
+    static constexpr int kBlocksPerCU = 3;
+    static constexpr int kBatch = 1;
+};
+template <>
+struct GemmTuning<Int8Weights, 1> {
+    static constexpr int kBlocksPerCU = 3;
+    static constexpr int kBatch = 2;
+};
+
+// NMAT = 2: gate/up, epilogue h[p][row] = bf16(silu(g) * u).
+// NMAT = 1: down, epilogue y[slot][row] = acc (FP32, slot = sorted_slot[p]).
+// S: K-parts per row block; U: units per weight batch (divides the units of
+// one K part in a slab).
+template <class Fmt, int NMAT, int S, int U>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(GemmTuning<Fmt, NMAT>::kBlocksPerCU)))
+void expert_gemm_kernel(const ExpertGemm g) {
+    constexpr int R = kWaves / S;              // row blocks per round
+    constexpr int SP = kSlabBlocks / S;        // LDS blocks of each K part per slab
+    constexpr int SPU = SP / Fmt::kBlocks;     // units of each K part per slab
+    constexpr int NB = SPU / U;                // full batches per full slab
+    static_assert(SPU >= 1 && SPU % U == 0, "batch must divide the slab part");
+    using Batch = typename Fmt::template Batch<NMAT, U>;
+    // K-slab buffers; after the slab loop the first buffer doubles as the
+    // K-part reduction area (3 x NMAT x 1 KB <= 16 KB).
+    __shared__ u32x4 xs[2][kSlabBlocks][kWave];
+    f32x4* red = reinterpret_cast<f32x4*>(&xs[0][0][0]);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int col = lane & 15;  // A row, B column and D column of this lane
+    const int kg = lane >> 4;   // K group of the operands, row quad of D
+    const int r = wave % R;     // row block of this wave within a round
+    const int kp = wave / R;    // K part of this wave
+    const int nrb = g.N / 16;
+    const int W = g.meta[0] * nrb;
+    const int nunits = g.K / (32 * Fmt::kBlocks);
+    const int kpu = (nunits + S - 1) / S;      // units per K part
+    const int u0 = min(nunits, kp * kpu);
+    const int u1 = min(nunits, u0 + kpu);
+    const int nslab = (kpu + SPU - 1) / SPU;
+
+    // this workgroup's row blocks: a balanced share of its XCD's slice
+    const int xcd = blockIdx.x % kXcds;
+    const int per = gridDim.x / kXcds;
+    const int li = blockIdx.x / kXcds;
+    const int sb = (int)((long long)xcd * W / kXcds);
+    const int n = (int)((long long)(xcd + 1) * W / kXcds) - sb;
+    const int rbeg = sb + (int)((long long)li * n / per);
+    const int rend = sb + (int)((long long)(li + 1) * n / per);
+
+    for (int r0 = rbeg; r0 < rend;) {
+        const int a = r0 / nrb;
+        const int r1 = min(min(r0 + R, rend), (a + 1) * nrb);
+        const int e = g.active[a];
+        const int beg = g.offsets[e];
+        const int m = g.offsets[e + 1] - beg;
+        const int my = r0 + r;
+        const bool has = my < r1;
+        const int row0 = (has ? my - a * nrb : 0) * 16;
+        const size_t arow = (size_t)e * g.N + row0 + col;   // this lane's weight row
+        const void* wp[2] = {Fmt::row_ptr(g.w0, arow, g.K, kg),
+                             Fmt::row_ptr(NMAT == 2 ? g.w1 : g.w0, arow, g.K, kg)};
+        const size_t srow = ((size_t)e * g.N + row0 + 4 * kg) * nunits;  // INT8 scale rows
+        const float* sp[2] = {g.s0 ? g.s0 + srow : nullptr,
+                              NMAT == 2 && g.s1 ? g.s1 + srow : nullptr};
+        const int nfull = has ? (u1 - u0) / U : 0;   // full batches of this wave
+        const int tail_u = u0 + nfull * U;           // tail units [tail_u, u1)
+        for (int c0 = 0; c0 < m; c0 += 16) {
+            const bool valid = c0 + col < m;
+            // padding columns (beyond the expert's tokens) repeat a real token
+            // row: an MFMA output column depends only on its own B column, and
+            // padding columns are never stored
+            const int q = beg + (valid ? c0 + col : 0);
+            const int brow = NMAT == 2 ? g.sorted_slot[q] / g.top_k : q;
+            const uint16_t* bp = g.b_src + (size_t)brow * g.b_pitch;
+            f32x4 acc[NMAT];
+#pragma unroll
+            for (int mm = 0; mm < NMAT; ++mm) acc[mm] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+            // slab j holds, for each K part pp, its units
+            // [start(pp) + j*SPU, +SPU) at blocks [pp*SP, pp*SP + SP)
+            auto stage = [&](int j, int bsel) {
+                for (int blk = wave; blk < kSlabBlocks; blk += kWaves) {
+                    const int pp = blk / SP;
+                    const int bb = blk - pp * SP;
+                    const int p0 = min(nunits, pp * kpu);
+                    const int p1 = min(nunits, p0 + kpu);
+                    const int u = p0 + j * SPU + bb / Fmt::kBlocks;
+                    if (u < p1) {
+                        const int off = u * 32 * Fmt::kBlocks +
+                                        Fmt::block_offset(bb % Fmt::kBlocks, kg);
+                        __builtin_amdgcn_global_load_lds((const void*)(bp + off),
+                                                         (lds_void_ptr)&xs[bsel][blk][0], 16, 0, 0);
+                    }
+                }
+            };
+            stage(0, 0);
+            // weight batches ping-pong between two register sets: batch bi
+            // lives in A when bi is even, in B when odd; the next batch is
+            // always requested before the current one is multiplied
+            constexpr int kLoads = Fmt::template loads<NMAT, U>();
+            Batch A, B;
+            if (nfull > 0) Fmt::template load<NMAT, U>(A, wp, sp, nunits, u0);
+            int bi = 0;
+            for (int j = 0; j < nslab; ++j) {
+                // this wave's staging loads are done (only the batch
+                // prefetched for this slab may still be in flight)
+                if (bi < nfull)
+                    wait_vmcnt<(kLoads < 63 ? kLoads : 63)>();
+                else
+                    wait_vmcnt<0>();
+                __syncthreads();
+                if (j + 1 < nslab) stage(j + 1, (j + 1) & 1);
+                const int slab_u0 = u0 + j * SPU;
+                const u32x4(*buf)[kWave] = &xs[j & 1][kp * SP];
+                const int bend = min(nfull, (j + 1) * NB);
+                for (; bi < bend; ++bi) {
+                    const u32x4(*bb)[kWave] = buf + (u0 + bi * U - slab_u0) * Fmt::kBlocks;
+                    if ((bi & 1) == 0) {
+                        if (bi + 1 < nfull)
+                            Fmt::template load<NMAT, U>(B, wp, sp, nunits, u0 + (bi + 1) * U);
+                        Fmt::template mma<NMAT, U>(A, bb, acc);
+                    } else {
+                        if (bi + 1 < nfull)
+                            Fmt::template load<NMAT, U>(A, wp, sp, nunits, u0 + (bi + 1) * U);
+                        Fmt::template mma<NMAT, U>(B, bb, acc);
+                    }
+                }
+                if (has && tail_u < u1 && tail_u >= slab_u0 && tail_u < slab_u0 + SPU)
+                    for (int u = tail_u; u < u1; ++u) {
+                        typename Fmt::template Batch<NMAT, 1> t;
+                        Fmt::template load<NMAT, 1>(t, wp, sp, nunits, u);
+                        Fmt::template mma<NMAT, 1>(t, buf + (u - slab_u0) * Fmt::kBlocks, acc);
+                    }
+            }
+            __syncthreads();
+            if constexpr (S > 1) {
+                if (kp > 0) {
+#pragma unroll
+                    for (int mm = 0; mm < NMAT; ++mm)
+                        red[((wave - R) * NMAT + mm) * kWave + lane] = acc[mm];
+                }
+                __syncthreads();
+                if (kp == 0) {
+#pragma unroll
+                    for (int pp = 1; pp < S; ++pp)
+#pragma unroll
+                        for (int mm = 0; mm < NMAT; ++mm)
+                            acc[mm] += red[(((pp - 1) * R + r) * NMAT + mm) * kWave + lane];
+                }
+            }
+            if (kp == 0 && has && valid) {
+                const size_t p = (size_t)beg + c0 + col;
+                if constexpr (NMAT == 2) {
+                    const f32x4 gv = acc[0], uv = acc[1];
+                    u32x2 packed;
+                    packed.x = (uint32_t)f32_to_bf16_bits(silu(gv.x) * uv.x) |
+                               ((uint32_t)f32_to_bf16_bits(silu(gv.y) * uv.y) << 16);
+                    packed.y = (uint32_t)f32_to_bf16_bits(silu(gv.z) * uv.z) |
+                               ((uint32_t)f32_to_bf16_bits(silu(gv.w) * uv.w) << 16);
+                    *reinterpret_cast<u32x2*>(g.h + p * g.N + row0 + kg * 4) = packed;
+                } else {
+                    const int slot = g.sorted_slot[p];
+                    *reinterpret_cast<f32x4*>(g.y + (size_t)slot * g.N + row0 + kg * 4) = acc[0];
+                }
+            }
+            if constexpr (S > 1) __syncthreads();
+        }
+        r0 = r1;
+    }
+}
+
+// Combine: out[t][c] = bf16( sum_{j ascending} w[t][j] * y[t*k + j][c] ),
+// skipping slots whose expert id is out of range.  Eight columns per thread;
+// the transposed [row x token] tiles of the down kernel are already stored
+// token-major in y, so this writes plain row-major rows.
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
+                                                      const int32_t* __restrict__ ids,
+                                                      const float* __restrict__ w,
+                                                      uint16_t* __restrict__ out, int T,
+                                                      int H, int k, int E) {
+    const int chunks = H / 8;
+    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= T * chunks) return;
+    const int t = idx / chunks;
+    const int c = (idx - t * chunks) * 8;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+        const int slot = t * k + j;
+        const int e = ids[slot];
+        if (e < 0 || e >= E) continue;
+        const float wj = w[slot];
+        const f32x4 a = *reinterpret_cast<const f32x4*>(y + (size_t)slot * H + c);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(y + (size_t)slot * H + c + 4);
+        acc[0] += wj * a.x; acc[1] += wj * a.y; acc[2] += wj * a.z; acc[3] += wj * a.w;
+        acc[4] += wj * b.x; acc[5] += wj * b.y; acc[6] += wj * b.z; acc[7] += wj * b.w;
+    }
+    u32x4 o;
+    o.x = (uint32_t)f32_to_bf16_bits(acc[0]) | ((uint32_t)f32_to_bf16_bits(acc[1]) << 16);
+    o.y = (uint32_t)f32_to_bf16_bits(acc[2]) | ((uint32_t)f32_to_bf16_bits(acc[3]) << 16);
+    o.z = (uint32_t)f32_to_bf16_bits(acc[4]) | ((uint32_t)f32_to_bf16_bits(acc[5]) << 16);
+    o.w = (uint32_t)f32_to_bf16_bits(acc[6]) | ((uint32_t)f32_to_bf16_bits(acc[7]) << 16);
+    *reinterpret_cast<u32x4*>(out + (size_t)t * H + c) = o;
+}
+
+// Launch shape of one grouped product: the smallest K split that gives
+// kMinWavesPerCU waves per CU a row block (counting the most experts the
+// routing can make active), and enough workgroups for the row blocks, up to
+// the resident limit, as a multiple of the XCD count.
+struct GemmShape {
+    int split, grid;
+};
+
+GemmShape gemm_shape(int64_t max_active, int N, int num_cu, int blocks_per_cu) {
+    const int64_t rows = max_active * (N / 16);
+    const int64_t resident = (int64_t)num_cu * blocks_per_cu;
+    int split = 1;
+    while (split < kWaves && rows * split < (int64_t)num_cu * kMinWavesPerCU) split *= 2;
+    const int R = kWaves / split;
+    int64_t grid = (rows + R - 1) / R;
+    if (grid > resident) grid = resident;
+    grid = (grid + kXcds - 1) / kXcds * kXcds;
+    return {split, (int)grid};
+}
+
+constexpr int cmin(int a, int b) { return a < b ? a : b; }
+
+// One launch of the grouped product; the batch never exceeds a slab part.
+template <class Fmt, int NMAT>
+hipError_t launch_gemm(const ExpertGemm& g, int64_t max_active, int num_cu,
+                       hipStream_t stream) {
+    using Tune = GemmTuning<Fmt, NMAT>;
+    constexpr int U = Tune::kBatch;
+    constexpr int units1 = kSlabBlocks / Fmt::kBlocks;   // units of a part per slab, S = 1
+    const GemmShape sh = gemm_shape(max_active, g.N, num_cu, Tune::kBlocksPerCU);
+    const dim3 grid(sh.grid), block(kThreads);
+    if (sh.split == 1)
+        hipLaunchKernelGGL((expert_gemm_kernel<Fmt, NMAT, 1, cmin(U, units1)>), grid, block, 0,
+                           stream, g);
+    else if (sh.split == 2)
+        hipLaunchKernelGGL((expert_gemm_kernel<Fmt, NMAT, 2, cmin(U, units1 / 2)>), grid, block,
+                           0, stream, g);
+    else
+        hipLaunchKernelGGL((expert_gemm_kernel<Fmt, NMAT, 4, cmin(U, units1 / 4)>), grid, block,
+                           0, stream, g);
+    return hipGetLastError();
+}
+
+template <class Fmt>
+hipError_t launch_ffn(const uint16_t* x, const int32_t* ids, const float* w,
+                      const FfnWeights& W, uint16_t* out, const FfnShape& s,
+                      const Workspace& ws, int num_cu, const StageEvents& ev,
+                      hipStream_t stream) {
+    hipError_t err = launch_permute(ids, s, ws, stream);
+    if (err == hipSuccess) err = ev.mark(0, stream);
+    if (err != hipSuccess) return err;
+    // upper bound of active experts: every slot could name a different one
+    const int64_t max_active = s.E < (int64_t)s.T * s.k ? s.E : (int64_t)s.T * s.k;
+
+    ExpertGemm gu{};
+    gu.b_src = x;
+    gu.w0 = W.gate;
+    gu.w1 = W.up;
+    gu.s0 = W.s_gate;
+    gu.s1 = W.s_up;
+    gu.meta = ws.meta;
+    gu.offsets = ws.offsets;
+    gu.active = ws.active;
+    gu.sorted_slot = ws.sorted_slot;
+    gu.h = ws.h;
+    gu.y = nullptr;
+    gu.b_pitch = s.H;
+    gu.N = s.I;
+    gu.K = s.H;
+    gu.top_k = s.k;
+    err = launch_gemm<Fmt, 2>(gu, max_active, num_cu, stream);
+    if (err == hipSuccess) err = ev.mark(1, stream);
+    if (err != hipSuccess) return err;
+
+    ExpertGemm dn = gu;
+    dn.b_src = ws.h;
+    dn.w0 = W.down;
+    dn.w1 = nullptr;
+    dn.s0 = W.s_down;
+    dn.s1 = nullptr;
+    dn.h = nullptr;
+    dn.y = ws.y;
+    dn.b_pitch = s.I;
+    dn.N = s.H;
+    dn.K = s.I;
+    err = launch_gemm<Fmt, 1>(dn, max_active, num_cu, stream);
+    if (err == hipSuccess) err = ev.mark(2, stream);
+    if (err != hipSuccess) return err;
+    err = launch_combine(ws.y, ids, w, out, s, stream);
+    if (err == hipSuccess) err = ev.mark(3, stream);
+    return err;
+}
+
+}  // namespace
+
+hipError_t launch_combine(const float* y, const int32_t* ids, const float* w,
+                          uint16_t* out, const FfnShape& s, hipStream_t stream) {
+    const int64_t n = (int64_t)s.T * (s.H / 8);
+    const int grid = (int)((n + 255) / 256);
+    hipLaunchKernelGGL(combine_kernel, dim3(grid), dim3(256), 0, stream, y, ids, w, out,
+                       s.T, s.H, s.k, s.E);
+    return hipGetLastError();
+}
+
+hipError_t launch_ffn_bf16(const uint16_t* x, const int32_t* ids, const float* w,
+                           const FfnWeights& W, uint16_t* out, const FfnShape& s,
+                           const Workspace& ws, int num_cu, const StageEvents& ev,
+                           hipStream_t stream) {
+    return launch_ffn<Bf16Weights>(x, ids, w, W, out, s, ws, num_cu, ev, stream);
+}
+
+hipError_t launch_ffn_int8(const uint16_t* x, const int32_t* ids, const float* w,
+                           const FfnWeights& W, uint16_t* out, const FfnShape& s,
+                           const Workspace& ws, int num_cu, const StageEvents& ev,
+                           hipStream_t stream) {
+    return launch_ffn<Int8Weights>(x, ids, w, W, out, s, ws, num_cu, ev, stream);
+}
+
+}  // namespace moe
