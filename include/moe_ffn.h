@@ -147,10 +147,14 @@ int moe_ffn_forward(const void* x, const int32_t* topk_ids, const float* topk_w,
  * Routed-expert FFN layer, INT8 weights with group scales (HiNa-MoE §8.1,
  * Fig. 11: symmetric group-wise INT8; group = MOE_FFN_INT8_GROUP along K).
  * As moe_ffn_forward, except every weight row r is int8 q[r][K] with one
- * float32 scale per group of 128: s[r][K/128], and each dot product is
- *   sum_g s[r][g] * (sum_{c in group g} v_c * q[r][c])   (FP32).
- *   Q_gate, Q_up [E][I][H] int8 with S_gate, S_up [E][I][H/128] float32;
- *   Q_down [E][H][I] int8 with S_down [E][H][I/128] float32.
+ * float32 scale s(r, g) per group g of 128 consecutive K, and each dot
+ * product is
+ *   sum_g s(r, g) * (sum_{c in group g} v_c * q[r][c])   (FP32).
+ * The int8 matrices are row-major like the BF16 ones; the scales are stored
+ * group-major, s(r, g) at [e][g][r], so that one load returns the scales of
+ * consecutive output rows:
+ *   Q_gate, Q_up [E][I][H] int8 with S_gate, S_up [E][H/128][I] float32;
+ *   Q_down [E][H][I] int8 with S_down [E][I/128][H] float32.
  * Sizes: H and I multiples of 128.  Scale pointers must be 16-byte aligned.
  */
 int moe_ffn_forward_int8(const void* x, const int32_t* topk_ids,

@@ -163,12 +163,22 @@ def moe_ffn_forward_int8(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.
                          S_up: torch.Tensor, Q_down: torch.Tensor, S_down: torch.Tensor,
                          out: Optional[torch.Tensor] = None,
                          workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Routed-expert FFN layer with INT8 group-quantised weights; returns ``out``."""
+    """Routed-expert FFN layer with INT8 group-quantised weights; returns ``out``.
+
+    Scales are group-major: S_gate/S_up [E, H/128, I], S_down [E, I/128, H]."""
     T, H = x.shape
     E, I, H2 = Q_gate.shape
     top_k = topk_ids.shape[1]
     if H2 != H or tuple(Q_down.shape) != (E, H, I):
         raise ValueError("weight shapes must be Q_gate/Q_up [E,I,H], Q_down [E,H,I]")
+    G = 128
+    if H % G or I % G:
+        raise ValueError("H and I must be multiples of 128")
+    for name, S, shape in (("S_gate", S_gate, (E, H // G, I)), ("S_up", S_up, (E, H // G, I)),
+                           ("S_down", S_down, (E, I // G, H))):
+        if tuple(S.shape) != shape:
+            raise ValueError(f"{name} must be group-major {list(shape)} (scale of row r, "
+                             f"group g at [e][g][r]), got {list(S.shape)}")
     if out is None:
         out = torch.empty_like(x)
     if workspace is None:

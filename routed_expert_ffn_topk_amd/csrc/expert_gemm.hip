@@ -55,7 +55,7 @@ struct ExpertGemm {
     const uint16_t* b_src;    // B rows: x (gate/up) or the gathered h rows (down)
     const void* w0;           // W_gate or W_down, [E][N][K] (BF16 or INT8)
     const void* w1;           // W_up (gate/up only)
-    const float* s0;          // INT8 only: group scales of w0, [E][N][K/128]
+    const float* s0;          // INT8 only: group scales of w0, [E][K/128][N]
     const float* s1;          // INT8 only: group scales of w1
     const int32_t* meta;      // [0] = active experts
     const int32_t* offsets;
@@ -131,27 +131,30 @@ __device__ __forceinline__ bf16x8 i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
 // use).  The group's FP32 partial tile is scaled by the per-row scale of each
 // of the lane's four output rows (4kg + j) and added to the accumulator:
 //   dot(row, v) = sum_g s[row][g] * (sum_{c in g} v_c * q[row][c]).
+// Scales are stored group-major, s[e][g][row]: the four output rows of a lane
+// are one aligned 16-byte load, and a wave's scales of one group sit in one
+// 64-byte segment (row-major scales would cost a cache line per row).
 struct Int8Weights {
     static constexpr int kBlocks = 4;
     template <int NMAT, int U>
     struct Batch {
         u32x4 w[U][NMAT][2];
-        float s[U][NMAT][4];
+        f32x4 s[U][NMAT];
     };
-    // two 16-byte weight loads and four scale loads per unit and matrix
+    // two 16-byte weight loads and one 16-byte scale load per unit and matrix
     template <int NMAT, int U>
-    static constexpr int loads() { return U * NMAT * 6; }
+    static constexpr int loads() { return U * NMAT * 3; }
     __device__ static int block_offset(int sub, int kg) {
         return (sub >> 1) * 64 + kg * 16 + (sub & 1) * 8;
     }
     __device__ static const void* row_ptr(const void* base, size_t row, int K, int kg) {
         return static_cast<const int8_t*>(base) + row * K + kg * 16;
     }
-    // a[m]: weight row at K offset 16*kg; sc[m]: scale row of output row
-    // 4*kg of the row block; ng: groups per row
+    // a[m]: weight row at K offset 16*kg; sc[m]: scales of group 0 of the
+    // lane's output rows 4*kg..4*kg+3; spitch: floats between groups (N)
     template <int NMAT, int U>
     __device__ static void load(Batch<NMAT, U>& d, const void* const* a, const float* const* sc,
-                                int ng, int u) {
+                                int spitch, int u) {
 #pragma unroll
         for (int i = 0; i < U; ++i)
 #pragma unroll
@@ -159,8 +162,7 @@ struct Int8Weights {
                 const int8_t* p = static_cast<const int8_t*>(a[m]) + (size_t)(u + i) * 128;
                 d.w[i][m][0] = load16(p);
                 d.w[i][m][1] = load16(p + 64);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) d.s[i][m][j] = sc[m][(size_t)j * ng + u + i];
+                d.s[i][m] = __builtin_bit_cast(f32x4, load16(sc[m] + (size_t)(u + i) * spitch));
             }
     }
     template <int NMAT, int U>
@@ -179,10 +181,7 @@ struct Int8Weights {
                     part = mfma16x16x32(i8x8_to_bf16x8(w.z, w.w),
                                         as_bf16x8(blk[4 * i + 2 * c + 1][lane]), part);
                 }
-                acc[m].x += d.s[i][m][0] * part.x;
-                acc[m].y += d.s[i][m][1] * part.y;
-                acc[m].z += d.s[i][m][2] * part.z;
-                acc[m].w += d.s[i][m][3] * part.w;
+                acc[m] += d.s[i][m] * part;
             }
         }
     }
@@ -268,7 +267,8 @@ void expert_gemm_kernel(const ExpertGemm g) {
         const size_t arow = (size_t)e * g.N + row0 + col;   // this lane's weight row
         const void* wp[2] = {Fmt::row_ptr(g.w0, arow, g.K, kg),
                              Fmt::row_ptr(NMAT == 2 ? g.w1 : g.w0, arow, g.K, kg)};
-        const size_t srow = ((size_t)e * g.N + row0 + 4 * kg) * nunits;  // INT8 scale rows
+        // INT8 scales of group 0 of this lane's output rows (group-major)
+        const size_t srow = (size_t)e * nunits * g.N + row0 + 4 * kg;
         const float* sp[2] = {g.s0 ? g.s0 + srow : nullptr,
                               NMAT == 2 && g.s1 ? g.s1 + srow : nullptr};
         const int nfull = has ? (u1 - u0) / U : 0;   // full batches of this wave
@@ -308,7 +308,7 @@ void expert_gemm_kernel(const ExpertGemm g) {
             // always requested before the current one is multiplied
             constexpr int kLoads = Fmt::template loads<NMAT, U>();
             Batch A, B;
-            if (nfull > 0) Fmt::template load<NMAT, U>(A, wp, sp, nunits, u0);
+            if (nfull > 0) Fmt::template load<NMAT, U>(A, wp, sp, g.N, u0);
             int bi = 0;
             for (int j = 0; j < nslab; ++j) {
                 // this wave's staging loads are done (only the batch
@@ -326,18 +326,18 @@ void expert_gemm_kernel(const ExpertGemm g) {
                     const u32x4(*bb)[kWave] = buf + (u0 + bi * U - slab_u0) * Fmt::kBlocks;
                     if ((bi & 1) == 0) {
                         if (bi + 1 < nfull)
-                            Fmt::template load<NMAT, U>(B, wp, sp, nunits, u0 + (bi + 1) * U);
+                            Fmt::template load<NMAT, U>(B, wp, sp, g.N, u0 + (bi + 1) * U);
                         Fmt::template mma<NMAT, U>(A, bb, acc);
                     } else {
                         if (bi + 1 < nfull)
-                            Fmt::template load<NMAT, U>(A, wp, sp, nunits, u0 + (bi + 1) * U);
+                            Fmt::template load<NMAT, U>(A, wp, sp, g.N, u0 + (bi + 1) * U);
                         Fmt::template mma<NMAT, U>(B, bb, acc);
                     }
                 }
                 if (has && tail_u < u1 && tail_u >= slab_u0 && tail_u < slab_u0 + SPU)
                     for (int u = tail_u; u < u1; ++u) {
                         typename Fmt::template Batch<NMAT, 1> t;
-                        Fmt::template load<NMAT, 1>(t, wp, sp, nunits, u);
+                        Fmt::template load<NMAT, 1>(t, wp, sp, g.N, u);
                         Fmt::template mma<NMAT, 1>(t, buf + (u - slab_u0) * Fmt::kBlocks, acc);
                     }
             }

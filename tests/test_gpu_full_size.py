@@ -59,8 +59,11 @@ def test_full_size_int8_sampled_rows(m):
     ids, w = oracle.route_topk(workloads.gen_logits(wl).numpy(), wl.k)
     Q = workloads.gen_weights_int8(wl, "cuda")
     ws = moe.alloc_workspace(wl.T, wl.H, wl.I, wl.E, wl.k)
+    Qg, Sg, Qu, Su, Qd, Sd = Q
+    gm = workloads.scales_group_major
     out = moe.moe_ffn_forward_int8(workloads.bits_to_bf16(xb).cuda(), torch.from_numpy(ids).cuda(),
-                                   torch.from_numpy(w).cuda(), *Q, workspace=ws)
+                                   torch.from_numpy(w).cuda(), Qg, gm(Sg), Qu, gm(Su), Qd, gm(Sd),
+                                   workspace=ws)
     torch.cuda.synchronize()
     got = workloads.bf16_bits(out)
     rows = sample_rows(wl.T)

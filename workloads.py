@@ -154,6 +154,12 @@ def quantize_groupwise(w: torch.Tensor, group: int = 128):
     return q.to(torch.int8).reshape(*lead, K), s.contiguous()
 
 
+def scales_group_major(s: torch.Tensor) -> torch.Tensor:
+    """Row-major group scales [..., N, K/group] -> group-major [..., K/group, N]
+    (the scale layout of the INT8 HIP path).  A layout change only."""
+    return s.transpose(-1, -2).contiguous()
+
+
 def gen_weights_int8(wl: Workload, device="cpu", experts: Optional[list] = None):
     """INT8 expert weights with per-group scales:
     (Qg [E,I,H], Sg [E,I,H/g], Qu, Su, Qd [E,H,I], Sd [E,H,I/g])."""
