@@ -1,22 +1,33 @@
 #!/usr/bin/env python3
 """Benchmark of the routed-expert MoE FFN layer on one MI355X.
 
-Workload: Mixtral-8x7B expert shape (hidden 4096, intermediate 14336, 8
-experts, top-2), BF16 row-major weights ~ N(0, 0.02), routing forced so that
-every expert gets exactly m tokens (T = 4m), m in {1, 2, 4, 8, 16}; router
-logits ~ N(0,1) (HiNa-MoE §7.3 and Table 3 shapes, 1-16 tokens per expert).
-One step = one layer call at each m (five layers).  Inputs are resident in
-HBM before timing; the router runs once per batch before the timed region.
+Default workload (``--workload mixtral8x7b_forced_m1-16``): Mixtral-8x7B expert
+shape (hidden 4096, intermediate 14336, 8 experts, top-2), BF16 row-major
+weights ~ N(0, 0.02), routing forced so that every expert gets exactly m
+tokens (T = 4m), m in {1, 2, 4, 8, 16}; router logits ~ N(0,1) (HiNa-MoE §7.3
+and Table 3 shapes, 1-16 tokens per expert).  One step = one layer call at
+each m (five layers).
 
-Printed (one JSON line): weight-stream throughput in GB/s (algorithmic bytes:
-active experts' weights + x + out + routing ids/weights, per layer) over the
-timed steps, microseconds per layer for each m, the roofline of the dominant
-kernel (gate/up) from per-kernel HIP events, and the CPU oracle timed on a
-bounded sample of the same workload.
+Other workloads: ``mixtral8x7b_int8_forced_m1-16`` (the same with INT8
+group-quantised weights), and any single layer of the workload registry
+(``deepseekv3_t16``, ``deepseekv3_zipf_t16``, ``mixtral8x22b_t{1,4,16}``,
+``qwen3_235b_t{1,4,16}``): one step = one call of that layer.  When the
+active experts' weights of a layer are small enough to stay in the 256 MB
+last-level cache between calls, the step cycles through several distinct
+weight sets (as consecutive layers of a model would), so that every call
+streams its weights from HBM.
+
+Inputs are resident in HBM before timing; the router runs once per batch
+before the timed region.  Printed (one JSON line): weight-stream throughput in
+GB/s (algorithmic bytes: active experts' weights + x + out + routing ids and
+weights, per layer) over the timed steps, microseconds per layer, the roofline
+of the dominant kernel (gate/up) from per-kernel HIP events, and the CPU
+oracle timed on a bounded sample of the same workload.
 """
 import argparse
 import hashlib
 import json
+import math
 import os
 import re
 import statistics
@@ -29,22 +40,42 @@ sys.path.insert(0, ROOT)
 METRIC = "µs per MoE FFN layer + weight-stream GB/s (% HBM peak), BF16, 1–16 tok/expert"
 HBM_PEAK_GBS = 8000.0
 MS = (1, 2, 4, 8, 16)
+DEFAULT_WORKLOAD = "mixtral8x7b_forced_m1-16"
+ROTATE_BELOW = 2 << 30         # a step streams >= 2 GiB (8x the 256 MB last-level cache)
+CPU_SAMPLE_MACS = 2.0e10       # oracle sample: multiply-adds per run ...
+CPU_SAMPLE_BYTES = 3 << 30     # ... and expert bytes copied to the host
 
 
-def layer_bytes(wl) -> int:
-    """Algorithmic HBM bytes of one layer: every active expert's three weight
-    matrices once, x read, out written, routing ids and weights read."""
+def suite_layers(name: str):
+    """Layers (workload registry entries) of one benchmark step."""
     import workloads
-    active = min(wl.E, wl.T * wl.k)    # forced routing: all experts active
-    return (active * workloads.weight_bytes_per_expert(wl) + 2 * wl.T * wl.H * 2
-            + wl.T * wl.k * 8)
+    if name == DEFAULT_WORKLOAD:
+        return [workloads.WORKLOADS[f"mixtral8x7b_m{m}"] for m in MS]
+    if name == "mixtral8x7b_int8_forced_m1-16":
+        return [workloads.WORKLOADS[f"mixtral8x7b_int8_m{m}"] for m in MS]
+    if name in workloads.WORKLOADS and name != "tiny":
+        return [workloads.WORKLOADS[name]]
+    raise SystemExit(f"bench.py: unknown workload {name!r}")
 
 
-def gateup_bytes(wl) -> int:
-    """Algorithmic bytes of one gate/up launch: W_gate and W_up of every active
-    expert plus the token rows (h is scratch and not credited)."""
-    active = min(wl.E, wl.T * wl.k)
-    return active * 2 * wl.I * wl.H * 2 + wl.T * wl.H * 2
+def expert_bytes(wl) -> int:
+    import workloads
+    return workloads.weight_bytes_per_expert(wl)
+
+
+def layer_bytes(wl, active: int) -> int:
+    """Algorithmic HBM bytes of one layer: every active expert's three weight
+    matrices (and INT8 scales) once, x read, out written, routing ids and
+    weights read."""
+    return active * expert_bytes(wl) + 2 * wl.T * wl.H * 2 + wl.T * wl.k * 8
+
+
+def gateup_bytes(wl, active: int) -> int:
+    """Algorithmic bytes of one gate/up launch: W_gate and W_up (and their
+    scales) of every active expert plus the token rows (h is scratch and not
+    credited)."""
+    per = wl.I * wl.H * (1 + 4 / wl.group) if wl.int8 else wl.I * wl.H * 2
+    return int(active * 2 * per) + wl.T * wl.H * 2
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "expert_gemm_mixtral8x7b_m1-16_hbm_traffic.md")
@@ -52,45 +83,67 @@ KERNEL_SOURCES = ("routed_expert_ffn_topk_amd/csrc/expert_gemm.hip",
                   "routed_expert_ffn_topk_amd/csrc/common.hpp")
 
 
-def recorded_traffic():
+def kernel_source_hash() -> str:
+    digests = "".join(hashlib.sha256(open(os.path.join(ROOT, f), "rb").read()).hexdigest()
+                      for f in KERNEL_SOURCES)
+    return hashlib.sha256(digests.encode()).hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
     """HBM bytes per gate/up launch from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE record (scaled by a plain copy of known size), or None when the
-    kernel sources have changed since the counters were taken."""
+    record is for another workload or the kernel sources have changed since
+    the counters were taken."""
     try:
         text = open(TRAFFIC_PROFILE).read()
-        digests = "".join(hashlib.sha256(open(os.path.join(ROOT, f), "rb").read()).hexdigest()
-                          for f in KERNEL_SOURCES)
+        digest = kernel_source_hash()
     except OSError:
         return None
-    rec = dict(re.findall(r"^(kernel_source_sha256_16|gateup_traffic_bytes_per_launch): (\S+)$",
-                          text, re.M))
-    if rec.get("kernel_source_sha256_16") != hashlib.sha256(digests.encode()).hexdigest()[:16]:
+    rec = dict(re.findall(r"^(kernel_source_sha256_16|workload|gateup_traffic_bytes_per_launch): "
+                          r"(\S+)$", text, re.M))
+    if rec.get("kernel_source_sha256_16") != digest or rec.get("workload") != workload:
         return None
     return int(rec["gateup_traffic_bytes_per_launch"])
 
 
-def cpu_baseline(wl, Wg, Wu, Wd, logits_cpu, x_cpu, reps=3):
-    """The CPU oracle on one m=1 layer (T=4: every expert streamed once)."""
-    import numpy as np
+def cpu_baseline(wl, host_weights, logits_cpu, x_cpu, reps=3):
+    """The CPU oracle on a bounded token sample of one layer of the workload:
+    the leading tokens, as many as fit CPU_SAMPLE_MACS multiply-adds and
+    CPU_SAMPLE_BYTES of expert weights copied to the host."""
+    import torch
 
     import oracle
     import workloads
     ids, w = oracle.route_topk(logits_cpu.numpy(), wl.k)
-    need = sorted(set(ids.reshape(-1).tolist()))
-    host = [{e: workloads.bf16_bits(W[e]) for e in need} for W in (Wg, Wu, Wd)]
-    xb = workloads.bf16_bits(x_cpu)
+    n, need = 0, set()
+    per_slot = 3 * wl.H * wl.I
+    while n < wl.T:
+        cand = need | set(ids[n].tolist())
+        if n > 0 and ((n + 1) * wl.k * per_slot > CPU_SAMPLE_MACS
+                      or len(cand) * expert_bytes(wl) > CPU_SAMPLE_BYTES):
+            break
+        need, n = cand, n + 1
+    need = sorted(need)
+    to_host = lambda t: (workloads.bf16_bits(t) if t.dtype == torch.bfloat16  # noqa: E731
+                         else t.cpu().numpy())
+    tables = [{e: to_host(W[e]) for e in need} for W in host_weights]
+    xb = workloads.bf16_bits(x_cpu[:n])
     times = []
     for _ in range(reps):
         t0 = time.perf_counter()
-        oracle.moe_ffn_bf16(xb, ids, w, host[0].get, host[1].get, host[2].get, E=wl.E)
+        if wl.int8:
+            oracle.moe_ffn_int8(xb, ids[:n], w[:n], *(t.get for t in tables), E=wl.E)
+        else:
+            oracle.moe_ffn_bf16(xb, ids[:n], w[:n], *(t.get for t in tables), E=wl.E)
         times.append(time.perf_counter() - t0)
     t = statistics.median(times)
-    del host
-    return {"value": round(layer_bytes(wl) / t / 1e9, 3), "unit": "GB/s",
+    sample_bytes = len(need) * expert_bytes(wl) + 2 * n * wl.H * 2 + n * wl.k * 8
+    return {"value": round(sample_bytes / t / 1e9, 3), "unit": "GB/s",
             "cores": oracle.num_threads(), "kind": "oracle",
             "us_per_layer": round(t * 1e6, 1),
-            "sample": f"one Mixtral-8x7B layer at m=1 (T=4, all 8 experts), median of {reps} "
-                      f"runs, plain C oracle (FP32 accumulation, per-token loops)"}
+            "sample": f"{wl.name}: the first {n} of {wl.T} tokens ({len(need)} experts), "
+                      f"median of {reps} runs, plain C oracle (FP32 accumulation, per-token "
+                      f"loops, {'INT8' if wl.int8 else 'BF16'} weights)"}
 
 
 def main():
@@ -98,6 +151,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB, 5 times "
@@ -114,8 +168,8 @@ def main():
         print(json.dumps({"copy_probe_bytes": n, "copies": 5}), flush=True)
         return
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported: this build runs the MoE FFN "
-              "layer on one GPU only (see the sharding notes in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py: --gpus {args.gpus} is not supported: the MoE FFN layer runs on one "
+              "GPU only here (the sharding notes are in DESIGN.md)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -125,27 +179,47 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    wls = [workloads.WORKLOADS[f"mixtral8x7b_m{m}"] for m in MS]
-    wl0 = wls[0]
-    Wg, Wu, Wd = workloads.gen_weights(wl0, "cuda")
+    layers = suite_layers(args.workload)
+    int8 = layers[0].int8
+    stream = torch.cuda.current_stream()
+
     batches = []
-    for wl in wls:
+    for wl in layers:
         x = workloads.gen_x(wl)
         lg = workloads.gen_logits(wl)
         ids, w = moe.moe_route_topk(lg.to(dev), wl.k)
-        batches.append(dict(wl=wl, x_cpu=x, lg_cpu=lg, x=x.to(dev), ids=ids, w=w,
+        active = len(set(ids.cpu().reshape(-1).tolist()))
+        batches.append(dict(wl=wl, x_cpu=x, lg_cpu=lg, x=x.to(dev), ids=ids, w=w, active=active,
                             out=torch.empty(wl.T, wl.H, dtype=torch.bfloat16, device=dev),
                             ws=moe.alloc_workspace(wl.T, wl.H, wl.I, wl.E, wl.k, dev)))
+    # distinct weight sets so that one step streams at least ROTATE_BELOW bytes
+    step_weight_bytes = sum(b["active"] * expert_bytes(b["wl"]) for b in batches)
+    n_sets = max(1, math.ceil(ROTATE_BELOW / step_weight_bytes)) \
+        if step_weight_bytes < ROTATE_BELOW else 1
+    wl0 = layers[0]
+    sets = []
+    for r in range(n_sets):
+        wlr = workloads.Workload(**{**wl0.__dict__, "seed": wl0.seed + r})
+        if int8:
+            Qg, Sg, Qu, Su, Qd, Sd = workloads.gen_weights_int8(wlr, dev)
+            sets.append((Qg, workloads.scales_group_major(Sg), Qu, workloads.scales_group_major(Su),
+                         Qd, workloads.scales_group_major(Sd)))
+            if r == 0:
+                host_rowmajor = (Qg, Sg, Qu, Su, Qd, Sd)
+            else:
+                del Sg, Su, Sd
+        else:
+            sets.append(workloads.gen_weights(wlr, dev))
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
+    fwd = moe.moe_ffn_forward_int8 if int8 else moe.moe_ffn_forward
 
-    def layer(b):
-        moe.moe_ffn_forward(b["x"], b["ids"], b["w"], Wg, Wu, Wd, out=b["out"],
-                            workspace=b["ws"], stream=stream)
+    def layer(b, s):
+        fwd(b["x"], b["ids"], b["w"], *sets[s], out=b["out"], workspace=b["ws"], stream=stream)
 
     def step():
         for b in batches:
-            layer(b)
+            for s in range(n_sets):
+                layer(b, s)
 
     for _ in range(args.warmup):
         step()
@@ -158,72 +232,79 @@ def main():
     t1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / args.steps
-    step_bytes = sum(layer_bytes(b["wl"]) for b in batches)
+    step_bytes = n_sets * sum(layer_bytes(b["wl"], b["active"]) for b in batches)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
-    # microseconds per layer at each m (same calls, timed per batch)
-    per_m = {}
+    # microseconds per layer (same calls, timed per batch)
+    per_layer = {}
     reps = max(5, args.steps // 2)
     for b in batches:
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for _ in range(reps):
-            layer(b)
+        for i in range(reps):
+            layer(b, i % n_sets)
         e1.record(stream)
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / reps
-        per_m[str(b["wl"].T // 4)] = {
-            "us": round(us, 1),
-            "GBps": round(layer_bytes(b["wl"]) / (us * 1e-6) / 1e9, 1),
-            "pct_hbm_peak": round(100 * layer_bytes(b["wl"]) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
+        lb = layer_bytes(b["wl"], b["active"])
+        per_layer[b["wl"].name] = {
+            "T": b["wl"].T, "active_experts": b["active"], "us": round(us, 1),
+            "GBps": round(lb / (us * 1e-6) / 1e9, 1),
+            "pct_hbm_peak": round(100 * lb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
         }
 
-    # per-kernel durations from HIP events recorded between the kernels of
-    # each call (stage 0 permute, 1 gate/up, 2 down, 3 combine)
+    # per-kernel durations from HIP events recorded on the launch stream
+    # between the kernels of each call (stage 0 permute, 1 gate/up, 2 down,
+    # 3 combine)
     names = ("permute", "gateup", "down", "combine")
     dur = {n: [] for n in names}
-    dur_m = {str(b["wl"].T // 4): {n: [] for n in names} for b in batches}
+    dur_l = {b["wl"].name: {n: [] for n in names} for b in batches}
     gu_bytes = []
-    for _ in range(max(3, args.steps // 5)):
+    for i in range(max(3, args.steps // 5)):
         for b in batches:
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
             for e in ev:
                 e.record(stream)          # materialise the HIP events
             ev[0].record(stream)
             moe.moe_ffn_set_stage_events(ev[1:])
-            layer(b)
+            layer(b, i % n_sets)
             torch.cuda.synchronize()
-            for i, n in enumerate(names):
-                d = ev[i].elapsed_time(ev[i + 1]) * 1e3
+            for j, n in enumerate(names):
+                d = ev[j].elapsed_time(ev[j + 1]) * 1e3
                 dur[n].append(d)
-                dur_m[str(b["wl"].T // 4)][n].append(d)
-            gu_bytes.append(gateup_bytes(b["wl"]))
-    for m, d in dur_m.items():
-        per_m[m]["stage_us"] = {n: round(statistics.mean(v), 1) for n, v in d.items()}
+                dur_l[b["wl"].name][n].append(d)
+            gu_bytes.append(gateup_bytes(b["wl"], b["active"]))
+    for name, d in dur_l.items():
+        per_layer[name]["stage_us"] = {n: round(statistics.mean(v), 1) for n, v in d.items()}
     gu_us = statistics.mean(dur["gateup"])
     achieved = statistics.mean(gu_bytes) / (gu_us * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "kernel": "expert_gemm_kernel (gate/up)",
+    kern = "expert_gemm_kernel<Int8Weights, 2, ...>" if int8 else \
+        "expert_gemm_kernel<Bf16Weights, 2, ...>"
+    roofline = {"bound": "hbm", "kernel": f"{kern} (gate/up, SiLU*up epilogue)",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": recorded_traffic(args.workload),
                 "algorithmic_bytes": int(statistics.mean(gu_bytes)), "avg_us": round(gu_us, 2),
                 "stage_us": {n: round(statistics.mean(v), 2) for n, v in dur.items()}}
 
+    wl = layers[0]
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "mixtral8x7b_forced_m1-16", "hidden": 4096,
-                   "intermediate": 14336, "experts": 8, "top_k": 2,
-                   "tokens_per_expert": list(MS), "layers_per_step": len(MS),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8-weights/bf16" if int8 else "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "hidden": wl.H, "intermediate": wl.I,
+                   "experts": wl.E, "top_k": wl.k, "tokens": [b["wl"].T for b in batches],
+                   "layers_per_step": len(batches) * n_sets, "weight_sets": n_sets,
                    "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
-                   "per_m": per_m, "device": torch.cuda.get_device_name(dev)},
+                   "per_layer": per_layer, "device": torch.cuda.get_device_name(dev)},
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
         b = batches[0]
-        result["cpu_baseline"] = cpu_baseline(b["wl"], Wg, Wu, Wd, b["lg_cpu"], b["x_cpu"])
+        host = host_rowmajor if int8 else sets[0]
+        result["cpu_baseline"] = cpu_baseline(b["wl"], host, b["lg_cpu"], b["x_cpu"])
     print(json.dumps(result), flush=True)
 
 
