@@ -16,11 +16,11 @@
 //
 // One kernel skeleton serves both projections and both weight formats.  Work
 // unit: a row block (16 output rows of one active expert, all its tokens).
-// The four waves of a workgroup form R row blocks x S K-parts (R * S = 4; S
-// chosen by the host from the problem size so that there are enough waves to
-// keep HBM busy).  Workgroups are persistent: each XCD owns a contiguous slice
-// of the expert-major row-block list, and each workgroup a balanced contiguous
-// range of that slice, walked in rounds of R row blocks of one expert.
+// The four waves of a workgroup form R row blocks x S K-parts (R * S = 4); a
+// round is R row blocks of one expert.  S is chosen on the device from the
+// actual number of active experts, so that the rounds fill the persistent
+// grid evenly.  Each XCD owns a contiguous slice of the expert-major round
+// list, and each workgroup a balanced contiguous share of that slice.
 //
 // B operand (the gathered tokens, i.e. the pages' matrix I): the workgroup
 // stages K-slabs of the 16-token tile in LDS, in MFMA fragment order (one
@@ -37,7 +37,6 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kSlabBlocks = 16;      // 32-wide K steps per LDS slab buffer (16 KB)
-constexpr int kMinWavesPerCU = 8;    // busy waves per CU that keep HBM streaming
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
@@ -66,6 +65,7 @@ struct ExpertGemm {
     int b_pitch;              // elements between B rows
     int N, K;                 // rows per expert matrix, reduction length
     int top_k;                // gate/up: B row of gathered row p is token sorted_slot[p] / top_k
+    int split;                // K parts per row block (1, 2 or 4); 0 = chosen on the device
 };
 
 // ---------------------------------------------------------------------------
@@ -76,6 +76,8 @@ struct ExpertGemm {
 
 struct Bf16Weights {
     static constexpr int kBlocks = 1;
+    static constexpr int kBytesPerWeight = 2;
+    static constexpr int kUnitBytes = kWave * 16;       // weight bytes a wave loads per unit
     template <int NMAT, int U>
     struct Batch {
         u32x4 w[U][NMAT];
@@ -136,6 +138,8 @@ __device__ __forceinline__ bf16x8 i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
 // 64-byte segment (row-major scales would cost a cache line per row).
 struct Int8Weights {
     static constexpr int kBlocks = 4;
+    static constexpr int kBytesPerWeight = 1;
+    static constexpr int kUnitBytes = kWave * 32;       // weight bytes a wave loads per unit
     template <int NMAT, int U>
     struct Batch {
         u32x4 w[U][NMAT][2];
@@ -214,23 +218,25 @@ struct GemmTuning<Int8Weights, 1> {
     static constexpr int kBatch = 2;
 };
 
-// NMAT = 2: gate/up, epilogue h[p][row] = bf16(silu(g) * u).
-// NMAT = 1: down, epilogue y[slot][row] = acc (FP32, slot = sorted_slot[p]).
 // S: K-parts per row block; U: units per weight batch (divides the units of
 // one K part in a slab).
+// A round is R row blocks of one expert (R = 4 / S), processed by the four
+// waves together: they share the LDS token slabs, and the S K parts of a row
+// block are summed in LDS.  Rounds never straddle two experts.  The rounds of
+// all active experts (expert-major) are dealt out in balanced contiguous
+// ranges: each XCD owns a contiguous slice, each workgroup of the XCD a
+// contiguous share of it (an equal number of rounds, +-1).
 template <class Fmt, int NMAT, int S, int U>
-__global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(GemmTuning<Fmt, NMAT>::kBlocksPerCU)))
-void expert_gemm_kernel(const ExpertGemm g) {
+__device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, int n_act, int grid,
+                                            u32x4 (*xs)[kSlabBlocks][kWave]) {
     constexpr int R = kWaves / S;              // row blocks per round
     constexpr int SP = kSlabBlocks / S;        // LDS blocks of each K part per slab
     constexpr int SPU = SP / Fmt::kBlocks;     // units of each K part per slab
     constexpr int NB = SPU / U;                // full batches per full slab
     static_assert(SPU >= 1 && SPU % U == 0, "batch must divide the slab part");
     using Batch = typename Fmt::template Batch<NMAT, U>;
-    // K-slab buffers; after the slab loop the first buffer doubles as the
-    // K-part reduction area (3 x NMAT x 1 KB <= 16 KB).
-    __shared__ u32x4 xs[2][kSlabBlocks][kWave];
+    // after the slab loop the first slab buffer doubles as the K-part
+    // reduction area (3 x NMAT x 1 KB <= 16 KB)
     f32x4* red = reinterpret_cast<f32x4*>(&xs[0][0][0]);
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -238,32 +244,33 @@ void expert_gemm_kernel(const ExpertGemm g) {
     const int kg = lane >> 4;   // K group of the operands, row quad of D
     const int r = wave % R;     // row block of this wave within a round
     const int kp = wave / R;    // K part of this wave
-    const int nrb = g.N / 16;
-    const int W = g.meta[0] * nrb;
+    const int nrb = g.N / 16;                 // row blocks per expert
+    const int rpe = (nrb + R - 1) / R;         // rounds per expert
+    const int Q = n_act * rpe;                 // rounds of the launch
     const int nunits = g.K / (32 * Fmt::kBlocks);
     const int kpu = (nunits + S - 1) / S;      // units per K part
     const int u0 = min(nunits, kp * kpu);
     const int u1 = min(nunits, u0 + kpu);
     const int nslab = (kpu + SPU - 1) / SPU;
 
-    // this workgroup's row blocks: a balanced share of its XCD's slice
+    // this workgroup's rounds: a balanced share of its XCD's slice
     const int xcd = blockIdx.x % kXcds;
-    const int per = gridDim.x / kXcds;
+    const int per = grid / kXcds;
     const int li = blockIdx.x / kXcds;
-    const int sb = (int)((long long)xcd * W / kXcds);
-    const int n = (int)((long long)(xcd + 1) * W / kXcds) - sb;
-    const int rbeg = sb + (int)((long long)li * n / per);
-    const int rend = sb + (int)((long long)(li + 1) * n / per);
+    const int qb = (int)((long long)xcd * Q / kXcds);
+    const int nq = (int)((long long)(xcd + 1) * Q / kXcds) - qb;
+    const int q0 = qb + (int)((long long)li * nq / per);
+    const int q1 = qb + (int)((long long)(li + 1) * nq / per);
 
-    for (int r0 = rbeg; r0 < rend;) {
-        const int a = r0 / nrb;
-        const int r1 = min(min(r0 + R, rend), (a + 1) * nrb);
+    for (int q = q0; q < q1; ++q) {
+        const int a = q / rpe;                   // active expert of the round
+        const int rb0 = (q - a * rpe) * R;       // its first row block
         const int e = g.active[a];
         const int beg = g.offsets[e];
         const int m = g.offsets[e + 1] - beg;
-        const int my = r0 + r;
-        const bool has = my < r1;
-        const int row0 = (has ? my - a * nrb : 0) * 16;
+        const int my = rb0 + r;
+        const bool has = my < nrb;
+        const int row0 = (has ? my : 0) * 16;
         const size_t arow = (size_t)e * g.N + row0 + col;   // this lane's weight row
         const void* wp[2] = {Fmt::row_ptr(g.w0, arow, g.K, kg),
                              Fmt::row_ptr(NMAT == 2 ? g.w1 : g.w0, arow, g.K, kg)};
@@ -374,8 +381,83 @@ void expert_gemm_kernel(const ExpertGemm g) {
             }
             if constexpr (S > 1) __syncthreads();
         }
-        r0 = r1;
     }
+}
+
+constexpr int cmin(int a, int b) { return a < b ? a : b; }
+
+// Rounds of a launch with K split S.
+__device__ __forceinline__ int rounds_for(int n_act, int nrb, int S) {
+    const int R = kWaves / S;
+    return n_act * ((nrb + R - 1) / R);
+}
+
+// Workgroups that take part in a launch of Q rounds: at most one round more
+// than the others each, and no idle workgroups between busy ones (idle ones
+// would share CUs unevenly with busy ones).  A multiple of the XCD count.
+__device__ __forceinline__ int busy_grid(int Q) {
+    const int q8 = (Q + kXcds - 1) / kXcds * kXcds;
+    return min((int)gridDim.x, q8);
+}
+
+// K parts per row block, from a latency/bandwidth model of one launch.  With
+// split S there are Q_S rounds on G_S = min(grid, Q_S) workgroups, so the
+// makespan is ceil(Q_S / G_S) rounds.  A round streams 16 rows x NMAT
+// matrices x K/S weights per wave, at the lower of the wave's own rate (its
+// bytes in flight, two weight batches, over the load latency) and its share
+// of HBM among the 4 * G_S busy waves, plus a barrier cost per LDS slab.
+// Constants measured on MI355X across the Mixtral-8x7B/8x22B, DeepSeek-V3 and
+// Qwen3-235B expert shapes at 2..103 active experts.
+constexpr float kHbmBytesPerUs = 6.5e6f;   // sustained HBM read rate (6.5 TB/s)
+constexpr float kLoadLatencyUs = 4.0f;     // loaded-memory latency of a batch
+constexpr float kSlabUs = 0.5f;            // barrier and staging wait per slab
+template <class Fmt, int NMAT, int U>
+__device__ __forceinline__ int choose_split(const ExpertGemm& g, int n_act) {
+    constexpr int units1 = kSlabBlocks / Fmt::kBlocks;
+    const int nrb = g.N / 16;
+    const int nslab = (g.K + 32 * kSlabBlocks - 1) / (32 * kSlabBlocks);
+    float best = 0.f;
+    int best_s = 1;
+    for (int S = 1; S <= kWaves; S *= 2) {
+        const int Q = rounds_for(n_act, nrb, S);
+        if (Q == 0) return 1;
+        const int G = busy_grid(Q);
+        const int rounds = (Q + G - 1) / G;
+        const int u = min(U, units1 / S);            // batch length used at this split
+        const float inflight = 2.f * u * NMAT * Fmt::kUnitBytes;
+        const float wave_bytes = 16.f * NMAT * (float)(g.K / S) * Fmt::kBytesPerWeight;
+        const float rate = fminf(inflight / kLoadLatencyUs, kHbmBytesPerUs / (4.f * G));
+        const float t = rounds * (wave_bytes / rate + nslab * kSlabUs);
+        if (S == 1 || t < best) {
+            best = t;
+            best_s = S;
+        }
+    }
+    return best_s;
+}
+
+// NMAT = 2: gate/up, epilogue h[p][row] = bf16(silu(g) * u).
+// NMAT = 1: down, epilogue y[slot][row] = acc (FP32, slot = sorted_slot[p]).
+// One kernel holds the three K splits; the split is uniform over the launch
+// (read from the device-side active-expert count, or forced by g.split).
+template <class Fmt, int NMAT>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(GemmTuning<Fmt, NMAT>::kBlocksPerCU)))
+void expert_gemm_kernel(const ExpertGemm g) {
+    constexpr int U = GemmTuning<Fmt, NMAT>::kBatch;
+    constexpr int units1 = kSlabBlocks / Fmt::kBlocks;   // units of a part per slab, S = 1
+    // K-slab buffers of the token tile, double-buffered
+    __shared__ u32x4 xs[2][kSlabBlocks][kWave];
+    const int n_act = g.meta[0];
+    const int S = g.split ? g.split : choose_split<Fmt, NMAT, U>(g, n_act);
+    const int G = busy_grid(rounds_for(n_act, g.N / 16, S));
+    if ((int)blockIdx.x >= G) return;
+    if (S == 1)
+        gemm_rounds<Fmt, NMAT, 1, cmin(U, units1)>(g, n_act, G, xs);
+    else if (S == 2)
+        gemm_rounds<Fmt, NMAT, 2, cmin(U, units1 / 2)>(g, n_act, G, xs);
+    else
+        gemm_rounds<Fmt, NMAT, 4, cmin(U, units1 / 4)>(g, n_act, G, xs);
 }
 
 // Combine: out[t][c] = bf16( sum_{j ascending} w[t][j] * y[t*k + j][c] ),
@@ -411,46 +493,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     *reinterpret_cast<u32x4*>(out + (size_t)t * H + c) = o;
 }
 
-// Launch shape of one grouped product: the smallest K split that gives
-// kMinWavesPerCU waves per CU a row block (counting the most experts the
-// routing can make active), and enough workgroups for the row blocks, up to
-// the resident limit, as a multiple of the XCD count.
-struct GemmShape {
-    int split, grid;
-};
-
-GemmShape gemm_shape(int64_t max_active, int N, int num_cu, int blocks_per_cu) {
-    const int64_t rows = max_active * (N / 16);
-    const int64_t resident = (int64_t)num_cu * blocks_per_cu;
-    int split = 1;
-    while (split < kWaves && rows * split < (int64_t)num_cu * kMinWavesPerCU) split *= 2;
-    const int R = kWaves / split;
-    int64_t grid = (rows + R - 1) / R;
-    if (grid > resident) grid = resident;
+// Grid of one grouped product: persistent, the resident workgroup count,
+// capped by the most rounds any K split can have (every row block its own
+// round, at the most experts the routing can activate), as a multiple of the
+// XCD count.  The K split itself is chosen on the device.
+int gemm_grid(int64_t max_active, int N, int num_cu, int blocks_per_cu) {
+    const int64_t rounds = max_active * (N / 16);
+    int64_t grid = (int64_t)num_cu * blocks_per_cu;
+    if (grid > rounds) grid = rounds;
     grid = (grid + kXcds - 1) / kXcds * kXcds;
-    return {split, (int)grid};
+    return (int)grid;
 }
 
-constexpr int cmin(int a, int b) { return a < b ? a : b; }
-
-// One launch of the grouped product; the batch never exceeds a slab part.
 template <class Fmt, int NMAT>
 hipError_t launch_gemm(const ExpertGemm& g, int64_t max_active, int num_cu,
                        hipStream_t stream) {
-    using Tune = GemmTuning<Fmt, NMAT>;
-    constexpr int U = Tune::kBatch;
-    constexpr int units1 = kSlabBlocks / Fmt::kBlocks;   // units of a part per slab, S = 1
-    const GemmShape sh = gemm_shape(max_active, g.N, num_cu, Tune::kBlocksPerCU);
-    const dim3 grid(sh.grid), block(kThreads);
-    if (sh.split == 1)
-        hipLaunchKernelGGL((expert_gemm_kernel<Fmt, NMAT, 1, cmin(U, units1)>), grid, block, 0,
-                           stream, g);
-    else if (sh.split == 2)
-        hipLaunchKernelGGL((expert_gemm_kernel<Fmt, NMAT, 2, cmin(U, units1 / 2)>), grid, block,
-                           0, stream, g);
-    else
-        hipLaunchKernelGGL((expert_gemm_kernel<Fmt, NMAT, 4, cmin(U, units1 / 4)>), grid, block,
-                           0, stream, g);
+    const int grid = gemm_grid(max_active, g.N, num_cu, GemmTuning<Fmt, NMAT>::kBlocksPerCU);
+    hipLaunchKernelGGL((expert_gemm_kernel<Fmt, NMAT>), dim3(grid), dim3(kThreads), 0, stream, g);
     return hipGetLastError();
 }
 
