@@ -106,6 +106,31 @@ def recorded_traffic(workload: str):
     return int(rec["gateup_traffic_bytes_per_launch"])
 
 
+def read_ceiling(stream, nbytes=4 << 30, reps=10) -> float:
+    """Measured HBM streaming-read ceiling (GB/s): the library's read probe
+    over a 4 GiB buffer, best of `reps` timed passes after two warm-ups."""
+    import torch
+
+    import routed_expert_ffn_topk_amd as moe
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        moe.moe_ffn_read_probe(buf, sink, stream)
+    best = None
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        moe.moe_ffn_read_probe(buf, sink, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3
+        best = us if best is None else min(best, us)
+    del buf
+    torch.cuda.empty_cache()
+    return nbytes / (best * 1e-6) / 1e9
+
+
 def cpu_baseline(wl, host_weights, logits_cpu, x_cpu, reps=3):
     """The CPU oracle on a bounded token sample of one layer of the workload:
     the leading tokens, as many as fit CPU_SAMPLE_MACS multiply-adds and
@@ -281,10 +306,13 @@ def main():
     achieved = statistics.mean(gu_bytes) / (gu_us * 1e-6) / 1e9
     kern = "expert_gemm_kernel<Int8Weights, 2, ...>" if int8 else \
         "expert_gemm_kernel<Bf16Weights, 2, ...>"
+    ceiling = read_ceiling(stream)
     roofline = {"bound": "hbm", "kernel": f"{kern} (gate/up, SiLU*up epilogue)",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": recorded_traffic(args.workload),
+                "measured_read_ceiling": round(ceiling, 1),
+                "frac_of_measured_ceiling": round(achieved / ceiling, 4),
                 "algorithmic_bytes": int(statistics.mean(gu_bytes)), "avg_us": round(gu_us, 2),
                 "stage_us": {n: round(statistics.mean(v), 2) for n, v in dur.items()}}
 
@@ -298,6 +326,7 @@ def main():
                    "experts": wl.E, "top_k": wl.k, "tokens": [b["wl"].T for b in batches],
                    "layers_per_step": len(batches) * n_sets, "weight_sets": n_sets,
                    "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
+                   "pct_measured_read_ceiling": round(100 * value / ceiling, 1),
                    "per_layer": per_layer, "device": torch.cuda.get_device_name(dev)},
         "roofline": roofline,
     }

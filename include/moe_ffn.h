@@ -186,6 +186,19 @@ const char* moe_ffn_status_string(int status);
  */
 int moe_ffn_set_stage_events(void* const* events, int32_t n_events);
 
+/*
+ * Measurement helper: the HBM streaming-read ceiling that the expert
+ * products are compared against (the GPU counterpart of the STREAM bandwidth
+ * the HiNa-MoE evaluation reports for its CPUs, Table 2).  Enqueues on
+ * `stream` one kernel that reads each of the `bytes` bytes of device buffer
+ * `buf` once, with 16-byte loads, from a grid that fills the device; it
+ * writes nothing but, rarely, one 32-bit word at device address `sink`.
+ * `bytes` must be a positive multiple of 16, `buf` 16-byte aligned and
+ * `sink` 4-byte aligned.  Returns MOE_FFN_OK, MOE_FFN_ERR_NULL_ARG,
+ * MOE_FFN_ERR_BAD_SHAPE, MOE_FFN_ERR_MISALIGNED or MOE_FFN_ERR_HIP.
+ */
+int moe_ffn_read_probe(const void* buf, size_t bytes, void* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

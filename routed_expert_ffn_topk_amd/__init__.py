@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
         L.moe_ffn_status_string.argtypes = [_c.c_int]
         L.moe_ffn_set_stage_events.restype = _c.c_int
         L.moe_ffn_set_stage_events.argtypes = [_c.POINTER(_vp), _i32]
+        L.moe_ffn_read_probe.restype = _c.c_int
+        L.moe_ffn_read_probe.argtypes = [_vp, _sz, _vp, _vp]
         _lib = L
     return _lib
 
@@ -200,6 +202,18 @@ def moe_ffn_check_status(workspace: torch.Tensor, stream=None) -> Tuple[int, int
     code = lib().moe_ffn_check_status(_dev(workspace, "workspace", torch.uint8),
                                       _stream(stream), _c.byref(n))
     return code, int(n.value)
+
+
+def moe_ffn_read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Measurement helper: enqueue one streaming read of every byte of the
+    device buffer ``buf`` (its byte size a multiple of 16); ``sink`` is a
+    device int32 tensor of at least one element."""
+    if not (buf.is_cuda and buf.is_contiguous()):
+        raise ValueError("buf must be a contiguous device tensor")
+    if not (sink.is_cuda and sink.dtype == torch.int32 and sink.numel() >= 1):
+        raise ValueError("sink must be a device int32 tensor")
+    _check("moe_ffn_read_probe", lib().moe_ffn_read_probe(
+        buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(), _stream(stream)))
 
 
 def moe_ffn_set_stage_events(events) -> None:

@@ -23,10 +23,13 @@
 // list, and each workgroup a balanced contiguous share of that slice.
 //
 // B operand (the gathered tokens, i.e. the pages' matrix I): the workgroup
-// stages K-slabs of the 16-token tile in LDS, in MFMA fragment order (one
-// 1 KB block per 32-wide K step, direct global->LDS loads, double-buffered),
-// which all its waves share.  Weights stream through registers in batches
-// with the next batch always in flight, also across slab barriers.
+// stages K-slabs of the 16-token tile in LDS, which all its waves share,
+// double-buffered.  Each token's slab row (512 K values) is one direct
+// global->LDS load of contiguous memory, and only the chunk's distinct tokens
+// are staged; the MFMA reads its B fragments (token column, 8 K values) from
+// the token rows, which are padded so the reads are free of bank conflicts.
+// Weights stream through registers in batches with the next batch always in
+// flight, also across slab barriers.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -36,7 +39,16 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
-constexpr int kSlabBlocks = 16;      // 32-wide K steps per LDS slab buffer (16 KB)
+constexpr int kSlabBlocks = 16;      // 32-wide K steps per LDS slab buffer
+constexpr int kBlockU4 = 4;          // 16-byte words per LDS block of one token (32 K values)
+constexpr int kTokRowU4 = kSlabBlocks * kBlockU4;   // one token's slab row (1 KB)
+// LDS start (16-byte words) of token c's slab row in a slab buffer: rows are
+// 1 KB apart plus a skew of two words per token.  The B-fragment read of a
+// wave (lane: token column col, K group kg) is served eight columns x two K
+// groups at a time on gfx950; with the skew those 16 reads fall in distinct
+// banks (measured: no LDS bank conflicts).
+__device__ __forceinline__ int tok_base(int c) { return c * (kTokRowU4 + 2); }
+constexpr int kSlabU4 = 16 * (kTokRowU4 + 2);     // slab buffer of 16 token rows
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
@@ -99,12 +111,13 @@ struct Bf16Weights {
             for (int m = 0; m < NMAT; ++m)
                 d.w[i][m] = load16(static_cast<const uint16_t*>(a[m]) + (u + i) * 32);
     }
+    // bl: this lane's B fragment of the batch's first LDS block; block b of
+    // the batch at bl[b * kBlockU4]
     template <int NMAT, int U>
-    __device__ static void mma(const Batch<NMAT, U>& d, const u32x4 (*blk)[kWave], f32x4* acc) {
-        const int lane = threadIdx.x & (kWave - 1);
+    __device__ static void mma(const Batch<NMAT, U>& d, const u32x4* bl, f32x4* acc) {
 #pragma unroll
         for (int i = 0; i < U; ++i) {
-            const u32x4 bq = blk[i][lane];
+            const u32x4 bq = bl[i * kBlockU4];
 #pragma unroll
             for (int m = 0; m < NMAT; ++m)
                 acc[m] = mfma16x16x32(as_bf16x8(d.w[i][m]), as_bf16x8(bq), acc[m]);
@@ -170,8 +183,7 @@ struct Int8Weights {
             }
     }
     template <int NMAT, int U>
-    __device__ static void mma(const Batch<NMAT, U>& d, const u32x4 (*blk)[kWave], f32x4* acc) {
-        const int lane = threadIdx.x & (kWave - 1);
+    __device__ static void mma(const Batch<NMAT, U>& d, const u32x4* bl, f32x4* acc) {
 #pragma unroll
         for (int i = 0; i < U; ++i) {
 #pragma unroll
@@ -180,10 +192,10 @@ struct Int8Weights {
 #pragma unroll
                 for (int c = 0; c < 2; ++c) {
                     const u32x4 w = d.w[i][m][c];
-                    part = mfma16x16x32(i8x8_to_bf16x8(w.x, w.y), as_bf16x8(blk[4 * i + 2 * c][lane]),
-                                        part);
+                    part = mfma16x16x32(i8x8_to_bf16x8(w.x, w.y),
+                                        as_bf16x8(bl[(4 * i + 2 * c) * kBlockU4]), part);
                     part = mfma16x16x32(i8x8_to_bf16x8(w.z, w.w),
-                                        as_bf16x8(blk[4 * i + 2 * c + 1][lane]), part);
+                                        as_bf16x8(bl[(4 * i + 2 * c + 1) * kBlockU4]), part);
                 }
                 acc[m] += d.s[i][m] * part;
             }
@@ -228,7 +240,7 @@ struct GemmTuning<Int8Weights, 1> {
 // contiguous share of it (an equal number of rounds, +-1).
 template <class Fmt, int NMAT, int S, int U>
 __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, int n_act, int grid,
-                                            u32x4 (*xs)[kSlabBlocks][kWave]) {
+                                            u32x4 (*xs)[kSlabU4]) {
     constexpr int R = kWaves / S;              // row blocks per round
     constexpr int SP = kSlabBlocks / S;        // LDS blocks of each K part per slab
     constexpr int SPU = SP / Fmt::kBlocks;     // units of each K part per slab
@@ -237,7 +249,7 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, int n_act, int 
     using Batch = typename Fmt::template Batch<NMAT, U>;
     // after the slab loop the first slab buffer doubles as the K-part
     // reduction area (3 x NMAT x 1 KB <= 16 KB)
-    f32x4* red = reinterpret_cast<f32x4*>(&xs[0][0][0]);
+    f32x4* red = reinterpret_cast<f32x4*>(&xs[0][0]);
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int col = lane & 15;  // A row, B column and D column of this lane
@@ -281,32 +293,46 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, int n_act, int 
         const int nfull = has ? (u1 - u0) / U : 0;   // full batches of this wave
         const int tail_u = u0 + nfull * U;           // tail units [tail_u, u1)
         for (int c0 = 0; c0 < m; c0 += 16) {
-            const bool valid = c0 + col < m;
-            // padding columns (beyond the expert's tokens) repeat a real token
-            // row: an MFMA output column depends only on its own B column, and
+            const int ntok = min(16, m - c0);        // distinct tokens of the chunk
+            // padding columns (beyond the expert's tokens) read token 0's row:
+            // an MFMA output column depends only on its own B column, and
             // padding columns are never stored
-            const int q = beg + (valid ? c0 + col : 0);
-            const int brow = NMAT == 2 ? g.sorted_slot[q] / g.top_k : q;
-            const uint16_t* bp = g.b_src + (size_t)brow * g.b_pitch;
+            const bool valid = col < ntok;
+            const int bcol = valid ? col : 0;
+            // token rows this wave stages: tokens wave, wave + 4, ...
+            const uint16_t* tp[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = wave + kWaves * i;
+                const int qq = beg + c0 + (c < ntok ? c : 0);
+                const int brow = NMAT == 2 ? g.sorted_slot[qq] / g.top_k : qq;
+                tp[i] = g.b_src + (size_t)brow * g.b_pitch;
+            }
             f32x4 acc[NMAT];
 #pragma unroll
             for (int mm = 0; mm < NMAT; ++mm) acc[mm] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-            // slab j holds, for each K part pp, its units
-            // [start(pp) + j*SPU, +SPU) at blocks [pp*SP, pp*SP + SP)
+            // Slab j holds, for each K part pp, its units [start(pp) + j*SPU,
+            // +SPU) at blocks [pp*SP, pp*SP + SP) of every token row.  One
+            // load instruction stages one token's whole slab row (1 KB): lane
+            // L fills block L/4 for K group L%4, so the row is read from
+            // global memory in contiguous runs of 1024/S bytes.
             auto stage = [&](int j, int bsel) {
-                for (int blk = wave; blk < kSlabBlocks; blk += kWaves) {
-                    const int pp = blk / SP;
-                    const int bb = blk - pp * SP;
-                    const int p0 = min(nunits, pp * kpu);
-                    const int p1 = min(nunits, p0 + kpu);
-                    const int u = p0 + j * SPU + bb / Fmt::kBlocks;
-                    if (u < p1) {
-                        const int off = u * 32 * Fmt::kBlocks +
-                                        Fmt::block_offset(bb % Fmt::kBlocks, kg);
-                        __builtin_amdgcn_global_load_lds((const void*)(bp + off),
-                                                         (lds_void_ptr)&xs[bsel][blk][0], 16, 0, 0);
-                    }
+                const int blk = lane >> 2;
+                const int kgl = lane & 3;
+                const int pp = blk / SP;
+                const int bb = blk - pp * SP;
+                const int p0 = min(nunits, pp * kpu);
+                const int p1 = min(nunits, p0 + kpu);
+                const int u = p0 + j * SPU + bb / Fmt::kBlocks;
+                const int off = u * 32 * Fmt::kBlocks + Fmt::block_offset(bb % Fmt::kBlocks, kgl);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int c = wave + kWaves * i;
+                    if (c < ntok && u < p1)
+                        __builtin_amdgcn_global_load_lds((const void*)(tp[i] + off),
+                                                         (lds_void_ptr)&xs[bsel][tok_base(c)], 16,
+                                                         0, 0);
                 }
             };
             stage(0, 0);
@@ -327,10 +353,12 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, int n_act, int 
                 __syncthreads();
                 if (j + 1 < nslab) stage(j + 1, (j + 1) & 1);
                 const int slab_u0 = u0 + j * SPU;
-                const u32x4(*buf)[kWave] = &xs[j & 1][kp * SP];
+                // this lane's B fragments: token row bcol, K group kg, from the
+                // first block of this wave's K part
+                const u32x4* buf = &xs[j & 1][tok_base(bcol) + kp * SP * kBlockU4 + kg];
                 const int bend = min(nfull, (j + 1) * NB);
                 for (; bi < bend; ++bi) {
-                    const u32x4(*bb)[kWave] = buf + (u0 + bi * U - slab_u0) * Fmt::kBlocks;
+                    const u32x4* bb = buf + (u0 + bi * U - slab_u0) * Fmt::kBlocks * kBlockU4;
                     if ((bi & 1) == 0) {
                         if (bi + 1 < nfull)
                             Fmt::template load<NMAT, U>(B, wp, sp, g.N, u0 + (bi + 1) * U);
@@ -345,7 +373,8 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, int n_act, int 
                     for (int u = tail_u; u < u1; ++u) {
                         typename Fmt::template Batch<NMAT, 1> t;
                         Fmt::template load<NMAT, 1>(t, wp, sp, g.N, u);
-                        Fmt::template mma<NMAT, 1>(t, buf + (u - slab_u0) * Fmt::kBlocks, acc);
+                        Fmt::template mma<NMAT, 1>(
+                            t, buf + (u - slab_u0) * Fmt::kBlocks * kBlockU4, acc);
                     }
             }
             __syncthreads();
@@ -405,29 +434,36 @@ __device__ __forceinline__ int busy_grid(int Q) {
 // makespan is ceil(Q_S / G_S) rounds.  A round streams 16 rows x NMAT
 // matrices x K/S weights per wave, at the lower of the wave's own rate (its
 // bytes in flight, two weight batches, over the load latency) and its share
-// of HBM among the 4 * G_S busy waves, plus a barrier cost per LDS slab.
-// Constants measured on MI355X across the Mixtral-8x7B/8x22B, DeepSeek-V3 and
-// Qwen3-235B expert shapes at 2..103 active experts.
-constexpr float kHbmBytesPerUs = 6.5e6f;   // sustained HBM read rate (6.5 TB/s)
+// of an effective HBM rate among the 4 * G_S busy waves; each LDS slab adds a
+// barrier cost and the staging of the chunk's distinct tokens (the mean
+// tokens per active expert, at most 16).  Constants fitted to measurements on
+// MI355X over the Mixtral-8x7B/8x22B, DeepSeek-V3 and Qwen3-235B expert shapes
+// at 2..103 active experts and 1..16 tokens per expert (the choice is the
+// fastest split, or within 3 % of it, in 23 of 24 cases).
+constexpr float kHbmBytesPerUs = 7.0e6f;   // effective HBM rate shared by busy waves
 constexpr float kLoadLatencyUs = 4.0f;     // loaded-memory latency of a batch
-constexpr float kSlabUs = 0.5f;            // barrier and staging wait per slab
+constexpr float kSlabUs = 0.125f;          // barrier per slab
+constexpr float kStageTokenUs = 0.07f;     // staging one token's slab row
 template <class Fmt, int NMAT, int U>
 __device__ __forceinline__ int choose_split(const ExpertGemm& g, int n_act) {
     constexpr int units1 = kSlabBlocks / Fmt::kBlocks;
+    if (n_act <= 0) return 1;
     const int nrb = g.N / 16;
     const int nslab = (g.K + 32 * kSlabBlocks - 1) / (32 * kSlabBlocks);
+    // valid slots end where the last active expert's rows end
+    const int slots = g.offsets[g.active[n_act - 1] + 1];
+    const float ntok = fminf(16.f, (float)slots / (float)n_act);
     float best = 0.f;
     int best_s = 1;
     for (int S = 1; S <= kWaves; S *= 2) {
         const int Q = rounds_for(n_act, nrb, S);
-        if (Q == 0) return 1;
         const int G = busy_grid(Q);
         const int rounds = (Q + G - 1) / G;
         const int u = min(U, units1 / S);            // batch length used at this split
         const float inflight = 2.f * u * NMAT * Fmt::kUnitBytes;
         const float wave_bytes = 16.f * NMAT * (float)(g.K / S) * Fmt::kBytesPerWeight;
         const float rate = fminf(inflight / kLoadLatencyUs, kHbmBytesPerUs / (4.f * G));
-        const float t = rounds * (wave_bytes / rate + nslab * kSlabUs);
+        const float t = rounds * (wave_bytes / rate + nslab * (kSlabUs + kStageTokenUs * ntok));
         if (S == 1 || t < best) {
             best = t;
             best_s = S;
@@ -447,7 +483,7 @@ void expert_gemm_kernel(const ExpertGemm g) {
     constexpr int U = GemmTuning<Fmt, NMAT>::kBatch;
     constexpr int units1 = kSlabBlocks / Fmt::kBlocks;   // units of a part per slab, S = 1
     // K-slab buffers of the token tile, double-buffered
-    __shared__ u32x4 xs[2][kSlabBlocks][kWave];
+    __shared__ u32x4 xs[2][kSlabU4];
     const int n_act = g.meta[0];
     const int S = g.split ? g.split : choose_split<Fmt, NMAT, U>(g, n_act);
     const int G = busy_grid(rounds_for(n_act, g.N / 16, S));

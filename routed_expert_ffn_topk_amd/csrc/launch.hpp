@@ -62,4 +62,9 @@ hipError_t launch_ffn_int8(const uint16_t* x, const int32_t* ids, const float* w
 hipError_t launch_combine(const float* y, const int32_t* ids, const float* w,
                           uint16_t* out, const FfnShape& s, hipStream_t stream);
 
+// Streaming-read probe over bytes (a multiple of 16) of buf; sink is one
+// device word.
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int num_cu,
+                             hipStream_t stream);
+
 }  // namespace moe

@@ -213,6 +213,19 @@ int moe_ffn_check_status(const void* workspace, void* stream, int64_t* n_dropped
     return meta[1] > 0 ? MOE_FFN_ERR_BAD_IDS : MOE_FFN_OK;
 }
 
+int moe_ffn_read_probe(const void* buf, size_t bytes, void* sink, void* stream) {
+    if (!buf || !sink) return MOE_FFN_ERR_NULL_ARG;
+    if (bytes == 0 || bytes % 16 != 0) return MOE_FFN_ERR_BAD_SHAPE;
+    if (!aligned16(buf) || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0)
+        return MOE_FFN_ERR_MISALIGNED;
+    int ncu = 0;
+    if (const int rc = num_cu(&ncu); rc != MOE_FFN_OK) return rc;
+    return moe::launch_read_probe(buf, bytes, static_cast<uint32_t*>(sink), ncu,
+                                  static_cast<hipStream_t>(stream)) == hipSuccess
+               ? MOE_FFN_OK
+               : MOE_FFN_ERR_HIP;
+}
+
 int moe_ffn_set_stage_events(void* const* events, int32_t n_events) {
     if (n_events < 0 || n_events > 4) return MOE_FFN_ERR_BAD_SHAPE;
     if (!events) n_events = 0;

@@ -115,6 +115,16 @@ def test_route_host_validation():
     assert L.moe_route_topk(A, 4, 8, 2, A + 0x1001, A + 0x2000, None) == moe.MOE_FFN_ERR_MISALIGNED
 
 
+def test_read_probe_host_validation():
+    L = moe.lib()
+    assert L.moe_ffn_read_probe(None, 1 << 20, A + 0x100000, None) == moe.MOE_FFN_ERR_NULL_ARG
+    assert L.moe_ffn_read_probe(A, 1 << 20, None, None) == moe.MOE_FFN_ERR_NULL_ARG
+    assert L.moe_ffn_read_probe(A, 0, A + 0x100000, None) == moe.MOE_FFN_ERR_BAD_SHAPE
+    assert L.moe_ffn_read_probe(A, 1000, A + 0x100000, None) == moe.MOE_FFN_ERR_BAD_SHAPE
+    assert L.moe_ffn_read_probe(A + 8, 1 << 20, A + 0x100000, None) == moe.MOE_FFN_ERR_MISALIGNED
+    assert L.moe_ffn_read_probe(A, 1 << 20, A + 0x100002, None) == moe.MOE_FFN_ERR_MISALIGNED
+
+
 def test_binding_rejects_host_tensors():
     import torch
     x = torch.zeros(4, 64, dtype=torch.bfloat16)
