@@ -155,15 +155,19 @@ int moe_ffn_forward(const void* x, const int32_t* topk_ids, const float* topk_w,
  * consecutive output rows:
  *   Q_gate, Q_up [E][I][H] int8 with S_gate, S_up [E][H/128][I] float32;
  *   Q_down [E][H][I] int8 with S_down [E][I/128][H] float32.
- * Sizes: H and I multiples of 128.  Scale pointers must be 16-byte aligned.
+ * `group` is the scale group length along K; this library implements
+ * group = MOE_FFN_INT8_GROUP (128) and returns MOE_FFN_ERR_BAD_SHAPE for any
+ * other value.  Sizes: H and I multiples of 128.  Scale pointers must be
+ * 16-byte aligned.
  */
 int moe_ffn_forward_int8(const void* x, const int32_t* topk_ids,
                          const float* topk_w, const int8_t* Q_gate,
                          const float* S_gate, const int8_t* Q_up,
                          const float* S_up, const int8_t* Q_down,
-                         const float* S_down, void* out, int64_t T, int64_t H,
-                         int64_t I, int32_t E, int32_t top_k, void* workspace,
-                         size_t workspace_bytes, void* stream);
+                         const float* S_down, int32_t group, void* out,
+                         int64_t T, int64_t H, int64_t I, int32_t E,
+                         int32_t top_k, void* workspace, size_t workspace_bytes,
+                         void* stream);
 
 /* Wait for `stream`, then read the workspace meta written by the last forward
  * call: MOE_FFN_ERR_BAD_IDS if it dropped slots with out-of-range ids,

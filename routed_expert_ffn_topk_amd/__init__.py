@@ -64,8 +64,8 @@ def lib() -> ctypes.CDLL:
         L.moe_ffn_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
                                       _i32, _i32, _vp, _sz, _vp]
         L.moe_ffn_forward_int8.restype = _c.c_int
-        L.moe_ffn_forward_int8.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                           _i64, _i64, _i64, _i32, _i32, _vp, _sz, _vp]
+        L.moe_ffn_forward_int8.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+                                           _vp, _i64, _i64, _i64, _i32, _i32, _vp, _sz, _vp]
         L.moe_ffn_check_status.restype = _c.c_int
         L.moe_ffn_check_status.argtypes = [_vp, _vp, _c.POINTER(_i64)]
         L.moe_ffn_status_string.restype = _c.c_char_p
@@ -190,7 +190,7 @@ def moe_ffn_forward_int8(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.
         _dev(topk_w, "topk_w", torch.float32), _dev(Q_gate, "Q_gate", torch.int8),
         _dev(S_gate, "S_gate", torch.float32), _dev(Q_up, "Q_up", torch.int8),
         _dev(S_up, "S_up", torch.float32), _dev(Q_down, "Q_down", torch.int8),
-        _dev(S_down, "S_down", torch.float32), _dev(out, "out", torch.bfloat16),
+        _dev(S_down, "S_down", torch.float32), G, _dev(out, "out", torch.bfloat16),
         T, H, I, E, top_k, _dev(workspace, "workspace", torch.uint8), workspace.numel(),
         _stream(stream)))
     return out

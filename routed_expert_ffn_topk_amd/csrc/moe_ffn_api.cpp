@@ -181,9 +181,10 @@ int moe_ffn_forward(const void* x, const int32_t* topk_ids, const float* topk_w,
 int moe_ffn_forward_int8(const void* x, const int32_t* topk_ids, const float* topk_w,
                          const int8_t* Q_gate, const float* S_gate, const int8_t* Q_up,
                          const float* S_up, const int8_t* Q_down, const float* S_down,
-                         void* out, int64_t T, int64_t H, int64_t I, int32_t E,
-                         int32_t top_k, void* workspace, size_t workspace_bytes,
+                         int32_t group, void* out, int64_t T, int64_t H, int64_t I,
+                         int32_t E, int32_t top_k, void* workspace, size_t workspace_bytes,
                          void* stream) {
+    if (group != MOE_FFN_INT8_GROUP) return MOE_FFN_ERR_BAD_SHAPE;
     moe_ffn_ws_layout L;
     int rc = check_forward(x, topk_ids, topk_w, out, T, H, I, E, top_k, workspace,
                            workspace_bytes, MOE_FFN_INT8_GROUP, &L);

@@ -96,13 +96,23 @@ def test_forward_host_validation():
 def test_forward_int8_requires_group_multiples():
     L = moe.lib()
     rc = L.moe_ffn_forward_int8(A, A + 0x100000, A + 0x200000, A + 0x1000000, A + 0x1800000,
-                                A + 0x2000000, A + 0x2800000, A + 0x3000000, A + 0x3800000,
+                                A + 0x2000000, A + 0x2800000, A + 0x3000000, A + 0x3800000, 128,
                                 A + 0x300000, 4, 96, 256, 8, 2, A + 0x4000000, 1 << 30, None)
     assert rc == moe.MOE_FFN_ERR_BAD_SHAPE
     rc = L.moe_ffn_forward_int8(A, A + 0x100000, A + 0x200000, A + 0x1000000, None,
-                                A + 0x2000000, A + 0x2800000, A + 0x3000000, A + 0x3800000,
+                                A + 0x2000000, A + 0x2800000, A + 0x3000000, A + 0x3800000, 128,
                                 A + 0x300000, 4, 128, 256, 8, 2, A + 0x4000000, 1 << 30, None)
     assert rc == moe.MOE_FFN_ERR_NULL_ARG
+
+
+@pytest.mark.parametrize("group", [0, 64, 256, -128])
+def test_forward_int8_rejects_other_groups(group):
+    L = moe.lib()
+    rc = L.moe_ffn_forward_int8(A, A + 0x100000, A + 0x200000, A + 0x1000000, A + 0x1800000,
+                                A + 0x2000000, A + 0x2800000, A + 0x3000000, A + 0x3800000,
+                                group, A + 0x300000, 4, 128, 256, 8, 2, A + 0x4000000, 1 << 30,
+                                None)
+    assert rc == moe.MOE_FFN_ERR_BAD_SHAPE
 
 
 def test_route_host_validation():
