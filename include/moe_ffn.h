@@ -191,6 +191,16 @@ const char* moe_ffn_status_string(int status);
 int moe_ffn_set_stage_events(void* const* events, int32_t n_events);
 
 /*
+ * Test hook: force the number of K parts per row block of the gate/up and of
+ * the down product (1, 2 or 4) for the forward calls (either weight format)
+ * made by the calling host thread from now on; 0 restores the choice the
+ * kernels make on the device from the active-expert count.  The result of a
+ * call does not depend on the split beyond FP32 summation order.  Returns
+ * MOE_FFN_OK, or MOE_FFN_ERR_BAD_SHAPE for a value outside {0, 1, 2, 4}.
+ */
+int moe_ffn_set_split(int32_t gate_up_split, int32_t down_split);
+
+/*
  * Measurement helper: the HBM streaming-read ceiling that the expert
  * products are compared against (the GPU counterpart of the STREAM bandwidth
  * the HiNa-MoE evaluation reports for its CPUs, Table 2).  Enqueues on

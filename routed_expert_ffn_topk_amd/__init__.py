@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
         L.moe_ffn_status_string.argtypes = [_c.c_int]
         L.moe_ffn_set_stage_events.restype = _c.c_int
         L.moe_ffn_set_stage_events.argtypes = [_c.POINTER(_vp), _i32]
+        L.moe_ffn_set_split.restype = _c.c_int
+        L.moe_ffn_set_split.argtypes = [_i32, _i32]
         L.moe_ffn_read_probe.restype = _c.c_int
         L.moe_ffn_read_probe.argtypes = [_vp, _sz, _vp, _vp]
         _lib = L
@@ -202,6 +204,13 @@ def moe_ffn_check_status(workspace: torch.Tensor, stream=None) -> Tuple[int, int
     code = lib().moe_ffn_check_status(_dev(workspace, "workspace", torch.uint8),
                                       _stream(stream), _c.byref(n))
     return code, int(n.value)
+
+
+def moe_ffn_set_split(gate_up: int = 0, down: int = 0) -> None:
+    """Test hook: force the K parts per row block (1, 2 or 4) of the gate/up
+    and down products for this thread's later calls; 0 = chosen on the
+    device."""
+    _check("moe_ffn_set_split", lib().moe_ffn_set_split(gate_up, down))
 
 
 def moe_ffn_read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:

@@ -553,7 +553,7 @@ template <class Fmt>
 hipError_t launch_ffn(const uint16_t* x, const int32_t* ids, const float* w,
                       const FfnWeights& W, uint16_t* out, const FfnShape& s,
                       const Workspace& ws, int num_cu, const StageEvents& ev,
-                      hipStream_t stream) {
+                      const SplitOverride& split, hipStream_t stream) {
     hipError_t err = launch_permute(ids, s, ws, stream);
     if (err == hipSuccess) err = ev.mark(0, stream);
     if (err != hipSuccess) return err;
@@ -576,6 +576,7 @@ hipError_t launch_ffn(const uint16_t* x, const int32_t* ids, const float* w,
     gu.N = s.I;
     gu.K = s.H;
     gu.top_k = s.k;
+    gu.split = split.gate_up;
     err = launch_gemm<Fmt, 2>(gu, max_active, num_cu, stream);
     if (err == hipSuccess) err = ev.mark(1, stream);
     if (err != hipSuccess) return err;
@@ -591,6 +592,7 @@ hipError_t launch_ffn(const uint16_t* x, const int32_t* ids, const float* w,
     dn.b_pitch = s.I;
     dn.N = s.H;
     dn.K = s.I;
+    dn.split = split.down;
     err = launch_gemm<Fmt, 1>(dn, max_active, num_cu, stream);
     if (err == hipSuccess) err = ev.mark(2, stream);
     if (err != hipSuccess) return err;
@@ -613,15 +615,15 @@ hipError_t launch_combine(const float* y, const int32_t* ids, const float* w,
 hipError_t launch_ffn_bf16(const uint16_t* x, const int32_t* ids, const float* w,
                            const FfnWeights& W, uint16_t* out, const FfnShape& s,
                            const Workspace& ws, int num_cu, const StageEvents& ev,
-                           hipStream_t stream) {
-    return launch_ffn<Bf16Weights>(x, ids, w, W, out, s, ws, num_cu, ev, stream);
+                           const SplitOverride& split, hipStream_t stream) {
+    return launch_ffn<Bf16Weights>(x, ids, w, W, out, s, ws, num_cu, ev, split, stream);
 }
 
 hipError_t launch_ffn_int8(const uint16_t* x, const int32_t* ids, const float* w,
                            const FfnWeights& W, uint16_t* out, const FfnShape& s,
                            const Workspace& ws, int num_cu, const StageEvents& ev,
-                           hipStream_t stream) {
-    return launch_ffn<Int8Weights>(x, ids, w, W, out, s, ws, num_cu, ev, stream);
+                           const SplitOverride& split, hipStream_t stream) {
+    return launch_ffn<Int8Weights>(x, ids, w, W, out, s, ws, num_cu, ev, split, stream);
 }
 
 }  // namespace moe

@@ -28,6 +28,13 @@ struct StageEvents {
     }
 };
 
+// K parts per row block forced on the two grouped products (0: chosen on the
+// device from the active-expert count); a test hook.
+struct SplitOverride {
+    int gate_up = 0;
+    int down = 0;
+};
+
 struct FfnShape {
     int T, H, I, E, k;
 };
@@ -51,12 +58,12 @@ hipError_t launch_permute(const int32_t* ids, const FfnShape& s, const Workspace
 hipError_t launch_ffn_bf16(const uint16_t* x, const int32_t* ids, const float* w,
                            const FfnWeights& W, uint16_t* out, const FfnShape& s,
                            const Workspace& ws, int num_cu, const StageEvents& ev,
-                           hipStream_t stream);
+                           const SplitOverride& split, hipStream_t stream);
 
 hipError_t launch_ffn_int8(const uint16_t* x, const int32_t* ids, const float* w,
                            const FfnWeights& W, uint16_t* out, const FfnShape& s,
                            const Workspace& ws, int num_cu, const StageEvents& ev,
-                           hipStream_t stream);
+                           const SplitOverride& split, hipStream_t stream);
 
 // Weighted combine shared by both weight formats.
 hipError_t launch_combine(const float* y, const int32_t* ids, const float* w,

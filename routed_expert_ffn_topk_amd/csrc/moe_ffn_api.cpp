@@ -39,6 +39,9 @@ std::atomic<int> g_num_cu[kMaxDevices];
 // call of this thread.
 thread_local moe::StageEvents t_stage_events = {{nullptr, nullptr, nullptr, nullptr}, 0};
 
+// Test hook (moe_ffn_set_split): K splits forced on this thread's calls.
+thread_local moe::SplitOverride t_split;
+
 moe::StageEvents take_stage_events() {
     const moe::StageEvents ev = t_stage_events;
     t_stage_events.n = 0;
@@ -174,7 +177,7 @@ int moe_ffn_forward(const void* x, const int32_t* topk_ids, const float* topk_w,
     const moe::FfnWeights W{W_gate, W_up, W_down, nullptr, nullptr, nullptr};
     const hipError_t err = moe::launch_ffn_bf16(
         static_cast<const uint16_t*>(x), topk_ids, topk_w, W, static_cast<uint16_t*>(out), s,
-        carve(workspace, L), ncu, take_stage_events(), static_cast<hipStream_t>(stream));
+        carve(workspace, L), ncu, take_stage_events(), t_split, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? MOE_FFN_OK : MOE_FFN_ERR_HIP;
 }
 
@@ -199,7 +202,7 @@ int moe_ffn_forward_int8(const void* x, const int32_t* topk_ids, const float* to
     const moe::FfnWeights W{Q_gate, Q_up, Q_down, S_gate, S_up, S_down};
     const hipError_t err = moe::launch_ffn_int8(
         static_cast<const uint16_t*>(x), topk_ids, topk_w, W, static_cast<uint16_t*>(out), s,
-        carve(workspace, L), ncu, take_stage_events(), static_cast<hipStream_t>(stream));
+        carve(workspace, L), ncu, take_stage_events(), t_split, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? MOE_FFN_OK : MOE_FFN_ERR_HIP;
 }
 
@@ -225,6 +228,14 @@ int moe_ffn_read_probe(const void* buf, size_t bytes, void* sink, void* stream) 
                                   static_cast<hipStream_t>(stream)) == hipSuccess
                ? MOE_FFN_OK
                : MOE_FFN_ERR_HIP;
+}
+
+int moe_ffn_set_split(int32_t gate_up_split, int32_t down_split) {
+    auto ok = [](int32_t v) { return v == 0 || v == 1 || v == 2 || v == 4; };
+    if (!ok(gate_up_split) || !ok(down_split)) return MOE_FFN_ERR_BAD_SHAPE;
+    t_split.gate_up = gate_up_split;
+    t_split.down = down_split;
+    return MOE_FFN_OK;
 }
 
 int moe_ffn_set_stage_events(void* const* events, int32_t n_events) {

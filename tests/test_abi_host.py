@@ -135,6 +135,16 @@ def test_read_probe_host_validation():
     assert L.moe_ffn_read_probe(A, 1 << 20, A + 0x100002, None) == moe.MOE_FFN_ERR_MISALIGNED
 
 
+def test_set_split_validation():
+    L = moe.lib()
+    for v in (0, 1, 2, 4):
+        assert L.moe_ffn_set_split(v, v) == moe.MOE_FFN_OK
+    for bad in (3, 8, -1):
+        assert L.moe_ffn_set_split(bad, 0) == moe.MOE_FFN_ERR_BAD_SHAPE
+        assert L.moe_ffn_set_split(0, bad) == moe.MOE_FFN_ERR_BAD_SHAPE
+    assert L.moe_ffn_set_split(0, 0) == moe.MOE_FFN_OK
+
+
 def test_binding_rejects_host_tensors():
     import torch
     x = torch.zeros(4, 64, dtype=torch.bfloat16)
