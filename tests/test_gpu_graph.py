@@ -1,0 +1,91 @@
+"""The layer captured in a HIP graph: every replay equals the eager result bit
+for bit (the forward call enqueues kernels only, with no memset or host
+synchronisation, so it can be captured; the gather index and the round
+split are recomputed on the device at every replay)."""
+import numpy as np
+import pytest
+import torch
+
+import routed_expert_ffn_topk_amd as moe
+import workloads
+from moe_cases import need_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _replays_match(call, outs, other_call, n_replays=3):
+    # the inputs were produced on the default stream; the side stream does
+    # not wait for it by itself
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    torch.cuda.synchronize()
+    for r in range(n_replays):
+        for o in outs:
+            o.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, ref_o in zip(outs, ref):
+            assert torch.equal(o, ref_o), f"replay {r} differs from the eager result"
+        other_call()                 # eager work between replays
+        torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen3_235b_t4", "mixtral8x7b_m16"])
+def test_bf16_layer_graph_replays_match_eager(name):
+    need_gpu()
+    say(f"graph replay bf16 {name}")
+    wl = workloads.WORKLOADS[name]
+    x = workloads.gen_x(wl).cuda()
+    ids, w = moe.moe_route_topk(workloads.gen_logits(wl).cuda(), wl.k)
+    W = workloads.gen_weights(wl, "cuda")
+    ws = moe.alloc_workspace(wl.T, wl.H, wl.I, wl.E, wl.k)
+    out = torch.empty_like(x)
+    # the eager work between replays reuses the workspace with other routing
+    ids2 = torch.roll(ids, 1, dims=0)
+
+    def call():
+        moe.moe_ffn_forward(x, ids, w, *W, out=out, workspace=ws,
+                            stream=torch.cuda.current_stream())
+
+    def other():
+        moe.moe_ffn_forward(x, ids2, w, *W, workspace=ws)
+
+    _replays_match(call, [out], other)
+    del W
+    torch.cuda.empty_cache()
+
+
+def test_int8_layer_graph_replays_match_eager():
+    need_gpu()
+    say("graph replay int8")
+    rng = np.random.default_rng(5)
+    T, H, I, E, k = 16, 512, 384, 8, 2
+    x = workloads.bits_to_bf16(workloads.bf16_bits(
+        torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(torch.bfloat16))).cuda()
+    gm = workloads.scales_group_major
+    Q = []
+    for N, K in ((I, H), (I, H), (H, I)):
+        q, sc = workloads.quantize_groupwise(
+            torch.from_numpy((rng.standard_normal((E, N, K)) * 0.05).astype(np.float32)))
+        Q += [q.cuda(), gm(sc).cuda()]
+    ids = torch.from_numpy(np.stack([rng.choice(E, size=k, replace=False)
+                                     for _ in range(T)]).astype(np.int32)).cuda()
+    w = torch.from_numpy(rng.uniform(0.05, 1.0, size=(T, k)).astype(np.float32)).cuda()
+    ws = moe.alloc_workspace(T, H, I, E, k)
+    out = torch.empty_like(x)
+
+    def call():
+        moe.moe_ffn_forward_int8(x, ids, w, *Q, out=out, workspace=ws,
+                                 stream=torch.cuda.current_stream())
+
+    def other():
+        moe.moe_ffn_forward_int8(x, torch.flip(ids, dims=[1]).contiguous(), w, *Q, workspace=ws)
+
+    _replays_match(call, [out], other)
