@@ -20,7 +20,7 @@
 // round is R row blocks of one expert.  S is chosen on the device from the
 // actual number of active experts, so that the rounds fill the persistent
 // grid evenly.  Each XCD owns a contiguous slice of the expert-major round
-// list, and each workgroup a balanced contiguous share of that slice.
+// list, and its workgroups take the slice's rounds interleaved.
 //
 // B operand (the gathered tokens, i.e. the pages' matrix I): the workgroup
 // stages K-slabs of the 16-token tile in LDS, which all its waves share,
@@ -235,9 +235,9 @@ struct GemmTuning<Int8Weights, 1> {
 // A round is R row blocks of one expert (R = 4 / S), processed by the four
 // waves together: they share the LDS token slabs, and the S K parts of a row
 // block are summed in LDS.  Rounds never straddle two experts.  The rounds of
-// all active experts (expert-major) are dealt out in balanced contiguous
-// ranges: each XCD owns a contiguous slice, each workgroup of the XCD a
-// contiguous share of it (an equal number of rounds, +-1).
+// all active experts (expert-major) are dealt out per XCD: each XCD owns a
+// contiguous slice, and its workgroups take the slice's rounds interleaved
+// (an equal number each, +-1).
 template <class Fmt, int NMAT, int S, int U>
 __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, int n_act, int grid,
                                             u32x4 (*xs)[kSlabU4]) {
@@ -265,16 +265,18 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, int n_act, int 
     const int u1 = min(nunits, u0 + kpu);
     const int nslab = (kpu + SPU - 1) / SPU;
 
-    // this workgroup's rounds: a balanced share of its XCD's slice
+    // this workgroup's rounds: every per-th round of its XCD's slice, from
+    // its index li in the XCD.  The XCD's workgroups work on neighbouring
+    // rounds at any moment, and each takes a mix of the experts of the slice
+    // (rounds of experts with more tokens cost more); measured 1-8 % faster
+    // than giving each workgroup a contiguous range.
     const int xcd = blockIdx.x % kXcds;
     const int per = grid / kXcds;
     const int li = blockIdx.x / kXcds;
     const int qb = (int)((long long)xcd * Q / kXcds);
-    const int nq = (int)((long long)(xcd + 1) * Q / kXcds) - qb;
-    const int q0 = qb + (int)((long long)li * nq / per);
-    const int q1 = qb + (int)((long long)(li + 1) * nq / per);
+    const int qe = (int)((long long)(xcd + 1) * Q / kXcds);
 
-    for (int q = q0; q < q1; ++q) {
+    for (int q = qb + li; q < qe; q += per) {
         const int a = q / rpe;                   // active expert of the round
         const int rb0 = (q - a * rpe) * R;       // its first row block
         const int e = g.active[a];
@@ -435,24 +437,20 @@ __device__ __forceinline__ int busy_grid(int Q) {
 // matrices x K/S weights per wave, at the lower of the wave's own rate (its
 // bytes in flight, two weight batches, over the load latency) and its share
 // of an effective HBM rate among the 4 * G_S busy waves; each LDS slab adds a
-// barrier cost and the staging of the chunk's distinct tokens (the mean
-// tokens per active expert, at most 16).  Constants fitted to measurements on
-// MI355X over the Mixtral-8x7B/8x22B, DeepSeek-V3 and Qwen3-235B expert shapes
-// at 2..103 active experts and 1..16 tokens per expert (the choice is the
-// fastest split, or within 3 % of it, in 23 of 24 cases).
-constexpr float kHbmBytesPerUs = 7.0e6f;   // effective HBM rate shared by busy waves
+// fixed cost (barrier, staging wait).  Constants fitted to forced-split
+// measurements on MI355X over the Mixtral-8x7B/8x22B, DeepSeek-V3 and
+// Qwen3-235B expert shapes at 2..103 active experts and 1..16 tokens per
+// expert (the choice costs 0.8 % on average against the fastest split, at
+// most 4.4 %).
+constexpr float kHbmBytesPerUs = 8.0e6f;   // effective HBM rate shared by busy waves
 constexpr float kLoadLatencyUs = 4.0f;     // loaded-memory latency of a batch
-constexpr float kSlabUs = 0.125f;          // barrier per slab
-constexpr float kStageTokenUs = 0.07f;     // staging one token's slab row
+constexpr float kSlabUs = 1.0f;            // fixed cost per slab
 template <class Fmt, int NMAT, int U>
 __device__ __forceinline__ int choose_split(const ExpertGemm& g, int n_act) {
     constexpr int units1 = kSlabBlocks / Fmt::kBlocks;
     if (n_act <= 0) return 1;
     const int nrb = g.N / 16;
     const int nslab = (g.K + 32 * kSlabBlocks - 1) / (32 * kSlabBlocks);
-    // valid slots end where the last active expert's rows end
-    const int slots = g.offsets[g.active[n_act - 1] + 1];
-    const float ntok = fminf(16.f, (float)slots / (float)n_act);
     float best = 0.f;
     int best_s = 1;
     for (int S = 1; S <= kWaves; S *= 2) {
@@ -463,7 +461,7 @@ __device__ __forceinline__ int choose_split(const ExpertGemm& g, int n_act) {
         const float inflight = 2.f * u * NMAT * Fmt::kUnitBytes;
         const float wave_bytes = 16.f * NMAT * (float)(g.K / S) * Fmt::kBytesPerWeight;
         const float rate = fminf(inflight / kLoadLatencyUs, kHbmBytesPerUs / (4.f * G));
-        const float t = rounds * (wave_bytes / rate + nslab * (kSlabUs + kStageTokenUs * ntok));
+        const float t = rounds * (wave_bytes / rate + nslab * kSlabUs);
         if (S == 1 || t < best) {
             best = t;
             best_s = S;
