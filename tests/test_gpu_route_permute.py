@@ -55,7 +55,11 @@ def test_route_empty_batch():
 
 @pytest.mark.parametrize("T,E,k,bad", [(16, 8, 2, 0), (16, 256, 8, 0), (40, 3, 2, 0),
                                        (300, 7, 3, 0), (16, 8, 2, 5), (1, 128, 8, 0),
-                                       (24, 1024, 4, 3)])
+                                       (24, 1024, 4, 3),
+                                       # one expert for every slot, two experts, all
+                                       # slots dropped, several chunks of 256 slots
+                                       (512, 1, 1, 0), (256, 2, 2, 0), (128, 64, 4, 7),
+                                       (171, 64, 3, 2), (4, 8, 2, 8)])
 def test_gather_index_matches_oracle(T, E, k, bad):
     need_gpu()
     rng = np.random.default_rng(T + 7 * E + bad)
