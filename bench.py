@@ -214,7 +214,8 @@ def main():
         lg = workloads.gen_logits(wl)
         ids, w = moe.moe_route_topk(lg.to(dev), wl.k)
         active = len(set(ids.cpu().reshape(-1).tolist()))
-        batches.append(dict(wl=wl, x_cpu=x, lg_cpu=lg, x=x.to(dev), ids=ids, w=w, active=active,
+        batches.append(dict(wl=wl, x_cpu=x, lg_cpu=lg, lg=lg.to(dev), x=x.to(dev), ids=ids, w=w,
+                            active=active,
                             out=torch.empty(wl.T, wl.H, dtype=torch.bfloat16, device=dev),
                             ws=moe.alloc_workspace(wl.T, wl.H, wl.I, wl.E, wl.k, dev)))
     # distinct weight sets so that one step streams at least ROTATE_BELOW bytes
@@ -278,6 +279,29 @@ def main():
             "GBps": round(lb / (us * 1e-6) / 1e9, 1),
             "pct_hbm_peak": round(100 * lb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
         }
+        if not int8:
+            # the same layer from router logits (router fused with the gather
+            # index); its ids / weights go to scratch tensors
+            rid = torch.empty_like(b["ids"])
+            rw = torch.empty_like(b["w"])
+            e0.record(stream)
+            for i in range(reps):
+                moe.moe_ffn_forward_logits(b["x"], b["lg"], b["wl"].k, *sets[i % n_sets],
+                                           out=b["out"], topk_ids=rid, topk_w=rw,
+                                           workspace=b["ws"], stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            per_layer[b["wl"].name]["us_from_logits"] = round(e0.elapsed_time(e1) * 1e3 / reps, 1)
+            # the same from two calls: the router, then the layer on its ids
+            e0.record(stream)
+            for i in range(reps):
+                moe.moe_route_topk(b["lg"], b["wl"].k, topk_ids=rid, topk_w=rw, stream=stream)
+                layer_ids = dict(b, ids=rid, w=rw)
+                layer(layer_ids, i % n_sets)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            per_layer[b["wl"].name]["us_route_then_layer"] = round(
+                e0.elapsed_time(e1) * 1e3 / reps, 1)
 
     # per-kernel durations from HIP events recorded on the launch stream
     # between the kernels of each call (stage 0 permute, 1 gate/up, 2 down,

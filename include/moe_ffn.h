@@ -144,6 +144,31 @@ int moe_ffn_forward(const void* x, const int32_t* topk_ids, const float* topk_w,
                     void* stream);
 
 /*
+ * Routed-expert FFN layer from router logits, BF16 weights: the top-k gate
+ * (HiNa-MoE §2.1 / Fig. 2) followed by the layer of moe_ffn_forward
+ * (§4.1 FFN equation), with the router and the per-expert gather index
+ * computed by one kernel for batches of up to 4096 slots (T*top_k), and by
+ * the router kernel of moe_route_topk followed by the gather-index kernel
+ * above that.
+ *   logits   [T][E] float32, device: router logits (each token needs at least
+ *            top_k finite values; NaN is not supported).
+ *   topk_ids [T][top_k] int32, device, written: as moe_route_topk.
+ *   topk_w   [T][top_k] float32, device, written: as moe_route_topk.
+ *   x, W_gate, W_up, W_down, out, workspace: as moe_ffn_forward; out equals
+ *            moe_ffn_forward(x, topk_ids, topk_w, ...) on the ids and weights
+ *            written here.
+ * Sizes as moe_ffn_forward, and top_k <= 64.  Errors: as moe_ffn_forward,
+ * plus MISALIGNED (logits, topk_ids or topk_w not 4-byte aligned) and ALIAS
+ * (topk_ids or topk_w overlap each other, logits, x, out or the workspace,
+ * or out overlaps logits).
+ */
+int moe_ffn_forward_logits(const void* x, const float* logits, int32_t* topk_ids,
+                           float* topk_w, const void* W_gate, const void* W_up,
+                           const void* W_down, void* out, int64_t T, int64_t H,
+                           int64_t I, int32_t E, int32_t top_k, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
  * Routed-expert FFN layer, INT8 weights with group scales (HiNa-MoE §8.1,
  * Fig. 11: symmetric group-wise INT8; group = MOE_FFN_INT8_GROUP along K).
  * As moe_ffn_forward, except every weight row r is int8 q[r][K] with one
@@ -182,8 +207,8 @@ const char* moe_ffn_status_string(int status);
  * Benchmark hook: per-kernel timing with HIP events.  After this call, the
  * next forward call made by the calling host thread (either weight format)
  * records events[i] on its stream right after enqueuing kernel i, for
- * i < n_events: 0 = gather index (permute), 1 = gate/up, 2 = down,
- * 3 = combine.  The events are hipEvent_t handles owned by the caller.  The
+ * i < n_events: 0 = gather index (permute; for moe_ffn_forward_logits the
+ * router and gather index), 1 = gate/up, 2 = down, 3 = combine.  The events are hipEvent_t handles owned by the caller.  The
  * setting is consumed by that one call; n_events = 0 (or events = NULL)
  * clears it.  Only the calling thread is affected.  Returns MOE_FFN_OK, or
  * MOE_FFN_ERR_BAD_SHAPE if n_events is outside [0, 4].

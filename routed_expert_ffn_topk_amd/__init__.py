@@ -63,6 +63,9 @@ def lib() -> ctypes.CDLL:
         L.moe_ffn_forward.restype = _c.c_int
         L.moe_ffn_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
                                       _i32, _i32, _vp, _sz, _vp]
+        L.moe_ffn_forward_logits.restype = _c.c_int
+        L.moe_ffn_forward_logits.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64,
+                                             _i64, _i32, _i32, _vp, _sz, _vp]
         L.moe_ffn_forward_int8.restype = _c.c_int
         L.moe_ffn_forward_int8.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                                            _vp, _i64, _i64, _i64, _i32, _i32, _vp, _sz, _vp]
@@ -160,6 +163,42 @@ def moe_ffn_forward(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tenso
         _dev(out, "out", torch.bfloat16), T, H, I, E, top_k,
         _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream)))
     return out
+
+
+def moe_ffn_forward_logits(x: torch.Tensor, logits: torch.Tensor, top_k: int,
+                           W_gate: torch.Tensor, W_up: torch.Tensor, W_down: torch.Tensor,
+                           out: Optional[torch.Tensor] = None,
+                           topk_ids: Optional[torch.Tensor] = None,
+                           topk_w: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None, stream=None
+                           ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Routed-expert FFN layer from router logits [T, E] float32 (BF16
+    weights); returns (out [T, H] bf16, topk_ids [T, k] int32, topk_w [T, k]
+    float32)."""
+    T, H = x.shape
+    E, I, H2 = W_gate.shape
+    if tuple(logits.shape) != (T, E):
+        raise ValueError(f"logits must be [T, E] = [{T}, {E}], got {list(logits.shape)}")
+    if H2 != H or tuple(W_up.shape) != (E, I, H) or tuple(W_down.shape) != (E, H, I):
+        raise ValueError("weight shapes must be W_gate/W_up [E,I,H], W_down [E,H,I]")
+    if out is None:
+        out = torch.empty_like(x)
+    if topk_ids is None:
+        topk_ids = torch.empty(T, top_k, dtype=torch.int32, device=x.device)
+    if topk_w is None:
+        topk_w = torch.empty(T, top_k, dtype=torch.float32, device=x.device)
+    if tuple(topk_ids.shape) != (T, top_k) or tuple(topk_w.shape) != (T, top_k):
+        raise ValueError("topk_ids and topk_w must be [T, top_k]")
+    if workspace is None:
+        workspace = alloc_workspace(T, H, I, E, top_k, x.device)
+    _check("moe_ffn_forward_logits", lib().moe_ffn_forward_logits(
+        _dev(x, "x", torch.bfloat16), _dev(logits, "logits", torch.float32),
+        _dev(topk_ids, "topk_ids", torch.int32), _dev(topk_w, "topk_w", torch.float32),
+        _dev(W_gate, "W_gate", torch.bfloat16), _dev(W_up, "W_up", torch.bfloat16),
+        _dev(W_down, "W_down", torch.bfloat16), _dev(out, "out", torch.bfloat16),
+        T, H, I, E, top_k, _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+        _stream(stream)))
+    return out, topk_ids, topk_w
 
 
 def moe_ffn_forward_int8(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor,

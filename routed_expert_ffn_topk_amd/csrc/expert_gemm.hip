@@ -548,11 +548,12 @@ hipError_t launch_gemm(const ExpertGemm& g, int64_t max_active, int num_cu,
 }
 
 template <class Fmt>
-hipError_t launch_ffn(const uint16_t* x, const int32_t* ids, const float* w,
-                      const FfnWeights& W, uint16_t* out, const FfnShape& s,
-                      const Workspace& ws, int num_cu, const StageEvents& ev,
-                      const SplitOverride& split, hipStream_t stream) {
-    hipError_t err = launch_permute(ids, s, ws, stream);
+hipError_t launch_ffn(const uint16_t* x, const Routing& route, const FfnWeights& W,
+                      uint16_t* out, const FfnShape& s, const Workspace& ws, int num_cu,
+                      const StageEvents& ev, const SplitOverride& split, hipStream_t stream) {
+    hipError_t err = route.logits
+                         ? launch_route_permute(route.logits, route.ids, route.w, s, ws, stream)
+                         : launch_permute(route.ids, s, ws, stream);
     if (err == hipSuccess) err = ev.mark(0, stream);
     if (err != hipSuccess) return err;
     // upper bound of active experts: every slot could name a different one
@@ -594,7 +595,7 @@ hipError_t launch_ffn(const uint16_t* x, const int32_t* ids, const float* w,
     err = launch_gemm<Fmt, 1>(dn, max_active, num_cu, stream);
     if (err == hipSuccess) err = ev.mark(2, stream);
     if (err != hipSuccess) return err;
-    err = launch_combine(ws.y, ids, w, out, s, stream);
+    err = launch_combine(ws.y, route.ids, route.w, out, s, stream);
     if (err == hipSuccess) err = ev.mark(3, stream);
     return err;
 }
@@ -610,18 +611,18 @@ hipError_t launch_combine(const float* y, const int32_t* ids, const float* w,
     return hipGetLastError();
 }
 
-hipError_t launch_ffn_bf16(const uint16_t* x, const int32_t* ids, const float* w,
-                           const FfnWeights& W, uint16_t* out, const FfnShape& s,
-                           const Workspace& ws, int num_cu, const StageEvents& ev,
-                           const SplitOverride& split, hipStream_t stream) {
-    return launch_ffn<Bf16Weights>(x, ids, w, W, out, s, ws, num_cu, ev, split, stream);
+hipError_t launch_ffn_bf16(const uint16_t* x, const Routing& route, const FfnWeights& W,
+                           uint16_t* out, const FfnShape& s, const Workspace& ws, int num_cu,
+                           const StageEvents& ev, const SplitOverride& split,
+                           hipStream_t stream) {
+    return launch_ffn<Bf16Weights>(x, route, W, out, s, ws, num_cu, ev, split, stream);
 }
 
-hipError_t launch_ffn_int8(const uint16_t* x, const int32_t* ids, const float* w,
-                           const FfnWeights& W, uint16_t* out, const FfnShape& s,
-                           const Workspace& ws, int num_cu, const StageEvents& ev,
-                           const SplitOverride& split, hipStream_t stream) {
-    return launch_ffn<Int8Weights>(x, ids, w, W, out, s, ws, num_cu, ev, split, stream);
+hipError_t launch_ffn_int8(const uint16_t* x, const Routing& route, const FfnWeights& W,
+                           uint16_t* out, const FfnShape& s, const Workspace& ws, int num_cu,
+                           const StageEvents& ev, const SplitOverride& split,
+                           hipStream_t stream) {
+    return launch_ffn<Int8Weights>(x, route, W, out, s, ws, num_cu, ev, split, stream);
 }
 
 }  // namespace moe

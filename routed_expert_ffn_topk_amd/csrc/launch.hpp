@@ -39,6 +39,15 @@ struct FfnShape {
     int T, H, I, E, k;
 };
 
+// Where a forward call's routing comes from: the caller's top-k ids and
+// weights (logits == nullptr; ids and w are only read), or router logits,
+// routed on the device into ids and w (written) before the gather index.
+struct Routing {
+    const float* logits;
+    int32_t* ids;
+    float* w;
+};
+
 // Weights of one layer: BF16 (q = NULL) or INT8 with per-128 group scales.
 struct FfnWeights {
     const void* gate;
@@ -55,15 +64,20 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
 hipError_t launch_permute(const int32_t* ids, const FfnShape& s, const Workspace& ws,
                           hipStream_t stream);
 
-hipError_t launch_ffn_bf16(const uint16_t* x, const int32_t* ids, const float* w,
-                           const FfnWeights& W, uint16_t* out, const FfnShape& s,
-                           const Workspace& ws, int num_cu, const StageEvents& ev,
-                           const SplitOverride& split, hipStream_t stream);
+// Router and gather index from logits [T][E]: writes ids / w [T][k] and the
+// workspace's gather index (one launch for decode-sized batches).
+hipError_t launch_route_permute(const float* logits, int32_t* ids, float* w,
+                                const FfnShape& s, const Workspace& ws, hipStream_t stream);
 
-hipError_t launch_ffn_int8(const uint16_t* x, const int32_t* ids, const float* w,
-                           const FfnWeights& W, uint16_t* out, const FfnShape& s,
-                           const Workspace& ws, int num_cu, const StageEvents& ev,
-                           const SplitOverride& split, hipStream_t stream);
+hipError_t launch_ffn_bf16(const uint16_t* x, const Routing& route, const FfnWeights& W,
+                           uint16_t* out, const FfnShape& s, const Workspace& ws, int num_cu,
+                           const StageEvents& ev, const SplitOverride& split,
+                           hipStream_t stream);
+
+hipError_t launch_ffn_int8(const uint16_t* x, const Routing& route, const FfnWeights& W,
+                           uint16_t* out, const FfnShape& s, const Workspace& ws, int num_cu,
+                           const StageEvents& ev, const SplitOverride& split,
+                           hipStream_t stream);
 
 // Weighted combine shared by both weight formats.
 hipError_t launch_combine(const float* y, const int32_t* ids, const float* w,

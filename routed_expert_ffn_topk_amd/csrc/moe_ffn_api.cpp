@@ -175,8 +175,44 @@ int moe_ffn_forward(const void* x, const int32_t* topk_ids, const float* topk_w,
     if ((rc = num_cu(&ncu)) != MOE_FFN_OK) return rc;
     const moe::FfnShape s{(int)T, (int)H, (int)I, E, top_k};
     const moe::FfnWeights W{W_gate, W_up, W_down, nullptr, nullptr, nullptr};
+    const moe::Routing route{nullptr, const_cast<int32_t*>(topk_ids), const_cast<float*>(topk_w)};
     const hipError_t err = moe::launch_ffn_bf16(
-        static_cast<const uint16_t*>(x), topk_ids, topk_w, W, static_cast<uint16_t*>(out), s,
+        static_cast<const uint16_t*>(x), route, W, static_cast<uint16_t*>(out), s,
+        carve(workspace, L), ncu, take_stage_events(), t_split, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? MOE_FFN_OK : MOE_FFN_ERR_HIP;
+}
+
+int moe_ffn_forward_logits(const void* x, const float* logits, int32_t* topk_ids,
+                           float* topk_w, const void* W_gate, const void* W_up,
+                           const void* W_down, void* out, int64_t T, int64_t H, int64_t I,
+                           int32_t E, int32_t top_k, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    if (top_k > 64) return MOE_FFN_ERR_BAD_SHAPE;
+    moe_ffn_ws_layout L;
+    int rc = check_forward(x, topk_ids, topk_w, out, T, H, I, E, top_k, workspace,
+                           workspace_bytes, 32, &L);
+    if (rc != MOE_FFN_OK || T == 0) return rc;
+    if (!logits || !W_gate || !W_up || !W_down) return MOE_FFN_ERR_NULL_ARG;
+    if (reinterpret_cast<uintptr_t>(logits) & 3u) return MOE_FFN_ERR_MISALIGNED;
+    if (!aligned16(W_gate) || !aligned16(W_up) || !aligned16(W_down))
+        return MOE_FFN_ERR_MISALIGNED;
+    // the routing outputs are written: they may overlap no input, each
+    // other, or the workspace
+    const size_t sb = (size_t)T * (size_t)top_k * 4;
+    const size_t lb = (size_t)T * (size_t)E * 4;
+    const size_t xb = (size_t)T * (size_t)H * 2;
+    if (overlap(topk_ids, sb, topk_w, sb) || overlap(logits, lb, topk_ids, sb) ||
+        overlap(logits, lb, topk_w, sb) || overlap(x, xb, topk_ids, sb) ||
+        overlap(x, xb, topk_w, sb) || overlap(workspace, L.total_bytes, topk_ids, sb) ||
+        overlap(workspace, L.total_bytes, topk_w, sb) || overlap(logits, lb, out, xb))
+        return MOE_FFN_ERR_ALIAS;
+    int ncu = 0;
+    if ((rc = num_cu(&ncu)) != MOE_FFN_OK) return rc;
+    const moe::FfnShape s{(int)T, (int)H, (int)I, E, top_k};
+    const moe::FfnWeights W{W_gate, W_up, W_down, nullptr, nullptr, nullptr};
+    const moe::Routing route{logits, topk_ids, topk_w};
+    const hipError_t err = moe::launch_ffn_bf16(
+        static_cast<const uint16_t*>(x), route, W, static_cast<uint16_t*>(out), s,
         carve(workspace, L), ncu, take_stage_events(), t_split, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? MOE_FFN_OK : MOE_FFN_ERR_HIP;
 }
@@ -200,8 +236,9 @@ int moe_ffn_forward_int8(const void* x, const int32_t* topk_ids, const float* to
     if ((rc = num_cu(&ncu)) != MOE_FFN_OK) return rc;
     const moe::FfnShape s{(int)T, (int)H, (int)I, E, top_k};
     const moe::FfnWeights W{Q_gate, Q_up, Q_down, S_gate, S_up, S_down};
+    const moe::Routing route{nullptr, const_cast<int32_t*>(topk_ids), const_cast<float*>(topk_w)};
     const hipError_t err = moe::launch_ffn_int8(
-        static_cast<const uint16_t*>(x), topk_ids, topk_w, W, static_cast<uint16_t*>(out), s,
+        static_cast<const uint16_t*>(x), route, W, static_cast<uint16_t*>(out), s,
         carve(workspace, L), ncu, take_stage_events(), t_split, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? MOE_FFN_OK : MOE_FFN_ERR_HIP;
 }

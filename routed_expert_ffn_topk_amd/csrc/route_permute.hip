@@ -1,8 +1,9 @@
 // Routing and gather-index kernels.
 //
-// route_topk: the top-k gate of HiNa-MoE §2.1 / Fig. 2 (k per Table 3).
-// permute:    the per-expert token lists that drive the gather of §4.1
-//             (each expert's routed tokens form one small matrix).
+// route_topk:    the top-k gate of HiNa-MoE §2.1 / Fig. 2 (k per Table 3).
+// permute:       the per-expert token lists that drive the gather of §4.1
+//                (each expert's routed tokens form one small matrix).
+// route_permute: both in one workgroup, for decode-sized batches.
 #include <climits>
 #include <cmath>
 
@@ -14,21 +15,137 @@ namespace moe {
 namespace {
 
 constexpr int kMaxExperts = 1024;          // matches MOE_FFN_MAX_EXPERTS
-constexpr int kPerLane = kMaxExperts / kWave;
+// Slots the gather-index kernels keep in LDS; larger batches take the
+// chunked scatter that reads the ids from memory.
+constexpr int kPermMaxSlots = 8192;
+// The fused router + gather index: batches of at most this many tokens and
+// slots (16 waves route up to four tokens each), with the logits staged in
+// LDS when the batch's T*E fits.
+constexpr int kRoutePermMaxTokens = 64;
+constexpr int kRoutePermMaxSlots = 4096;
+constexpr int kRoutePermMaxLogits = 16384;
 
-// (value, expert) ordering of the router: larger logit first, then lower id.
-// e == INT_MAX marks "no candidate", which loses to everything.
-__device__ __forceinline__ bool route_better(float va, int ea, float vb, int eb) {
-    if (ea == INT_MAX) return false;
-    if (eb == INT_MAX) return true;
-    return va > vb || (va == vb && ea < eb);
+// ---------------------------------------------------------------------------
+// Wave-wide reductions with DPP (data-parallel primitives: a VALU operand
+// read from another lane of the same row).  Inclusive scan over the 64
+// lanes: shifts by 1, 2, 4 and 8 lanes within each row of 16, then the last
+// lane of row 0 / row 2 into rows 1 / 3 (row_bcast:15), then lane 31 into
+// rows 2 and 3 (row_bcast:31).  Lane 63 ends with the total.  Lanes whose
+// source is outside the row, or rows masked off, take the identity.
+// ---------------------------------------------------------------------------
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114,
+              kDppRowShr8 = 0x118, kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+template <class Op>
+__device__ __forceinline__ int wave_scan_i32(int v, int identity, Op op) {
+    v = op(v, __builtin_amdgcn_update_dpp(identity, v, kDppRowShr1, 0xf, 0xf, false));
+    v = op(v, __builtin_amdgcn_update_dpp(identity, v, kDppRowShr2, 0xf, 0xf, false));
+    v = op(v, __builtin_amdgcn_update_dpp(identity, v, kDppRowShr4, 0xf, 0xf, false));
+    v = op(v, __builtin_amdgcn_update_dpp(identity, v, kDppRowShr8, 0xf, 0xf, false));
+    v = op(v, __builtin_amdgcn_update_dpp(identity, v, kDppRowBcast15, 0xa, 0xf, false));
+    v = op(v, __builtin_amdgcn_update_dpp(identity, v, kDppRowBcast31, 0xc, 0xf, false));
+    return v;
 }
 
-// One wave per token.  Lane l holds logits l, l+64, l+128, ...; k rounds of
-// a wave-wide arg-max pick the experts in descending order.  The weights are
-// exp(l_j - l_max) / sum over the chosen of exp(l_i - l_max): the softmax
-// over all E experts renormalised over the chosen ones, with the common
-// denominator cancelled.
+__device__ __forceinline__ int wave_max_i32(int v) {
+    v = wave_scan_i32(v, INT_MIN, [](int a, int b) { return a > b ? a : b; });
+    return __builtin_amdgcn_readlane(v, kWave - 1);
+}
+
+__device__ __forceinline__ int wave_min_i32(int v) {
+    v = wave_scan_i32(v, INT_MAX, [](int a, int b) { return a < b ? a : b; });
+    return __builtin_amdgcn_readlane(v, kWave - 1);
+}
+
+// Inclusive prefix sum over the lanes.
+__device__ __forceinline__ int wave_prefix_sum_i32(int v) {
+    return wave_scan_i32(v, 0, [](int a, int b) { return a + b; });
+}
+
+// Sum over the lanes, in the fixed order of the scan.
+__device__ __forceinline__ float wave_sum_f32(float v) {
+    auto add = [](int a, int b) {
+        return __builtin_bit_cast(int, __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b));
+    };
+    const int r = wave_scan_i32(__builtin_bit_cast(int, v), 0, add);
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(r, kWave - 1));
+}
+
+// Order-preserving integer key of a float (not NaN): keys compare as the
+// values do, and -0 is mapped to +0 so that the two tie.  INT_MIN is the key
+// of no float (it would be a NaN pattern) and marks "no candidate".
+__device__ __forceinline__ int route_key(float f) {
+    const int b = __builtin_bit_cast(int, f + 0.0f);
+    return b >= 0 ? b : b ^ 0x7fffffff;
+}
+__device__ __forceinline__ float route_key_value(int key) {
+    return __builtin_bit_cast(float, key >= 0 ? key : key ^ 0x7fffffff);
+}
+
+// Routes one token with one wave (all 64 lanes active).  Lane l holds the
+// logits of experts l, l+64, ..., l+64(PL-1); k rounds each pick the
+// remaining expert with the largest logit (ties: the lower id) with a
+// wave-wide max over the keys, then a wave-wide min over the ids holding
+// that key.  The weights are exp(l_j - l_max) / sum over the chosen of
+// exp(l_i - l_max): the softmax over all E experts renormalised over the
+// chosen ones (the common denominator cancels).  Lane j < k returns the
+// j-th choice in (*id, *wt); the other lanes return id -1, weight 0.
+template <int PL>
+__device__ __forceinline__ void route_token(const float* __restrict__ l, int E, int k,
+                                            int lane, int* id, float* wt) {
+    int key[PL];
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+        const int e = lane + kWave * i;
+        key[i] = e < E ? route_key(l[e]) : INT_MIN;
+    }
+    int my_key = INT_MIN;
+    int my_e = -1;
+    int top_key = INT_MIN;
+    for (int j = 0; j < k; ++j) {
+        // this lane's best candidate: largest key, then lowest expert id
+        int bk = INT_MIN, be = INT_MAX;
+#pragma unroll
+        for (int i = 0; i < PL; ++i)
+            if (key[i] > bk) {
+                bk = key[i];
+                be = lane + kWave * i;
+            }
+        const int K = wave_max_i32(bk);
+        const int W = wave_min_i32(bk == K ? be : INT_MAX);
+        if (j == 0) top_key = K;
+        if (lane == j) {
+            my_key = K;
+            my_e = W;
+        }
+#pragma unroll
+        for (int i = 0; i < PL; ++i)
+            if (lane + kWave * i == W) key[i] = INT_MIN;
+    }
+    const float mx = route_key_value(top_key);
+    const float ex = lane < k ? expf(route_key_value(my_key) - mx) : 0.0f;
+    const float sum = wave_sum_f32(ex);
+    *id = lane < k ? my_e : -1;
+    *wt = lane < k ? ex / sum : 0.0f;
+}
+
+// route_token for the expert count E (the candidates per lane are a
+// compile-time count).
+__device__ __forceinline__ void route_token_any(const float* __restrict__ l, int E, int k,
+                                                int lane, int* id, float* wt) {
+    if (E <= 64)
+        route_token<1>(l, E, k, lane, id, wt);
+    else if (E <= 128)
+        route_token<2>(l, E, k, lane, id, wt);
+    else if (E <= 256)
+        route_token<4>(l, E, k, lane, id, wt);
+    else if (E <= 512)
+        route_token<8>(l, E, k, lane, id, wt);
+    else
+        route_token<16>(l, E, k, lane, id, wt);
+}
+
+// One wave per token.
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits,
                                                          int T, int E, int k,
                                                          int32_t* __restrict__ ids,
@@ -36,143 +153,201 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
     const int lane = threadIdx.x & (kWave - 1);
     const int t = blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
     if (t >= T) return;
-    const float* l = logits + (size_t)t * E;
-    float v[kPerLane];
-    unsigned taken = 0;
-#pragma unroll
-    for (int i = 0; i < kPerLane; ++i) {
-        const int e = lane + kWave * i;
-        v[i] = e < E ? l[e] : -INFINITY;
-        if (e >= E) taken |= 1u << i;
-    }
-    float my_v = -INFINITY;
-    int my_e = -1;
-    for (int j = 0; j < k; ++j) {
-        float bv = -INFINITY;
-        int be = INT_MAX;
-#pragma unroll
-        for (int i = 0; i < kPerLane; ++i) {
-            // candidates of one lane come in ascending expert order, so a
-            // strict comparison keeps the lower id on ties
-            if (!((taken >> i) & 1u) && (be == INT_MAX || v[i] > bv)) {
-                bv = v[i];
-                be = lane + kWave * i;
-            }
-        }
-#pragma unroll
-        for (int off = kWave / 2; off > 0; off >>= 1) {
-            const float ov = __shfl_xor(bv, off, kWave);
-            const int oe = __shfl_xor(be, off, kWave);
-            if (route_better(ov, oe, bv, be)) {
-                bv = ov;
-                be = oe;
-            }
-        }
-        if (lane == j) {
-            my_v = bv;
-            my_e = be;
-        }
-        if ((be & (kWave - 1)) == lane) taken |= 1u << (be / kWave);
-    }
-    const float mx = __shfl(my_v, 0, kWave);
-    const float ex = lane < k ? expf(my_v - mx) : 0.0f;
-    float sum = ex;
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, kWave);
+    int id;
+    float wt;
+    route_token_any(logits + (size_t)t * E, E, k, lane, &id, &wt);
     if (lane < k) {
-        ids[(size_t)t * k + lane] = my_e;
-        w[(size_t)t * k + lane] = ex / sum;
+        ids[(size_t)t * k + lane] = id;
+        w[(size_t)t * k + lane] = wt;
     }
 }
 
-// Stable counting sort of the T*k slots by expert, in one workgroup.
-// Writes counts, offsets (exclusive prefix), the ascending list of active
-// experts, and sorted_slot (expert-major, slot order within an expert).
-// Slots with ids outside [0, E) are left out and counted in meta[1].
-constexpr int kPermThreads = 256;
+// ---------------------------------------------------------------------------
+// Gather index: stable counting sort of the n slots by expert.  Writes
+// counts, offsets (exclusive prefix), the ascending list of active experts,
+// and sorted_slot (expert-major, slot order within an expert).  Slots with
+// ids outside [0, E) are left out and counted in meta[1].
+// ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(kPermThreads) void permute_kernel(
-    const int32_t* __restrict__ ids, int n_slots, int E, int32_t* __restrict__ meta,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ active, int32_t* __restrict__ sorted_slot) {
-    __shared__ int cnt[kMaxExperts];
-    __shared__ int base[kMaxExperts];
-    __shared__ int run[kMaxExperts];
-    __shared__ int scan_c[kPermThreads];
-    __shared__ int scan_a[kPermThreads];
-    __shared__ int chunk_e[kPermThreads];
-    __shared__ int nbad;
+// Per-expert counts of the n slots (all NT threads), then the exclusive scan
+// and the tables (wave 0 alone: each lane owns a run of up to 16 consecutive
+// experts).  base[] receives the offsets.  Ends with a barrier.
+template <int NT, class Ids>
+__device__ __forceinline__ void count_and_scan(Ids ids, int n, int E, int* cnt, int* base,
+                                               int* nbad, int32_t* __restrict__ meta,
+                                               int32_t* __restrict__ counts,
+                                               int32_t* __restrict__ offsets,
+                                               int32_t* __restrict__ active) {
     const int tid = threadIdx.x;
-
-    for (int e = tid; e < E; e += kPermThreads) {
-        cnt[e] = 0;
-        run[e] = 0;
-    }
-    if (tid == 0) nbad = 0;
+    for (int e = tid; e < E; e += NT) cnt[e] = 0;
+    if (tid == 0) *nbad = 0;
     __syncthreads();
-    for (int s = tid; s < n_slots; s += kPermThreads) {
-        const int e = ids[s];
+    for (int s = tid; s < n; s += NT) {
+        const int e = ids(s);
         if (e >= 0 && e < E)
             atomicAdd(&cnt[e], 1);
         else
-            atomicAdd(&nbad, 1);
+            atomicAdd(nbad, 1);
     }
     __syncthreads();
+    if (tid < kWave) {
+        const int per = (E + kWave - 1) / kWave;
+        const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
+        int lc = 0, la = 0;
+        for (int e = e0; e < e1; ++e) {
+            lc += cnt[e];
+            la += cnt[e] > 0;
+        }
+        const int ic = wave_prefix_sum_i32(lc);
+        const int ia = wave_prefix_sum_i32(la);
+        int bc = ic - lc, ba = ia - la;
+        for (int e = e0; e < e1; ++e) {
+            base[e] = bc;
+            offsets[e] = bc;
+            counts[e] = cnt[e];
+            if (cnt[e] > 0) active[ba++] = e;
+            bc += cnt[e];
+        }
+        if (tid == kWave - 1) {
+            offsets[E] = ic;
+            meta[0] = ia;
+            meta[1] = *nbad;
+        }
+    }
+    __syncthreads();
+}
 
-    // Each thread owns a run of consecutive experts; scan the per-thread
-    // totals of slots and of active experts across the workgroup.
-    const int per = (E + kPermThreads - 1) / kPermThreads;
-    const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
-    int lc = 0, la = 0;
-    for (int e = e0; e < e1; ++e) {
-        lc += cnt[e];
-        la += cnt[e] > 0;
+// Stable scatter by wave 0 over the slots in LDS, 64 at a time: a slot's
+// place is its expert's offset, plus the slots of that expert in earlier
+// chunks (run[e]), plus the lanes below it in this chunk with the same
+// expert.  Lanes with equal ids are found bit by bit with ballots; the last
+// lane of each group advances run[e].  run[] is the base[] table, advanced in
+// place (LDS operations of one wave complete in order).
+__device__ __forceinline__ void scatter_wave(const int* __restrict__ sid, int n, int E,
+                                             int* run, int32_t* __restrict__ sorted_slot) {
+    const int lane = threadIdx.x;
+    for (int c0 = 0; c0 < n; c0 += kWave) {
+        const int s = c0 + lane;
+        const int e = s < n ? sid[s] : -1;
+        const bool ok = e >= 0 && e < E;
+        const int key = ok ? e : kMaxExperts;   // every dropped slot in one group
+        unsigned long long eq = ~0ull;
+#pragma unroll
+        for (int b = 0; b < 11; ++b) {          // ids < 2048
+            const bool bit = (key >> b) & 1;
+            const unsigned long long m = __ballot(bit);
+            eq &= bit ? m : ~m;
+        }
+        const int below = __builtin_amdgcn_mbcnt_hi(
+            (unsigned)(eq >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)eq, 0u));
+        const int group = __popcll(eq);
+        int pos = 0;
+        if (ok) pos = run[e] + below;
+        if (ok) sorted_slot[pos] = s;
+        if (ok && below == group - 1) run[e] = pos + 1;
     }
-    scan_c[tid] = lc;
-    scan_a[tid] = la;
-    __syncthreads();
-    for (int d = 1; d < kPermThreads; d <<= 1) {
-        const int vc = tid >= d ? scan_c[tid - d] : 0;
-        const int va = tid >= d ? scan_a[tid - d] : 0;
-        __syncthreads();
-        scan_c[tid] += vc;
-        scan_a[tid] += va;
-        __syncthreads();
-    }
-    int bc = scan_c[tid] - lc;
-    int ba = scan_a[tid] - la;
-    for (int e = e0; e < e1; ++e) {
-        base[e] = bc;
-        offsets[e] = bc;
-        counts[e] = cnt[e];
-        if (cnt[e] > 0) active[ba++] = e;
-        bc += cnt[e];
-    }
-    if (tid == kPermThreads - 1) {
-        offsets[E] = scan_c[kPermThreads - 1];
-        meta[0] = scan_a[kPermThreads - 1];
-        meta[1] = nbad;
-    }
-    __syncthreads();
+}
 
-    // Stable scatter, one chunk of slots at a time: a slot's place is its
-    // expert's base, plus the slots of that expert in earlier chunks, plus
-    // the earlier slots of that expert in this chunk.
-    for (int c0 = 0; c0 < n_slots; c0 += kPermThreads) {
+// The chunked scatter for batches beyond the LDS copy: all threads, one
+// chunk of NT slots at a time, the rank within a chunk by a scan over the
+// lower threads' ids.
+template <int NT>
+__device__ __forceinline__ void scatter_chunks(const int32_t* __restrict__ ids, int n, int E,
+                                               int* run, int* chunk_e,
+                                               int32_t* __restrict__ sorted_slot) {
+    const int tid = threadIdx.x;
+    for (int c0 = 0; c0 < n; c0 += NT) {
         const int s = c0 + tid;
-        const int e = s < n_slots ? ids[s] : -1;
+        const int e = s < n ? ids[s] : -1;
         const bool ok = e >= 0 && e < E;
         chunk_e[tid] = ok ? e : -1;
         __syncthreads();
         if (ok) {
             int rank = 0;
             for (int j = 0; j < tid; ++j) rank += chunk_e[j] == e;
-            sorted_slot[base[e] + run[e] + rank] = s;
+            sorted_slot[run[e] + rank] = s;
         }
         __syncthreads();
         if (ok) atomicAdd(&run[e], 1);
         __syncthreads();
     }
+}
+
+constexpr int kPermThreads = 256;
+
+struct GlobalIds {
+    const int32_t* p;
+    __device__ int operator()(int s) const { return p[s]; }
+};
+struct LdsIds {
+    const int* p;
+    __device__ int operator()(int s) const { return p[s]; }
+};
+
+__global__ __launch_bounds__(kPermThreads) void permute_kernel(
+    const int32_t* __restrict__ ids, int n, int E, int32_t* __restrict__ meta,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ active, int32_t* __restrict__ sorted_slot) {
+    __shared__ int cnt[kMaxExperts];
+    __shared__ int base[kMaxExperts];
+    __shared__ int sid[kPermMaxSlots];
+    __shared__ int chunk_e[kPermThreads];
+    __shared__ int nbad;
+    if (n <= kPermMaxSlots) {
+        for (int s = threadIdx.x; s < n; s += kPermThreads) sid[s] = ids[s];
+        __syncthreads();
+        count_and_scan<kPermThreads>(LdsIds{sid}, n, E, cnt, base, &nbad, meta, counts, offsets,
+                                     active);
+        if (threadIdx.x < kWave) scatter_wave(sid, n, E, base, sorted_slot);
+    } else {
+        count_and_scan<kPermThreads>(GlobalIds{ids}, n, E, cnt, base, &nbad, meta, counts,
+                                     offsets, active);
+        scatter_chunks<kPermThreads>(ids, n, E, base, chunk_e, sorted_slot);
+    }
+}
+
+// Router and gather index in one workgroup (decode-sized batches).  The
+// batch's logits are first staged in LDS by all threads at once (one memory
+// latency instead of one per token and wave) when T*E fits; each wave then
+// routes tokens wave, wave + 16, ...; the chosen ids go to the caller's
+// topk_ids / topk_w and to LDS, and the gather index reads them from LDS.
+// One launch instead of two, with no round trip through memory.
+constexpr int kRoutePermThreads = 1024;
+
+__global__ __launch_bounds__(kRoutePermThreads) void route_permute_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ ids,
+    float* __restrict__ w, int32_t* __restrict__ meta, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ active,
+    int32_t* __restrict__ sorted_slot) {
+    __shared__ float slg[kRoutePermMaxLogits];
+    __shared__ int sid[kRoutePermMaxSlots];
+    __shared__ int cnt[kMaxExperts];
+    __shared__ int base[kMaxExperts];
+    __shared__ int nbad;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int n_logits = T * E;
+    const bool staged = n_logits <= kRoutePermMaxLogits;
+    if (staged) {
+        for (int i = threadIdx.x; i < n_logits; i += kRoutePermThreads) slg[i] = logits[i];
+        __syncthreads();
+    }
+    const float* src = staged ? slg : logits;
+    for (int t = wave; t < T; t += kRoutePermThreads / kWave) {
+        int id;
+        float wt;
+        route_token_any(src + (size_t)t * E, E, k, lane, &id, &wt);
+        if (lane < k) {
+            ids[(size_t)t * k + lane] = id;
+            w[(size_t)t * k + lane] = wt;
+            sid[t * k + lane] = id;
+        }
+    }
+    __syncthreads();
+    const int n = T * k;
+    count_and_scan<kRoutePermThreads>(LdsIds{sid}, n, E, cnt, base, &nbad, meta, counts,
+                                      offsets, active);
+    if (threadIdx.x < kWave) scatter_wave(sid, n, E, base, sorted_slot);
 }
 
 }  // namespace
@@ -184,6 +359,19 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
     const int grid = (T + tokens_per_block - 1) / tokens_per_block;
     hipLaunchKernelGGL(route_topk_kernel, dim3(grid), dim3(256), 0, stream, logits, T, E,
                        k, ids, w);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_permute(const float* logits, int32_t* ids, float* w,
+                                const FfnShape& s, const Workspace& ws, hipStream_t stream) {
+    if (s.T > kRoutePermMaxTokens || (int64_t)s.T * s.k > kRoutePermMaxSlots) {
+        // larger batches: the router on one wave per token, then the sort
+        hipError_t err = launch_route_topk(logits, s.T, s.E, s.k, ids, w, stream);
+        return err == hipSuccess ? launch_permute(ids, s, ws, stream) : err;
+    }
+    hipLaunchKernelGGL(route_permute_kernel, dim3(1), dim3(kRoutePermThreads), 0, stream,
+                       logits, s.T, s.E, s.k, ids, w, ws.meta, ws.counts, ws.offsets,
+                       ws.active, ws.sorted_slot);
     return hipGetLastError();
 }
 

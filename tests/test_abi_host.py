@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert {"moe_ffn_forward", "moe_ffn_forward_int8", "moe_route_topk",
+    assert {"moe_ffn_forward", "moe_ffn_forward_int8", "moe_ffn_forward_logits", "moe_route_topk",
             "moe_ffn_workspace_bytes", "moe_ffn_workspace_layout", "moe_ffn_check_status",
             "moe_ffn_status_string"} <= set(names)
     L = ctypes.CDLL(moe.LIB_PATH)
@@ -91,6 +91,36 @@ def test_forward_host_validation():
     assert fwd(ws=A + 0x4000000 + 16) == moe.MOE_FFN_ERR_MISALIGNED
     assert fwd(out=A + 64) == moe.MOE_FFN_ERR_ALIAS          # out overlaps x
     assert fwd(ws=A + 0x300000 - 256) == moe.MOE_FFN_ERR_ALIAS  # workspace overlaps out
+
+
+def fwd_logits(**kw):
+    a = dict(x=A, lg=A + 0x500000, ids=A + 0x100000, w=A + 0x200000, wg=A + 0x1000000,
+             wu=A + 0x2000000, wd=A + 0x3000000, out=A + 0x300000, T=4, H=64, I=96, E=8, k=2,
+             ws=A + 0x4000000, wsb=1 << 30)
+    a.update(kw)
+    return moe.lib().moe_ffn_forward_logits(a["x"], a["lg"], a["ids"], a["w"], a["wg"], a["wu"],
+                                            a["wd"], a["out"], a["T"], a["H"], a["I"], a["E"],
+                                            a["k"], a["ws"], a["wsb"], None)
+
+
+def test_forward_logits_host_validation():
+    assert fwd_logits(T=0) == moe.MOE_FFN_OK
+    assert fwd_logits(k=65, E=128) == moe.MOE_FFN_ERR_BAD_SHAPE    # router handles k <= 64
+    assert fwd_logits(k=9) == moe.MOE_FFN_ERR_BAD_SHAPE
+    assert fwd_logits(H=48) == moe.MOE_FFN_ERR_BAD_SHAPE
+    assert fwd_logits(lg=None) == moe.MOE_FFN_ERR_NULL_ARG
+    assert fwd_logits(ids=None) == moe.MOE_FFN_ERR_NULL_ARG
+    assert fwd_logits(wu=None) == moe.MOE_FFN_ERR_NULL_ARG
+    assert fwd_logits(lg=A + 0x500002) == moe.MOE_FFN_ERR_MISALIGNED
+    assert fwd_logits(ids=A + 0x100002) == moe.MOE_FFN_ERR_MISALIGNED
+    # written routing outputs may not overlap each other, logits, x, out or the workspace
+    assert fwd_logits(w=A + 0x100004) == moe.MOE_FFN_ERR_ALIAS
+    assert fwd_logits(ids=A + 0x500010) == moe.MOE_FFN_ERR_ALIAS
+    assert fwd_logits(w=A + 0x40) == moe.MOE_FFN_ERR_ALIAS
+    assert fwd_logits(ids=A + 0x300010) == moe.MOE_FFN_ERR_ALIAS
+    assert fwd_logits(w=A + 0x4000100) == moe.MOE_FFN_ERR_ALIAS
+    assert fwd_logits(lg=A + 0x300000 - 16) == moe.MOE_FFN_ERR_ALIAS
+    assert fwd_logits(out=A + 64) == moe.MOE_FFN_ERR_ALIAS
 
 
 def test_forward_int8_requires_group_multiples():

@@ -6,7 +6,8 @@ import torch
 import oracle
 import routed_expert_ffn_topk_amd as moe
 import workloads
-from moe_cases import need_gpu, random_case, read_workspace, say
+from moe_cases import (TOL_BF16, assert_close, assert_close_scaled, need_gpu, random_case,
+                       read_workspace, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -84,3 +85,80 @@ def test_gather_index_matches_oracle(T, E, k, bad):
     assert np.array_equal(r["sorted_slot"][:n], p["sorted_slot"])
     assert dropped == p["n_invalid"] == bad
     assert code == (moe.MOE_FFN_ERR_BAD_IDS if bad else moe.MOE_FFN_OK)
+
+
+# Router and gather index fused into one kernel (T*k <= 4096 slots), and the
+# two-kernel path above that: ids and the gather index bit-exact against the
+# oracle's router and permutation, weights within FP32 rounding, and the layer
+# output against the oracle layer on those ids.
+@pytest.mark.parametrize("T,H,I,E,k,kind", [
+    (16, 256, 512, 8, 2, "normal"),      # the Tiny layer's shape
+    (16, 64, 96, 256, 8, "normal"),      # DeepSeek-V3 routing shape
+    (16, 64, 96, 256, 8, "zipf"),
+    (1, 64, 64, 128, 8, "normal"),       # Qwen3-235B at one token
+    (33, 64, 64, 8, 2, "ties"),
+    (64, 32, 64, 64, 64, "normal"),      # k = 64: every lane of the wave chooses
+    (5, 64, 64, 1024, 8, "masked"),
+    (9, 32, 32, 1, 1, "normal"),
+    (512, 32, 64, 64, 8, "normal"),      # 4096 slots: the largest fused batch
+    (600, 32, 64, 64, 8, "ties"),        # 4800 slots: router kernel, then the sort
+])
+def test_forward_logits_matches_oracle(T, H, I, E, k, kind):
+    need_gpu()
+    rng = np.random.default_rng(1000 * T + 7 * E + k)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    if kind == "ties":
+        lg = rng.integers(-2, 3, size=(T, E)).astype(np.float32)
+    if kind == "zipf":
+        p = (rng.permutation(E) + 1.0) ** -1.1
+        lg = (lg + np.log(p / p.sum())[None, :]).astype(np.float32)
+    if kind == "masked":
+        keep = rng.random((T, E)) < 0.02
+        keep[np.arange(T)[:, None], rng.integers(0, E, size=(T, k))] = True
+        keep[:, :k] = True
+        lg = np.where(keep, lg, -np.inf).astype(np.float32)
+    rid, rw = oracle.route_topk(lg, k)
+    case = random_case(T + E, T, H, I, E, k, ids=rid, w=rw)
+    x, _, _ = case.device_inputs()
+    ws = moe.alloc_workspace(T, H, I, E, k)
+    say(f"forward_logits T={T} H={H} I={I} E={E} k={k} {kind}")
+    out, ids, w = moe.moe_ffn_forward_logits(x, torch.from_numpy(lg).cuda(), k, case.Wg,
+                                             case.Wu, case.Wd, workspace=ws)
+    code, dropped = moe.moe_ffn_check_status(ws)
+    assert code == moe.MOE_FFN_OK and dropped == 0
+    assert np.array_equal(ids.cpu().numpy(), rid)
+    np.testing.assert_allclose(w.cpu().numpy(), rw, rtol=1e-5, atol=1e-7)
+    r = read_workspace(ws, moe.moe_ffn_workspace_layout(T, H, I, E, k), T, H, I, E, k)
+    p = oracle.permute(rid, E)
+    assert np.array_equal(r["counts"], p["counts"])
+    assert np.array_equal(r["offsets"], p["offsets"])
+    assert r["n_active"] == p["n_active"]
+    assert np.array_equal(r["active"], p["active"])
+    assert np.array_equal(r["sorted_slot"][: p["offsets"][E]], p["sorted_slot"])
+    # the oracle layer on the oracle's routing weights (the GPU's are equal
+    # to them within FP32 rounding)
+    ref = case.oracle()
+    got = workloads.bf16_bits(out)
+    assert_close(got, ref, TOL_BF16)
+    assert_close_scaled(got, ref, 1e-2)
+
+
+@pytest.mark.parametrize("name", ["tiny", "deepseekv3_zipf_t16", "qwen3_235b_t4"])
+def test_forward_logits_equals_two_step_layer(name):
+    """The logits entry point gives bit-identical output to moe_route_topk
+    followed by moe_ffn_forward (same kernels after the gather index)."""
+    need_gpu()
+    wl = workloads.WORKLOADS[name]
+    if wl.H > 1024:    # the real expert shapes, shrunk: routing is what differs here
+        wl = workloads.Workload(**{**wl.__dict__, "H": 256, "I": 128})
+    lg = workloads.gen_logits(wl).cuda()
+    x = workloads.gen_x(wl).cuda()
+    Wg, Wu, Wd = workloads.gen_weights(wl, "cuda")
+    say(f"forward_logits vs two-step {name}")
+    out, ids, w = moe.moe_ffn_forward_logits(x, lg, wl.k, Wg, Wu, Wd)
+    ids2, w2 = moe.moe_route_topk(lg, wl.k)
+    out2 = moe.moe_ffn_forward(x, ids2, w2, Wg, Wu, Wd)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2)
+    assert torch.equal(w, w2)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
