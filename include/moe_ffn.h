@@ -60,12 +60,19 @@ extern "C" {
  * Workspace layout.  The workspace is caller-owned device memory, at least
  * total_bytes long and 256-byte aligned; each region starts at the given byte
  * offset.  Regions (T tokens, k = top_k, S = T*k slots, slot s = t*k + j):
- *   meta        int32[8]   [0] number of active experts A, [1] number of slots
- *                          whose expert id was outside [0, E) (those slots
- *                          contribute nothing to the output)
+ *   meta        int32[8]   [0] number of experts listed in `active`, [1] number
+ *                          of slots whose expert id was outside [0, E) (those
+ *                          slots contribute nothing to the output), [2] number
+ *                          of experts listed in `large`
  *   counts      int32[E]   tokens routed to each expert
  *   offsets     int32[E+1] start of each expert's run in sorted_slot
- *   active      int32[E]   the A experts with counts > 0, ascending
+ *   active      int32[E]   experts with counts > 0 that the small-m product
+ *                          handles, ascending
+ *   large       int32[E]   experts that the tiled (many-token) product
+ *                          handles, ascending: those with more than 32 tokens
+ *                          when the batch has T > 64 tokens and BF16 weights;
+ *                          otherwise none, and `active` lists every expert
+ *                          with counts > 0
  *   sorted_slot int32[S]   slots grouped by expert (ascending), ascending
  *                          slot order within an expert (the gather order)
  *   h           bf16[S][I] SiLU(gate)*up of each gathered row, in
@@ -80,6 +87,7 @@ typedef struct moe_ffn_ws_layout {
     size_t counts;
     size_t offsets;
     size_t active;
+    size_t large;
     size_t sorted_slot;
     size_t h;
     size_t y;
@@ -147,9 +155,9 @@ int moe_ffn_forward(const void* x, const int32_t* topk_ids, const float* topk_w,
  * Routed-expert FFN layer from router logits, BF16 weights: the top-k gate
  * (HiNa-MoE §2.1 / Fig. 2) followed by the layer of moe_ffn_forward
  * (§4.1 FFN equation), with the router and the per-expert gather index
- * computed by one kernel for batches of up to 4096 slots (T*top_k), and by
- * the router kernel of moe_route_topk followed by the gather-index kernel
- * above that.
+ * computed by one kernel for batches of up to 64 tokens and 512 slots
+ * (T*top_k), and by the router kernel of moe_route_topk followed by the
+ * gather-index kernel above that.
  *   logits   [T][E] float32, device: router logits (each token needs at least
  *            top_k finite values; NaN is not supported).
  *   topk_ids [T][top_k] int32, device, written: as moe_route_topk.

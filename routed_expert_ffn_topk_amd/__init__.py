@@ -28,7 +28,8 @@ MOE_FFN_ERR_BAD_IDS = -7
 MOE_FFN_MAX_EXPERTS = 1024
 MOE_FFN_INT8_GROUP = 128
 
-LAYOUT_FIELDS = ("total_bytes", "meta", "counts", "offsets", "active", "sorted_slot", "h", "y")
+LAYOUT_FIELDS = ("total_bytes", "meta", "counts", "offsets", "active", "large", "sorted_slot",
+                 "h", "y")
 
 
 class MoeFfnError(RuntimeError):

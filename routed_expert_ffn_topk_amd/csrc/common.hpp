@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <climits>
+
 namespace moe {
 
 constexpr int kWave = 64;
@@ -46,5 +48,63 @@ __device__ __forceinline__ float silu(float g) {
 // Number of XCDs (accelerator dies with private L2) on gfx950; workgroups of
 // a launch are handed to them round-robin by workgroup id.
 constexpr int kXcds = 8;
+
+// LDS address space (destination of the direct global->LDS loads).
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// Wait until at most N vector-memory loads of this wave are outstanding
+// (loads complete in issue order), leaving LDS and export counters alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// ---------------------------------------------------------------------------
+// Wave-wide reductions with DPP (data-parallel primitives: a VALU operand
+// read from another lane of the same row).  Inclusive scan over the 64
+// lanes: shifts by 1, 2, 4 and 8 lanes within each row of 16, then the last
+// lane of row 0 / row 2 into rows 1 / 3 (row_bcast:15), then lane 31 into
+// rows 2 and 3 (row_bcast:31).  Lane 63 ends with the total.  Lanes whose
+// source is outside the row, or rows masked off, take the identity.  All 64
+// lanes must be active.
+// ---------------------------------------------------------------------------
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114,
+              kDppRowShr8 = 0x118, kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+template <class Op>
+__device__ __forceinline__ int wave_scan_i32(int v, int identity, Op op) {
+    v = op(v, __builtin_amdgcn_update_dpp(identity, v, kDppRowShr1, 0xf, 0xf, false));
+    v = op(v, __builtin_amdgcn_update_dpp(identity, v, kDppRowShr2, 0xf, 0xf, false));
+    v = op(v, __builtin_amdgcn_update_dpp(identity, v, kDppRowShr4, 0xf, 0xf, false));
+    v = op(v, __builtin_amdgcn_update_dpp(identity, v, kDppRowShr8, 0xf, 0xf, false));
+    v = op(v, __builtin_amdgcn_update_dpp(identity, v, kDppRowBcast15, 0xa, 0xf, false));
+    v = op(v, __builtin_amdgcn_update_dpp(identity, v, kDppRowBcast31, 0xc, 0xf, false));
+    return v;
+}
+
+__device__ __forceinline__ int wave_max_i32(int v) {
+    v = wave_scan_i32(v, INT_MIN, [](int a, int b) { return a > b ? a : b; });
+    return __builtin_amdgcn_readlane(v, kWave - 1);
+}
+
+__device__ __forceinline__ int wave_min_i32(int v) {
+    v = wave_scan_i32(v, INT_MAX, [](int a, int b) { return a < b ? a : b; });
+    return __builtin_amdgcn_readlane(v, kWave - 1);
+}
+
+// Inclusive prefix sum over the lanes.
+__device__ __forceinline__ int wave_prefix_sum_i32(int v) {
+    return wave_scan_i32(v, 0, [](int a, int b) { return a + b; });
+}
+
+// Sum over the lanes, in the fixed order of the scan.
+__device__ __forceinline__ float wave_sum_f32(float v) {
+    auto add = [](int a, int b) {
+        return __builtin_bit_cast(int, __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b));
+    };
+    const int r = wave_scan_i32(__builtin_bit_cast(int, v), 0, add);
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(r, kWave - 1));
+}
 
 }  // namespace moe

@@ -50,16 +50,6 @@ constexpr int kTokRowU4 = kSlabBlocks * kBlockU4;   // one token's slab row (1 K
 __device__ __forceinline__ int tok_base(int c) { return c * (kTokRowU4 + 2); }
 constexpr int kSlabU4 = 16 * (kTokRowU4 + 2);     // slab buffer of 16 token rows
 
-typedef __attribute__((address_space(3))) void* lds_void_ptr;
-
-// Wait until at most N vector-memory loads of this wave are outstanding
-// (loads complete in issue order), leaving LDS and export counters alone.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 // One grouped expert product: for every active expert e and gathered row p
 // of e, out[p][n] = sum_k W[e][n][k] * B[p][k].
 struct ExpertGemm {
@@ -551,9 +541,13 @@ template <class Fmt>
 hipError_t launch_ffn(const uint16_t* x, const Routing& route, const FfnWeights& W,
                       uint16_t* out, const FfnShape& s, const Workspace& ws, int num_cu,
                       const StageEvents& ev, const SplitOverride& split, hipStream_t stream) {
-    hipError_t err = route.logits
-                         ? launch_route_permute(route.logits, route.ids, route.w, s, ws, stream)
-                         : launch_permute(route.ids, s, ws, stream);
+    // experts with many tokens go to the tiled product (BF16 weights, batches
+    // large enough that an expert can have more than kTiledMinTokens)
+    const bool tiled = Fmt::kBytesPerWeight == 2 && s.T > kTiledMinBatch;
+    const int m_split = tiled ? kTiledMinTokens : INT_MAX;
+    hipError_t err =
+        route.logits ? launch_route_permute(route.logits, route.ids, route.w, s, ws, m_split, stream)
+                     : launch_permute(route.ids, s, ws, m_split, stream);
     if (err == hipSuccess) err = ev.mark(0, stream);
     if (err != hipSuccess) return err;
     // upper bound of active experts: every slot could name a different one
@@ -577,6 +571,7 @@ hipError_t launch_ffn(const uint16_t* x, const Routing& route, const FfnWeights&
     gu.top_k = s.k;
     gu.split = split.gate_up;
     err = launch_gemm<Fmt, 2>(gu, max_active, num_cu, stream);
+    if (err == hipSuccess && tiled) err = launch_tiled_gate_up(x, W, s, ws, num_cu, stream);
     if (err == hipSuccess) err = ev.mark(1, stream);
     if (err != hipSuccess) return err;
 
@@ -593,6 +588,7 @@ hipError_t launch_ffn(const uint16_t* x, const Routing& route, const FfnWeights&
     dn.K = s.I;
     dn.split = split.down;
     err = launch_gemm<Fmt, 1>(dn, max_active, num_cu, stream);
+    if (err == hipSuccess && tiled) err = launch_tiled_down(W, s, ws, num_cu, stream);
     if (err == hipSuccess) err = ev.mark(2, stream);
     if (err != hipSuccess) return err;
     err = launch_combine(ws.y, route.ids, route.w, out, s, stream);

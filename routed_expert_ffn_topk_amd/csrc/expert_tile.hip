@@ -1,0 +1,291 @@
+// Tiled grouped expert product for experts with many routed tokens
+// (prefill-sized batches).
+//
+// HiNa-MoE §5.1: with long prompts the gathered token matrix I of an expert
+// grows until the FFN is compute-bound (the prefill FFN rates of Table 5);
+// the FFN equation of §4.1 and the BF16 operands with FP32 accumulation of
+// §4.2.1 are unchanged.  Weights stay in their row-major layout and only the
+// gathered rows are rearranged, as in the small-m product; what changes is
+// the reuse: a weight tile now serves up to 128 tokens, so both operands go
+// through LDS in tiles and the matrix unit, not HBM, sets the pace.
+//
+// Work unit: a tile of 128 weight rows x 128 gathered rows of one expert.
+// The four waves split it 2 x 2 (64 x 64 each, 4 x 4 MFMA 16x16x32 blocks
+// per matrix).  Per pipeline stage (K = 32) every operand tile (128 rows x 32
+// K, 8 KB) is written to LDS by direct global->LDS 16-byte loads, with the
+// gather of the token rows folded into the load addresses; three stages are
+// in flight.  Rows are stored 64 bytes apart with their four 16-byte chunks
+// XOR-swizzled by bit 2 of the row, so that the MFMA fragment reads (eight
+// rows x two K chunks at a time) hit distinct LDS banks.
+//
+// Schedule: the tiles of all experts on the large list, ordered (expert, row
+// tile, token tile) with token tiles fastest, are dealt out per XCD like the
+// small-m product's rounds (a contiguous slice per XCD, interleaved over its
+// workgroups): the token tiles that share a weight tile run at the same time
+// on one XCD, so the weight tile comes from HBM once and from L2 after that.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int kTileN = 128;                       // weight rows per tile
+constexpr int kTileM = 128;                       // gathered rows per tile
+constexpr int kTileK = 32;                        // K per pipeline stage
+constexpr int kTileStages = 3;
+constexpr int kTileWaves = 4;                     // 2 x 2 waves of 64 x 64
+constexpr int kTileThreads = kTileWaves * kWave;
+constexpr int kRowWords = kTileK / 8;             // 16-byte words of a row per stage
+constexpr int kOperandWords = 128 * kRowWords;    // one 128-row operand tile (8 KB)
+constexpr int kMaxLarge = 1024;                   // matches MOE_FFN_MAX_EXPERTS
+
+// LDS word of row r, logical 16-byte chunk c (K values 8c .. 8c+7 of the
+// stage) in an operand tile.
+__device__ __forceinline__ int tile_word(int r, int c) {
+    return r * kRowWords + (c ^ ((r >> 1) & 2));
+}
+
+struct TiledGemm {
+    const uint16_t* b_src;    // gathered rows: x (gate/up) or h (down)
+    const uint16_t* w0;       // W_gate or W_down, [E][N][K] BF16
+    const uint16_t* w1;       // W_up (gate/up only)
+    const int32_t* meta;      // [2] = experts on the large list
+    const int32_t* offsets;
+    const int32_t* large;
+    const int32_t* sorted_slot;
+    uint16_t* h;              // gate/up output, row p at p * N
+    float* y;                 // down output, slot s at s * N
+    int b_pitch;              // elements between B rows
+    int N, K;
+    int top_k;
+};
+
+// Resident workgroups per CU (LDS: 3 stages x (NMAT + 1) x 8 KB + 4 KB).
+template <int NMAT>
+struct TileTuning;
+template <>
+struct TileTuning<2> {
+    static constexpr int kBlocksPerCU = 2;
+};
+template <>
+struct TileTuning<1> {
+    static constexpr int kBlocksPerCU = 3;
+};
+
+template <int NMAT>
+__global__ __launch_bounds__(kTileThreads)
+__attribute__((amdgpu_waves_per_eu(TileTuning<NMAT>::kBlocksPerCU)))
+void expert_tile_kernel(const TiledGemm g) {
+    constexpr int kStageWords = (NMAT + 1) * kOperandWords;
+    constexpr int kLoads = 2 * (NMAT + 1);        // load instructions per wave and stage
+    __shared__ u32x4 lds[kTileStages * kStageWords];
+    __shared__ int pre[kMaxLarge + 1];
+
+    const int n_large = g.meta[2];
+    if (n_large <= 0) return;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int rt_n = (g.N + kTileN - 1) / kTileN;     // row tiles per expert
+
+    // tiles before large expert a: pre[a] (wave 0, one run of experts per lane)
+    if (wave == 0) {
+        const int per = (n_large + kWave - 1) / kWave;
+        const int a0 = min(n_large, lane * per), a1 = min(n_large, a0 + per);
+        int cnt = 0;
+        for (int a = a0; a < a1; ++a) {
+            const int e = g.large[a];
+            cnt += rt_n * ((g.offsets[e + 1] - g.offsets[e] + kTileM - 1) / kTileM);
+        }
+        const int inc = wave_prefix_sum_i32(cnt);
+        int b = inc - cnt;
+        for (int a = a0; a < a1; ++a) {
+            pre[a] = b;
+            const int e = g.large[a];
+            b += rt_n * ((g.offsets[e + 1] - g.offsets[e] + kTileM - 1) / kTileM);
+        }
+        if (lane == kWave - 1) pre[n_large] = inc;
+    }
+    __syncthreads();
+    const int Q = pre[n_large];
+    const int G = min((int)gridDim.x, (Q + kXcds - 1) / kXcds * kXcds);
+    if ((int)blockIdx.x >= G) return;
+
+    const int xcd = blockIdx.x % kXcds;
+    const int per = G / kXcds;
+    const int li = blockIdx.x / kXcds;
+    const int qb = (int)((long long)xcd * Q / kXcds);
+    const int qe = (int)((long long)(xcd + 1) * Q / kXcds);
+    const int wr = wave & 1;          // 64-row half of the weight tile
+    const int wm = wave >> 1;         // 64-row half of the token tile
+    const int col = lane & 15;        // A row, B column and D column of this lane
+    const int kg = lane >> 4;         // K chunk of the operands, row quad of D
+    // staging: load instruction i of this wave fills rows 16 (wave + 4i) ..
+    // +16 of an operand tile; lane L brings row + (L >> 2), logical chunk cl
+    const int cl = (lane & 3) ^ ((lane >> 3) & 2);
+    const int nk = g.K / kTileK;
+
+    for (int q = qb + li; q < qe; q += per) {
+        int lo = 0, hi = n_large - 1;                 // last a with pre[a] <= q
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (pre[mid] <= q)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        const int e = g.large[lo];
+        const int beg = g.offsets[e];
+        const int m = g.offsets[e + 1] - beg;
+        const int mt_n = (m + kTileM - 1) / kTileM;
+        const int r = q - pre[lo];
+        const int rt = r / mt_n;
+        const int row0 = rt * kTileN;
+        const int p0 = (r - rt * mt_n) * kTileM;
+
+        // per-lane source rows of the staging loads (rows past the matrix or
+        // past the expert's tokens repeat a valid row; their results are
+        // never stored)
+        const uint16_t* wsrc[NMAT][2];
+        const uint16_t* bsrc[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int rr = 16 * (wave + 4 * i) + (lane >> 2);
+            const size_t wrow = (size_t)e * g.N + min(row0 + rr, g.N - 1);
+            wsrc[0][i] = g.w0 + wrow * g.K + cl * 8;
+            if constexpr (NMAT == 2) wsrc[1][i] = g.w1 + wrow * g.K + cl * 8;
+            const int pp = beg + min(p0 + rr, m - 1);
+            const int brow = NMAT == 2 ? g.sorted_slot[pp] / g.top_k : pp;
+            bsrc[i] = g.b_src + (size_t)brow * g.b_pitch + cl * 8;
+        }
+        auto issue = [&](int s) {
+            u32x4* buf = lds + (s % kTileStages) * kStageWords;
+            const int k0 = s * kTileK;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int dst = (wave + 4 * i) * kWave;
+#pragma unroll
+                for (int mm = 0; mm < NMAT; ++mm)
+                    __builtin_amdgcn_global_load_lds((const void*)(wsrc[mm][i] + k0),
+                                                     (lds_void_ptr)&buf[mm * kOperandWords + dst],
+                                                     16, 0, 0);
+                __builtin_amdgcn_global_load_lds((const void*)(bsrc[i] + k0),
+                                                 (lds_void_ptr)&buf[NMAT * kOperandWords + dst],
+                                                 16, 0, 0);
+            }
+        };
+
+        f32x4 acc[NMAT][4][4];
+#pragma unroll
+        for (int mm = 0; mm < NMAT; ++mm)
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) acc[mm][rb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        issue(0);
+        if (nk > 1) issue(1);
+        for (int s = 0; s < nk; ++s) {
+            // this wave's loads of stage s are done (stage s + 1 may still be
+            // in flight), then everyone's: the stage is complete in LDS and
+            // every wave has finished with the buffer stage s + 2 reuses
+            if (s + 1 < nk)
+                wait_vmcnt<kLoads>();
+            else
+                wait_vmcnt<0>();
+            __syncthreads();
+            if (s + 2 < nk) issue(s + 2);
+            const u32x4* buf = lds + (s % kTileStages) * kStageWords;
+            u32x4 af[NMAT][4];
+#pragma unroll
+            for (int mm = 0; mm < NMAT; ++mm)
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb)
+                    af[mm][rb] = buf[mm * kOperandWords + tile_word(64 * wr + 16 * rb + col, kg)];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                const u32x4 bf = buf[NMAT * kOperandWords + tile_word(64 * wm + 16 * tb + col, kg)];
+#pragma unroll
+                for (int mm = 0; mm < NMAT; ++mm)
+#pragma unroll
+                    for (int rb = 0; rb < 4; ++rb)
+                        acc[mm][rb][tb] =
+                            mfma16x16x32(as_bf16x8(af[mm][rb]), as_bf16x8(bf), acc[mm][rb][tb]);
+            }
+        }
+        // every wave is done with the stage buffers before the next tile's
+        // first stages overwrite them
+        __syncthreads();
+
+        // epilogue: lane holds rows n .. n+3 of token column p for each block
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+            const int n = row0 + 64 * wr + 16 * rb + 4 * kg;
+            if (n >= g.N) continue;
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                const int p = p0 + 64 * wm + 16 * tb + col;
+                if (p >= m) continue;
+                if constexpr (NMAT == 2) {
+                    const f32x4 gv = acc[0][rb][tb], uv = acc[1][rb][tb];
+                    u32x2 packed;
+                    packed.x = (uint32_t)f32_to_bf16_bits(silu(gv.x) * uv.x) |
+                               ((uint32_t)f32_to_bf16_bits(silu(gv.y) * uv.y) << 16);
+                    packed.y = (uint32_t)f32_to_bf16_bits(silu(gv.z) * uv.z) |
+                               ((uint32_t)f32_to_bf16_bits(silu(gv.w) * uv.w) << 16);
+                    *reinterpret_cast<u32x2*>(g.h + (size_t)(beg + p) * g.N + n) = packed;
+                } else {
+                    const int slot = g.sorted_slot[beg + p];
+                    *reinterpret_cast<f32x4*>(g.y + (size_t)slot * g.N + n) = acc[0][rb][tb];
+                }
+            }
+        }
+    }
+}
+
+template <int NMAT>
+hipError_t launch_tile(const TiledGemm& g, int num_cu, hipStream_t stream) {
+    int grid = num_cu * TileTuning<NMAT>::kBlocksPerCU;
+    grid = (grid + kXcds - 1) / kXcds * kXcds;
+    hipLaunchKernelGGL((expert_tile_kernel<NMAT>), dim3(grid), dim3(kTileThreads), 0, stream, g);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_tiled_gate_up(const uint16_t* x, const FfnWeights& W, const FfnShape& s,
+                                const Workspace& ws, int num_cu, hipStream_t stream) {
+    TiledGemm g{};
+    g.b_src = x;
+    g.w0 = static_cast<const uint16_t*>(W.gate);
+    g.w1 = static_cast<const uint16_t*>(W.up);
+    g.meta = ws.meta;
+    g.offsets = ws.offsets;
+    g.large = ws.large;
+    g.sorted_slot = ws.sorted_slot;
+    g.h = ws.h;
+    g.b_pitch = s.H;
+    g.N = s.I;
+    g.K = s.H;
+    g.top_k = s.k;
+    return launch_tile<2>(g, num_cu, stream);
+}
+
+hipError_t launch_tiled_down(const FfnWeights& W, const FfnShape& s, const Workspace& ws,
+                             int num_cu, hipStream_t stream) {
+    TiledGemm g{};
+    g.b_src = ws.h;
+    g.w0 = static_cast<const uint16_t*>(W.down);
+    g.meta = ws.meta;
+    g.offsets = ws.offsets;
+    g.large = ws.large;
+    g.sorted_slot = ws.sorted_slot;
+    g.y = ws.y;
+    g.b_pitch = s.I;
+    g.N = s.H;
+    g.K = s.I;
+    g.top_k = s.k;
+    return launch_tile<1>(g, num_cu, stream);
+}
+
+}  // namespace moe

@@ -9,10 +9,11 @@ namespace moe {
 
 // Pointers into the caller's workspace, carved by the C-ABI layer.
 struct Workspace {
-    int32_t* meta;         // [0] active experts, [1] dropped slots
+    int32_t* meta;         // [0] experts of active, [1] dropped slots, [2] experts of large
     int32_t* counts;       // [E]
     int32_t* offsets;      // [E+1]
-    int32_t* active;       // [E]
+    int32_t* active;       // [E] experts of the small-m product
+    int32_t* large;        // [E] experts of the tiled product
     int32_t* sorted_slot;  // [T*k]
     uint16_t* h;           // [T*k][I] bf16, sorted order
     float* y;              // [T*k][H] f32, slot order
@@ -61,13 +62,16 @@ struct FfnWeights {
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids,
                              float* w, hipStream_t stream);
 
+// Gather index of ids [T][k]; experts with more than m_split slots are listed
+// for the tiled product (INT_MAX: none).
 hipError_t launch_permute(const int32_t* ids, const FfnShape& s, const Workspace& ws,
-                          hipStream_t stream);
+                          int m_split, hipStream_t stream);
 
 // Router and gather index from logits [T][E]: writes ids / w [T][k] and the
 // workspace's gather index (one launch for decode-sized batches).
 hipError_t launch_route_permute(const float* logits, int32_t* ids, float* w,
-                                const FfnShape& s, const Workspace& ws, hipStream_t stream);
+                                const FfnShape& s, const Workspace& ws, int m_split,
+                                hipStream_t stream);
 
 hipError_t launch_ffn_bf16(const uint16_t* x, const Routing& route, const FfnWeights& W,
                            uint16_t* out, const FfnShape& s, const Workspace& ws, int num_cu,
@@ -78,6 +82,18 @@ hipError_t launch_ffn_int8(const uint16_t* x, const Routing& route, const FfnWei
                            uint16_t* out, const FfnShape& s, const Workspace& ws, int num_cu,
                            const StageEvents& ev, const SplitOverride& split,
                            hipStream_t stream);
+
+// Tiled products (BF16) over the workspace's large list: gate/up with the
+// SiLU*up epilogue into h, and down into y.
+hipError_t launch_tiled_gate_up(const uint16_t* x, const FfnWeights& W, const FfnShape& s,
+                                const Workspace& ws, int num_cu, hipStream_t stream);
+hipError_t launch_tiled_down(const FfnWeights& W, const FfnShape& s, const Workspace& ws,
+                             int num_cu, hipStream_t stream);
+
+// The tiled product takes experts with more than kTiledMinTokens tokens in
+// batches of more than kTiledMinBatch tokens (BF16 weights).
+constexpr int kTiledMinBatch = 64;
+constexpr int kTiledMinTokens = 32;
 
 // Weighted combine shared by both weight formats.
 hipError_t launch_combine(const float* y, const int32_t* ids, const float* w,

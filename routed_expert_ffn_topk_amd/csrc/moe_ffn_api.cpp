@@ -76,6 +76,7 @@ moe::Workspace carve(void* base, const moe_ffn_ws_layout& L) {
     ws.counts = reinterpret_cast<int32_t*>(b + L.counts);
     ws.offsets = reinterpret_cast<int32_t*>(b + L.offsets);
     ws.active = reinterpret_cast<int32_t*>(b + L.active);
+    ws.large = reinterpret_cast<int32_t*>(b + L.large);
     ws.sorted_slot = reinterpret_cast<int32_t*>(b + L.sorted_slot);
     ws.h = reinterpret_cast<uint16_t*>(b + L.h);
     ws.y = reinterpret_cast<float*>(b + L.y);
@@ -124,6 +125,8 @@ int moe_ffn_workspace_layout(int64_t T, int64_t H, int64_t I, int32_t E, int32_t
     layout->offsets = off;
     off += round_up(((size_t)E + 1) * sizeof(int32_t));
     layout->active = off;
+    off += round_up((size_t)E * sizeof(int32_t));
+    layout->large = off;
     off += round_up((size_t)E * sizeof(int32_t));
     layout->sorted_slot = off;
     off += round_up((S ? S : 1) * sizeof(int32_t));

@@ -4,7 +4,6 @@
 // permute:       the per-expert token lists that drive the gather of §4.1
 //                (each expert's routed tokens form one small matrix).
 // route_permute: both in one workgroup, for decode-sized batches.
-#include <climits>
 #include <cmath>
 
 #include "common.hpp"
@@ -15,61 +14,12 @@ namespace moe {
 namespace {
 
 constexpr int kMaxExperts = 1024;          // matches MOE_FFN_MAX_EXPERTS
-// Slots the gather-index kernels keep in LDS; larger batches take the
-// chunked scatter that reads the ids from memory.
-constexpr int kPermMaxSlots = 8192;
 // The fused router + gather index: batches of at most this many tokens and
-// slots (16 waves route up to four tokens each), with the logits staged in
-// LDS when the batch's T*E fits.
+// slots (16 waves route up to four tokens each; one wave places the slots),
+// with the logits staged in LDS when the batch's T*E fits.
 constexpr int kRoutePermMaxTokens = 64;
-constexpr int kRoutePermMaxSlots = 4096;
+constexpr int kRoutePermMaxSlots = 512;
 constexpr int kRoutePermMaxLogits = 16384;
-
-// ---------------------------------------------------------------------------
-// Wave-wide reductions with DPP (data-parallel primitives: a VALU operand
-// read from another lane of the same row).  Inclusive scan over the 64
-// lanes: shifts by 1, 2, 4 and 8 lanes within each row of 16, then the last
-// lane of row 0 / row 2 into rows 1 / 3 (row_bcast:15), then lane 31 into
-// rows 2 and 3 (row_bcast:31).  Lane 63 ends with the total.  Lanes whose
-// source is outside the row, or rows masked off, take the identity.
-// ---------------------------------------------------------------------------
-constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114,
-              kDppRowShr8 = 0x118, kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
-
-template <class Op>
-__device__ __forceinline__ int wave_scan_i32(int v, int identity, Op op) {
-    v = op(v, __builtin_amdgcn_update_dpp(identity, v, kDppRowShr1, 0xf, 0xf, false));
-    v = op(v, __builtin_amdgcn_update_dpp(identity, v, kDppRowShr2, 0xf, 0xf, false));
-    v = op(v, __builtin_amdgcn_update_dpp(identity, v, kDppRowShr4, 0xf, 0xf, false));
-    v = op(v, __builtin_amdgcn_update_dpp(identity, v, kDppRowShr8, 0xf, 0xf, false));
-    v = op(v, __builtin_amdgcn_update_dpp(identity, v, kDppRowBcast15, 0xa, 0xf, false));
-    v = op(v, __builtin_amdgcn_update_dpp(identity, v, kDppRowBcast31, 0xc, 0xf, false));
-    return v;
-}
-
-__device__ __forceinline__ int wave_max_i32(int v) {
-    v = wave_scan_i32(v, INT_MIN, [](int a, int b) { return a > b ? a : b; });
-    return __builtin_amdgcn_readlane(v, kWave - 1);
-}
-
-__device__ __forceinline__ int wave_min_i32(int v) {
-    v = wave_scan_i32(v, INT_MAX, [](int a, int b) { return a < b ? a : b; });
-    return __builtin_amdgcn_readlane(v, kWave - 1);
-}
-
-// Inclusive prefix sum over the lanes.
-__device__ __forceinline__ int wave_prefix_sum_i32(int v) {
-    return wave_scan_i32(v, 0, [](int a, int b) { return a + b; });
-}
-
-// Sum over the lanes, in the fixed order of the scan.
-__device__ __forceinline__ float wave_sum_f32(float v) {
-    auto add = [](int a, int b) {
-        return __builtin_bit_cast(int, __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b));
-    };
-    const int r = wave_scan_i32(__builtin_bit_cast(int, v), 0, add);
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(r, kWave - 1));
-}
 
 // Order-preserving integer key of a float (not NaN): keys compare as the
 // values do, and -0 is mapped to +0 so that the two tie.  INT_MIN is the key
@@ -164,20 +114,63 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
 
 // ---------------------------------------------------------------------------
 // Gather index: stable counting sort of the n slots by expert.  Writes
-// counts, offsets (exclusive prefix), the ascending list of active experts,
-// and sorted_slot (expert-major, slot order within an expert).  Slots with
-// ids outside [0, E) are left out and counted in meta[1].
+// counts, offsets (exclusive prefix), the ascending lists of active experts
+// (split by token count between the small-m and the tiled product), and
+// sorted_slot (expert-major, slot order within an expert).  Slots with ids
+// outside [0, E) are left out and counted in meta[1].
 // ---------------------------------------------------------------------------
 
-// Per-expert counts of the n slots (all NT threads), then the exclusive scan
-// and the tables (wave 0 alone: each lane owns a run of up to 16 consecutive
-// experts).  base[] receives the offsets.  Ends with a barrier.
+// The experts' offsets (exclusive scan of cnt[]) and lists, by wave 0 alone
+// (each lane owns a run of up to 16 consecutive experts).  Experts with more
+// than m_split slots go to the large list (the tiled product), the other
+// active ones to the active list (the small-m product).  base[] receives the
+// offsets.
+__device__ __forceinline__ void scan_experts(const int* cnt, int E, int m_split, int nbad,
+                                             int* base, int32_t* __restrict__ meta,
+                                             int32_t* __restrict__ counts,
+                                             int32_t* __restrict__ offsets,
+                                             int32_t* __restrict__ active,
+                                             int32_t* __restrict__ large) {
+    const int lane = threadIdx.x;
+    const int per = (E + kWave - 1) / kWave;
+    const int e0 = min(E, lane * per), e1 = min(E, e0 + per);
+    int lc = 0, la = 0, ll = 0;
+    for (int e = e0; e < e1; ++e) {
+        lc += cnt[e];
+        la += cnt[e] > 0 && cnt[e] <= m_split;
+        ll += cnt[e] > m_split;
+    }
+    const int ic = wave_prefix_sum_i32(lc);
+    const int ia = wave_prefix_sum_i32(la);
+    const int il = wave_prefix_sum_i32(ll);
+    int bc = ic - lc, ba = ia - la, bl = il - ll;
+    for (int e = e0; e < e1; ++e) {
+        base[e] = bc;
+        offsets[e] = bc;
+        counts[e] = cnt[e];
+        if (cnt[e] > m_split)
+            large[bl++] = e;
+        else if (cnt[e] > 0)
+            active[ba++] = e;
+        bc += cnt[e];
+    }
+    if (lane == kWave - 1) {
+        offsets[E] = ic;
+        meta[0] = ia;
+        meta[1] = nbad;
+        meta[2] = il;
+    }
+}
+
+// Per-expert counts of the n slots (all NT threads), then scan_experts.
+// Ends with a barrier.
 template <int NT, class Ids>
-__device__ __forceinline__ void count_and_scan(Ids ids, int n, int E, int* cnt, int* base,
-                                               int* nbad, int32_t* __restrict__ meta,
+__device__ __forceinline__ void count_and_scan(Ids ids, int n, int E, int m_split, int* cnt,
+                                               int* base, int* nbad, int32_t* __restrict__ meta,
                                                int32_t* __restrict__ counts,
                                                int32_t* __restrict__ offsets,
-                                               int32_t* __restrict__ active) {
+                                               int32_t* __restrict__ active,
+                                               int32_t* __restrict__ large) {
     const int tid = threadIdx.x;
     for (int e = tid; e < E; e += NT) cnt[e] = 0;
     if (tid == 0) *nbad = 0;
@@ -190,46 +183,27 @@ __device__ __forceinline__ void count_and_scan(Ids ids, int n, int E, int* cnt, 
             atomicAdd(nbad, 1);
     }
     __syncthreads();
-    if (tid < kWave) {
-        const int per = (E + kWave - 1) / kWave;
-        const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
-        int lc = 0, la = 0;
-        for (int e = e0; e < e1; ++e) {
-            lc += cnt[e];
-            la += cnt[e] > 0;
-        }
-        const int ic = wave_prefix_sum_i32(lc);
-        const int ia = wave_prefix_sum_i32(la);
-        int bc = ic - lc, ba = ia - la;
-        for (int e = e0; e < e1; ++e) {
-            base[e] = bc;
-            offsets[e] = bc;
-            counts[e] = cnt[e];
-            if (cnt[e] > 0) active[ba++] = e;
-            bc += cnt[e];
-        }
-        if (tid == kWave - 1) {
-            offsets[E] = ic;
-            meta[0] = ia;
-            meta[1] = *nbad;
-        }
-    }
+    if (tid < kWave) scan_experts(cnt, E, m_split, *nbad, base, meta, counts, offsets, active, large);
     __syncthreads();
 }
 
-// Stable scatter by wave 0 over the slots in LDS, 64 at a time: a slot's
-// place is its expert's offset, plus the slots of that expert in earlier
-// chunks (run[e]), plus the lanes below it in this chunk with the same
-// expert.  Lanes with equal ids are found bit by bit with ballots; the last
-// lane of each group advances run[e].  run[] is the base[] table, advanced in
-// place (LDS operations of one wave complete in order).
-__device__ __forceinline__ void scatter_wave(const int* __restrict__ sid, int n, int E,
-                                             int* run, int32_t* __restrict__ sorted_slot) {
-    const int lane = threadIdx.x;
-    for (int c0 = 0; c0 < n; c0 += kWave) {
+// Stable scatter of slots [s0, s1) by one wave, 64 at a time (the next
+// chunk's ids are requested before this one is placed): a slot's place is
+// run[e] (its expert's offset plus the slots of that expert placed before
+// this chunk) plus the lanes below it in this chunk with the same expert.
+// Lanes with equal ids are found bit by bit with ballots; the last lane of
+// each group advances run[e] (LDS operations of one wave complete in order).
+template <class Ids>
+__device__ __forceinline__ void scatter_range(Ids ids, int s0, int s1, int E, int* run,
+                                              int32_t* __restrict__ sorted_slot) {
+    const int lane = threadIdx.x & (kWave - 1);
+    int e_next = s0 + lane < s1 ? ids(s0 + lane) : -1;
+    for (int c0 = s0; c0 < s1; c0 += kWave) {
         const int s = c0 + lane;
-        const int e = s < n ? sid[s] : -1;
-        const bool ok = e >= 0 && e < E;
+        const int e = e_next;
+        const int sn = s + kWave;
+        e_next = sn < s1 ? ids(sn) : -1;
+        const bool ok = s < s1 && e >= 0 && e < E;
         const int key = ok ? e : kMaxExperts;   // every dropped slot in one group
         unsigned long long eq = ~0ull;
 #pragma unroll
@@ -248,32 +222,13 @@ __device__ __forceinline__ void scatter_wave(const int* __restrict__ sid, int n,
     }
 }
 
-// The chunked scatter for batches beyond the LDS copy: all threads, one
-// chunk of NT slots at a time, the rank within a chunk by a scan over the
-// lower threads' ids.
-template <int NT>
-__device__ __forceinline__ void scatter_chunks(const int32_t* __restrict__ ids, int n, int E,
-                                               int* run, int* chunk_e,
-                                               int32_t* __restrict__ sorted_slot) {
-    const int tid = threadIdx.x;
-    for (int c0 = 0; c0 < n; c0 += NT) {
-        const int s = c0 + tid;
-        const int e = s < n ? ids[s] : -1;
-        const bool ok = e >= 0 && e < E;
-        chunk_e[tid] = ok ? e : -1;
-        __syncthreads();
-        if (ok) {
-            int rank = 0;
-            for (int j = 0; j < tid; ++j) rank += chunk_e[j] == e;
-            sorted_slot[run[e] + rank] = s;
-        }
-        __syncthreads();
-        if (ok) atomicAdd(&run[e], 1);
-        __syncthreads();
-    }
-}
-
-constexpr int kPermThreads = 256;
+// Batches up to this many slots: ids staged in LDS, counted by all threads,
+// placed by one wave.  Larger batches: every wave counts, then places, a
+// contiguous range of slots, starting from the slots of each expert in the
+// ranges before it.
+constexpr int kOneWaveSlots = 512;
+constexpr int kPermThreads = 1024;
+constexpr int kPermWaves = kPermThreads / kWave;
 
 struct GlobalIds {
     const int32_t* p;
@@ -285,25 +240,76 @@ struct LdsIds {
 };
 
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(
-    const int32_t* __restrict__ ids, int n, int E, int32_t* __restrict__ meta,
+    const int32_t* __restrict__ ids, int n, int E, int m_split, int32_t* __restrict__ meta,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ active, int32_t* __restrict__ sorted_slot) {
+    int32_t* __restrict__ active, int32_t* __restrict__ large,
+    int32_t* __restrict__ sorted_slot) {
     __shared__ int cnt[kMaxExperts];
     __shared__ int base[kMaxExperts];
-    __shared__ int sid[kPermMaxSlots];
-    __shared__ int chunk_e[kPermThreads];
+    __shared__ int sid[kOneWaveSlots];
+    __shared__ int hist[kPermWaves * kMaxExperts];   // per-wave counts, then runs
+    __shared__ int nbad_w[kPermWaves];
     __shared__ int nbad;
-    if (n <= kPermMaxSlots) {
-        for (int s = threadIdx.x; s < n; s += kPermThreads) sid[s] = ids[s];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    if (n <= kOneWaveSlots) {
+        for (int s = tid; s < n; s += kPermThreads) sid[s] = ids[s];
         __syncthreads();
-        count_and_scan<kPermThreads>(LdsIds{sid}, n, E, cnt, base, &nbad, meta, counts, offsets,
-                                     active);
-        if (threadIdx.x < kWave) scatter_wave(sid, n, E, base, sorted_slot);
-    } else {
-        count_and_scan<kPermThreads>(GlobalIds{ids}, n, E, cnt, base, &nbad, meta, counts,
-                                     offsets, active);
-        scatter_chunks<kPermThreads>(ids, n, E, base, chunk_e, sorted_slot);
+        count_and_scan<kPermThreads>(LdsIds{sid}, n, E, m_split, cnt, base, &nbad, meta, counts,
+                                     offsets, active, large);
+        if (tid < kWave) scatter_range(LdsIds{sid}, 0, n, E, base, sorted_slot);
+        return;
     }
+    int* my = hist + wave * kMaxExperts;
+    for (int i = tid; i < kPermWaves * kMaxExperts; i += kPermThreads) hist[i] = 0;
+    __syncthreads();
+    const int s0 = (int)((long long)n * wave / kPermWaves);
+    const int s1 = (int)((long long)n * (wave + 1) / kPermWaves);
+    int bad = 0;
+    for (int c0 = s0; c0 < s1; c0 += 4 * kWave) {
+        int ev[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int s = c0 + u * kWave + lane;
+            ev[u] = s < s1 ? ids[s] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int s = c0 + u * kWave + lane;
+            if (s >= s1) continue;
+            if (ev[u] >= 0 && ev[u] < E)
+                atomicAdd(&my[ev[u]], 1);
+            else
+                ++bad;
+        }
+    }
+    bad = wave_prefix_sum_i32(bad);
+    if (lane == kWave - 1) nbad_w[wave] = bad;
+    __syncthreads();
+    // totals, and each wave's start within its expert's slots
+    for (int e = tid; e < E; e += kPermThreads) {
+        int c = 0;
+        for (int w = 0; w < kPermWaves; ++w) {
+            const int h = hist[w * kMaxExperts + e];
+            hist[w * kMaxExperts + e] = c;
+            c += h;
+        }
+        cnt[e] = c;
+    }
+    __syncthreads();
+    if (tid < kWave) {
+        int nb = 0;
+        for (int w = 0; w < kPermWaves; ++w) nb += nbad_w[w];
+        scan_experts(cnt, E, m_split, nb, base, meta, counts, offsets, active, large);
+    }
+    __syncthreads();
+    for (int i = tid; i < kPermWaves * E; i += kPermThreads) {
+        const int w = i / E, e = i - w * E;
+        hist[w * kMaxExperts + e] += base[e];
+    }
+    __syncthreads();
+    scatter_range(GlobalIds{ids}, s0, s1, E, my, sorted_slot);
 }
 
 // Router and gather index in one workgroup (decode-sized batches).  The
@@ -317,7 +323,7 @@ constexpr int kRoutePermThreads = 1024;
 __global__ __launch_bounds__(kRoutePermThreads) void route_permute_kernel(
     const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ ids,
     float* __restrict__ w, int32_t* __restrict__ meta, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ active,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ active, int32_t* __restrict__ large,
     int32_t* __restrict__ sorted_slot) {
     __shared__ float slg[kRoutePermMaxLogits];
     __shared__ int sid[kRoutePermMaxSlots];
@@ -345,9 +351,10 @@ __global__ __launch_bounds__(kRoutePermThreads) void route_permute_kernel(
     }
     __syncthreads();
     const int n = T * k;
-    count_and_scan<kRoutePermThreads>(LdsIds{sid}, n, E, cnt, base, &nbad, meta, counts,
-                                      offsets, active);
-    if (threadIdx.x < kWave) scatter_wave(sid, n, E, base, sorted_slot);
+    // decode-sized batches: every expert goes to the small-m product
+    count_and_scan<kRoutePermThreads>(LdsIds{sid}, n, E, INT_MAX, cnt, base, &nbad, meta,
+                                      counts, offsets, active, large);
+    if (threadIdx.x < kWave) scatter_range(LdsIds{sid}, 0, n, E, base, sorted_slot);
 }
 
 }  // namespace
@@ -363,23 +370,25 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
 }
 
 hipError_t launch_route_permute(const float* logits, int32_t* ids, float* w,
-                                const FfnShape& s, const Workspace& ws, hipStream_t stream) {
-    if (s.T > kRoutePermMaxTokens || (int64_t)s.T * s.k > kRoutePermMaxSlots) {
+                                const FfnShape& s, const Workspace& ws, int m_split,
+                                hipStream_t stream) {
+    if (s.T > kRoutePermMaxTokens || (int64_t)s.T * s.k > kRoutePermMaxSlots ||
+        m_split != INT_MAX) {
         // larger batches: the router on one wave per token, then the sort
         hipError_t err = launch_route_topk(logits, s.T, s.E, s.k, ids, w, stream);
-        return err == hipSuccess ? launch_permute(ids, s, ws, stream) : err;
+        return err == hipSuccess ? launch_permute(ids, s, ws, m_split, stream) : err;
     }
     hipLaunchKernelGGL(route_permute_kernel, dim3(1), dim3(kRoutePermThreads), 0, stream,
                        logits, s.T, s.E, s.k, ids, w, ws.meta, ws.counts, ws.offsets,
-                       ws.active, ws.sorted_slot);
+                       ws.active, ws.large, ws.sorted_slot);
     return hipGetLastError();
 }
 
 hipError_t launch_permute(const int32_t* ids, const FfnShape& s, const Workspace& ws,
-                          hipStream_t stream) {
+                          int m_split, hipStream_t stream) {
     hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), 0, stream, ids,
-                       s.T * s.k, s.E, ws.meta, ws.counts, ws.offsets, ws.active,
-                       ws.sorted_slot);
+                       s.T * s.k, s.E, m_split, ws.meta, ws.counts, ws.offsets, ws.active,
+                       ws.large, ws.sorted_slot);
     return hipGetLastError();
 }
 

@@ -141,6 +141,32 @@ def workload_case(name: str, device="cuda"):
     return wl, Case(x, ids, w, Wg, Wu, Wd, wl.E)
 
 
+# The layer hands experts with more than TILED_MIN_TOKENS tokens to the
+# tiled product when the batch has more than TILED_MIN_BATCH tokens and BF16
+# weights (the workspace's `large` list); every other active expert goes to
+# the small-m product (`active`).
+TILED_MIN_BATCH = 64
+TILED_MIN_TOKENS = 32
+
+
+def expected_lists(p: dict, T: int, int8: bool = False):
+    """(active, large) lists the gather index must produce, from the oracle's
+    permutation ``p``."""
+    act = p["active"]
+    if int8 or T <= TILED_MIN_BATCH:
+        return act, act[:0]
+    big = p["counts"][act] > TILED_MIN_TOKENS
+    return act[~big], act[big]
+
+
+def check_lists(r: dict, p: dict, T: int, int8: bool = False):
+    small, large = expected_lists(p, T, int8)
+    assert r["n_active"] == len(small)
+    assert np.array_equal(r["active"], small)
+    assert r["n_large"] == len(large)
+    assert np.array_equal(r["large"], large)
+
+
 def read_workspace(ws: torch.Tensor, L: dict, T: int, H: int, I: int, E: int, k: int):
     """Host copies of the workspace regions after a forward call."""
     b = ws.cpu().numpy()
@@ -153,6 +179,8 @@ def read_workspace(ws: torch.Tensor, L: dict, T: int, H: int, I: int, E: int, k:
         "counts": i32(L["counts"], E),
         "offsets": i32(L["offsets"], E + 1),
         "active": i32(L["active"], E)[: meta[0]],
+        "n_large": int(meta[2]),
+        "large": i32(L["large"], E)[: meta[2]],
         "sorted_slot": i32(L["sorted_slot"], S),
         "h": b[L["h"]:L["h"] + S * I * 2].view(np.uint16).reshape(S, I).copy(),
         "y": b[L["y"]:L["y"] + S * H * 4].view(np.float32).reshape(S, H).copy(),

@@ -46,7 +46,8 @@ def test_workspace_layout_regions_fit_and_align():
     T, H, I, E, k = 16, 7168, 2048, 256, 8
     L = moe.moe_ffn_workspace_layout(T, H, I, E, k)
     regions = [("meta", 8 * 4), ("counts", E * 4), ("offsets", (E + 1) * 4),
-               ("active", E * 4), ("sorted_slot", T * k * 4), ("h", T * k * I * 2),
+               ("active", E * 4), ("large", E * 4), ("sorted_slot", T * k * 4),
+               ("h", T * k * I * 2),
                ("y", T * k * H * 4)]
     end = 0
     for name, size in regions:

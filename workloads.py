@@ -72,6 +72,12 @@ def _registry() -> Dict[str, Workload]:
                                            E=8, k=2, T=T)
         w[f"qwen3_235b_t{T}"] = Workload(f"qwen3_235b_t{T}", H=4096, I=1536,
                                          E=128, k=8, T=T)
+    # prefill-sized batches (many tokens per expert) at the same expert shapes
+    for T in (512, 2048):
+        w[f"mixtral8x7b_t{T}"] = Workload(f"mixtral8x7b_t{T}", H=4096, I=14336,
+                                          E=8, k=2, T=T)
+    w["qwen3_235b_t2048"] = Workload("qwen3_235b_t2048", H=4096, I=1536, E=128, k=8, T=2048)
+    w["deepseekv3_t4096"] = Workload("deepseekv3_t4096", H=7168, I=2048, E=256, k=8, T=4096)
     return w
 
 
