@@ -11,11 +11,14 @@ each m (five layers).
 Other workloads: ``mixtral8x7b_int8_forced_m1-16`` (the same with INT8
 group-quantised weights), and any single layer of the workload registry
 (``deepseekv3_t16``, ``deepseekv3_zipf_t16``, ``mixtral8x22b_t{1,4,16}``,
-``qwen3_235b_t{1,4,16}``): one step = one call of that layer.  When the
-active experts' weights of a layer are small enough to stay in the 256 MB
-last-level cache between calls, the step cycles through several distinct
-weight sets (as consecutive layers of a model would), so that every call
-streams its weights from HBM.
+``qwen3_235b_t{1,4,16}``, and the prefill-sized ``mixtral8x7b_t{512,2048}``,
+``qwen3_235b_t2048``, ``deepseekv3_t4096``): one step = one call of that
+layer.  When the active experts' weights of a layer are small enough to stay
+in the 256 MB last-level cache between calls, the step cycles through several
+distinct weight sets (as consecutive layers of a model would), so that every
+call streams its weights from HBM.  Prefill-sized layers (more than 64 tokens,
+BF16) run the tiled product, which the matrix unit bounds: their roofline is
+reported in TFLOP/s against the dense BF16 peak.
 
 Inputs are resident in HBM before timing; the router runs once per batch
 before the timed region.  Printed (one JSON line): weight-stream throughput in
@@ -39,6 +42,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "µs per MoE FFN layer + weight-stream GB/s (% HBM peak), BF16, 1–16 tok/expert"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense BF16 matrix-unit peak of MI355X
+TILED_MIN_BATCH = 64             # batches above this take the tiled product (BF16)
 MS = (1, 2, 4, 8, 16)
 DEFAULT_WORKLOAD = "mixtral8x7b_forced_m1-16"
 ROTATE_BELOW = 2 << 30         # a step streams >= 2 GiB (8x the 256 MB last-level cache)
@@ -70,6 +75,15 @@ def layer_bytes(wl, active: int) -> int:
     return active * expert_bytes(wl) + 2 * wl.T * wl.H * 2 + wl.T * wl.k * 8
 
 
+def layer_flops(wl) -> float:
+    """Multiply-add FLOPs of one layer: 3 products of H x I per routed slot."""
+    return 6.0 * wl.T * wl.k * wl.H * wl.I
+
+
+def uses_tiled(wl) -> bool:
+    return not wl.int8 and wl.T > TILED_MIN_BATCH
+
+
 def gateup_bytes(wl, active: int) -> int:
     """Algorithmic bytes of one gate/up launch: W_gate and W_up (and their
     scales) of every active expert plus the token rows (h is scratch and not
@@ -78,32 +92,40 @@ def gateup_bytes(wl, active: int) -> int:
     return int(active * 2 * per) + wl.T * wl.H * 2
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "expert_gemm_mixtral8x7b_m1-16_hbm_traffic.md")
-KERNEL_SOURCES = ("routed_expert_ffn_topk_amd/csrc/expert_gemm.hip",
-                  "routed_expert_ffn_topk_amd/csrc/common.hpp")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
-def kernel_source_hash() -> str:
+def source_hash(files) -> str:
+    """First 16 hex digits of SHA-256 over the SHA-256 hex digests of the
+    given source files (paths relative to the repository root)."""
     digests = "".join(hashlib.sha256(open(os.path.join(ROOT, f), "rb").read()).hexdigest()
-                      for f in KERNEL_SOURCES)
+                      for f in files)
     return hashlib.sha256(digests.encode()).hexdigest()[:16]
 
 
 def recorded_traffic(workload: str):
-    """HBM bytes per gate/up launch from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE record (scaled by a plain copy of known size), or None when the
-    record is for another workload or the kernel sources have changed since
-    the counters were taken."""
-    try:
-        text = open(TRAFFIC_PROFILE).read()
-        digest = kernel_source_hash()
-    except OSError:
-        return None
-    rec = dict(re.findall(r"^(kernel_source_sha256_16|workload|gateup_traffic_bytes_per_launch): "
-                          r"(\S+)$", text, re.M))
-    if rec.get("kernel_source_sha256_16") != digest or rec.get("workload") != workload:
-        return None
-    return int(rec["gateup_traffic_bytes_per_launch"])
+    """HBM bytes per gate/up launch from a committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE record (profiles/*_hbm_traffic.md, scaled by a plain copy of
+    known size) for this workload, or None when there is none or the kernel
+    sources it names have changed since the counters were taken."""
+    import glob
+    for path in sorted(glob.glob(os.path.join(PROFILES, "*_hbm_traffic.md"))):
+        try:
+            text = open(path).read()
+        except OSError:
+            continue
+        rec = dict(re.findall(r"^(kernel_sources|kernel_source_sha256_16|workload|"
+                              r"gateup_traffic_bytes_per_launch): (\S+)$", text, re.M))
+        if rec.get("workload") != workload or "kernel_sources" not in rec:
+            continue
+        try:
+            digest = source_hash(rec["kernel_sources"].split(","))
+        except OSError:
+            return None
+        if rec.get("kernel_source_sha256_16") != digest:
+            return None
+        return int(rec["gateup_traffic_bytes_per_launch"])
+    return None
 
 
 def read_ceiling(stream, nbytes=4 << 30, reps=10) -> float:
@@ -278,6 +300,7 @@ def main():
             "T": b["wl"].T, "active_experts": b["active"], "us": round(us, 1),
             "GBps": round(lb / (us * 1e-6) / 1e9, 1),
             "pct_hbm_peak": round(100 * lb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
+            "TFLOPs": round(layer_flops(b["wl"]) / (us * 1e-6) / 1e12, 1),
         }
         if not int8:
             # the same layer from router logits (router fused with the gather
@@ -327,18 +350,35 @@ def main():
     for name, d in dur_l.items():
         per_layer[name]["stage_us"] = {n: round(statistics.mean(v), 1) for n, v in d.items()}
     gu_us = statistics.mean(dur["gateup"])
-    achieved = statistics.mean(gu_bytes) / (gu_us * 1e-6) / 1e9
-    kern = "expert_gemm_kernel<Int8Weights, 2, ...>" if int8 else \
-        "expert_gemm_kernel<Bf16Weights, 2, ...>"
     ceiling = read_ceiling(stream)
-    roofline = {"bound": "hbm", "kernel": f"{kern} (gate/up, SiLU*up epilogue)",
-                "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": recorded_traffic(args.workload),
-                "measured_read_ceiling": round(ceiling, 1),
-                "frac_of_measured_ceiling": round(achieved / ceiling, 4),
-                "algorithmic_bytes": int(statistics.mean(gu_bytes)), "avg_us": round(gu_us, 2),
-                "stage_us": {n: round(statistics.mean(v), 2) for n, v in dur.items()}}
+    if all(uses_tiled(b["wl"]) for b in batches):
+        # many tokens per expert: the tiled product is bound by the matrix
+        # unit; achieved = gate/up FLOPs per launch over the gate/up stage
+        # (the small-m launch before it finds no expert and exits)
+        gu_flops = statistics.mean(4.0 * b["wl"].T * b["wl"].k * b["wl"].H * b["wl"].I
+                                   for b in batches)
+        achieved = gu_flops / (gu_us * 1e-6) / 1e12
+        roofline = {"bound": "mfma",
+                    "kernel": "expert_tile_kernel<2> (gate/up, SiLU*up epilogue, tiled)",
+                    "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "traffic": recorded_traffic(args.workload),
+                    "algorithmic_flops": gu_flops, "avg_us": round(gu_us, 2),
+                    "measured_read_ceiling": round(ceiling, 1),
+                    "stage_us": {n: round(statistics.mean(v), 2) for n, v in dur.items()}}
+    else:
+        achieved = statistics.mean(gu_bytes) / (gu_us * 1e-6) / 1e9
+        kern = "expert_gemm_kernel<Int8Weights, 2, ...>" if int8 else \
+            "expert_gemm_kernel<Bf16Weights, 2, ...>"
+        roofline = {"bound": "hbm", "kernel": f"{kern} (gate/up, SiLU*up epilogue)",
+                    "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": recorded_traffic(args.workload),
+                    "measured_read_ceiling": round(ceiling, 1),
+                    "frac_of_measured_ceiling": round(achieved / ceiling, 4),
+                    "algorithmic_bytes": int(statistics.mean(gu_bytes)),
+                    "avg_us": round(gu_us, 2),
+                    "stage_us": {n: round(statistics.mean(v), 2) for n, v in dur.items()}}
 
     wl = layers[0]
     result = {
@@ -350,6 +390,8 @@ def main():
                    "experts": wl.E, "top_k": wl.k, "tokens": [b["wl"].T for b in batches],
                    "layers_per_step": len(batches) * n_sets, "weight_sets": n_sets,
                    "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
+                   "TFLOPs": round(sum(layer_flops(b["wl"]) for b in batches) * n_sets /
+                                   (ms_per_step * 1e-3) / 1e12, 1),
                    "pct_measured_read_ceiling": round(100 * value / ceiling, 1),
                    "per_layer": per_layer, "device": torch.cuda.get_device_name(dev)},
         "roofline": roofline,

@@ -222,13 +222,15 @@ __device__ __forceinline__ void scatter_range(Ids ids, int s0, int s1, int E, in
     }
 }
 
-// Batches up to this many slots: ids staged in LDS, counted by all threads,
-// placed by one wave.  Larger batches: every wave counts, then places, a
+// Batches up to this many slots: ids staged in LDS, counted by the 256
+// threads of permute_kernel, placed by one wave.  Larger batches
+// (permute_large_kernel, 16 waves): every wave counts, then places, a
 // contiguous range of slots, starting from the slots of each expert in the
 // ranges before it.
 constexpr int kOneWaveSlots = 512;
-constexpr int kPermThreads = 1024;
-constexpr int kPermWaves = kPermThreads / kWave;
+constexpr int kPermThreads = 256;
+constexpr int kPermLargeThreads = 1024;
+constexpr int kPermWaves = kPermLargeThreads / kWave;
 
 struct GlobalIds {
     const int32_t* p;
@@ -247,22 +249,28 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     __shared__ int cnt[kMaxExperts];
     __shared__ int base[kMaxExperts];
     __shared__ int sid[kOneWaveSlots];
+    __shared__ int nbad;
+    for (int s = threadIdx.x; s < n; s += kPermThreads) sid[s] = ids[s];
+    __syncthreads();
+    count_and_scan<kPermThreads>(LdsIds{sid}, n, E, m_split, cnt, base, &nbad, meta, counts,
+                                 offsets, active, large);
+    if (threadIdx.x < kWave) scatter_range(LdsIds{sid}, 0, n, E, base, sorted_slot);
+}
+
+__global__ __launch_bounds__(kPermLargeThreads) void permute_large_kernel(
+    const int32_t* __restrict__ ids, int n, int E, int m_split, int32_t* __restrict__ meta,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ active, int32_t* __restrict__ large,
+    int32_t* __restrict__ sorted_slot) {
+    __shared__ int cnt[kMaxExperts];
+    __shared__ int base[kMaxExperts];
     __shared__ int hist[kPermWaves * kMaxExperts];   // per-wave counts, then runs
     __shared__ int nbad_w[kPermWaves];
-    __shared__ int nbad;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
-    if (n <= kOneWaveSlots) {
-        for (int s = tid; s < n; s += kPermThreads) sid[s] = ids[s];
-        __syncthreads();
-        count_and_scan<kPermThreads>(LdsIds{sid}, n, E, m_split, cnt, base, &nbad, meta, counts,
-                                     offsets, active, large);
-        if (tid < kWave) scatter_range(LdsIds{sid}, 0, n, E, base, sorted_slot);
-        return;
-    }
     int* my = hist + wave * kMaxExperts;
-    for (int i = tid; i < kPermWaves * kMaxExperts; i += kPermThreads) hist[i] = 0;
+    for (int i = tid; i < kPermWaves * kMaxExperts; i += kPermLargeThreads) hist[i] = 0;
     __syncthreads();
     const int s0 = (int)((long long)n * wave / kPermWaves);
     const int s1 = (int)((long long)n * (wave + 1) / kPermWaves);
@@ -288,7 +296,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     if (lane == kWave - 1) nbad_w[wave] = bad;
     __syncthreads();
     // totals, and each wave's start within its expert's slots
-    for (int e = tid; e < E; e += kPermThreads) {
+    for (int e = tid; e < E; e += kPermLargeThreads) {
         int c = 0;
         for (int w = 0; w < kPermWaves; ++w) {
             const int h = hist[w * kMaxExperts + e];
@@ -304,7 +312,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
         scan_experts(cnt, E, m_split, nb, base, meta, counts, offsets, active, large);
     }
     __syncthreads();
-    for (int i = tid; i < kPermWaves * E; i += kPermThreads) {
+    for (int i = tid; i < kPermWaves * E; i += kPermLargeThreads) {
         const int w = i / E, e = i - w * E;
         hist[w * kMaxExperts + e] += base[e];
     }
@@ -386,9 +394,15 @@ hipError_t launch_route_permute(const float* logits, int32_t* ids, float* w,
 
 hipError_t launch_permute(const int32_t* ids, const FfnShape& s, const Workspace& ws,
                           int m_split, hipStream_t stream) {
-    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), 0, stream, ids,
-                       s.T * s.k, s.E, m_split, ws.meta, ws.counts, ws.offsets, ws.active,
-                       ws.large, ws.sorted_slot);
+    const int n = s.T * s.k;
+    if (n <= kOneWaveSlots)
+        hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), 0, stream, ids, n, s.E,
+                           m_split, ws.meta, ws.counts, ws.offsets, ws.active, ws.large,
+                           ws.sorted_slot);
+    else
+        hipLaunchKernelGGL(permute_large_kernel, dim3(1), dim3(kPermLargeThreads), 0, stream,
+                           ids, n, s.E, m_split, ws.meta, ws.counts, ws.offsets, ws.active,
+                           ws.large, ws.sorted_slot);
     return hipGetLastError();
 }
 
