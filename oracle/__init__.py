@@ -64,6 +64,10 @@ def lib() -> ctypes.CDLL:
             _u16p, _i32p, _f32p, _vpp, _vpp, _vpp, ctypes.c_int64,
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
             _u16p, _f32p, _u16p, _f32p]
+        L.oracle_attn_decode.restype = ctypes.c_int
+        L.oracle_attn_decode.argtypes = [_u16p, _u16p, _u16p, _i32p, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_float, _u16p]
         L.oracle_moe_ffn_int8.restype = ctypes.c_int
         L.oracle_moe_ffn_int8.argtypes = [
             _u16p, _i32p, _f32p, _vpp, _vpp, _vpp, _vpp, _vpp, _vpp,
@@ -270,3 +274,30 @@ def expert_ffn_bf16(x_row: np.ndarray, Wg: np.ndarray, Wu: np.ndarray,
                                  _ptr(Wu, ctypes.c_uint16), _ptr(Wd, ctypes.c_uint16),
                                  H, I, _ptr(h, ctypes.c_uint16), _ptr(y, ctypes.c_float))
     return h, y
+
+
+# --------------------------------------------------------------------------
+# Decode attention with grouped-query heads.
+# --------------------------------------------------------------------------
+
+def attn_decode(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
+                lens: np.ndarray, scale: Optional[float] = None) -> np.ndarray:
+    """Decode SDPA: q [B, h_q, d], k / v [B, h_kv, max_len, d] (BF16 bits),
+    lens [B] int32 -> out [B, h_q, d] BF16 bits.  ``scale`` defaults to
+    1/sqrt(d)."""
+    qb = np.ascontiguousarray(q_bits, dtype=np.uint16)
+    kb = np.ascontiguousarray(k_bits, dtype=np.uint16)
+    vb = np.ascontiguousarray(v_bits, dtype=np.uint16)
+    ln = np.ascontiguousarray(lens, dtype=np.int32)
+    B, h_q, d = qb.shape
+    _, h_kv, max_len, d2 = kb.shape
+    assert d2 == d and vb.shape == kb.shape and ln.shape == (B,)
+    if scale is None:
+        scale = float(np.float32(1.0) / np.sqrt(np.float32(d)))
+    out = np.empty((B, h_q, d), dtype=np.uint16)
+    rc = lib().oracle_attn_decode(_ptr(qb, ctypes.c_uint16), _ptr(kb, ctypes.c_uint16),
+                                  _ptr(vb, ctypes.c_uint16), _ptr(ln, ctypes.c_int32), B, h_q,
+                                  h_kv, d, max_len, scale, _ptr(out, ctypes.c_uint16))
+    if rc != 0:
+        raise ValueError(f"oracle_attn_decode failed ({rc})")
+    return out

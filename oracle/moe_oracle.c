@@ -26,6 +26,9 @@
  *     is written as the operand of the next (down) product, i.e. as BF16
  *     (§4.1, second transform).
  *   - §8.1 (Fig. 11): an INT8 variant with symmetric group-wise quantisation.
+ *   - §6.1 (SDPA in decoding, GQA): each KV head is shared by h_q/h_kv query
+ *     heads; per query head, scaled dot-product scores against the l_seq keys,
+ *     a softmax over the sequence, and the weighted sum of the values.
  *
  * Readings where the pages are silent (each is listed in the design notes):
  *   - router: softmax over all experts, the k largest kept (ties -> lower
@@ -36,6 +39,10 @@
  *   - a slot whose expert id is outside [0, E) contributes nothing;
  *   - INT8: w = q * s with one FP32 scale s per 128 consecutive K elements of
  *     a row; g = sum_groups s_g * (sum_{c in group} x_c * q_c), in FP32.
+ *   - attention: query head h reads KV head h / (h_q / h_kv); the score scale
+ *     is 1/sqrt(d) unless the caller gives another; scores, softmax and the
+ *     weighted sum in FP32 (BF16 inputs); the output rounded once to BF16; an
+ *     empty sequence gives a zero output.
  */
 #include <math.h>
 #include <omp.h>
@@ -303,4 +310,75 @@ int oracle_moe_ffn_int8(const uint16_t* x, const int32_t* topk_ids,
     return moe_layer(1, x, topk_ids, topk_w, (const void* const*)Q_gate, S_gate,
                      (const void* const*)Q_up, S_up, (const void* const*)Q_down,
                      S_down, group, T, H, I, E, k, out, out_f32, h_out, y_out);
+}
+
+/* ---------------------------------------------------------------------- */
+/* Decode attention with grouped-query heads (§6.1).                       */
+/* ---------------------------------------------------------------------- */
+
+/* q   [B][h_q][d] BF16: one query vector per sequence and query head.
+ * k, v [B][h_kv][max_len][d] BF16: the cached keys and values; sequence b
+ *     uses its first len[b] positions (0 <= len[b] <= max_len).
+ * out [B][h_q][d] BF16.
+ * For sequence b and query head h (KV head j = h / (h_q / h_kv)):
+ *   s_t = scale * sum_{c < d} q[c] * k[t][c]          (FP32, ascending c)
+ *   m = max_t s_t;  e_t = exp(s_t - m);  L = sum_t e_t (FP32, ascending t)
+ *   out[c] = RNE_bf16( (sum_t e_t * v[t][c]) / L )    (FP32, ascending t)
+ * which is softmax(s) weighted over v; len[b] = 0 gives out = 0.
+ * Returns ORACLE_OK, or ORACLE_ERR_ARG for inconsistent sizes. */
+int oracle_attn_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                       const int32_t* len, int32_t B, int32_t h_q, int32_t h_kv,
+                       int32_t d, int32_t max_len, float scale, uint16_t* out) {
+    if (B < 0 || h_q < 1 || h_kv < 1 || d < 1 || max_len < 0 || h_q % h_kv != 0)
+        return ORACLE_ERR_ARG;
+    for (int32_t b = 0; b < B; ++b)
+        if (len[b] < 0 || len[b] > max_len) return ORACLE_ERR_ARG;
+    const int32_t g = h_q / h_kv;
+    int status = ORACLE_OK;
+#pragma omp parallel for schedule(dynamic) collapse(2)
+    for (int32_t b = 0; b < B; ++b) {
+        for (int32_t h = 0; h < h_q; ++h) {
+            const int32_t j = h / g;
+            const int32_t n = len[b];
+            const uint16_t* qh = q + ((size_t)b * h_q + h) * d;
+            const uint16_t* kh = k + ((size_t)b * h_kv + j) * (size_t)max_len * d;
+            const uint16_t* vh = v + ((size_t)b * h_kv + j) * (size_t)max_len * d;
+            uint16_t* oh = out + ((size_t)b * h_q + h) * d;
+            if (n == 0) {
+                for (int32_t c = 0; c < d; ++c) oh[c] = 0;
+                continue;
+            }
+            float* s = (float*)malloc(sizeof(float) * (size_t)n);
+            float* acc = (float*)malloc(sizeof(float) * (size_t)d);
+            if (!s || !acc) {
+                free(s);
+                free(acc);
+#pragma omp atomic write
+                status = ORACLE_ERR_NOMEM;
+                continue;
+            }
+            for (int32_t t = 0; t < n; ++t) {
+                float dot = 0.0f;
+                for (int32_t c = 0; c < d; ++c)
+                    dot += oracle_bf16_to_f32(qh[c]) * oracle_bf16_to_f32(kh[(size_t)t * d + c]);
+                s[t] = scale * dot;
+            }
+            float m = s[0];
+            for (int32_t t = 1; t < n; ++t)
+                if (s[t] > m) m = s[t];
+            float L = 0.0f;
+            for (int32_t t = 0; t < n; ++t) {
+                s[t] = expf(s[t] - m);
+                L += s[t];
+            }
+            for (int32_t c = 0; c < d; ++c) acc[c] = 0.0f;
+            for (int32_t t = 0; t < n; ++t)
+                for (int32_t c = 0; c < d; ++c)
+                    acc[c] += s[t] * oracle_bf16_to_f32(vh[(size_t)t * d + c]);
+            for (int32_t c = 0; c < d; ++c) oh[c] = oracle_f32_to_bf16(acc[c] / L);
+            free(s);
+            free(acc);
+        }
+    }
+    return status;
 }

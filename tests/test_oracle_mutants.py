@@ -38,7 +38,20 @@ MUTANTS = {
     "bf16_truncate": ("u += 0x7fffu + keep_lsb;", "u += 0u * keep_lsb;"),
     "int8_scale_dropped": ("acc += s[g0 / group] * part;", "acc += part;"),
     "int8_group_index": ("acc += s[g0 / group] * part;", "acc += s[0] * part;"),
+    # decode attention (pins in test_oracle_attn_pins.py)
+    "attn_head_mapping": ("const int32_t j = h / g;", "const int32_t j = h % h_kv;"),
+    "attn_no_scale": ("s[t] = scale * dot;", "s[t] = dot;"),
+    "attn_values_from_keys": ("acc[c] += s[t] * oracle_bf16_to_f32(vh[(size_t)t * d + c]);",
+                              "acc[c] += s[t] * oracle_bf16_to_f32(kh[(size_t)t * d + c]);"),
+    "attn_last_position_dropped": ("for (int32_t t = 0; t < n; ++t)\n                for (int32_t c = 0; c < d; ++c)\n                    acc[c]",
+                                   "for (int32_t t = 0; t < n - 1; ++t)\n                for (int32_t c = 0; c < d; ++c)\n                    acc[c]"),
+    "attn_not_normalised": ("oh[c] = oracle_f32_to_bf16(acc[c] / L);",
+                            "oh[c] = oracle_f32_to_bf16(acc[c]);"),
 }
+
+
+def pin_file(name: str) -> str:
+    return "test_oracle_attn_pins.py" if name.startswith("attn_") else "test_oracle_pins.py"
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
@@ -53,7 +66,7 @@ def test_pins_catch_mutant(name, tmp_path):
                     "-std=c11", str(src), "-o", str(lib), "-lm"], check=True)
     env = dict(os.environ, ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        os.path.join(ROOT, "tests", pin_file(name))],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"pins did not catch mutant {name}:\n{r.stdout[-2000:]}"
     assert "failed" in r.stdout or "Error" in r.stdout

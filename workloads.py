@@ -33,6 +33,7 @@ import numpy as np
 import torch
 
 TAG_X, TAG_LOGITS, TAG_WG, TAG_WU, TAG_WD, TAG_ZIPF = range(6)
+TAG_Q, TAG_K, TAG_V, TAG_LENS = range(6, 10)
 WEIGHT_STD = 0.02
 
 
@@ -200,3 +201,85 @@ def weight_bytes_per_expert(wl: Workload) -> int:
     if wl.int8:
         return n + 3 * (wl.H * wl.I // wl.group) * 4
     return 2 * n
+
+
+# --------------------------------------------------------------------------
+# Decode attention with grouped-query heads (HiNa-MoE §6.1): the query heads
+# that share one KV head form a small block; the KV cache holds, per sequence
+# and KV head, a [max_len][d] matrix of which the first len positions are
+# valid.  Head layouts of the models the pages decode with (Qwen3-30B-A3B:
+# 32 query heads over 4 KV heads; Mixtral-8x7B: 32 over 8; Qwen2-57B-A14B:
+# 28 over 4; head dimension 128).
+#   * q [B][h_q][d], k / v [B][h_kv][max_len][d] ~ N(0,1) in BF16 (k and v
+#     drawn on the device that holds them, one seeded generator per
+#     (tensor, sequence)).
+#   * lens: "full" (every sequence max_len long) or "ragged" (uniform in
+#     [1, max_len], seeded).
+# --------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class AttnWorkload:
+    name: str
+    B: int           # sequences in the decode batch
+    h_q: int         # query heads
+    h_kv: int        # KV heads (h_q / h_kv query heads share one)
+    d: int           # head dimension
+    max_len: int     # KV cache capacity per sequence
+    lens: str = "full"    # "full" | "ragged"
+    seed: int = 0
+
+
+def _attn_registry() -> Dict[str, AttnWorkload]:
+    w = {}
+    w["attn_tiny"] = AttnWorkload("attn_tiny", B=3, h_q=8, h_kv=2, d=64, max_len=300,
+                                  lens="ragged")
+    for B, L in ((1, 32768), (32, 32768)):
+        w[f"attn_qwen3_30b_b{B}_l{L}"] = AttnWorkload(f"attn_qwen3_30b_b{B}_l{L}", B=B,
+                                                      h_q=32, h_kv=4, d=128, max_len=L)
+    w["attn_qwen3_30b_b32_ragged"] = AttnWorkload("attn_qwen3_30b_b32_ragged", B=32, h_q=32,
+                                                  h_kv=4, d=128, max_len=32768,
+                                                  lens="ragged")
+    w["attn_mixtral8x7b_b16_l16384"] = AttnWorkload("attn_mixtral8x7b_b16_l16384", B=16,
+                                                    h_q=32, h_kv=8, d=128, max_len=16384)
+    w["attn_qwen2_57b_b16_l16384"] = AttnWorkload("attn_qwen2_57b_b16_l16384", B=16, h_q=28,
+                                                  h_kv=4, d=128, max_len=16384)
+    return w
+
+
+ATTN_WORKLOADS: Dict[str, AttnWorkload] = _attn_registry()
+
+
+def gen_attn_q(wl: AttnWorkload) -> torch.Tensor:
+    """Query vectors [B, h_q, d], BF16, CPU."""
+    g = _gen("cpu", seed_for(wl.seed, TAG_Q))
+    return torch.randn(wl.B, wl.h_q, wl.d, generator=g, dtype=torch.float32).to(torch.bfloat16)
+
+
+def gen_attn_lens(wl: AttnWorkload) -> torch.Tensor:
+    """Valid positions per sequence [B], int32, CPU."""
+    if wl.lens == "full":
+        return torch.full((wl.B,), wl.max_len, dtype=torch.int32)
+    if wl.lens == "ragged":
+        rng = np.random.default_rng(seed_for(wl.seed, TAG_LENS))
+        return torch.from_numpy(rng.integers(1, wl.max_len + 1, size=wl.B).astype(np.int32))
+    raise ValueError(f"unknown length recipe {wl.lens!r}")
+
+
+def gen_attn_kv(wl: AttnWorkload, device="cpu", sequences: Optional[list] = None):
+    """KV cache (k, v), each [B, h_kv, max_len, d] BF16.  ``sequences`` limits
+    the draw to those sequences (the others stay zero)."""
+    seqs = range(wl.B) if sequences is None else sequences
+    shape = (wl.B, wl.h_kv, wl.max_len, wl.d)
+    k = torch.zeros(shape, dtype=torch.bfloat16, device=device)
+    v = torch.zeros(shape, dtype=torch.bfloat16, device=device)
+    for b in seqs:
+        for t, tag in ((k, TAG_K), (v, TAG_V)):
+            g = _gen(device, seed_for(wl.seed, tag, b))
+            t[b] = torch.randn(shape[1:], generator=g, device=device,
+                               dtype=torch.float32).to(torch.bfloat16)
+    return k, v
+
+
+def attn_kv_bytes(wl: AttnWorkload, lens) -> int:
+    """K and V bytes the valid positions of a batch occupy."""
+    return int(sum(int(n) for n in lens)) * wl.h_kv * wl.d * 2 * 2
