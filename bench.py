@@ -20,6 +20,12 @@ call streams its weights from HBM.  Prefill-sized layers (more than 64 tokens,
 BF16) run the tiled product, which the matrix unit bounds: their roofline is
 reported in TFLOP/s against the dense BF16 peak.
 
+Decode attention (HiNa-MoE §6.1; ``--workload attn_*``: Qwen3-30B-A3B,
+Mixtral-8x7B and Qwen2-57B-A14B head layouts, batches of 1-32 sequences of up
+to 32768 positions): one step = one ``moe_attn_decode`` call over the batch;
+value = K and V bytes of the valid positions (+ q and out) per second, the
+roofline that of the split kernel, which streams every K and V byte.
+
 Inputs are resident in HBM before timing; the router runs once per batch
 before the timed region.  Printed (one JSON line): weight-stream throughput in
 GB/s (algorithmic bytes: active experts' weights + x + out + routing ids and
@@ -193,6 +199,126 @@ def cpu_baseline(wl, host_weights, logits_cpu, x_cpu, reps=3):
                       f"loops, {'INT8' if wl.int8 else 'BF16'} weights)"}
 
 
+ATTN_METRIC = "decode GQA attention: KV-stream GB/s (% HBM peak) and µs per call, BF16"
+
+
+def cpu_baseline_attn(wl, q, k_host, v_host, lens, reps=3):
+    """The CPU oracle on a bounded sample of the same attention batch: the
+    leading sequences whose KV positions total at most 2^23 (a few seconds of
+    CPU work), median of `reps` runs, in the same GB/s unit."""
+    import oracle
+    import workloads
+    n, pos = 0, 0
+    while n < wl.B and (n == 0 or pos + int(lens[n]) <= (1 << 23)):
+        pos += int(lens[n])
+        n += 1
+    qb = workloads.bf16_bits(q[:n])
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        oracle.attn_decode(qb, k_host[:n], v_host[:n], lens[:n].numpy())
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    nbytes = pos * wl.h_kv * wl.d * 4 + 2 * n * wl.h_q * wl.d * 2
+    return {"value": round(nbytes / t / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "us_per_call": round(t * 1e6, 1),
+            "sample": f"{wl.name}: the first {n} of {wl.B} sequences ({pos} KV positions), "
+                      f"median of {reps} runs, plain C oracle (FP32 scores, softmax and "
+                      f"value sums, BF16 inputs)"}
+
+
+def run_attn(args):
+    """Decode attention: one step = one moe_attn_decode call over the batch
+    (several distinct KV caches in turn when one is small enough to stay in
+    the last-level cache)."""
+    import torch
+
+    import routed_expert_ffn_topk_amd as moe
+    import workloads
+    wl = workloads.ATTN_WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    q = workloads.gen_attn_q(wl)
+    lens = workloads.gen_attn_lens(wl)
+    kv_bytes = workloads.attn_kv_bytes(wl, lens)
+    n_sets = max(1, math.ceil(ROTATE_BELOW / kv_bytes)) if kv_bytes < ROTATE_BELOW else 1
+    sets = [workloads.gen_attn_kv(workloads.AttnWorkload(**{**wl.__dict__, "seed": wl.seed + r}),
+                                  dev) for r in range(n_sets)]
+    qd, ld = q.to(dev), lens.to(dev)
+    out = torch.empty_like(qd)
+    ws = torch.empty(moe.moe_attn_decode_workspace_bytes(wl.B, wl.h_q, wl.h_kv, wl.d, wl.max_len),
+                     dtype=torch.uint8, device=dev)
+
+    def call(i):
+        k, v = sets[i % n_sets]
+        moe.moe_attn_decode(qd, k, v, ld, out=out, workspace=ws, stream=stream)
+
+    def step():
+        for i in range(n_sets):
+            call(i)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    call_bytes = kv_bytes + 2 * wl.B * wl.h_q * wl.d * 2
+    value = n_sets * call_bytes / (ms_per_step * 1e-3) / 1e9
+    # per-kernel durations from HIP events on the launch stream: split kernel
+    # (the dominant one: every K and V byte), then the merge of the splits
+    split_us, merge_us = [], []
+    for i in range(max(5, args.steps)):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        for e in ev:
+            e.record(stream)
+        ev[0].record(stream)
+        moe.moe_ffn_set_stage_events(ev[1:])
+        call(i)
+        torch.cuda.synchronize()
+        split_us.append(ev[0].elapsed_time(ev[1]) * 1e3)
+        merge_us.append(ev[1].elapsed_time(ev[2]) * 1e3)
+    s_us = statistics.mean(split_us)
+    algo = kv_bytes + wl.B * wl.h_q * wl.d * 2
+    achieved = algo / (s_us * 1e-6) / 1e9
+    ceiling = read_ceiling(stream)
+    result = {
+        "metric": ATTN_METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.B, "q_heads": wl.h_q, "kv_heads": wl.h_kv,
+                   "head_dim": wl.d, "max_len": wl.max_len, "lengths": wl.lens,
+                   "kv_positions": int(lens.sum()), "kv_sets": n_sets,
+                   "us_per_call": round(ms_per_step * 1e3 / n_sets, 1),
+                   "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
+                   "pct_measured_read_ceiling": round(100 * value / ceiling, 1),
+                   "device": torch.cuda.get_device_name(dev)},
+        "roofline": {"bound": "hbm", "kernel": "attn_split_kernel (scores, softmax, values)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(args.workload),
+                     "measured_read_ceiling": round(ceiling, 1),
+                     "frac_of_measured_ceiling": round(achieved / ceiling, 4),
+                     "algorithmic_bytes": algo, "avg_us": round(s_us, 2),
+                     "stage_us": {"split": round(s_us, 2),
+                                  "merge": round(statistics.mean(merge_us), 2)}},
+    }
+    if not args.no_cpu_baseline:
+        k, v = sets[0]
+        n_host = min(wl.B, 64)
+        kh = workloads.bf16_bits(k[:n_host])
+        vh = workloads.bf16_bits(v[:n_host])
+        result["cpu_baseline"] = cpu_baseline_attn(wl, q, kh, vh, lens)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -219,10 +345,14 @@ def main():
               "GPU only here (the sharding notes are in DESIGN.md)", file=sys.stderr)
         sys.exit(2)
 
+    import workloads
+    if args.workload in workloads.ATTN_WORKLOADS:
+        run_attn(args)
+        return
+
     import torch
 
     import routed_expert_ffn_topk_amd as moe
-    import workloads
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

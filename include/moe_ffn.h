@@ -202,6 +202,45 @@ int moe_ffn_forward_int8(const void* x, const int32_t* topk_ids,
                          int32_t top_k, void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/*
+ * Decode attention with grouped-query heads (HiNa-MoE §6.1: in decoding the
+ * h_q / h_kv query heads that share one KV head form a small block, and
+ * scoring it against the head's keys, then weighting its values, are small
+ * matrix products).
+ *   q        [B][h_q][d] bf16, device: one query vector per sequence and
+ *            query head.
+ *   k_cache, v_cache [B][h_kv][max_len][d] bf16, device: the KV cache;
+ *            sequence b uses its first seq_lens[b] positions.
+ *   seq_lens [B] int32, device: valid positions per sequence, in
+ *            [0, max_len] (values outside are clamped into that range).
+ *   out      [B][h_q][d] bf16, device, fully overwritten: for query head h
+ *            (KV head j = h / (h_q / h_kv)) and sequence b,
+ *              s_t = scale * (q . k_t)   (BF16 products, FP32 accumulation)
+ *              out = RNE_bf16( sum_t softmax(s)_t * v_t )
+ *            over t < seq_lens[b] (the softmax weights enter the value
+ *            product as BF16); an empty sequence gives zeros.
+ *   scale    the score scale (1/sqrt(d) for standard attention).
+ *   workspace / workspace_bytes: at least
+ *            moe_attn_decode_workspace_bytes(...) bytes, 256-byte aligned,
+ *            device; contents on entry are ignored (per-split partial
+ *            results).
+ * Sizes: B >= 0 (B = 0 is a no-op), h_kv >= 1, h_q a multiple of h_kv with
+ * h_q / h_kv <= 16, d in {64, 128, 256}, max_len >= 0.
+ * Errors: NULL_ARG, BAD_SHAPE, MISALIGNED (q, k_cache, v_cache, out not
+ * 16-byte aligned, seq_lens not 4-byte aligned, workspace not 256-byte
+ * aligned), ALIAS (out or the workspace overlap an input or each other),
+ * WORKSPACE, HIP.
+ */
+int moe_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* seq_lens, void* out, int32_t B, int32_t h_q,
+                    int32_t h_kv, int32_t d, int32_t max_len, float scale,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes moe_attn_decode needs for these sizes (a positive multiple
+ * of 256), or 0 if the sizes are invalid.  Pure host computation. */
+size_t moe_attn_decode_workspace_bytes(int32_t B, int32_t h_q, int32_t h_kv,
+                                       int32_t d, int32_t max_len);
+
 /* Wait for `stream`, then read the workspace meta written by the last forward
  * call: MOE_FFN_ERR_BAD_IDS if it dropped slots with out-of-range ids,
  * MOE_FFN_OK otherwise (MOE_FFN_ERR_HIP if the wait or the read fails).  If
@@ -216,7 +255,9 @@ const char* moe_ffn_status_string(int status);
  * next forward call made by the calling host thread (either weight format)
  * records events[i] on its stream right after enqueuing kernel i, for
  * i < n_events: 0 = gather index (permute; for moe_ffn_forward_logits the
- * router and gather index), 1 = gate/up, 2 = down, 3 = combine.  The events are hipEvent_t handles owned by the caller.  The
+ * router and gather index), 1 = gate/up, 2 = down, 3 = combine; for
+ * moe_attn_decode, 0 = the split kernel (scores, softmax and values per
+ * split of positions) and 1 = the merge of the splits.  The events are hipEvent_t handles owned by the caller.  The
  * setting is consumed by that one call; n_events = 0 (or events = NULL)
  * clears it.  Only the calling thread is affected.  Returns MOE_FFN_OK, or
  * MOE_FFN_ERR_BAD_SHAPE if n_events is outside [0, 4].

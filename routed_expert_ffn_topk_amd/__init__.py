@@ -67,6 +67,11 @@ def lib() -> ctypes.CDLL:
         L.moe_ffn_forward_logits.restype = _c.c_int
         L.moe_ffn_forward_logits.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64,
                                              _i64, _i32, _i32, _vp, _sz, _vp]
+        L.moe_attn_decode.restype = _c.c_int
+        L.moe_attn_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                      _c.c_float, _vp, _sz, _vp]
+        L.moe_attn_decode_workspace_bytes.restype = _sz
+        L.moe_attn_decode_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]
         L.moe_ffn_forward_int8.restype = _c.c_int
         L.moe_ffn_forward_int8.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                                            _vp, _i64, _i64, _i64, _i32, _i32, _vp, _sz, _vp]
@@ -273,3 +278,37 @@ def moe_ffn_set_stage_events(events) -> None:
     handles = [e.cuda_event if hasattr(e, "cuda_event") else int(e) for e in events]
     arr = (_vp * max(1, len(handles)))(*handles)
     _check("moe_ffn_set_stage_events", lib().moe_ffn_set_stage_events(arr, len(handles)))
+
+
+def moe_attn_decode_workspace_bytes(B: int, h_q: int, h_kv: int, d: int, max_len: int) -> int:
+    return int(lib().moe_attn_decode_workspace_bytes(B, h_q, h_kv, d, max_len))
+
+
+def moe_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                    seq_lens: torch.Tensor, scale: Optional[float] = None,
+                    out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """Decode attention with grouped-query heads: q [B, h_q, d], k_cache /
+    v_cache [B, h_kv, max_len, d] (bf16), seq_lens [B] int32 -> out [B, h_q, d]
+    bf16.  ``scale`` defaults to 1/sqrt(d)."""
+    B, h_q, d = q.shape
+    B2, h_kv, max_len, d2 = k_cache.shape
+    if B2 != B or d2 != d or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache / v_cache must be [B, h_kv, max_len, d] matching q")
+    if tuple(seq_lens.shape) != (B,):
+        raise ValueError("seq_lens must be [B]")
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        n = moe_attn_decode_workspace_bytes(B, h_q, h_kv, d, max_len)
+        if n == 0:
+            raise MoeFfnError("moe_attn_decode_workspace_bytes", MOE_FFN_ERR_BAD_SHAPE)
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    _check("moe_attn_decode", lib().moe_attn_decode(
+        _dev(q, "q", torch.bfloat16), _dev(k_cache, "k_cache", torch.bfloat16),
+        _dev(v_cache, "v_cache", torch.bfloat16), _dev(seq_lens, "seq_lens", torch.int32),
+        _dev(out, "out", torch.bfloat16), B, h_q, h_kv, d, max_len, float(scale),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream)))
+    return out

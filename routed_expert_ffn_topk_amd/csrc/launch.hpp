@@ -99,6 +99,15 @@ constexpr int kTiledMinTokens = 32;
 hipError_t launch_combine(const float* y, const int32_t* ids, const float* w,
                           uint16_t* out, const FfnShape& s, hipStream_t stream);
 
+// Decode attention with grouped-query heads: workspace bytes, and the split
+// kernel + merge kernel on the caller's stream (sizes validated by the C ABI).
+int attn_chunk(int B, int h_kv, int max_len);
+size_t attn_workspace_bytes(int B, int h_kv, int d, int max_len);
+hipError_t launch_attn_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              const int32_t* lens, uint16_t* out, int B, int h_q, int h_kv,
+                              int d, int max_len, float scale, void* workspace,
+                              const StageEvents& ev, hipStream_t stream);
+
 // Streaming-read probe over bytes (a multiple of 16) of buf; sink is one
 // device word.
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int num_cu,

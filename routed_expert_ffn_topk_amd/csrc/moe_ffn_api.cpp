@@ -246,6 +246,63 @@ int moe_ffn_forward_int8(const void* x, const int32_t* topk_ids, const float* to
     return err == hipSuccess ? MOE_FFN_OK : MOE_FFN_ERR_HIP;
 }
 
+namespace {
+
+bool attn_shape_ok(int32_t B, int32_t h_q, int32_t h_kv, int32_t d, int32_t max_len) {
+    if (B < 0 || h_q < 1 || h_kv < 1 || max_len < 0) return false;
+    if (h_q % h_kv != 0 || h_q / h_kv > 16) return false;
+    if (d != 64 && d != 128 && d != 256) return false;
+    // element offsets of the KV cache fit in 64 bits; grid dims in range
+    if ((int64_t)B * h_kv * (int64_t)max_len * d >= ((int64_t)1 << 62)) return false;
+    if ((int64_t)B * h_kv >= ((int64_t)1 << 31)) return false;
+    // the merge grid is (h_q, B); the split grid (B * h_kv, max_len / 128)
+    if (B > 65535 || (int64_t)max_len / 128 > 65535) return false;
+    return true;
+}
+
+}  // namespace
+
+size_t moe_attn_decode_workspace_bytes(int32_t B, int32_t h_q, int32_t h_kv, int32_t d,
+                                       int32_t max_len) {
+    if (!attn_shape_ok(B, h_q, h_kv, d, max_len)) return 0;
+    const size_t n = moe::attn_workspace_bytes(B, h_kv, d, max_len);
+    return n == 0 ? kAlign : (n + kAlign - 1) / kAlign * kAlign;
+}
+
+int moe_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* seq_lens, void* out, int32_t B, int32_t h_q, int32_t h_kv,
+                    int32_t d, int32_t max_len, float scale, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    if (!attn_shape_ok(B, h_q, h_kv, d, max_len)) return MOE_FFN_ERR_BAD_SHAPE;
+    if (B == 0) return MOE_FFN_OK;
+    if (!q || !seq_lens || !out) return MOE_FFN_ERR_NULL_ARG;
+    if (max_len > 0 && (!k_cache || !v_cache)) return MOE_FFN_ERR_NULL_ARG;
+    if (!workspace) return MOE_FFN_ERR_WORKSPACE;
+    if (workspace_bytes < moe_attn_decode_workspace_bytes(B, h_q, h_kv, d, max_len))
+        return MOE_FFN_ERR_WORKSPACE;
+    if (!aligned16(q) || !aligned16(out) || (max_len > 0 && (!aligned16(k_cache) ||
+                                                              !aligned16(v_cache))))
+        return MOE_FFN_ERR_MISALIGNED;
+    if ((reinterpret_cast<uintptr_t>(seq_lens) & 3u) ||
+        reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
+        return MOE_FFN_ERR_MISALIGNED;
+    const size_t qb = (size_t)B * h_q * d * 2;
+    const size_t kvb = (size_t)B * h_kv * (size_t)max_len * d * 2;
+    const size_t wb = moe_attn_decode_workspace_bytes(B, h_q, h_kv, d, max_len);
+    if (overlap(out, qb, q, qb) || overlap(out, qb, workspace, wb) ||
+        overlap(out, qb, seq_lens, (size_t)B * 4) ||
+        (max_len > 0 && (overlap(out, qb, k_cache, kvb) || overlap(out, qb, v_cache, kvb) ||
+                         overlap(workspace, wb, k_cache, kvb) ||
+                         overlap(workspace, wb, v_cache, kvb))) ||
+        overlap(workspace, wb, q, qb) || overlap(workspace, wb, seq_lens, (size_t)B * 4))
+        return MOE_FFN_ERR_ALIAS;
+    const hipError_t err = moe::launch_attn_decode(
+        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
+        static_cast<const uint16_t*>(v_cache), seq_lens, static_cast<uint16_t*>(out), B, h_q,
+        h_kv, d, max_len, scale, workspace, take_stage_events(), static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? MOE_FFN_OK : MOE_FFN_ERR_HIP;
+}
+
 int moe_ffn_check_status(const void* workspace, void* stream, int64_t* n_dropped) {
     if (!workspace) return MOE_FFN_ERR_NULL_ARG;
     if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess)

@@ -185,3 +185,38 @@ def test_binding_rejects_host_tensors():
                             torch.zeros(8, 96, 64, dtype=torch.bfloat16),
                             torch.zeros(8, 64, 96, dtype=torch.bfloat16),
                             workspace=torch.zeros(16, dtype=torch.uint8))
+
+
+def attn(**kw):
+    a = dict(q=A, k=A + 0x1000000, v=A + 0x2000000, lens=A + 0x100000, out=A + 0x200000, B=2,
+             h_q=8, h_kv=2, d=128, L=64, scale=0.125, ws=A + 0x4000000, wsb=1 << 30)
+    a.update(kw)
+    return moe.lib().moe_attn_decode(a["q"], a["k"], a["v"], a["lens"], a["out"], a["B"],
+                                     a["h_q"], a["h_kv"], a["d"], a["L"], a["scale"], a["ws"],
+                                     a["wsb"], None)
+
+
+def test_attn_host_validation():
+    assert attn(B=0) == moe.MOE_FFN_OK
+    assert attn(d=96) == moe.MOE_FFN_ERR_BAD_SHAPE            # d in {64, 128, 256}
+    assert attn(h_q=6, h_kv=4) == moe.MOE_FFN_ERR_BAD_SHAPE    # not a multiple
+    assert attn(h_q=34, h_kv=2) == moe.MOE_FFN_ERR_BAD_SHAPE   # group of 17
+    assert attn(L=-1) == moe.MOE_FFN_ERR_BAD_SHAPE
+    assert attn(q=None) == moe.MOE_FFN_ERR_NULL_ARG
+    assert attn(k=None) == moe.MOE_FFN_ERR_NULL_ARG
+    assert attn(ws=None) == moe.MOE_FFN_ERR_WORKSPACE
+    assert attn(wsb=256) == moe.MOE_FFN_ERR_WORKSPACE
+    assert attn(q=A + 8) == moe.MOE_FFN_ERR_MISALIGNED
+    assert attn(lens=A + 0x100002) == moe.MOE_FFN_ERR_MISALIGNED
+    assert attn(ws=A + 0x4000000 + 64) == moe.MOE_FFN_ERR_MISALIGNED
+    assert attn(out=A + 0x200) == moe.MOE_FFN_ERR_ALIAS       # out overlaps q
+    assert attn(out=A + 0x1000100) == moe.MOE_FFN_ERR_ALIAS   # out overlaps the keys
+    assert attn(ws=A + 0x2000000) == moe.MOE_FFN_ERR_ALIAS    # workspace on the values
+
+
+def test_attn_workspace_bytes():
+    n = moe.moe_attn_decode_workspace_bytes(32, 32, 4, 128, 32768)
+    assert n > 0 and n % 256 == 0
+    assert moe.moe_attn_decode_workspace_bytes(0, 8, 2, 64, 16) == 256
+    assert moe.moe_attn_decode_workspace_bytes(1, 8, 2, 100, 16) == 0
+    assert moe.moe_attn_decode_workspace_bytes(1, 8, 3, 64, 16) == 0
