@@ -110,10 +110,10 @@ def source_hash(files) -> str:
 
 
 def recorded_traffic(workload: str):
-    """HBM bytes per gate/up launch from a committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE record (profiles/*_hbm_traffic.md, scaled by a plain copy of
-    known size) for this workload, or None when there is none or the kernel
-    sources it names have changed since the counters were taken."""
+    """HBM bytes per launch of the workload's dominant kernel from a committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE record (profiles/*_hbm_traffic.md,
+    scaled by a plain copy of known size), or None when there is none or the
+    kernel sources it names have changed since the counters were taken."""
     import glob
     for path in sorted(glob.glob(os.path.join(PROFILES, "*_hbm_traffic.md"))):
         try:
@@ -121,7 +121,8 @@ def recorded_traffic(workload: str):
         except OSError:
             continue
         rec = dict(re.findall(r"^(kernel_sources|kernel_source_sha256_16|workload|"
-                              r"gateup_traffic_bytes_per_launch): (\S+)$", text, re.M))
+                              r"gateup_traffic_bytes_per_launch|traffic_bytes_per_launch): "
+                              r"(\S+)$", text, re.M))
         if rec.get("workload") != workload or "kernel_sources" not in rec:
             continue
         try:
@@ -130,7 +131,7 @@ def recorded_traffic(workload: str):
             return None
         if rec.get("kernel_source_sha256_16") != digest:
             return None
-        return int(rec["gateup_traffic_bytes_per_launch"])
+        return int(rec.get("traffic_bytes_per_launch") or rec["gateup_traffic_bytes_per_launch"])
     return None
 
 
