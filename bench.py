@@ -8,8 +8,9 @@ tokens (T = 4m), m in {1, 2, 4, 8, 16}; router logits ~ N(0,1) (HiNa-MoE §7.3
 and Table 3 shapes, 1-16 tokens per expert).  One step = one layer call at
 each m (five layers).
 
-Other workloads: ``mixtral8x7b_int8_forced_m1-16`` (the same with INT8
-group-quantised weights), and any single layer of the workload registry
+Other workloads: ``mixtral8x7b_int8_forced_m1-16`` and
+``mixtral8x7b_int4_forced_m1-16`` (the same with INT8 / INT4 group-quantised
+weights), and any single layer of the workload registry
 (``deepseekv3_t16``, ``deepseekv3_zipf_t16``, ``mixtral8x22b_t{1,4,16}``,
 ``qwen3_235b_t{1,4,16}``, and the prefill-sized ``mixtral8x7b_t{512,2048}``,
 ``qwen3_235b_t2048``, ``deepseekv3_t4096``): one step = one call of that
@@ -64,6 +65,8 @@ def suite_layers(name: str):
         return [workloads.WORKLOADS[f"mixtral8x7b_m{m}"] for m in MS]
     if name == "mixtral8x7b_int8_forced_m1-16":
         return [workloads.WORKLOADS[f"mixtral8x7b_int8_m{m}"] for m in MS]
+    if name == "mixtral8x7b_int4_forced_m1-16":
+        return [workloads.WORKLOADS[f"mixtral8x7b_int4_m{m}"] for m in MS]
     if name in workloads.WORKLOADS and name != "tiny":
         return [workloads.WORKLOADS[name]]
     raise SystemExit(f"bench.py: unknown workload {name!r}")
@@ -87,14 +90,19 @@ def layer_flops(wl) -> float:
 
 
 def uses_tiled(wl) -> bool:
-    return not wl.int8 and wl.T > TILED_MIN_BATCH
+    return not wl.int8 and not wl.int4 and wl.T > TILED_MIN_BATCH
 
 
 def gateup_bytes(wl, active: int) -> int:
     """Algorithmic bytes of one gate/up launch: W_gate and W_up (and their
     scales) of every active expert plus the token rows (h is scratch and not
     credited)."""
-    per = wl.I * wl.H * (1 + 4 / wl.group) if wl.int8 else wl.I * wl.H * 2
+    if wl.int8:
+        per = wl.I * wl.H * (1 + 4 / wl.group)
+    elif wl.int4:
+        per = wl.I * wl.H * (0.5 + 4 / wl.group)
+    else:
+        per = wl.I * wl.H * 2
     return int(active * 2 * per) + wl.T * wl.H * 2
 
 
@@ -185,7 +193,8 @@ def cpu_baseline(wl, host_weights, logits_cpu, x_cpu, reps=3):
     times = []
     for _ in range(reps):
         t0 = time.perf_counter()
-        if wl.int8:
+        if wl.int8 or wl.int4:
+            # INT4 is the INT8 definition on values in [-7, 7] (unpacked here)
             oracle.moe_ffn_int8(xb, ids[:n], w[:n], *(t.get for t in tables), E=wl.E)
         else:
             oracle.moe_ffn_bf16(xb, ids[:n], w[:n], *(t.get for t in tables), E=wl.E)
@@ -197,7 +206,7 @@ def cpu_baseline(wl, host_weights, logits_cpu, x_cpu, reps=3):
             "us_per_layer": round(t * 1e6, 1),
             "sample": f"{wl.name}: the first {n} of {wl.T} tokens ({len(need)} experts), "
                       f"median of {reps} runs, plain C oracle (FP32 accumulation, per-token "
-                      f"loops, {'INT8' if wl.int8 else 'BF16'} weights)"}
+                      f"loops, {'INT8' if wl.int8 else 'INT4' if wl.int4 else 'BF16'} weights)"}
 
 
 ATTN_METRIC = "decode GQA attention: KV-stream GB/s (% HBM peak) and µs per call, BF16"
@@ -359,6 +368,8 @@ def main():
     torch.cuda.set_device(dev)
     layers = suite_layers(args.workload)
     int8 = layers[0].int8
+    int4 = layers[0].int4
+    quant = int8 or int4
     stream = torch.cuda.current_stream()
 
     batches = []
@@ -379,18 +390,21 @@ def main():
     sets = []
     for r in range(n_sets):
         wlr = workloads.Workload(**{**wl0.__dict__, "seed": wl0.seed + r})
-        if int8:
-            Qg, Sg, Qu, Su, Qd, Sd = workloads.gen_weights_int8(wlr, dev)
-            sets.append((Qg, workloads.scales_group_major(Sg), Qu, workloads.scales_group_major(Su),
-                         Qd, workloads.scales_group_major(Sd)))
+        if quant:
+            gen = workloads.gen_weights_int8 if int8 else workloads.gen_weights_int4
+            Qg, Sg, Qu, Su, Qd, Sd = gen(wlr, dev)
+            store = (lambda q: q) if int8 else workloads.pack_int4  # noqa: E731
+            gm = workloads.scales_group_major
+            sets.append((store(Qg), gm(Sg), store(Qu), gm(Su), store(Qd), gm(Sd)))
             if r == 0:
                 host_rowmajor = (Qg, Sg, Qu, Su, Qd, Sd)
             else:
-                del Sg, Su, Sd
+                del Qg, Qu, Qd, Sg, Su, Sd
         else:
             sets.append(workloads.gen_weights(wlr, dev))
     torch.cuda.synchronize()
-    fwd = moe.moe_ffn_forward_int8 if int8 else moe.moe_ffn_forward
+    fwd = (moe.moe_ffn_forward_int8 if int8 else moe.moe_ffn_forward_int4 if int4
+           else moe.moe_ffn_forward)
 
     def layer(b, s):
         fwd(b["x"], b["ids"], b["w"], *sets[s], out=b["out"], workspace=b["ws"], stream=stream)
@@ -433,7 +447,7 @@ def main():
             "pct_hbm_peak": round(100 * lb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
             "TFLOPs": round(layer_flops(b["wl"]) / (us * 1e-6) / 1e12, 1),
         }
-        if not int8:
+        if not quant:
             # the same layer from router logits (router fused with the gather
             # index); its ids / weights go to scratch tensors
             rid = torch.empty_like(b["ids"])
@@ -499,8 +513,9 @@ def main():
                     "stage_us": {n: round(statistics.mean(v), 2) for n, v in dur.items()}}
     else:
         achieved = statistics.mean(gu_bytes) / (gu_us * 1e-6) / 1e9
-        kern = "expert_gemm_kernel<Int8Weights, 2, ...>" if int8 else \
-            "expert_gemm_kernel<Bf16Weights, 2, ...>"
+        kern = ("expert_gemm_kernel<Int8Weights, 2, ...>" if int8 else
+                "expert_gemm_kernel<Int4Weights, 2, ...>" if int4 else
+                "expert_gemm_kernel<Bf16Weights, 2, ...>")
         roofline = {"bound": "hbm", "kernel": f"{kern} (gate/up, SiLU*up epilogue)",
                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -516,7 +531,8 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int8-weights/bf16" if int8 else "bf16", "data": "synthetic",
+        "dtype": "int8-weights/bf16" if int8 else "int4-weights/bf16" if int4 else "bf16",
+        "data": "synthetic",
         "config": {"workload": args.workload, "hidden": wl.H, "intermediate": wl.I,
                    "experts": wl.E, "top_k": wl.k, "tokens": [b["wl"].T for b in batches],
                    "layers_per_step": len(batches) * n_sets, "weight_sets": n_sets,
@@ -529,7 +545,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         b = batches[0]
-        host = host_rowmajor if int8 else sets[0]
+        host = host_rowmajor if quant else sets[0]
         result["cpu_baseline"] = cpu_baseline(b["wl"], host, b["lg_cpu"], b["x_cpu"])
     print(json.dumps(result), flush=True)
 

@@ -70,7 +70,8 @@ extern "C" {
  *                          handles, ascending
  *   large       int32[E]   experts that the tiled (many-token) product
  *                          handles, ascending: those with more than 32 tokens
- *                          when the batch has T > 64 tokens and BF16 weights;
+ *                          when the batch has T > 64 tokens and BF16 weights
+ *                          (moe_ffn_forward, moe_ffn_forward_logits);
  *                          otherwise none, and `active` lists every expert
  *                          with counts > 0
  *   sorted_slot int32[S]   slots grouped by expert (ascending), ascending
@@ -240,6 +241,30 @@ int moe_attn_decode(const void* q, const void* k_cache, const void* v_cache,
  * of 256), or 0 if the sizes are invalid.  Pure host computation. */
 size_t moe_attn_decode_workspace_bytes(int32_t B, int32_t h_q, int32_t h_kv,
                                        int32_t d, int32_t max_len);
+
+/*
+ * Routed-expert FFN layer, INT4 weights with group scales (the low-bit
+ * counterpart of moe_ffn_forward_int8; HiNa-MoE §8.1 / Fig. 11 quantises
+ * symmetrically per group, and the summary of the paper notes that low-bit
+ * packing changes the weights' layout).  Identical arithmetic to
+ * moe_ffn_forward_int8 on integer weights q in [-7, 7] (any value in
+ * [-8, 7] is accepted), stored two per byte as offset-binary nibbles
+ * u = q + 8: K element 2i of a row in the low nibble of byte i, element
+ * 2i + 1 in the high nibble.
+ *   P_gate, P_up [E][I][H/2] uint8 with S_gate, S_up [E][H/128][I] float32;
+ *   P_down [E][H][I/2] uint8 with S_down [E][I/128][H] float32
+ * (scales group-major as for INT8).  `group` must be MOE_FFN_INT8_GROUP
+ * (128).  Sizes: H and I multiples of 128.  Pointers 16-byte aligned.
+ * Batches of any size take the small-m product (no tiled INT4 product).
+ */
+int moe_ffn_forward_int4(const void* x, const int32_t* topk_ids,
+                         const float* topk_w, const uint8_t* P_gate,
+                         const float* S_gate, const uint8_t* P_up,
+                         const float* S_up, const uint8_t* P_down,
+                         const float* S_down, int32_t group, void* out,
+                         int64_t T, int64_t H, int64_t I, int32_t E,
+                         int32_t top_k, void* workspace, size_t workspace_bytes,
+                         void* stream);
 
 /* Wait for `stream`, then read the workspace meta written by the last forward
  * call: MOE_FFN_ERR_BAD_IDS if it dropped slots with out-of-range ids,

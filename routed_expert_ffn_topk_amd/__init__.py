@@ -67,6 +67,9 @@ def lib() -> ctypes.CDLL:
         L.moe_ffn_forward_logits.restype = _c.c_int
         L.moe_ffn_forward_logits.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64,
                                              _i64, _i32, _i32, _vp, _sz, _vp]
+        L.moe_ffn_forward_int4.restype = _c.c_int
+        L.moe_ffn_forward_int4.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+                                           _vp, _i64, _i64, _i64, _i32, _i32, _vp, _sz, _vp]
         L.moe_attn_decode.restype = _c.c_int
         L.moe_attn_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                       _c.c_float, _vp, _sz, _vp]
@@ -237,6 +240,41 @@ def moe_ffn_forward_int8(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.
         _dev(topk_w, "topk_w", torch.float32), _dev(Q_gate, "Q_gate", torch.int8),
         _dev(S_gate, "S_gate", torch.float32), _dev(Q_up, "Q_up", torch.int8),
         _dev(S_up, "S_up", torch.float32), _dev(Q_down, "Q_down", torch.int8),
+        _dev(S_down, "S_down", torch.float32), G, _dev(out, "out", torch.bfloat16),
+        T, H, I, E, top_k, _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+        _stream(stream)))
+    return out
+
+
+def moe_ffn_forward_int4(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor,
+                         P_gate: torch.Tensor, S_gate: torch.Tensor, P_up: torch.Tensor,
+                         S_up: torch.Tensor, P_down: torch.Tensor, S_down: torch.Tensor,
+                         out: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Routed-expert FFN layer with INT4 group-quantised weights, two
+    offset-binary nibbles per byte (P_gate/P_up [E, I, H/2], P_down [E, H, I/2]
+    uint8); scales group-major as for INT8.  Returns ``out``."""
+    T, H = x.shape
+    E, I, H2 = P_gate.shape
+    top_k = topk_ids.shape[1]
+    if 2 * H2 != H or tuple(P_up.shape) != (E, I, H // 2) or tuple(P_down.shape) != (E, H, I // 2):
+        raise ValueError("packed weights must be P_gate/P_up [E,I,H/2], P_down [E,H,I/2]")
+    G = 128
+    if H % G or I % G:
+        raise ValueError("H and I must be multiples of 128")
+    for name, S, shape in (("S_gate", S_gate, (E, H // G, I)), ("S_up", S_up, (E, H // G, I)),
+                           ("S_down", S_down, (E, I // G, H))):
+        if tuple(S.shape) != shape:
+            raise ValueError(f"{name} must be group-major {list(shape)}, got {list(S.shape)}")
+    if out is None:
+        out = torch.empty_like(x)
+    if workspace is None:
+        workspace = alloc_workspace(T, H, I, E, top_k, x.device)
+    _check("moe_ffn_forward_int4", lib().moe_ffn_forward_int4(
+        _dev(x, "x", torch.bfloat16), _dev(topk_ids, "topk_ids", torch.int32),
+        _dev(topk_w, "topk_w", torch.float32), _dev(P_gate, "P_gate", torch.uint8),
+        _dev(S_gate, "S_gate", torch.float32), _dev(P_up, "P_up", torch.uint8),
+        _dev(S_up, "S_up", torch.float32), _dev(P_down, "P_down", torch.uint8),
         _dev(S_down, "S_down", torch.float32), G, _dev(out, "out", torch.bfloat16),
         T, H, I, E, top_k, _dev(workspace, "workspace", torch.uint8), workspace.numel(),
         _stream(stream)))

@@ -78,7 +78,7 @@ struct ExpertGemm {
 
 struct Bf16Weights {
     static constexpr int kBlocks = 1;
-    static constexpr int kBytesPerWeight = 2;
+    static constexpr float kBytesPerWeight = 2.0f;
     static constexpr int kUnitBytes = kWave * 16;       // weight bytes a wave loads per unit
     template <int NMAT, int U>
     struct Batch {
@@ -141,7 +141,7 @@ __device__ __forceinline__ bf16x8 i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
 // 64-byte segment (row-major scales would cost a cache line per row).
 struct Int8Weights {
     static constexpr int kBlocks = 4;
-    static constexpr int kBytesPerWeight = 1;
+    static constexpr float kBytesPerWeight = 1.0f;
     static constexpr int kUnitBytes = kWave * 32;       // weight bytes a wave loads per unit
     template <int NMAT, int U>
     struct Batch {
@@ -193,10 +193,88 @@ struct Int8Weights {
     }
 };
 
+// INT4 with one FP32 scale per 128 consecutive K of a row, stored two per
+// byte as offset-binary nibbles u = q + 8 (K element 2i in the low nibble of
+// byte i).  A unit is one group: each lane loads the 16 bytes (32 K values)
+// of its row at group offset 32 kg, and word t of them (8 K values) feeds
+// MFMA t.  The BF16 with bits 0x4300 | u is exactly 128 + u, so one AND-OR
+// turns two nibbles into two BF16 operands: (w & 0x000F000F) | 0x43004300
+// holds K elements 0 and 4 of the word, and the shifts by 4, 8, 12 give
+// (1, 5), (2, 6), (3, 7).  The matrix unit then forms
+//   sum_k (128 + u_k) x_k = sum_k q_k x_k + 136 sum_k x_k,
+// and one more MFMA against the constant 136 (shared by the matrices)
+// forms the second term, subtracted before the group scale.  The token
+// values are read in the matching K order: LDS block t of K group kg holds K
+// values 32 kg + 8 t .. +8 of the group, and each B fragment's BF16 halves
+// are interleaved (0, 4, 1, 5, 2, 6, 3, 7).  About one VALU operation per
+// weight.
+struct Int4Weights {
+    static constexpr int kBlocks = 4;
+    static constexpr float kBytesPerWeight = 0.5f;
+    static constexpr int kUnitBytes = kWave * 16;       // weight bytes a wave loads per unit
+    template <int NMAT, int U>
+    struct Batch {
+        u32x4 w[U][NMAT];
+        f32x4 s[U][NMAT];
+    };
+    // one 16-byte weight load and one 16-byte scale load per unit and matrix
+    template <int NMAT, int U>
+    static constexpr int loads() { return U * NMAT * 2; }
+    __device__ static int block_offset(int sub, int kg) { return kg * 32 + sub * 8; }
+    __device__ static const void* row_ptr(const void* base, size_t row, int K, int kg) {
+        return static_cast<const uint8_t*>(base) + row * (size_t)(K / 2) + kg * 16;
+    }
+    template <int NMAT, int U>
+    __device__ static void load(Batch<NMAT, U>& d, const void* const* a, const float* const* sc,
+                                int spitch, int u) {
+#pragma unroll
+        for (int i = 0; i < U; ++i)
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m) {
+                d.w[i][m] = load16(static_cast<const uint8_t*>(a[m]) + (size_t)(u + i) * 64);
+                d.s[i][m] = __builtin_bit_cast(f32x4, load16(sc[m] + (size_t)(u + i) * spitch));
+            }
+    }
+    __device__ static u32x4 nibbles_to_bf16(uint32_t w) {
+        constexpr uint32_t kMask = 0x000F000Fu, kBias = 0x43004300u;
+        return u32x4{(w & kMask) | kBias, ((w >> 4) & kMask) | kBias,
+                     ((w >> 8) & kMask) | kBias, ((w >> 12) & kMask) | kBias};
+    }
+    // token values (x0..x7) -> (x0, x4, x1, x5, x2, x6, x3, x7)
+    __device__ static u32x4 interleave(u32x4 b) {
+        return u32x4{(b.x & 0xffffu) | (b.z << 16), (b.x >> 16) | (b.z & 0xffff0000u),
+                     (b.y & 0xffffu) | (b.w << 16), (b.y >> 16) | (b.w & 0xffff0000u)};
+    }
+    template <int NMAT, int U>
+    __device__ static void mma(const Batch<NMAT, U>& d, const u32x4* bl, f32x4* acc) {
+        const u32x4 k136 = {0x43084308u, 0x43084308u, 0x43084308u, 0x43084308u};  // BF16 136
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            u32x4 bx[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) bx[t] = interleave(bl[(4 * i + t) * kBlockU4]);
+            f32x4 corr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) corr = mfma16x16x32(as_bf16x8(k136), as_bf16x8(bx[t]), corr);
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m) {
+                const u32x4 w = d.w[i][m];
+                const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+                f32x4 part = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    part = mfma16x16x32(as_bf16x8(nibbles_to_bf16(words[t])), as_bf16x8(bx[t]),
+                                        part);
+                acc[m] += d.s[i][m] * (part - corr);
+            }
+        }
+    }
+};
+
 // Tuning per weight format and projection, measured on MI355X over the
 // Mixtral-8x7B, DeepSeek-V3, Qwen3-235B and Mixtral-8x22B expert shapes at
-// 1-16 tokens per expert: batch length U (units) and resident workgroups per
-// CU (LDS: 32 KB per workgroup).
+// 1-16 tokens per expert (INT4: the Mixtral-8x7B shape): batch length U
+// (units) and resident workgroups per CU (LDS: 32 KB per workgroup).
 template <class Fmt, int NMAT>
 struct GemmTuning;
 template <>
@@ -218,6 +296,16 @@ template <>
 struct GemmTuning<Int8Weights, 1> {
     static constexpr int kBlocksPerCU = 3;
     static constexpr int kBatch = 2;
+};
+template <>
+struct GemmTuning<Int4Weights, 2> {
+    static constexpr int kBlocksPerCU = 3;
+    static constexpr int kBatch = 1;
+};
+template <>
+struct GemmTuning<Int4Weights, 1> {
+    static constexpr int kBlocksPerCU = 2;
+    static constexpr int kBatch = 4;
 };
 
 // S: K-parts per row block; U: units per weight batch (divides the units of
@@ -543,7 +631,7 @@ hipError_t launch_ffn(const uint16_t* x, const Routing& route, const FfnWeights&
                       const StageEvents& ev, const SplitOverride& split, hipStream_t stream) {
     // experts with many tokens go to the tiled product (BF16 weights, batches
     // large enough that an expert can have more than kTiledMinTokens)
-    const bool tiled = Fmt::kBytesPerWeight == 2 && s.T > kTiledMinBatch;
+    const bool tiled = Fmt::kBytesPerWeight == 2.0f && s.T > kTiledMinBatch;
     const int m_split = tiled ? kTiledMinTokens : INT_MAX;
     hipError_t err =
         route.logits ? launch_route_permute(route.logits, route.ids, route.w, s, ws, m_split, stream)
@@ -612,6 +700,13 @@ hipError_t launch_ffn_bf16(const uint16_t* x, const Routing& route, const FfnWei
                            const StageEvents& ev, const SplitOverride& split,
                            hipStream_t stream) {
     return launch_ffn<Bf16Weights>(x, route, W, out, s, ws, num_cu, ev, split, stream);
+}
+
+hipError_t launch_ffn_int4(const uint16_t* x, const Routing& route, const FfnWeights& W,
+                           uint16_t* out, const FfnShape& s, const Workspace& ws, int num_cu,
+                           const StageEvents& ev, const SplitOverride& split,
+                           hipStream_t stream) {
+    return launch_ffn<Int4Weights>(x, route, W, out, s, ws, num_cu, ev, split, stream);
 }
 
 hipError_t launch_ffn_int8(const uint16_t* x, const Routing& route, const FfnWeights& W,

@@ -49,7 +49,8 @@ struct Routing {
     float* w;
 };
 
-// Weights of one layer: BF16 (q = NULL) or INT8 with per-128 group scales.
+// Weights of one layer: BF16 (no scales), or INT8 / INT4 (packed nibbles)
+// with per-128 group scales.
 struct FfnWeights {
     const void* gate;
     const void* up;
@@ -74,6 +75,11 @@ hipError_t launch_route_permute(const float* logits, int32_t* ids, float* w,
                                 hipStream_t stream);
 
 hipError_t launch_ffn_bf16(const uint16_t* x, const Routing& route, const FfnWeights& W,
+                           uint16_t* out, const FfnShape& s, const Workspace& ws, int num_cu,
+                           const StageEvents& ev, const SplitOverride& split,
+                           hipStream_t stream);
+
+hipError_t launch_ffn_int4(const uint16_t* x, const Routing& route, const FfnWeights& W,
                            uint16_t* out, const FfnShape& s, const Workspace& ws, int num_cu,
                            const StageEvents& ev, const SplitOverride& split,
                            hipStream_t stream);

@@ -405,3 +405,25 @@ def test_int8_quantiser_invariants():
                 assert abs(qq[r, g, grp[r, g]]) == 127
     err = np.abs(wn.reshape(64, 4, 128) - qq * s[..., None])
     assert np.all(err <= s[..., None] * 0.5 * (1 + 1e-6) + 1e-12)
+
+
+def test_int4_quantiser_and_packing():
+    """INT4 (the INT8 definition on values in [-7, 7], stored as two
+    offset-binary nibbles per byte): quantiser range and extremes, packing
+    layout (element 2i low nibble), exact round trip."""
+    rng = np.random.default_rng(23)
+    w = torch.from_numpy((rng.standard_normal((32, 256)) * 0.02).astype(np.float32))
+    q, s = workloads.quantize_groupwise(w, 128, 7)
+    qn, sn = q.numpy().astype(np.int32), s.numpy()
+    assert np.abs(qn).max() <= 7
+    grp = np.abs(w.numpy().reshape(32, 2, 128)).argmax(-1)
+    for r in range(32):
+        for g in range(2):
+            assert abs(qn.reshape(32, 2, 128)[r, g, grp[r, g]]) == 7
+    np.testing.assert_allclose(sn, np.abs(w.numpy()).reshape(32, 2, 128).max(-1) / 7, rtol=1e-6)
+    p = workloads.pack_int4(q).numpy()
+    assert p.shape == (32, 128) and p.dtype == np.uint8
+    assert np.array_equal(p & 0xF, (qn[:, 0::2] + 8).astype(np.uint8))
+    assert np.array_equal(p >> 4, (qn[:, 1::2] + 8).astype(np.uint8))
+    every = torch.arange(-8, 8, dtype=torch.int8).repeat(4).reshape(2, 32)
+    assert torch.equal(workloads.unpack_int4(workloads.pack_int4(every)), every)

@@ -25,6 +25,10 @@ nearest-even by torch's dtype cast):
     of 128 consecutive K elements of a row: s = max|w| / 127 (float32),
     q = clamp(round_half_even(w / s), -127, 127); an all-zero group gets
     s = 0 and q = 0.
+  * INT4 weights: the same with s = max|w| / 7 and q in [-7, 7], stored two
+    per byte as offset-binary nibbles (q + 8): K element 2i in the low
+    nibble of byte i, element 2i + 1 in the high nibble (a storage layout
+    only; the arithmetic is the INT8 variant's, on values of q in [-7, 7]).
 """
 from dataclasses import dataclass, replace
 from typing import Dict, Optional
@@ -49,6 +53,7 @@ class Workload:
     routing: str = "uniform"   # "uniform" | "forced" | "zipf"
     zipf_s: float = 0.0
     int8: bool = False
+    int4: bool = False
     group: int = 128
     seed: int = 0
 
@@ -65,6 +70,9 @@ def _registry() -> Dict[str, Workload]:
         w[f"mixtral8x7b_int8_m{m}"] = Workload(f"mixtral8x7b_int8_m{m}", H=4096,
                                                I=14336, E=8, k=2, T=4 * m,
                                                routing="forced", int8=True)
+        w[f"mixtral8x7b_int4_m{m}"] = Workload(f"mixtral8x7b_int4_m{m}", H=4096,
+                                               I=14336, E=8, k=2, T=4 * m,
+                                               routing="forced", int4=True)
     w["deepseekv3_t16"] = Workload("deepseekv3_t16", H=7168, I=2048, E=256, k=8, T=16)
     w["deepseekv3_zipf_t16"] = Workload("deepseekv3_zipf_t16", H=7168, I=2048,
                                         E=256, k=8, T=16, routing="zipf", zipf_s=1.1)
@@ -146,17 +154,18 @@ def gen_weights(wl: Workload, device="cpu", experts: Optional[list] = None):
     return Wg, Wu, Wd
 
 
-def quantize_groupwise(w: torch.Tensor, group: int = 128):
-    """Symmetric INT8 per-group quantisation along the last dim of ``w``.
+def quantize_groupwise(w: torch.Tensor, group: int = 128, qmax: int = 127):
+    """Symmetric per-group quantisation along the last dim of ``w`` to
+    integers in [-qmax, qmax] (127: INT8, 7: INT4).
 
     Returns (q int8 with w's shape, s float32 of shape [..., K/group]).
     """
     *lead, K = w.shape
     assert K % group == 0
     wg = w.float().reshape(*lead, K // group, group)
-    s = wg.abs().amax(dim=-1) / 127.0
+    s = wg.abs().amax(dim=-1) / float(qmax)
     safe = torch.where(s > 0, s, torch.ones_like(s))
-    q = torch.round(wg / safe[..., None]).clamp_(-127, 127)
+    q = torch.round(wg / safe[..., None]).clamp_(-qmax, qmax)
     q = torch.where((s > 0)[..., None], q, torch.zeros_like(q))
     return q.to(torch.int8).reshape(*lead, K), s.contiguous()
 
@@ -185,6 +194,40 @@ def gen_weights_int8(wl: Workload, device="cpu", experts: Optional[list] = None)
     return Qg, Sg, Qu, Su, Qd, Sd
 
 
+def pack_int4(q: torch.Tensor) -> torch.Tensor:
+    """INT4 values (int8 tensor in [-8, 7], last dim even) -> uint8 with two
+    offset-binary nibbles per byte: element 2i in the low nibble, 2i + 1 in
+    the high one.  A storage layout only."""
+    u = (q.to(torch.int16) + 8).to(torch.uint8)
+    return (u[..., 0::2] | (u[..., 1::2] << 4)).contiguous()
+
+
+def unpack_int4(p: torch.Tensor) -> torch.Tensor:
+    """Inverse of pack_int4: uint8 [..., K/2] -> int8 [..., K] in [-8, 7]."""
+    lo = (p & 0xF).to(torch.int16) - 8
+    hi = (p >> 4).to(torch.int16) - 8
+    return torch.stack([lo, hi], dim=-1).reshape(*p.shape[:-1], 2 * p.shape[-1]).to(torch.int8)
+
+
+def gen_weights_int4(wl: Workload, device="cpu", experts: Optional[list] = None):
+    """INT4 expert weights with per-group scales, unpacked (as int8 values in
+    [-7, 7], the oracle's input): (Qg, Sg, Qu, Su, Qd, Sd) shaped like
+    gen_weights_int8's.  pack_int4 gives the stored form."""
+    ex = range(wl.E) if experts is None else experts
+    gsz = wl.group
+    Qg = torch.zeros(wl.E, wl.I, wl.H, dtype=torch.int8, device=device)
+    Qu = torch.zeros(wl.E, wl.I, wl.H, dtype=torch.int8, device=device)
+    Qd = torch.zeros(wl.E, wl.H, wl.I, dtype=torch.int8, device=device)
+    Sg = torch.zeros(wl.E, wl.I, wl.H // gsz, dtype=torch.float32, device=device)
+    Su = torch.zeros(wl.E, wl.I, wl.H // gsz, dtype=torch.float32, device=device)
+    Sd = torch.zeros(wl.E, wl.H, wl.I // gsz, dtype=torch.float32, device=device)
+    for e in ex:
+        Qg[e], Sg[e] = quantize_groupwise(_draw(wl, TAG_WG, e, wl.I, wl.H, device), gsz, 7)
+        Qu[e], Su[e] = quantize_groupwise(_draw(wl, TAG_WU, e, wl.I, wl.H, device), gsz, 7)
+        Qd[e], Sd[e] = quantize_groupwise(_draw(wl, TAG_WD, e, wl.H, wl.I, device), gsz, 7)
+    return Qg, Sg, Qu, Su, Qd, Sd
+
+
 def bf16_bits(t: torch.Tensor) -> np.ndarray:
     """BF16 tensor -> numpy uint16 bit patterns (host copy)."""
     return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
@@ -200,6 +243,8 @@ def weight_bytes_per_expert(wl: Workload) -> int:
     n = 3 * wl.H * wl.I
     if wl.int8:
         return n + 3 * (wl.H * wl.I // wl.group) * 4
+    if wl.int4:
+        return n // 2 + 3 * (wl.H * wl.I // wl.group) * 4
     return 2 * n
 
 
