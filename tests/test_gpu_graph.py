@@ -89,3 +89,81 @@ def test_int8_layer_graph_replays_match_eager():
         moe.moe_ffn_forward_int8(x, torch.flip(ids, dims=[1]).contiguous(), w, *Q, workspace=ws)
 
     _replays_match(call, [out], other)
+
+
+@pytest.mark.parametrize("T", [16, 300])
+def test_logits_layer_graph_replays_match_eager(T):
+    """Router + gather index + layer from logits (fused decode kernel at 16
+    tokens; router, sort and the tiled product at 300)."""
+    need_gpu()
+    say(f"graph replay logits layer T={T}")
+    wl = workloads.Workload("g", H=256, I=384, E=16, k=2, T=T)
+    x = workloads.gen_x(wl).cuda()
+    lg = workloads.gen_logits(wl).cuda()
+    W = workloads.gen_weights(wl, "cuda")
+    ws = moe.alloc_workspace(wl.T, wl.H, wl.I, wl.E, wl.k)
+    out = torch.empty_like(x)
+    ids = torch.empty(T, wl.k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, wl.k, dtype=torch.float32, device="cuda")
+    lg2 = torch.flip(lg, dims=[0]).contiguous()
+
+    def call():
+        moe.moe_ffn_forward_logits(x, lg, wl.k, *W, out=out, topk_ids=ids, topk_w=w,
+                                   workspace=ws, stream=torch.cuda.current_stream())
+
+    def other():
+        moe.moe_ffn_forward_logits(x, lg2, wl.k, *W, workspace=ws)
+
+    _replays_match(call, [out, ids, w], other)
+
+
+def test_int4_layer_graph_replays_match_eager():
+    need_gpu()
+    say("graph replay int4")
+    rng = np.random.default_rng(6)
+    T, H, I, E, k = 16, 512, 384, 8, 2
+    x = workloads.bits_to_bf16(workloads.bf16_bits(
+        torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(torch.bfloat16))).cuda()
+    gm = workloads.scales_group_major
+    P = []
+    for N, K in ((I, H), (I, H), (H, I)):
+        q, sc = workloads.quantize_groupwise(
+            torch.from_numpy((rng.standard_normal((E, N, K)) * 0.05).astype(np.float32)), 128, 7)
+        P += [workloads.pack_int4(q).cuda(), gm(sc).cuda()]
+    ids = torch.from_numpy(np.stack([rng.choice(E, size=k, replace=False)
+                                     for _ in range(T)]).astype(np.int32)).cuda()
+    w = torch.from_numpy(rng.uniform(0.05, 1.0, size=(T, k)).astype(np.float32)).cuda()
+    ws = moe.alloc_workspace(T, H, I, E, k)
+    out = torch.empty_like(x)
+
+    def call():
+        moe.moe_ffn_forward_int4(x, ids, w, *P, out=out, workspace=ws,
+                                 stream=torch.cuda.current_stream())
+
+    def other():
+        moe.moe_ffn_forward_int4(x, torch.flip(ids, dims=[1]).contiguous(), w, *P, workspace=ws)
+
+    _replays_match(call, [out], other)
+
+
+def test_attn_graph_replays_match_eager():
+    need_gpu()
+    say("graph replay attention")
+    wl = workloads.ATTN_WORKLOADS["attn_tiny"]
+    q = workloads.gen_attn_q(wl).cuda()
+    lens = workloads.gen_attn_lens(wl).cuda()
+    k, v = workloads.gen_attn_kv(wl, "cuda")
+    ws = torch.empty(moe.moe_attn_decode_workspace_bytes(wl.B, wl.h_q, wl.h_kv, wl.d,
+                                                         wl.max_len),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    lens2 = torch.flip(lens, dims=[0]).contiguous()
+
+    def call():
+        moe.moe_attn_decode(q, k, v, lens, out=out, workspace=ws,
+                            stream=torch.cuda.current_stream())
+
+    def other():
+        moe.moe_attn_decode(q, k, v, lens2, workspace=ws)
+
+    _replays_match(call, [out], other)
