@@ -379,6 +379,12 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, int n_act, int 
             // padding columns are never stored
             const bool valid = col < ntok;
             const int bcol = valid ? col : 0;
+            // the first weight batch needs only the expert and the row:
+            // request it before the token rows, whose addresses take two
+            // dependent loads (the first slab then waits for everything)
+            constexpr int kLoads = Fmt::template loads<NMAT, U>();
+            typename Fmt::template Batch<NMAT, U> A, B;
+            if (nfull > 0) Fmt::template load<NMAT, U>(A, wp, sp, g.N, u0);
             // token rows this wave stages: tokens wave, wave + 4, ...
             const uint16_t* tp[4];
 #pragma unroll
@@ -419,14 +425,14 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, int n_act, int 
             // weight batches ping-pong between two register sets: batch bi
             // lives in A when bi is even, in B when odd; the next batch is
             // always requested before the current one is multiplied
-            constexpr int kLoads = Fmt::template loads<NMAT, U>();
-            Batch A, B;
-            if (nfull > 0) Fmt::template load<NMAT, U>(A, wp, sp, g.N, u0);
             int bi = 0;
             for (int j = 0; j < nslab; ++j) {
                 // this wave's staging loads are done (only the batch
-                // prefetched for this slab may still be in flight)
-                if (bi < nfull)
+                // prefetched for this slab may still be in flight; at slab
+                // 0, whose staging follows the first batch, everything)
+                if (j == 0)
+                    wait_vmcnt<0>();
+                else if (bi < nfull)
                     wait_vmcnt<(kLoads < 63 ? kLoads : 63)>();
                 else
                     wait_vmcnt<0>();
