@@ -10,11 +10,13 @@
 // through LDS in tiles and the matrix unit, not HBM, sets the pace.
 //
 // Work unit: a tile of 128 weight rows x 128 gathered rows of one expert.
-// The four waves split it 2 x 2 (64 x 64 each, 4 x 4 MFMA 16x16x32 blocks
-// per matrix).  Per pipeline stage (K = 32) every operand tile (128 rows x 32
-// K, 8 KB) is written to LDS by direct global->LDS 16-byte loads, with the
-// gather of the token rows folded into the load addresses; three stages are
-// in flight.  Rows are stored 64 bytes apart with their four 16-byte chunks
+// Eight waves split it, 4 x 2 for gate/up (32 rows x 64 tokens each, 2 x 4
+// MFMA 16x16x32 blocks per matrix) and 2 x 4 for down (64 x 32); eight
+// rather than four waves per tile keep more waves on each SIMD to cover the
+// per-stage barrier and load waits.  Per pipeline stage (K = 32) every
+// operand tile (128 rows x 32 K, 8 KB) is written to LDS by direct
+// global->LDS 16-byte loads, with the gather of the token rows folded into
+// the load addresses; three stages are in flight.  Rows are stored 64 bytes apart with their four 16-byte chunks
 // XOR-swizzled by bit 2 of the row, so that the MFMA fragment reads (eight
 // rows x two K chunks at a time) hit distinct LDS banks.
 //
@@ -34,8 +36,6 @@ constexpr int kTileN = 128;                       // weight rows per tile
 constexpr int kTileM = 128;                       // gathered rows per tile
 constexpr int kTileK = 32;                        // K per pipeline stage
 constexpr int kTileStages = 3;
-constexpr int kTileWaves = 4;                     // 2 x 2 waves of 64 x 64
-constexpr int kTileThreads = kTileWaves * kWave;
 constexpr int kRowWords = kTileK / 8;             // 16-byte words of a row per stage
 constexpr int kOperandWords = 128 * kRowWords;    // one 128-row operand tile (8 KB)
 constexpr int kMaxLarge = 1024;                   // matches MOE_FFN_MAX_EXPERTS
@@ -61,24 +61,39 @@ struct TiledGemm {
     int top_k;
 };
 
-// Resident workgroups per CU (LDS: 3 stages x (NMAT + 1) x 8 KB + 4 KB).
+// Waves per workgroup, arranged kWaveRows (along the weight rows) x
+// kWaves / kWaveRows (along the tokens), and resident workgroups per CU
+// (LDS: 3 stages x (NMAT + 1) x 8 KB + 4 KB).
 template <int NMAT>
 struct TileTuning;
 template <>
 struct TileTuning<2> {
+    static constexpr int kWaves = 8;
+    static constexpr int kWaveRows = 4;
     static constexpr int kBlocksPerCU = 2;
 };
 template <>
 struct TileTuning<1> {
+    static constexpr int kWaves = 8;
+    static constexpr int kWaveRows = 2;
     static constexpr int kBlocksPerCU = 3;
 };
 
 template <int NMAT>
-__global__ __launch_bounds__(kTileThreads)
-__attribute__((amdgpu_waves_per_eu(TileTuning<NMAT>::kBlocksPerCU)))
+__global__ __launch_bounds__(TileTuning<NMAT>::kWaves * kWave)
+__attribute__((amdgpu_waves_per_eu(TileTuning<NMAT>::kBlocksPerCU *
+                                   TileTuning<NMAT>::kWaves / 4)))
 void expert_tile_kernel(const TiledGemm g) {
+    constexpr int W = TileTuning<NMAT>::kWaves;
+    constexpr int WR = TileTuning<NMAT>::kWaveRows;
+    static_assert((W == 4 || W == 8) && W % WR == 0, "waves per workgroup");
+    constexpr int IL = 8 / W;                     // staging loads per wave and operand
+    constexpr int RPW = kTileN / WR;              // weight rows per wave
+    constexpr int TPW = kTileM / (W / WR);        // tokens per wave
+    constexpr int RB = RPW / 16;                  // 16-row blocks per wave
+    constexpr int TB = TPW / 16;                  // 16-token blocks per wave
     constexpr int kStageWords = (NMAT + 1) * kOperandWords;
-    constexpr int kLoads = 2 * (NMAT + 1);        // load instructions per wave and stage
+    constexpr int kLoads = IL * (NMAT + 1);       // load instructions per wave and stage
     __shared__ u32x4 lds[kTileStages * kStageWords];
     __shared__ int pre[kMaxLarge + 1];
 
@@ -116,11 +131,11 @@ void expert_tile_kernel(const TiledGemm g) {
     const int li = blockIdx.x / kXcds;
     const int qb = (int)((long long)xcd * Q / kXcds);
     const int qe = (int)((long long)(xcd + 1) * Q / kXcds);
-    const int wr = wave & 1;          // 64-row half of the weight tile
-    const int wm = wave >> 1;         // 64-row half of the token tile
+    const int wr = wave % WR;         // this wave's share of the weight rows
+    const int wm = wave / WR;         // this wave's share of the token tile
     const int col = lane & 15;        // A row, B column and D column of this lane
     const int kg = lane >> 4;         // K chunk of the operands, row quad of D
-    // staging: load instruction i of this wave fills rows 16 (wave + 4i) ..
+    // staging: load instruction i of this wave fills rows 16 (wave + W i) ..
     // +16 of an operand tile; lane L brings row + (L >> 2), logical chunk cl
     const int cl = (lane & 3) ^ ((lane >> 3) & 2);
     const int nk = g.K / kTileK;
@@ -146,11 +161,11 @@ void expert_tile_kernel(const TiledGemm g) {
         // per-lane source rows of the staging loads (rows past the matrix or
         // past the expert's tokens repeat a valid row; their results are
         // never stored)
-        const uint16_t* wsrc[NMAT][2];
-        const uint16_t* bsrc[2];
+        const uint16_t* wsrc[NMAT][IL];
+        const uint16_t* bsrc[IL];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int rr = 16 * (wave + 4 * i) + (lane >> 2);
+        for (int i = 0; i < IL; ++i) {
+            const int rr = 16 * (wave + W * i) + (lane >> 2);
             const size_t wrow = (size_t)e * g.N + min(row0 + rr, g.N - 1);
             wsrc[0][i] = g.w0 + wrow * g.K + cl * 8;
             if constexpr (NMAT == 2) wsrc[1][i] = g.w1 + wrow * g.K + cl * 8;
@@ -162,8 +177,8 @@ void expert_tile_kernel(const TiledGemm g) {
             u32x4* buf = lds + (s % kTileStages) * kStageWords;
             const int k0 = s * kTileK;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int dst = (wave + 4 * i) * kWave;
+            for (int i = 0; i < IL; ++i) {
+                const int dst = (wave + W * i) * kWave;
 #pragma unroll
                 for (int mm = 0; mm < NMAT; ++mm)
                     __builtin_amdgcn_global_load_lds((const void*)(wsrc[mm][i] + k0),
@@ -175,13 +190,13 @@ void expert_tile_kernel(const TiledGemm g) {
             }
         };
 
-        f32x4 acc[NMAT][4][4];
+        f32x4 acc[NMAT][RB][TB];
 #pragma unroll
         for (int mm = 0; mm < NMAT; ++mm)
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
+            for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-                for (int tb = 0; tb < 4; ++tb) acc[mm][rb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int tb = 0; tb < TB; ++tb) acc[mm][rb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
         issue(0);
         if (nk > 1) issue(1);
@@ -196,19 +211,19 @@ void expert_tile_kernel(const TiledGemm g) {
             __syncthreads();
             if (s + 2 < nk) issue(s + 2);
             const u32x4* buf = lds + (s % kTileStages) * kStageWords;
-            u32x4 af[NMAT][4];
+            u32x4 af[NMAT][RB];
 #pragma unroll
             for (int mm = 0; mm < NMAT; ++mm)
 #pragma unroll
-                for (int rb = 0; rb < 4; ++rb)
-                    af[mm][rb] = buf[mm * kOperandWords + tile_word(64 * wr + 16 * rb + col, kg)];
+                for (int rb = 0; rb < RB; ++rb)
+                    af[mm][rb] = buf[mm * kOperandWords + tile_word(RPW * wr + 16 * rb + col, kg)];
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                const u32x4 bf = buf[NMAT * kOperandWords + tile_word(64 * wm + 16 * tb + col, kg)];
+            for (int tb = 0; tb < TB; ++tb) {
+                const u32x4 bf = buf[NMAT * kOperandWords + tile_word(TPW * wm + 16 * tb + col, kg)];
 #pragma unroll
                 for (int mm = 0; mm < NMAT; ++mm)
 #pragma unroll
-                    for (int rb = 0; rb < 4; ++rb)
+                    for (int rb = 0; rb < RB; ++rb)
                         acc[mm][rb][tb] =
                             mfma16x16x32(as_bf16x8(af[mm][rb]), as_bf16x8(bf), acc[mm][rb][tb]);
             }
@@ -219,12 +234,12 @@ void expert_tile_kernel(const TiledGemm g) {
 
         // epilogue: lane holds rows n .. n+3 of token column p for each block
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-            const int n = row0 + 64 * wr + 16 * rb + 4 * kg;
+        for (int rb = 0; rb < RB; ++rb) {
+            const int n = row0 + RPW * wr + 16 * rb + 4 * kg;
             if (n >= g.N) continue;
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                const int p = p0 + 64 * wm + 16 * tb + col;
+            for (int tb = 0; tb < TB; ++tb) {
+                const int p = p0 + TPW * wm + 16 * tb + col;
                 if (p >= m) continue;
                 if constexpr (NMAT == 2) {
                     const f32x4 gv = acc[0][rb][tb], uv = acc[1][rb][tb];
@@ -247,7 +262,8 @@ template <int NMAT>
 hipError_t launch_tile(const TiledGemm& g, int num_cu, hipStream_t stream) {
     int grid = num_cu * TileTuning<NMAT>::kBlocksPerCU;
     grid = (grid + kXcds - 1) / kXcds * kXcds;
-    hipLaunchKernelGGL((expert_tile_kernel<NMAT>), dim3(grid), dim3(kTileThreads), 0, stream, g);
+    hipLaunchKernelGGL((expert_tile_kernel<NMAT>), dim3(grid),
+                       dim3(TileTuning<NMAT>::kWaves * kWave), 0, stream, g);
     return hipGetLastError();
 }
 
