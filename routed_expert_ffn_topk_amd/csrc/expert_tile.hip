@@ -34,16 +34,25 @@ namespace {
 
 constexpr int kTileN = 128;                       // weight rows per tile
 constexpr int kTileM = 128;                       // gathered rows per tile
-constexpr int kTileK = 32;                        // K per pipeline stage
-constexpr int kTileStages = 3;
-constexpr int kRowWords = kTileK / 8;             // 16-byte words of a row per stage
-constexpr int kOperandWords = 128 * kRowWords;    // one 128-row operand tile (8 KB)
 constexpr int kMaxLarge = 1024;                   // matches MOE_FFN_MAX_EXPERTS
+
+// An operand tile of one stage holds 128 rows of RW 16-byte words (K = 8 RW
+// values per row).  The words of a row are XOR-swizzled by bits of the row
+// so that a fragment read (eight consecutive rows x two adjacent words)
+// touches distinct LDS banks.
+template <int RW>
+__device__ __forceinline__ int row_swizzle(int r) {
+    if constexpr (RW == 4)
+        return (r >> 1) & 2;
+    else
+        return ((r >> 1) & 3) << 1;
+}
 
 // LDS word of row r, logical 16-byte chunk c (K values 8c .. 8c+7 of the
 // stage) in an operand tile.
+template <int RW>
 __device__ __forceinline__ int tile_word(int r, int c) {
-    return r * kRowWords + (c ^ ((r >> 1) & 2));
+    return r * RW + (c ^ row_swizzle<RW>(r));
 }
 
 struct TiledGemm {
@@ -62,20 +71,25 @@ struct TiledGemm {
 };
 
 // Waves per workgroup, arranged kWaveRows (along the weight rows) x
-// kWaves / kWaveRows (along the tokens), and resident workgroups per CU
-// (LDS: 3 stages x (NMAT + 1) x 8 KB + 4 KB).
+// kWaves / kWaveRows (along the tokens); K per pipeline stage (32 or 64) and
+// stages in flight; resident workgroups per CU (LDS: kStages x (NMAT + 1) x
+// 128 rows x 2 kK bytes + 4 KB).
 template <int NMAT>
 struct TileTuning;
 template <>
 struct TileTuning<2> {
     static constexpr int kWaves = 8;
     static constexpr int kWaveRows = 4;
+    static constexpr int kK = 32;
+    static constexpr int kStages = 3;
     static constexpr int kBlocksPerCU = 2;
 };
 template <>
 struct TileTuning<1> {
     static constexpr int kWaves = 8;
     static constexpr int kWaveRows = 2;
+    static constexpr int kK = 32;
+    static constexpr int kStages = 3;
     static constexpr int kBlocksPerCU = 3;
 };
 
@@ -86,15 +100,21 @@ __attribute__((amdgpu_waves_per_eu(TileTuning<NMAT>::kBlocksPerCU *
 void expert_tile_kernel(const TiledGemm g) {
     constexpr int W = TileTuning<NMAT>::kWaves;
     constexpr int WR = TileTuning<NMAT>::kWaveRows;
+    constexpr int KS = TileTuning<NMAT>::kK;      // K per stage
+    constexpr int S = TileTuning<NMAT>::kStages;
     static_assert((W == 4 || W == 8) && W % WR == 0, "waves per workgroup");
-    constexpr int IL = 8 / W;                     // staging loads per wave and operand
+    static_assert((KS == 32 || KS == 64) && S >= 2, "stage shape");
+    constexpr int RW = KS / 8;                    // 16-byte words of a row per stage
+    constexpr int kOperandWords = 128 * RW;       // one 128-row operand tile
+    constexpr int RPI = kWave / RW;               // rows per staging load instruction
+    constexpr int IL = 128 / RPI / W;             // staging loads per wave and operand
     constexpr int RPW = kTileN / WR;              // weight rows per wave
     constexpr int TPW = kTileM / (W / WR);        // tokens per wave
     constexpr int RB = RPW / 16;                  // 16-row blocks per wave
     constexpr int TB = TPW / 16;                  // 16-token blocks per wave
     constexpr int kStageWords = (NMAT + 1) * kOperandWords;
     constexpr int kLoads = IL * (NMAT + 1);       // load instructions per wave and stage
-    __shared__ u32x4 lds[kTileStages * kStageWords];
+    __shared__ u32x4 lds[S * kStageWords];
     __shared__ int pre[kMaxLarge + 1];
 
     const int n_large = g.meta[2];
@@ -135,10 +155,14 @@ void expert_tile_kernel(const TiledGemm g) {
     const int wm = wave / WR;         // this wave's share of the token tile
     const int col = lane & 15;        // A row, B column and D column of this lane
     const int kg = lane >> 4;         // K chunk of the operands, row quad of D
-    // staging: load instruction i of this wave fills rows 16 (wave + W i) ..
-    // +16 of an operand tile; lane L brings row + (L >> 2), logical chunk cl
-    const int cl = (lane & 3) ^ ((lane >> 3) & 2);
-    const int nk = g.K / kTileK;
+    // staging: load instruction i of this wave fills rows RPI (wave + W i) ..
+    // +RPI of an operand tile; lane L brings row + L / RW, logical chunk cl
+    // (the instruction's first row is a multiple of 8, so the swizzle of the
+    // row depends on L alone)
+    const int cl = (lane % RW) ^ row_swizzle<RW>(lane / RW);
+    // stages; K is a multiple of 32, so with 64 per stage the last one may
+    // hold only its first half
+    const int nk = (g.K + KS - 1) / KS;
 
     for (int q = qb + li; q < qe; q += per) {
         int lo = 0, hi = n_large - 1;                 // last a with pre[a] <= q
@@ -165,7 +189,7 @@ void expert_tile_kernel(const TiledGemm g) {
         const uint16_t* bsrc[IL];
 #pragma unroll
         for (int i = 0; i < IL; ++i) {
-            const int rr = 16 * (wave + W * i) + (lane >> 2);
+            const int rr = RPI * (wave + W * i) + lane / RW;
             const size_t wrow = (size_t)e * g.N + min(row0 + rr, g.N - 1);
             wsrc[0][i] = g.w0 + wrow * g.K + cl * 8;
             if constexpr (NMAT == 2) wsrc[1][i] = g.w1 + wrow * g.K + cl * 8;
@@ -174,8 +198,11 @@ void expert_tile_kernel(const TiledGemm g) {
             bsrc[i] = g.b_src + (size_t)brow * g.b_pitch + cl * 8;
         }
         auto issue = [&](int s) {
-            u32x4* buf = lds + (s % kTileStages) * kStageWords;
-            const int k0 = s * kTileK;
+            u32x4* buf = lds + (s % S) * kStageWords;
+            int k0 = s * KS;
+            // the second half of a half stage re-reads the first (in bounds;
+            // never used)
+            if (KS > 32 && k0 + 8 * cl >= g.K) k0 -= 32;
 #pragma unroll
             for (int i = 0; i < IL; ++i) {
                 const int dst = (wave + W * i) * kWave;
@@ -198,34 +225,42 @@ void expert_tile_kernel(const TiledGemm g) {
 #pragma unroll
                 for (int tb = 0; tb < TB; ++tb) acc[mm][rb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        issue(0);
-        if (nk > 1) issue(1);
+#pragma unroll
+        for (int s = 0; s < S - 1; ++s)
+            if (s < nk) issue(s);
         for (int s = 0; s < nk; ++s) {
-            // this wave's loads of stage s are done (stage s + 1 may still be
-            // in flight), then everyone's: the stage is complete in LDS and
-            // every wave has finished with the buffer stage s + 2 reuses
-            if (s + 1 < nk)
-                wait_vmcnt<kLoads>();
+            // this wave's loads of stage s are done (the next S - 2 stages may
+            // still be in flight), then everyone's: the stage is complete in
+            // LDS and every wave has finished with the buffer stage s + S - 1
+            // reuses
+            if (s + S - 2 < nk)
+                wait_vmcnt<(S - 2) * kLoads>();
             else
                 wait_vmcnt<0>();
             __syncthreads();
-            if (s + 2 < nk) issue(s + 2);
-            const u32x4* buf = lds + (s % kTileStages) * kStageWords;
-            u32x4 af[NMAT][RB];
+            if (s + S - 1 < nk) issue(s + S - 1);
+            const u32x4* buf = lds + (s % S) * kStageWords;
 #pragma unroll
-            for (int mm = 0; mm < NMAT; ++mm)
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-                    af[mm][rb] = buf[mm * kOperandWords + tile_word(RPW * wr + 16 * rb + col, kg)];
-#pragma unroll
-            for (int tb = 0; tb < TB; ++tb) {
-                const u32x4 bf = buf[NMAT * kOperandWords + tile_word(TPW * wm + 16 * tb + col, kg)];
+            for (int j = 0; j < KS / 32; ++j) {
+                if (j > 0 && s * KS + 32 * j >= g.K) break;      // half stage
+                u32x4 af[NMAT][RB];
 #pragma unroll
                 for (int mm = 0; mm < NMAT; ++mm)
 #pragma unroll
                     for (int rb = 0; rb < RB; ++rb)
-                        acc[mm][rb][tb] =
-                            mfma16x16x32(as_bf16x8(af[mm][rb]), as_bf16x8(bf), acc[mm][rb][tb]);
+                        af[mm][rb] = buf[mm * kOperandWords +
+                                         tile_word<RW>(RPW * wr + 16 * rb + col, 4 * j + kg)];
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) {
+                    const u32x4 bf = buf[NMAT * kOperandWords +
+                                         tile_word<RW>(TPW * wm + 16 * tb + col, 4 * j + kg)];
+#pragma unroll
+                    for (int mm = 0; mm < NMAT; ++mm)
+#pragma unroll
+                        for (int rb = 0; rb < RB; ++rb)
+                            acc[mm][rb][tb] = mfma16x16x32(as_bf16x8(af[mm][rb]), as_bf16x8(bf),
+                                                           acc[mm][rb][tb]);
+                }
             }
         }
         // every wave is done with the stage buffers before the next tile's
