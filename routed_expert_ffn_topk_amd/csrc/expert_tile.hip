@@ -32,7 +32,7 @@ namespace moe {
 
 namespace {
 
-constexpr int kTileN = 128;                       // weight rows per tile
+constexpr int kTileN = 128;                       // weight rows per block
 constexpr int kTileM = 128;                       // gathered rows per tile
 constexpr int kMaxLarge = 1024;                   // matches MOE_FFN_MAX_EXPERTS
 
@@ -70,14 +70,18 @@ struct TiledGemm {
     int top_k;
 };
 
-// Waves per workgroup, arranged kWaveRows (along the weight rows) x
-// kWaves / kWaveRows (along the tokens); K per pipeline stage (32 or 64) and
-// stages in flight; resident workgroups per CU (LDS: kStages x (NMAT + 1) x
-// 128 rows x 2 kK bytes + 4 KB).
-template <int NMAT>
+// Per product (gate/up, down): weight blocks of 128 rows per tile
+// (gate/up: the same rows of W_gate and W_up; down: kBlocks consecutive
+// 128-row blocks of W_down, so a tile covers 128 kBlocks output rows), waves
+// per workgroup arranged kWaveRows (along the weight rows) x kWaves /
+// kWaveRows (along the tokens), K per pipeline stage (32 or 64), stages in
+// flight, and resident workgroups per CU (LDS: kStages x (kBlocks + 1) x 128
+// rows x 2 kK bytes + 4 KB).
+template <bool kDown>
 struct TileTuning;
 template <>
-struct TileTuning<2> {
+struct TileTuning<false> {
+    static constexpr int kBlocks = 2;
     static constexpr int kWaves = 8;
     static constexpr int kWaveRows = 4;
     static constexpr int kK = 32;
@@ -85,7 +89,8 @@ struct TileTuning<2> {
     static constexpr int kBlocksPerCU = 2;
 };
 template <>
-struct TileTuning<1> {
+struct TileTuning<true> {
+    static constexpr int kBlocks = 1;
     static constexpr int kWaves = 8;
     static constexpr int kWaveRows = 2;
     static constexpr int kK = 32;
@@ -93,15 +98,19 @@ struct TileTuning<1> {
     static constexpr int kBlocksPerCU = 3;
 };
 
-template <int NMAT>
-__global__ __launch_bounds__(TileTuning<NMAT>::kWaves * kWave)
-__attribute__((amdgpu_waves_per_eu(TileTuning<NMAT>::kBlocksPerCU *
-                                   TileTuning<NMAT>::kWaves / 4)))
+template <bool kDown>
+__global__ __launch_bounds__(TileTuning<kDown>::kWaves * kWave)
+__attribute__((amdgpu_waves_per_eu(TileTuning<kDown>::kBlocksPerCU *
+                                   TileTuning<kDown>::kWaves / 4)))
 void expert_tile_kernel(const TiledGemm g) {
-    constexpr int W = TileTuning<NMAT>::kWaves;
-    constexpr int WR = TileTuning<NMAT>::kWaveRows;
-    constexpr int KS = TileTuning<NMAT>::kK;      // K per stage
-    constexpr int S = TileTuning<NMAT>::kStages;
+    using Tu = TileTuning<kDown>;
+    constexpr int NMAT = Tu::kBlocks;             // weight blocks per tile
+    constexpr int W = Tu::kWaves;
+    constexpr int WR = Tu::kWaveRows;
+    constexpr int KS = Tu::kK;                    // K per stage
+    constexpr int S = Tu::kStages;
+    constexpr int kRows = kDown ? kTileN * NMAT : kTileN;   // output rows per tile
+    static_assert(kDown || NMAT == 2, "gate/up tiles hold W_gate and W_up");
     static_assert((W == 4 || W == 8) && W % WR == 0, "waves per workgroup");
     static_assert((KS == 32 || KS == 64) && S >= 2, "stage shape");
     constexpr int RW = KS / 8;                    // 16-byte words of a row per stage
@@ -121,7 +130,7 @@ void expert_tile_kernel(const TiledGemm g) {
     if (n_large <= 0) return;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const int rt_n = (g.N + kTileN - 1) / kTileN;     // row tiles per expert
+    const int rt_n = (g.N + kRows - 1) / kRows;       // row tiles per expert
 
     // tiles before large expert a: pre[a] (wave 0, one run of experts per lane)
     if (wave == 0) {
@@ -179,7 +188,7 @@ void expert_tile_kernel(const TiledGemm g) {
         const int mt_n = (m + kTileM - 1) / kTileM;
         const int r = q - pre[lo];
         const int rt = r / mt_n;
-        const int row0 = rt * kTileN;
+        const int row0 = rt * kRows;
         const int p0 = (r - rt * mt_n) * kTileM;
 
         // per-lane source rows of the staging loads (rows past the matrix or
@@ -190,11 +199,14 @@ void expert_tile_kernel(const TiledGemm g) {
 #pragma unroll
         for (int i = 0; i < IL; ++i) {
             const int rr = RPI * (wave + W * i) + lane / RW;
-            const size_t wrow = (size_t)e * g.N + min(row0 + rr, g.N - 1);
-            wsrc[0][i] = g.w0 + wrow * g.K + cl * 8;
-            if constexpr (NMAT == 2) wsrc[1][i] = g.w1 + wrow * g.K + cl * 8;
+#pragma unroll
+            for (int mm = 0; mm < NMAT; ++mm) {
+                const int row = kDown ? row0 + kTileN * mm + rr : row0 + rr;
+                const size_t wrow = (size_t)e * g.N + min(row, g.N - 1);
+                wsrc[mm][i] = (kDown || mm == 0 ? g.w0 : g.w1) + wrow * g.K + cl * 8;
+            }
             const int pp = beg + min(p0 + rr, m - 1);
-            const int brow = NMAT == 2 ? g.sorted_slot[pp] / g.top_k : pp;
+            const int brow = kDown ? pp : g.sorted_slot[pp] / g.top_k;
             bsrc[i] = g.b_src + (size_t)brow * g.b_pitch + cl * 8;
         }
         auto issue = [&](int s) {
@@ -269,14 +281,23 @@ void expert_tile_kernel(const TiledGemm g) {
 
         // epilogue: lane holds rows n .. n+3 of token column p for each block
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            const int n = row0 + RPW * wr + 16 * rb + 4 * kg;
-            if (n >= g.N) continue;
+        for (int tb = 0; tb < TB; ++tb) {
+            const int p = p0 + TPW * wm + 16 * tb + col;
+            if (p >= m) continue;
+            if constexpr (kDown) {
+                float* yrow = g.y + (size_t)g.sorted_slot[beg + p] * g.N;
 #pragma unroll
-            for (int tb = 0; tb < TB; ++tb) {
-                const int p = p0 + TPW * wm + 16 * tb + col;
-                if (p >= m) continue;
-                if constexpr (NMAT == 2) {
+                for (int mm = 0; mm < NMAT; ++mm)
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb) {
+                        const int n = row0 + kTileN * mm + RPW * wr + 16 * rb + 4 * kg;
+                        if (n < g.N) *reinterpret_cast<f32x4*>(yrow + n) = acc[mm][rb][tb];
+                    }
+            } else {
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    const int n = row0 + RPW * wr + 16 * rb + 4 * kg;
+                    if (n >= g.N) continue;
                     const f32x4 gv = acc[0][rb][tb], uv = acc[1][rb][tb];
                     u32x2 packed;
                     packed.x = (uint32_t)f32_to_bf16_bits(silu(gv.x) * uv.x) |
@@ -284,21 +305,18 @@ void expert_tile_kernel(const TiledGemm g) {
                     packed.y = (uint32_t)f32_to_bf16_bits(silu(gv.z) * uv.z) |
                                ((uint32_t)f32_to_bf16_bits(silu(gv.w) * uv.w) << 16);
                     *reinterpret_cast<u32x2*>(g.h + (size_t)(beg + p) * g.N + n) = packed;
-                } else {
-                    const int slot = g.sorted_slot[beg + p];
-                    *reinterpret_cast<f32x4*>(g.y + (size_t)slot * g.N + n) = acc[0][rb][tb];
                 }
             }
         }
     }
 }
 
-template <int NMAT>
+template <bool kDown>
 hipError_t launch_tile(const TiledGemm& g, int num_cu, hipStream_t stream) {
-    int grid = num_cu * TileTuning<NMAT>::kBlocksPerCU;
+    int grid = num_cu * TileTuning<kDown>::kBlocksPerCU;
     grid = (grid + kXcds - 1) / kXcds * kXcds;
-    hipLaunchKernelGGL((expert_tile_kernel<NMAT>), dim3(grid),
-                       dim3(TileTuning<NMAT>::kWaves * kWave), 0, stream, g);
+    hipLaunchKernelGGL((expert_tile_kernel<kDown>), dim3(grid),
+                       dim3(TileTuning<kDown>::kWaves * kWave), 0, stream, g);
     return hipGetLastError();
 }
 
@@ -319,7 +337,7 @@ hipError_t launch_tiled_gate_up(const uint16_t* x, const FfnWeights& W, const Ff
     g.N = s.I;
     g.K = s.H;
     g.top_k = s.k;
-    return launch_tile<2>(g, num_cu, stream);
+    return launch_tile<false>(g, num_cu, stream);
 }
 
 hipError_t launch_tiled_down(const FfnWeights& W, const FfnShape& s, const Workspace& ws,
@@ -336,7 +354,7 @@ hipError_t launch_tiled_down(const FfnWeights& W, const FfnShape& s, const Works
     g.N = s.H;
     g.K = s.I;
     g.top_k = s.k;
-    return launch_tile<1>(g, num_cu, stream);
+    return launch_tile<true>(g, num_cu, stream);
 }
 
 }  // namespace moe
