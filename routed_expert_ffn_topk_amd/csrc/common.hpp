@@ -23,6 +23,16 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
 
+// The four values of a lane's quad (lanes 4j .. 4j+3), in quad order: DPP
+// quad_perm broadcasts of quad positions 0, 1, 2, 3.
+__device__ __forceinline__ f32x4 quad_gather_f32(float v) {
+    const int b = __builtin_bit_cast(int, v);
+    return f32x4{__builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(b, 0x00, 0xf, 0xf, false)),
+                 __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(b, 0x55, 0xf, 0xf, false)),
+                 __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(b, 0xaa, 0xf, 0xf, false)),
+                 __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(b, 0xff, 0xf, 0xf, false))};
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
     return __builtin_bit_cast(bf16x8, v);
 }

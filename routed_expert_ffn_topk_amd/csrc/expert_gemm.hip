@@ -56,8 +56,8 @@ struct ExpertGemm {
     const uint16_t* b_src;    // B rows: x (gate/up) or the gathered h rows (down)
     const void* w0;           // W_gate or W_down, [E][N][K] (BF16 or INT8)
     const void* w1;           // W_up (gate/up only)
-    const float* s0;          // INT8 only: group scales of w0, [E][K/128][N]
-    const float* s1;          // INT8 only: group scales of w1
+    const float* s0;          // INT8/INT4: group scales of w0, [E][K/128][N]
+    const float* s1;          // INT8/INT4: group scales of w1
     const int32_t* meta;      // [0] = active experts
     const int32_t* offsets;
     const int32_t* active;
@@ -77,6 +77,7 @@ struct ExpertGemm {
 // ---------------------------------------------------------------------------
 
 struct Bf16Weights {
+    static constexpr bool kQuadScales = false;
     static constexpr int kBlocks = 1;
     static constexpr float kBytesPerWeight = 2.0f;
     static constexpr int kUnitBytes = kWave * 16;       // weight bytes a wave loads per unit
@@ -143,6 +144,7 @@ struct Int8Weights {
     static constexpr int kBlocks = 4;
     static constexpr float kBytesPerWeight = 1.0f;
     static constexpr int kUnitBytes = kWave * 32;       // weight bytes a wave loads per unit
+    static constexpr bool kQuadScales = false;
     template <int NMAT, int U>
     struct Batch {
         u32x4 w[U][NMAT][2];
@@ -212,12 +214,18 @@ struct Int4Weights {
     static constexpr int kBlocks = 4;
     static constexpr float kBytesPerWeight = 0.5f;
     static constexpr int kUnitBytes = kWave * 16;       // weight bytes a wave loads per unit
+    // each lane loads the scale of one output row, 4kg + (lane & 3), with a
+    // 4-byte load, and the quad's four are gathered with DPP broadcasts: a
+    // 16-byte load of the lane's four rows would cost the load pipeline as
+    // much as the weights, and the registers saved let four workgroups share
+    // a CU
+    static constexpr bool kQuadScales = true;
     template <int NMAT, int U>
     struct Batch {
         u32x4 w[U][NMAT];
-        f32x4 s[U][NMAT];
+        float s[U][NMAT];
     };
-    // one 16-byte weight load and one 16-byte scale load per unit and matrix
+    // one 16-byte weight load and one 4-byte scale load per unit and matrix
     template <int NMAT, int U>
     static constexpr int loads() { return U * NMAT * 2; }
     __device__ static int block_offset(int sub, int kg) { return kg * 32 + sub * 8; }
@@ -232,7 +240,7 @@ struct Int4Weights {
 #pragma unroll
             for (int m = 0; m < NMAT; ++m) {
                 d.w[i][m] = load16(static_cast<const uint8_t*>(a[m]) + (size_t)(u + i) * 64);
-                d.s[i][m] = __builtin_bit_cast(f32x4, load16(sc[m] + (size_t)(u + i) * spitch));
+                d.s[i][m] = sc[m][(size_t)(u + i) * spitch];
             }
     }
     __device__ static u32x4 nibbles_to_bf16(uint32_t w) {
@@ -265,7 +273,7 @@ struct Int4Weights {
                 for (int t = 0; t < 4; ++t)
                     part = mfma16x16x32(as_bf16x8(nibbles_to_bf16(words[t])), as_bf16x8(bx[t]),
                                         part);
-                acc[m] += d.s[i][m] * (part - corr);
+                acc[m] += quad_gather_f32(d.s[i][m]) * (part - corr);
             }
         }
     }
@@ -299,7 +307,7 @@ struct GemmTuning<Int8Weights, 1> {
 };
 template <>
 struct GemmTuning<Int4Weights, 2> {
-    static constexpr int kBlocksPerCU = 3;
+    static constexpr int kBlocksPerCU = 4;
     static constexpr int kBatch = 1;
 };
 template <>
@@ -366,8 +374,11 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, int n_act, int 
         const size_t arow = (size_t)e * g.N + row0 + col;   // this lane's weight row
         const void* wp[2] = {Fmt::row_ptr(g.w0, arow, g.K, kg),
                              Fmt::row_ptr(NMAT == 2 ? g.w1 : g.w0, arow, g.K, kg)};
-        // INT8 scales of group 0 of this lane's output rows (group-major)
-        const size_t srow = (size_t)e * nunits * g.N + row0 + 4 * kg;
+        // scales of group 0 of this lane's output rows 4kg..4kg+3 (group-major;
+        // with quad scales, of row 4kg + (lane & 3) alone: the lanes of a quad
+        // share kg)
+        const size_t srow = (size_t)e * nunits * g.N + row0 + 4 * kg +
+                            (Fmt::kQuadScales ? (lane & 3) : 0);
         const float* sp[2] = {g.s0 ? g.s0 + srow : nullptr,
                               NMAT == 2 && g.s1 ? g.s1 + srow : nullptr};
         const int nfull = has ? (u1 - u0) / U : 0;   // full batches of this wave
