@@ -504,7 +504,7 @@ def main():
                                    for b in batches)
         achieved = gu_flops / (gu_us * 1e-6) / 1e12
         roofline = {"bound": "mfma",
-                    "kernel": "expert_tile_kernel<2> (gate/up, SiLU*up epilogue, tiled)",
+                    "kernel": "expert_tile_kernel<false> (gate/up, SiLU*up epilogue, tiled)",
                     "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                     "traffic": recorded_traffic(args.workload),
