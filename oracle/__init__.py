@@ -73,6 +73,11 @@ def lib() -> ctypes.CDLL:
             _u16p, _i32p, _f32p, _vpp, _vpp, _vpp, _vpp, _vpp, _vpp,
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
             ctypes.c_int32, ctypes.c_int32, _u16p, _f32p, _u16p, _f32p]
+        L.oracle_moe_ffn_resplit.restype = ctypes.c_int
+        L.oracle_moe_ffn_resplit.argtypes = [
+            _u16p, _i32p, _f32p] + [_vpp] * 12 + [
+            ctypes.POINTER(ctypes.c_uint8), ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _u16p, _f32p, _u16p, _f32p]
         _LIB = L
     return _LIB
 
@@ -255,6 +260,56 @@ def moe_ffn_int8(x: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray,
         _opt(h, ctypes.c_uint16), _opt(y, ctypes.c_float))
     if rc != 0:
         raise ValueError(f"oracle_moe_ffn_int8 failed ({rc})")
+    if aux:
+        return {"out": out, "out_f32": out_f32, "h": h, "y": y}
+    return out
+
+
+def moe_ffn_resplit(x: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray,
+                    Q_gate: WeightTable, S_gate: WeightTable, R_gate: WeightTable,
+                    SR_gate: WeightTable, Q_up: WeightTable, S_up: WeightTable,
+                    R_up: WeightTable, SR_up: WeightTable, Q_down_lo: WeightTable,
+                    S_down_lo: WeightTable, Q_down_hi: WeightTable, S_down_hi: WeightTable,
+                    critical: np.ndarray, E: int, group: int = 128, aux: bool = False):
+    """Routed-expert FFN layer with residual-split low-bit weights.
+
+    Q_* / R_*: per-expert int8 arrays of the quantised weight and of the
+    quantised residual ([I,H] for gate/up), S_* / SR_* their group scales
+    ([I,H/group] float32); Q_down_lo / Q_down_hi: the low- and
+    high-precision copies of down ([H,I]) with their scales; critical [E]:
+    nonzero for the experts that run in high precision.  Only the tables a
+    valid slot needs are read (a callable table is called for those alone).
+    """
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    ids = np.ascontiguousarray(topk_ids, dtype=np.int32)
+    w = np.ascontiguousarray(topk_w, dtype=np.float32)
+    crit = np.ascontiguousarray(critical, dtype=np.uint8)
+    assert crit.shape == (E,)
+    T, H = x.shape
+    k = ids.shape[1]
+    keep: list = []
+    need = _needed(ids, E)
+    hi = [e for e in need if crit[e]]
+    lo = [e for e in need if not crit[e]]
+    qg = _table(Q_gate, need, E, np.int8, keep)
+    I = keep[0].shape[0] if need else 1
+    tabs = [qg, _table(S_gate, need, E, np.float32, keep),
+            _table(R_gate, hi, E, np.int8, keep), _table(SR_gate, hi, E, np.float32, keep),
+            _table(Q_up, need, E, np.int8, keep), _table(S_up, need, E, np.float32, keep),
+            _table(R_up, hi, E, np.int8, keep), _table(SR_up, hi, E, np.float32, keep),
+            _table(Q_down_lo, lo, E, np.int8, keep), _table(S_down_lo, lo, E, np.float32, keep),
+            _table(Q_down_hi, hi, E, np.int8, keep), _table(S_down_hi, hi, E, np.float32, keep)]
+    out = np.empty((T, H), dtype=np.uint16)
+    out_f32 = np.empty((T, H), dtype=np.float32) if aux else None
+    h = np.empty((T * k, I), dtype=np.uint16) if aux else None
+    y = np.empty((T * k, H), dtype=np.float32) if aux else None
+    rc = lib().oracle_moe_ffn_resplit(
+        _ptr(x, ctypes.c_uint16), _ptr(ids, ctypes.c_int32), _ptr(w, ctypes.c_float),
+        *[ctypes.cast(t, _vpp) for t in tabs], _ptr(crit, ctypes.c_uint8), group, T, H, I, E,
+        k, _ptr(out, ctypes.c_uint16), _opt(out_f32, ctypes.c_float),
+        _opt(h, ctypes.c_uint16), _opt(y, ctypes.c_float))
+    if rc != 0:
+        raise ValueError(f"oracle_moe_ffn_resplit failed ({rc})")
     if aux:
         return {"out": out, "out_f32": out_f32, "h": h, "y": y}
     return out

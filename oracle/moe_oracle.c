@@ -29,6 +29,12 @@
  *   - §6.1 (SDPA in decoding, GQA): each KV head is shared by h_q/h_kv query
  *     heads; per query head, scaled dot-product scores against the l_seq keys,
  *     a softmax over the sequence, and the weighted sum of the values.
+ * and, for the residual-split weights, "RapidMoE" (the page on hybrid
+ * CPU-GPU MoE inference): "Residual-Split Representation" (W^Q, then the
+ * residual W - W^Q quantised as W^R; high precision W^Q + W^R, low W^Q),
+ * "GLU Architecture Adoption" (the split for gate/up only, two quantised
+ * copies of down) and "Expert-Residual Offloading" (h_gate/up = W^Q x +
+ * W^R x).
  *
  * Readings where the pages are silent (each is listed in the design notes):
  *   - router: softmax over all experts, the k largest kept (ties -> lower
@@ -39,6 +45,9 @@
  *   - a slot whose expert id is outside [0, E) contributes nothing;
  *   - INT8: w = q * s with one FP32 scale s per 128 consecutive K elements of
  *     a row; g = sum_groups s_g * (sum_{c in group} x_c * q_c), in FP32.
+ *   - residual split: W^Q, W^R and the low-precision down copy are INT4
+ *     (integers in [-8, 7]), the high-precision down copy INT8, each with one
+ *     FP32 scale per 128 K; a per-expert flag chooses the precision;
  *   - attention: query head h reads KV head h / (h_q / h_kv); the score scale
  *     is 1/sqrt(d) unless the caller gives another; scores, softmax and the
  *     weighted sum in FP32 (BF16 inputs); the output rounded once to BF16; an
@@ -310,6 +319,104 @@ int oracle_moe_ffn_int8(const uint16_t* x, const int32_t* topk_ids,
     return moe_layer(1, x, topk_ids, topk_w, (const void* const*)Q_gate, S_gate,
                      (const void* const*)Q_up, S_up, (const void* const*)Q_down,
                      S_down, group, T, H, I, E, k, out, out_f32, h_out, y_out);
+}
+
+/* ---------------------------------------------------------------------- */
+/* Residual-split low-bit weights (RapidMoE: "Residual-Split               */
+/* Representation", "GLU Architecture Adoption", "Expert-Residual          */
+/* Offloading").                                                           */
+/* ---------------------------------------------------------------------- */
+
+/* W^Q is the weight quantised group-wise; W^R is the residual W - W^Q
+ * quantised the same way.  The high-precision gate and up projections use
+ * W^H = W^Q + W^R through the linear split x W^H = x W^Q + x W^R; the low
+ * precision ones use W^Q alone.  down_proj is not split: it is stored as two
+ * separately quantised copies, one of high and one of low precision.  An
+ * expert flagged critical runs in high precision, every other in low.
+ *
+ * One expert on one token:
+ *   g = gdot(x, Q_gate, S_gate) [+ gdot(x, R_gate, SR_gate) if critical]
+ *   u = gdot(x, Q_up,   S_up)   [+ gdot(x, R_up,   SR_up)   if critical]
+ *   h = RNE_bf16( silu(g) * u )
+ *   y = gdot(h, Q_down, S_down)   (the high or the low copy)
+ * with gdot the grouped dot product above, each term in FP32 and the two
+ * terms added in the written order.  All q arrays hold integers as int8. */
+void oracle_expert_ffn_resplit(const uint16_t* x, const int8_t* Qg, const float* Sg,
+                               const int8_t* Rg, const float* SRg, const int8_t* Qu,
+                               const float* Su, const int8_t* Ru, const float* SRu,
+                               const int8_t* Qd, const float* Sd, int critical,
+                               int64_t group, int64_t H, int64_t I, uint16_t* h,
+                               float* y) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < I; ++i) {
+        float g = grouped_dot(x, Qg + i * H, Sg + i * (H / group), H, group);
+        float u = grouped_dot(x, Qu + i * H, Su + i * (H / group), H, group);
+        if (critical) {
+            g = g + grouped_dot(x, Rg + i * H, SRg + i * (H / group), H, group);
+            u = u + grouped_dot(x, Ru + i * H, SRu + i * (H / group), H, group);
+        }
+        float silu_g = g / (1.0f + expf(-g));
+        h[i] = oracle_f32_to_bf16(silu_g * u);
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < H; ++n)
+        y[n] = grouped_dot(h, Qd + n * I, Sd + n * (I / group), I, group);
+}
+
+/* The layer as in moe_layer, with the precision of each slot's expert taken
+ * from critical[e] (nonzero: high).  Tables are per expert; those of a
+ * precision that no valid slot uses may be NULL (R, SR and the high down copy
+ * of non-critical experts, the low down copy of critical ones). */
+int oracle_moe_ffn_resplit(const uint16_t* x, const int32_t* ids, const float* w,
+                           const int8_t* const* Qg, const float* const* Sg,
+                           const int8_t* const* Rg, const float* const* SRg,
+                           const int8_t* const* Qu, const float* const* Su,
+                           const int8_t* const* Ru, const float* const* SRu,
+                           const int8_t* const* Qd_lo, const float* const* Sd_lo,
+                           const int8_t* const* Qd_hi, const float* const* Sd_hi,
+                           const uint8_t* critical, int64_t group, int64_t T, int64_t H,
+                           int64_t I, int32_t E, int32_t k, uint16_t* out,
+                           float* out_f32, uint16_t* h_out, float* y_out) {
+    if (T < 0 || H <= 0 || I <= 0 || E <= 0 || k <= 0) return ORACLE_ERR_ARG;
+    if (group <= 0 || H % group != 0 || I % group != 0) return ORACLE_ERR_ARG;
+    float* acc = (float*)malloc(sizeof(float) * (size_t)H);
+    float* y = (float*)malloc(sizeof(float) * (size_t)H);
+    uint16_t* h = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)I);
+    if (!acc || !y || !h) { free(acc); free(y); free(h); return ORACLE_ERR_NOMEM; }
+    int rc = ORACLE_OK;
+    for (int64_t t = 0; t < T && rc == ORACLE_OK; ++t) {
+        for (int64_t n = 0; n < H; ++n) acc[n] = 0.0f;
+        for (int32_t j = 0; j < k; ++j) {
+            int64_t slot = t * k + j;
+            int32_t e = ids[slot];
+            if (h_out) memset(h_out + slot * I, 0, sizeof(uint16_t) * (size_t)I);
+            if (y_out) memset(y_out + slot * H, 0, sizeof(float) * (size_t)H);
+            if (e < 0 || e >= E) continue; /* dropped slot */
+            int crit = critical[e] != 0;
+            const int8_t* qd = crit ? Qd_hi[e] : Qd_lo[e];
+            const float* sd = crit ? Sd_hi[e] : Sd_lo[e];
+            if (!Qg[e] || !Sg[e] || !Qu[e] || !Su[e] || !qd || !sd ||
+                (crit && (!Rg[e] || !SRg[e] || !Ru[e] || !SRu[e]))) {
+                rc = ORACLE_ERR_MISSING_EXPERT;
+                break;
+            }
+            oracle_expert_ffn_resplit(x + t * H, Qg[e], Sg[e], crit ? Rg[e] : NULL,
+                                      crit ? SRg[e] : NULL, Qu[e], Su[e],
+                                      crit ? Ru[e] : NULL, crit ? SRu[e] : NULL, qd, sd,
+                                      crit, group, H, I, h, y);
+            for (int64_t n = 0; n < H; ++n) acc[n] += w[slot] * y[n];
+            if (h_out) memcpy(h_out + slot * I, h, sizeof(uint16_t) * (size_t)I);
+            if (y_out) memcpy(y_out + slot * H, y, sizeof(float) * (size_t)H);
+        }
+        for (int64_t n = 0; n < H; ++n) {
+            out[t * H + n] = oracle_f32_to_bf16(acc[n]);
+            if (out_f32) out_f32[t * H + n] = acc[n];
+        }
+    }
+    free(acc);
+    free(y);
+    free(h);
+    return rc;
 }
 
 /* ---------------------------------------------------------------------- */

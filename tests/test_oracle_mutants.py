@@ -47,11 +47,27 @@ MUTANTS = {
                                    "for (int32_t t = 0; t < n - 1; ++t)\n                for (int32_t c = 0; c < d; ++c)\n                    acc[c]"),
     "attn_not_normalised": ("oh[c] = oracle_f32_to_bf16(acc[c] / L);",
                             "oh[c] = oracle_f32_to_bf16(acc[c]);"),
+    # residual-split weights (pins in test_oracle_resplit_pins.py)
+    "resplit_gate_residual_dropped": (
+        "g = g + grouped_dot(x, Rg + i * H, SRg + i * (H / group), H, group);", "g = g;"),
+    "resplit_up_residual_dropped": (
+        "u = u + grouped_dot(x, Ru + i * H, SRu + i * (H / group), H, group);", "u = u;"),
+    "resplit_residual_with_first_scales": (
+        "g = g + grouped_dot(x, Rg + i * H, SRg + i * (H / group), H, group);",
+        "g = g + grouped_dot(x, Rg + i * H, Sg + i * (H / group), H, group);"),
+    "resplit_down_copies_swapped": (
+        "const int8_t* qd = crit ? Qd_hi[e] : Qd_lo[e];\n            const float* sd = crit ? Sd_hi[e] : Sd_lo[e];",
+        "const int8_t* qd = crit ? Qd_lo[e] : Qd_hi[e];\n            const float* sd = crit ? Sd_lo[e] : Sd_hi[e];"),
+    "resplit_flag_by_slot": ("int crit = critical[e] != 0;", "int crit = critical[slot % E] != 0;"),
 }
 
 
 def pin_file(name: str) -> str:
-    return "test_oracle_attn_pins.py" if name.startswith("attn_") else "test_oracle_pins.py"
+    if name.startswith("attn_"):
+        return "test_oracle_attn_pins.py"
+    if name.startswith("resplit_"):
+        return "test_oracle_resplit_pins.py"
+    return "test_oracle_pins.py"
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))

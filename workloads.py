@@ -38,6 +38,7 @@ import torch
 
 TAG_X, TAG_LOGITS, TAG_WG, TAG_WU, TAG_WD, TAG_ZIPF = range(6)
 TAG_Q, TAG_K, TAG_V, TAG_LENS = range(6, 10)
+TAG_CRIT = 10
 WEIGHT_STD = 0.02
 
 
@@ -226,6 +227,46 @@ def gen_weights_int4(wl: Workload, device="cpu", experts: Optional[list] = None)
         Qu[e], Su[e] = quantize_groupwise(_draw(wl, TAG_WU, e, wl.I, wl.H, device), gsz, 7)
         Qd[e], Sd[e] = quantize_groupwise(_draw(wl, TAG_WD, e, wl.H, wl.I, device), gsz, 7)
     return Qg, Sg, Qu, Su, Qd, Sd
+
+
+def quantize_residual_split(w: torch.Tensor, group: int = 128, qmax: int = 7):
+    """Two-stage group-wise quantisation: q, s = quantize(w); the residual
+    w - q*s (FP32) quantised the same way gives r, sr.  Returns (q, s, r, sr);
+    q*s + r*sr is the high-precision weight, q*s the low-precision one."""
+    q, s = quantize_groupwise(w, group, qmax)
+    *lead, K = w.shape
+    deq = (q.float().reshape(*lead, K // group, group) * s[..., None]).reshape(*lead, K)
+    r, sr = quantize_groupwise(w.float() - deq, group, qmax)
+    return q, s, r, sr
+
+
+def gen_weights_resplit(wl: Workload, device="cpu", experts: Optional[list] = None):
+    """Residual-split expert weights, unpacked (int8 values):
+    (Qg, Sg, Rg, SRg, Qu, Su, Ru, SRu, Qd_lo, Sd_lo, Qd_hi, Sd_hi): INT4 W^Q
+    and INT4 residual W^R of gate and up, an INT4 (low) and an INT8 (high)
+    copy of down, each with row-major group scales [.., N, K/group]."""
+    ex = range(wl.E) if experts is None else experts
+    gsz = wl.group
+    z8 = lambda N, K: torch.zeros(wl.E, N, K, dtype=torch.int8, device=device)  # noqa: E731
+    zs = lambda N, K: torch.zeros(wl.E, N, K // gsz, dtype=torch.float32, device=device)  # noqa: E731
+    out = [z8(wl.I, wl.H), zs(wl.I, wl.H), z8(wl.I, wl.H), zs(wl.I, wl.H),
+           z8(wl.I, wl.H), zs(wl.I, wl.H), z8(wl.I, wl.H), zs(wl.I, wl.H),
+           z8(wl.H, wl.I), zs(wl.H, wl.I), z8(wl.H, wl.I), zs(wl.H, wl.I)]
+    for e in ex:
+        for base, tag in ((0, TAG_WG), (4, TAG_WU)):
+            q, s_, r, sr = quantize_residual_split(_draw(wl, tag, e, wl.I, wl.H, device), gsz, 7)
+            out[base][e], out[base + 1][e], out[base + 2][e], out[base + 3][e] = q, s_, r, sr
+        wd = _draw(wl, TAG_WD, e, wl.H, wl.I, device)
+        out[8][e], out[9][e] = quantize_groupwise(wd, gsz, 7)
+        out[10][e], out[11][e] = quantize_groupwise(wd, gsz, 127)
+    return tuple(out)
+
+
+def gen_critical(wl: Workload, frac: float = 0.5) -> np.ndarray:
+    """Seeded per-expert precision flags: about ``frac`` of the experts
+    critical (1), the rest 0."""
+    rng = np.random.default_rng([wl.seed, TAG_CRIT])
+    return (rng.random(wl.E) < frac).astype(np.uint8)
 
 
 def bf16_bits(t: torch.Tensor) -> np.ndarray:
