@@ -387,7 +387,7 @@ int oracle_moe_ffn_resplit(const uint16_t* x, const int32_t* ids, const float* w
     for (int64_t t = 0; t < T && rc == ORACLE_OK; ++t) {
         for (int64_t n = 0; n < H; ++n) acc[n] = 0.0f;
         for (int32_t j = 0; j < k; ++j) {
-            int64_t slot = t * k + j;
+            int64_t slot = t * (int64_t)k + j;
             int32_t e = ids[slot];
             if (h_out) memset(h_out + slot * I, 0, sizeof(uint16_t) * (size_t)I);
             if (y_out) memset(y_out + slot * H, 0, sizeof(float) * (size_t)H);
@@ -404,7 +404,8 @@ int oracle_moe_ffn_resplit(const uint16_t* x, const int32_t* ids, const float* w
                                       crit ? SRg[e] : NULL, Qu[e], Su[e],
                                       crit ? Ru[e] : NULL, crit ? SRu[e] : NULL, qd, sd,
                                       crit, group, H, I, h, y);
-            for (int64_t n = 0; n < H; ++n) acc[n] += w[slot] * y[n];
+            const float wt = w[slot];
+            for (int64_t n = 0; n < H; ++n) acc[n] += wt * y[n];
             if (h_out) memcpy(h_out + slot * I, h, sizeof(uint16_t) * (size_t)I);
             if (y_out) memcpy(y_out + slot * H, y, sizeof(float) * (size_t)H);
         }
