@@ -67,6 +67,8 @@ def suite_layers(name: str):
         return [workloads.WORKLOADS[f"mixtral8x7b_int8_m{m}"] for m in MS]
     if name == "mixtral8x7b_int4_forced_m1-16":
         return [workloads.WORKLOADS[f"mixtral8x7b_int4_m{m}"] for m in MS]
+    if name == "mixtral8x7b_resplit_forced_m1-16":
+        return [workloads.WORKLOADS[f"mixtral8x7b_resplit_m{m}"] for m in MS]
     if name in workloads.WORKLOADS and name != "tiny":
         return [workloads.WORKLOADS[name]]
     raise SystemExit(f"bench.py: unknown workload {name!r}")
@@ -77,11 +79,13 @@ def expert_bytes(wl) -> int:
     return workloads.weight_bytes_per_expert(wl)
 
 
-def layer_bytes(wl, active: int) -> int:
+def layer_bytes(wl, active: int, weight_bytes=None) -> int:
     """Algorithmic HBM bytes of one layer: every active expert's three weight
-    matrices (and INT8 scales) once, x read, out written, routing ids and
-    weights read."""
-    return active * expert_bytes(wl) + 2 * wl.T * wl.H * 2 + wl.T * wl.k * 8
+    matrices (and scales) once, x read, out written, routing ids and weights
+    read.  ``weight_bytes`` overrides active * expert_bytes (residual split,
+    where an expert's bytes depend on its precision)."""
+    wb = active * expert_bytes(wl) if weight_bytes is None else weight_bytes
+    return wb + 2 * wl.T * wl.H * 2 + wl.T * wl.k * 8
 
 
 def layer_flops(wl) -> float:
@@ -90,13 +94,17 @@ def layer_flops(wl) -> float:
 
 
 def uses_tiled(wl) -> bool:
-    return not wl.int8 and not wl.int4 and wl.T > TILED_MIN_BATCH
+    return not wl.int8 and not wl.int4 and not wl.resplit and wl.T > TILED_MIN_BATCH
 
 
-def gateup_bytes(wl, active: int) -> int:
+def gateup_bytes(wl, active: int, n_critical: int = 0) -> int:
     """Algorithmic bytes of one gate/up launch: W_gate and W_up (and their
     scales) of every active expert plus the token rows (h is scratch and not
-    credited)."""
+    credited).  Residual split: n_critical of the active experts also read
+    W^R and its scales."""
+    if wl.resplit:
+        per = wl.I * wl.H * (0.5 + 4 / wl.group)
+        return int((active + n_critical) * 2 * per) + wl.T * wl.H * 2
     if wl.int8:
         per = wl.I * wl.H * (1 + 4 / wl.group)
     elif wl.int4:
@@ -168,7 +176,7 @@ def read_ceiling(stream, nbytes=4 << 30, reps=10) -> float:
     return nbytes / (best * 1e-6) / 1e9
 
 
-def cpu_baseline(wl, host_weights, logits_cpu, x_cpu, reps=3):
+def cpu_baseline(wl, host_weights, logits_cpu, x_cpu, reps=3, critical=None):
     """The CPU oracle on a bounded token sample of one layer of the workload:
     the leading tokens, as many as fit CPU_SAMPLE_MACS multiply-adds and
     CPU_SAMPLE_BYTES of expert weights copied to the host."""
@@ -193,20 +201,25 @@ def cpu_baseline(wl, host_weights, logits_cpu, x_cpu, reps=3):
     times = []
     for _ in range(reps):
         t0 = time.perf_counter()
-        if wl.int8 or wl.int4:
+        if wl.resplit:
+            oracle.moe_ffn_resplit(xb, ids[:n], w[:n], *(t.get for t in tables), critical,
+                                   E=wl.E)
+        elif wl.int8 or wl.int4:
             # INT4 is the INT8 definition on values in [-7, 7] (unpacked here)
             oracle.moe_ffn_int8(xb, ids[:n], w[:n], *(t.get for t in tables), E=wl.E)
         else:
             oracle.moe_ffn_bf16(xb, ids[:n], w[:n], *(t.get for t in tables), E=wl.E)
         times.append(time.perf_counter() - t0)
     t = statistics.median(times)
-    sample_bytes = len(need) * expert_bytes(wl) + 2 * n * wl.H * 2 + n * wl.k * 8
+    wbytes = (sum(workloads.weight_bytes_per_expert(wl, bool(critical[e])) for e in need)
+              if wl.resplit else len(need) * expert_bytes(wl))
+    sample_bytes = wbytes + 2 * n * wl.H * 2 + n * wl.k * 8
     return {"value": round(sample_bytes / t / 1e9, 3), "unit": "GB/s",
             "cores": oracle.num_threads(), "kind": "oracle",
             "us_per_layer": round(t * 1e6, 1),
             "sample": f"{wl.name}: the first {n} of {wl.T} tokens ({len(need)} experts), "
                       f"median of {reps} runs, plain C oracle (FP32 accumulation, per-token "
-                      f"loops, {'INT8' if wl.int8 else 'INT4' if wl.int4 else 'BF16'} weights)"}
+                      f"loops, {'residual-split INT4/INT8' if wl.resplit else 'INT8' if wl.int8 else 'INT4' if wl.int4 else 'BF16'} weights)"}
 
 
 ATTN_METRIC = "decode GQA attention: KV-stream GB/s (% HBM peak) and µs per call, BF16"
@@ -369,7 +382,10 @@ def main():
     layers = suite_layers(args.workload)
     int8 = layers[0].int8
     int4 = layers[0].int4
-    quant = int8 or int4
+    resplit = layers[0].resplit
+    quant = int8 or int4 or resplit
+    # residual split: one set of per-expert precision flags for the suite
+    crit = workloads.gen_critical(layers[0]) if resplit else None
     stream = torch.cuda.current_stream()
 
     batches = []
@@ -377,20 +393,34 @@ def main():
         x = workloads.gen_x(wl)
         lg = workloads.gen_logits(wl)
         ids, w = moe.moe_route_topk(lg.to(dev), wl.k)
-        active = len(set(ids.cpu().reshape(-1).tolist()))
+        act = sorted(set(ids.cpu().reshape(-1).tolist()))
+        active = len(act)
+        wbytes = (sum(workloads.weight_bytes_per_expert(wl, bool(crit[e])) for e in act)
+                  if resplit else active * expert_bytes(wl))
+        n_crit = int(sum(int(crit[e]) for e in act)) if resplit else 0
         batches.append(dict(wl=wl, x_cpu=x, lg_cpu=lg, lg=lg.to(dev), x=x.to(dev), ids=ids, w=w,
-                            active=active,
+                            active=active, wbytes=wbytes, n_crit=n_crit,
                             out=torch.empty(wl.T, wl.H, dtype=torch.bfloat16, device=dev),
                             ws=moe.alloc_workspace(wl.T, wl.H, wl.I, wl.E, wl.k, dev)))
     # distinct weight sets so that one step streams at least ROTATE_BELOW bytes
-    step_weight_bytes = sum(b["active"] * expert_bytes(b["wl"]) for b in batches)
+    step_weight_bytes = sum(b["wbytes"] for b in batches)
     n_sets = max(1, math.ceil(ROTATE_BELOW / step_weight_bytes)) \
         if step_weight_bytes < ROTATE_BELOW else 1
     wl0 = layers[0]
     sets = []
     for r in range(n_sets):
         wlr = workloads.Workload(**{**wl0.__dict__, "seed": wl0.seed + r})
-        if quant:
+        if resplit:
+            tens = workloads.gen_weights_resplit(wlr, dev)
+            p4, gm = workloads.pack_int4, workloads.scales_group_major
+            Qg, Sg, Rg, SRg, Qu, Su, Ru, SRu, Qdl, Sdl, Qdh, Sdh = tens
+            sets.append((p4(Qg), gm(Sg), p4(Rg), gm(SRg), p4(Qu), gm(Su), p4(Ru), gm(SRu),
+                         p4(Qdl), gm(Sdl), Qdh, gm(Sdh), torch.from_numpy(crit).to(dev)))
+            if r == 0:
+                host_rowmajor = tens
+            else:
+                del tens, Qg, Sg, Rg, SRg, Qu, Su, Ru, SRu, Qdl, Sdl, Qdh, Sdh
+        elif quant:
             gen = workloads.gen_weights_int8 if int8 else workloads.gen_weights_int4
             Qg, Sg, Qu, Su, Qd, Sd = gen(wlr, dev)
             store = (lambda q: q) if int8 else workloads.pack_int4  # noqa: E731
@@ -404,7 +434,7 @@ def main():
             sets.append(workloads.gen_weights(wlr, dev))
     torch.cuda.synchronize()
     fwd = (moe.moe_ffn_forward_int8 if int8 else moe.moe_ffn_forward_int4 if int4
-           else moe.moe_ffn_forward)
+           else moe.moe_ffn_forward_resplit if resplit else moe.moe_ffn_forward)
 
     def layer(b, s):
         fwd(b["x"], b["ids"], b["w"], *sets[s], out=b["out"], workspace=b["ws"], stream=stream)
@@ -425,7 +455,7 @@ def main():
     t1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / args.steps
-    step_bytes = n_sets * sum(layer_bytes(b["wl"], b["active"]) for b in batches)
+    step_bytes = n_sets * sum(layer_bytes(b["wl"], b["active"], b["wbytes"]) for b in batches)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     # microseconds per layer (same calls, timed per batch)
@@ -440,7 +470,7 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / reps
-        lb = layer_bytes(b["wl"], b["active"])
+        lb = layer_bytes(b["wl"], b["active"], b["wbytes"])
         per_layer[b["wl"].name] = {
             "T": b["wl"].T, "active_experts": b["active"], "us": round(us, 1),
             "GBps": round(lb / (us * 1e-6) / 1e9, 1),
@@ -491,7 +521,7 @@ def main():
                 d = ev[j].elapsed_time(ev[j + 1]) * 1e3
                 dur[n].append(d)
                 dur_l[b["wl"].name][n].append(d)
-            gu_bytes.append(gateup_bytes(b["wl"], b["active"]))
+            gu_bytes.append(gateup_bytes(b["wl"], b["active"], b["n_crit"]))
     for name, d in dur_l.items():
         per_layer[name]["stage_us"] = {n: round(statistics.mean(v), 1) for n, v in d.items()}
     gu_us = statistics.mean(dur["gateup"])
@@ -515,7 +545,8 @@ def main():
         achieved = statistics.mean(gu_bytes) / (gu_us * 1e-6) / 1e9
         kern = ("expert_gemm_kernel<Int8Weights, 2, ...>" if int8 else
                 "expert_gemm_kernel<Int4Weights, 2, ...>" if int4 else
-                "expert_gemm_kernel<Bf16Weights, 2, ...>")
+                "expert_gemm_kernel<MixedWeights<Int4Weights, Int4ResidualWeights>, 2, ...>"
+                if resplit else "expert_gemm_kernel<Bf16Weights, 2, ...>")
         roofline = {"bound": "hbm", "kernel": f"{kern} (gate/up, SiLU*up epilogue)",
                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -531,7 +562,8 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int8-weights/bf16" if int8 else "int4-weights/bf16" if int4 else "bf16",
+        "dtype": ("int8-weights/bf16" if int8 else "int4-weights/bf16" if int4 else
+                  "int4+int4-residual/int8-weights/bf16" if resplit else "bf16"),
         "data": "synthetic",
         "config": {"workload": args.workload, "hidden": wl.H, "intermediate": wl.I,
                    "experts": wl.E, "top_k": wl.k, "tokens": [b["wl"].T for b in batches],
@@ -546,7 +578,8 @@ def main():
     if not args.no_cpu_baseline:
         b = batches[0]
         host = host_rowmajor if quant else sets[0]
-        result["cpu_baseline"] = cpu_baseline(b["wl"], host, b["lg_cpu"], b["x_cpu"])
+        result["cpu_baseline"] = cpu_baseline(b["wl"], host, b["lg_cpu"], b["x_cpu"],
+                                              critical=crit)
     print(json.dumps(result), flush=True)
 
 

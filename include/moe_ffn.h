@@ -266,6 +266,47 @@ int moe_ffn_forward_int4(const void* x, const int32_t* topk_ids,
                          int32_t top_k, void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/*
+ * Routed-expert FFN layer with residual-split low-bit weights and a precision
+ * chosen per expert (RapidMoE: "Residual-Split Representation", "GLU
+ * Architecture Adoption", "Expert-Residual Offloading").  Each weight of gate
+ * and up is held as W^Q, its INT4 group quantisation, plus W^R, the INT4
+ * group quantisation of the residual W - W^Q; down is held as two separately
+ * quantised copies, INT4 (low precision) and INT8 (high).  An expert with
+ * critical[e] != 0 runs in high precision:
+ *   g = x W^Q_gate + x W^R_gate,  u = x W^Q_up + x W^R_up,  y = h W_down(INT8)
+ * every other expert in low precision:
+ *   g = x W^Q_gate,  u = x W^Q_up,  y = h W_down(INT4)
+ * with h = RNE_bf16(silu(g) * u) and the combine of moe_ffn_forward.  Each
+ * term is a grouped product as in moe_ffn_forward_int8 (FP32 group sums
+ * times the group scale).  Choosing which experts are critical (the pages
+ * derive it from the router scores, averaged over a batch's tokens) is the
+ * caller's.
+ *   P_gate, R_gate, P_up, R_up [E][I][H/2] uint8 (W^Q and W^R, the INT4
+ *            nibble layout of moe_ffn_forward_int4) with S_gate, SR_gate,
+ *            S_up, SR_up [E][H/128][I] float32 (group-major);
+ *   P_down_lo [E][H][I/2] uint8 with S_down_lo [E][I/128][H] float32;
+ *   Q_down_hi [E][H][I] int8 with S_down_hi [E][I/128][H] float32;
+ *   critical [E] uint8, device.
+ * Only the tensors an expert's precision needs are read: R_*, SR_* and the
+ * high down copy of critical experts, the low down copy of the others.
+ * `group` must be MOE_FFN_INT8_GROUP (128).  Sizes: H and I multiples of 128.
+ * Weight and scale pointers 16-byte aligned.  Batches of any size take the
+ * small-m product.  Errors as for moe_ffn_forward_int8 (NULL_ARG also for a
+ * null critical).
+ */
+int moe_ffn_forward_resplit(const void* x, const int32_t* topk_ids,
+                            const float* topk_w, const uint8_t* P_gate,
+                            const float* S_gate, const uint8_t* R_gate,
+                            const float* SR_gate, const uint8_t* P_up,
+                            const float* S_up, const uint8_t* R_up,
+                            const float* SR_up, const uint8_t* P_down_lo,
+                            const float* S_down_lo, const int8_t* Q_down_hi,
+                            const float* S_down_hi, const uint8_t* critical,
+                            int32_t group, void* out, int64_t T, int64_t H,
+                            int64_t I, int32_t E, int32_t top_k, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
 /* Wait for `stream`, then read the workspace meta written by the last forward
  * call: MOE_FFN_ERR_BAD_IDS if it dropped slots with out-of-range ids,
  * MOE_FFN_OK otherwise (MOE_FFN_ERR_HIP if the wait or the read fails).  If

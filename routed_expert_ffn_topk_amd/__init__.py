@@ -70,6 +70,9 @@ def lib() -> ctypes.CDLL:
         L.moe_ffn_forward_int4.restype = _c.c_int
         L.moe_ffn_forward_int4.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                                            _vp, _i64, _i64, _i64, _i32, _i32, _vp, _sz, _vp]
+        L.moe_ffn_forward_resplit.restype = _c.c_int
+        L.moe_ffn_forward_resplit.argtypes = [_vp] * 16 + [_i32, _vp, _i64, _i64, _i64, _i32,
+                                                           _i32, _vp, _sz, _vp]
         L.moe_attn_decode.restype = _c.c_int
         L.moe_attn_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                       _c.c_float, _vp, _sz, _vp]
@@ -278,6 +281,51 @@ def moe_ffn_forward_int4(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.
         _dev(S_down, "S_down", torch.float32), G, _dev(out, "out", torch.bfloat16),
         T, H, I, E, top_k, _dev(workspace, "workspace", torch.uint8), workspace.numel(),
         _stream(stream)))
+    return out
+
+
+def moe_ffn_forward_resplit(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor,
+                            P_gate: torch.Tensor, S_gate: torch.Tensor, R_gate: torch.Tensor,
+                            SR_gate: torch.Tensor, P_up: torch.Tensor, S_up: torch.Tensor,
+                            R_up: torch.Tensor, SR_up: torch.Tensor, P_down_lo: torch.Tensor,
+                            S_down_lo: torch.Tensor, Q_down_hi: torch.Tensor,
+                            S_down_hi: torch.Tensor, critical: torch.Tensor,
+                            out: Optional[torch.Tensor] = None,
+                            workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Routed-expert FFN layer with residual-split weights: gate/up as INT4
+    W^Q plus INT4 residual W^R (packed [E, I, H/2] uint8), down as an INT4
+    ([E, H, I/2] uint8) and an INT8 ([E, H, I] int8) copy, scales group-major;
+    experts with ``critical[e]`` (uint8 [E]) nonzero use W^Q + W^R and the
+    INT8 down, the others W^Q and the INT4 down.  Returns ``out``."""
+    T, H = x.shape
+    E, I, H2 = P_gate.shape
+    top_k = topk_ids.shape[1]
+    G = 128
+    if 2 * H2 != H or H % G or I % G:
+        raise ValueError("P_gate must be [E,I,H/2] with H and I multiples of 128")
+    shapes = {"R_gate": (R_gate, (E, I, H // 2)), "P_up": (P_up, (E, I, H // 2)),
+              "R_up": (R_up, (E, I, H // 2)), "P_down_lo": (P_down_lo, (E, H, I // 2)),
+              "Q_down_hi": (Q_down_hi, (E, H, I)), "S_gate": (S_gate, (E, H // G, I)),
+              "SR_gate": (SR_gate, (E, H // G, I)), "S_up": (S_up, (E, H // G, I)),
+              "SR_up": (SR_up, (E, H // G, I)), "S_down_lo": (S_down_lo, (E, I // G, H)),
+              "S_down_hi": (S_down_hi, (E, I // G, H)), "critical": (critical, (E,))}
+    for name, (t, shape) in shapes.items():
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be {list(shape)}, got {list(t.shape)}")
+    if out is None:
+        out = torch.empty_like(x)
+    if workspace is None:
+        workspace = alloc_workspace(T, H, I, E, top_k, x.device)
+    u8, f32 = torch.uint8, torch.float32
+    _check("moe_ffn_forward_resplit", lib().moe_ffn_forward_resplit(
+        _dev(x, "x", torch.bfloat16), _dev(topk_ids, "topk_ids", torch.int32),
+        _dev(topk_w, "topk_w", f32), _dev(P_gate, "P_gate", u8), _dev(S_gate, "S_gate", f32),
+        _dev(R_gate, "R_gate", u8), _dev(SR_gate, "SR_gate", f32), _dev(P_up, "P_up", u8),
+        _dev(S_up, "S_up", f32), _dev(R_up, "R_up", u8), _dev(SR_up, "SR_up", f32),
+        _dev(P_down_lo, "P_down_lo", u8), _dev(S_down_lo, "S_down_lo", f32),
+        _dev(Q_down_hi, "Q_down_hi", torch.int8), _dev(S_down_hi, "S_down_hi", f32),
+        _dev(critical, "critical", u8), G, _dev(out, "out", torch.bfloat16), T, H, I, E, top_k,
+        _dev(workspace, "workspace", u8), workspace.numel(), _stream(stream)))
     return out
 
 

@@ -58,6 +58,13 @@ struct ExpertGemm {
     const void* w1;           // W_up (gate/up only)
     const float* s0;          // INT8/INT4: group scales of w0, [E][K/128][N]
     const float* s1;          // INT8/INT4: group scales of w1
+    // second weight set: the quantised residuals W^R of w0/w1 (residual-split
+    // gate/up) or the high-precision copy of W_down, with their scales
+    const void* hw0;
+    const void* hw1;
+    const float* hs0;
+    const float* hs1;
+    const uint8_t* critical;  // [E], mixed-precision launches: nonzero = high precision
     const int32_t* meta;      // [0] = active experts
     const int32_t* offsets;
     const int32_t* active;
@@ -76,7 +83,19 @@ struct ExpertGemm {
 //   INT8: one 128-wide scale group = four MFMAs per matrix, four LDS blocks.
 // ---------------------------------------------------------------------------
 
+// Per-lane weight and scale pointers of one round: this lane's weight row at
+// its K group, and the scales of group 0 of its output rows (group-major,
+// spitch floats between groups).  r / sr: the second set (residuals).
+struct WeightSrc {
+    const void* w[2];
+    const float* s[2];
+    const void* r[2];
+    const float* sr[2];
+    int spitch;
+};
+
 struct Bf16Weights {
+    static constexpr bool kResidual = false;
     static constexpr bool kQuadScales = false;
     static constexpr int kBlocks = 1;
     static constexpr float kBytesPerWeight = 2.0f;
@@ -94,13 +113,12 @@ struct Bf16Weights {
         return static_cast<const uint16_t*>(base) + row * K + kg * 8;
     }
     template <int NMAT, int U>
-    __device__ static void load(Batch<NMAT, U>& d, const void* const* a, const float* const*,
-                                int, int u) {
+    __device__ static void load(Batch<NMAT, U>& d, const WeightSrc& src, int u) {
 #pragma unroll
         for (int i = 0; i < U; ++i)
 #pragma unroll
             for (int m = 0; m < NMAT; ++m)
-                d.w[i][m] = load16(static_cast<const uint16_t*>(a[m]) + (u + i) * 32);
+                d.w[i][m] = load16(static_cast<const uint16_t*>(src.w[m]) + (u + i) * 32);
     }
     // bl: this lane's B fragment of the batch's first LDS block; block b of
     // the batch at bl[b * kBlockU4]
@@ -141,6 +159,7 @@ __device__ __forceinline__ bf16x8 i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
 // are one aligned 16-byte load, and a wave's scales of one group sit in one
 // 64-byte segment (row-major scales would cost a cache line per row).
 struct Int8Weights {
+    static constexpr bool kResidual = false;
     static constexpr int kBlocks = 4;
     static constexpr float kBytesPerWeight = 1.0f;
     static constexpr int kUnitBytes = kWave * 32;       // weight bytes a wave loads per unit
@@ -162,16 +181,16 @@ struct Int8Weights {
     // a[m]: weight row at K offset 16*kg; sc[m]: scales of group 0 of the
     // lane's output rows 4*kg..4*kg+3; spitch: floats between groups (N)
     template <int NMAT, int U>
-    __device__ static void load(Batch<NMAT, U>& d, const void* const* a, const float* const* sc,
-                                int spitch, int u) {
+    __device__ static void load(Batch<NMAT, U>& d, const WeightSrc& src, int u) {
 #pragma unroll
         for (int i = 0; i < U; ++i)
 #pragma unroll
             for (int m = 0; m < NMAT; ++m) {
-                const int8_t* p = static_cast<const int8_t*>(a[m]) + (size_t)(u + i) * 128;
+                const int8_t* p = static_cast<const int8_t*>(src.w[m]) + (size_t)(u + i) * 128;
                 d.w[i][m][0] = load16(p);
                 d.w[i][m][1] = load16(p + 64);
-                d.s[i][m] = __builtin_bit_cast(f32x4, load16(sc[m] + (size_t)(u + i) * spitch));
+                d.s[i][m] = __builtin_bit_cast(
+                    f32x4, load16(src.s[m] + (size_t)(u + i) * src.spitch));
             }
     }
     template <int NMAT, int U>
@@ -211,6 +230,7 @@ struct Int8Weights {
 // are interleaved (0, 4, 1, 5, 2, 6, 3, 7).  About one VALU operation per
 // weight.
 struct Int4Weights {
+    static constexpr bool kResidual = false;
     static constexpr int kBlocks = 4;
     static constexpr float kBytesPerWeight = 0.5f;
     static constexpr int kUnitBytes = kWave * 16;       // weight bytes a wave loads per unit
@@ -233,14 +253,13 @@ struct Int4Weights {
         return static_cast<const uint8_t*>(base) + row * (size_t)(K / 2) + kg * 16;
     }
     template <int NMAT, int U>
-    __device__ static void load(Batch<NMAT, U>& d, const void* const* a, const float* const* sc,
-                                int spitch, int u) {
+    __device__ static void load(Batch<NMAT, U>& d, const WeightSrc& src, int u) {
 #pragma unroll
         for (int i = 0; i < U; ++i)
 #pragma unroll
             for (int m = 0; m < NMAT; ++m) {
-                d.w[i][m] = load16(static_cast<const uint8_t*>(a[m]) + (size_t)(u + i) * 64);
-                d.s[i][m] = sc[m][(size_t)(u + i) * spitch];
+                d.w[i][m] = load16(static_cast<const uint8_t*>(src.w[m]) + (size_t)(u + i) * 64);
+                d.s[i][m] = src.s[m][(size_t)(u + i) * src.spitch];
             }
     }
     __device__ static u32x4 nibbles_to_bf16(uint32_t w) {
@@ -279,6 +298,115 @@ struct Int4Weights {
     }
 };
 
+// Residual-split INT4 (RapidMoE, "Residual-Split Representation" and
+// "Expert-Residual Offloading"): the high-precision weight is W^Q + W^R, W^Q
+// the INT4 weight and W^R its INT4-quantised residual, both in the INT4
+// layout with their own group scales, and by linearity
+//   x (W^Q + W^R) = x W^Q + x W^R.
+// A unit is one group of both: two 16-byte weight loads and two 4-byte scale
+// loads per matrix.  The token fragments and the bias product (136 sum x) are
+// shared by the two terms and the two matrices:
+//   acc += s_Q (sum (128 + u_Q) x - 136 sum x) + s_R (sum (128 + u_R) x - 136 sum x).
+struct Int4ResidualWeights {
+    static constexpr bool kResidual = true;
+    static constexpr bool kQuadScales = true;
+    static constexpr int kBlocks = 4;
+    static constexpr float kBytesPerWeight = 1.0f;
+    static constexpr int kUnitBytes = 2 * kWave * 16;
+    template <int NMAT, int U>
+    struct Batch {
+        u32x4 w[U][NMAT];
+        u32x4 r[U][NMAT];
+        float s[U][NMAT];
+        float sr[U][NMAT];
+    };
+    template <int NMAT, int U>
+    static constexpr int loads() { return U * NMAT * 4; }
+    __device__ static int block_offset(int sub, int kg) {
+        return Int4Weights::block_offset(sub, kg);
+    }
+    __device__ static const void* row_ptr(const void* base, size_t row, int K, int kg) {
+        return Int4Weights::row_ptr(base, row, K, kg);
+    }
+    template <int NMAT, int U>
+    __device__ static void load(Batch<NMAT, U>& d, const WeightSrc& src, int u) {
+#pragma unroll
+        for (int i = 0; i < U; ++i)
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m) {
+                const size_t wo = (size_t)(u + i) * 64, so = (size_t)(u + i) * src.spitch;
+                d.w[i][m] = load16(static_cast<const uint8_t*>(src.w[m]) + wo);
+                d.r[i][m] = load16(static_cast<const uint8_t*>(src.r[m]) + wo);
+                d.s[i][m] = src.s[m][so];
+                d.sr[i][m] = src.sr[m][so];
+            }
+    }
+    template <int NMAT, int U>
+    __device__ static void mma(const Batch<NMAT, U>& d, const u32x4* bl, f32x4* acc) {
+        const u32x4 k136 = {0x43084308u, 0x43084308u, 0x43084308u, 0x43084308u};  // BF16 136
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            u32x4 bx[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) bx[t] = Int4Weights::interleave(bl[(4 * i + t) * kBlockU4]);
+            f32x4 corr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) corr = mfma16x16x32(as_bf16x8(k136), as_bf16x8(bx[t]), corr);
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m) {
+                const u32x4 w = d.w[i][m], r = d.r[i][m];
+                const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+                const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
+                f32x4 pq = {0.f, 0.f, 0.f, 0.f}, pr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    pq = mfma16x16x32(as_bf16x8(Int4Weights::nibbles_to_bf16(ww[t])),
+                                      as_bf16x8(bx[t]), pq);
+                    pr = mfma16x16x32(as_bf16x8(Int4Weights::nibbles_to_bf16(rw[t])),
+                                      as_bf16x8(bx[t]), pr);
+                }
+                acc[m] += quad_gather_f32(d.s[i][m]) * (pq - corr) +
+                          quad_gather_f32(d.sr[i][m]) * (pr - corr);
+            }
+        }
+    }
+};
+
+// A launch whose experts run in one of two formats, chosen per expert (per
+// round) by ExpertGemm::critical: Hi where it is nonzero, Lo elsewhere.  With
+// kHiSecond, Hi reads its weights and scales from the second set (a separate
+// high-precision copy); otherwise Hi is a format that reads both sets.
+template <class Lo, class Hi, bool kHiSecond>
+struct MixedWeights {
+    using LoFmt = Lo;
+    using HiFmt = Hi;
+    static constexpr bool kHiReadsSecond = kHiSecond;
+    static_assert(Lo::kBlocks == Hi::kBlocks, "one LDS unit layout for both formats");
+    static constexpr int kBlocks = Lo::kBlocks;
+    static constexpr float kBytesPerWeight = Hi::kBytesPerWeight;
+    static constexpr int kUnitBytes = Hi::kUnitBytes;
+};
+template <class F>
+struct IsMixed {
+    static constexpr bool value = false;
+};
+template <class Lo, class Hi, bool b>
+struct IsMixed<MixedWeights<Lo, Hi, b>> {
+    static constexpr bool value = true;
+};
+// the format of one round, and whether it reads the second weight set as
+// its first
+template <class F, bool kSecond>
+struct RoundFmt {
+    using Fmt = F;
+    static constexpr bool kFromSecond = kSecond;
+};
+
+// Residual-split gate/up: critical experts W^Q + W^R, the others W^Q.
+using ResidualGateUp = MixedWeights<Int4Weights, Int4ResidualWeights, false>;
+// Two-copy down: critical experts the INT8 copy, the others the INT4 one.
+using DualDown = MixedWeights<Int4Weights, Int8Weights, true>;
+
 // Tuning per weight format and projection, measured on MI355X over the
 // Mixtral-8x7B, DeepSeek-V3, Qwen3-235B and Mixtral-8x22B expert shapes at
 // 1-16 tokens per expert (INT4: the Mixtral-8x7B shape): batch length U
@@ -311,6 +439,16 @@ struct GemmTuning<Int4Weights, 2> {
     static constexpr int kBatch = 1;
 };
 template <>
+struct GemmTuning<ResidualGateUp, 2> {
+    static constexpr int kBlocksPerCU = 2;
+    static constexpr int kBatch = 1;
+};
+template <>
+struct GemmTuning<DualDown, 1> {
+    static constexpr int kBlocksPerCU = 3;
+    static constexpr int kBatch = 2;
+};
+template <>
 struct GemmTuning<Int4Weights, 1> {
     static constexpr int kBlocksPerCU = 2;
     static constexpr int kBatch = 4;
@@ -332,7 +470,6 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, int n_act, int 
     constexpr int SPU = SP / Fmt::kBlocks;     // units of each K part per slab
     constexpr int NB = SPU / U;                // full batches per full slab
     static_assert(SPU >= 1 && SPU % U == 0, "batch must divide the slab part");
-    using Batch = typename Fmt::template Batch<NMAT, U>;
     // after the slab loop the first slab buffer doubles as the K-part
     // reduction area (3 x NMAT x 1 KB <= 16 KB)
     f32x4* red = reinterpret_cast<f32x4*>(&xs[0][0]);
@@ -372,140 +509,167 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, int n_act, int 
         const bool has = my < nrb;
         const int row0 = (has ? my : 0) * 16;
         const size_t arow = (size_t)e * g.N + row0 + col;   // this lane's weight row
-        const void* wp[2] = {Fmt::row_ptr(g.w0, arow, g.K, kg),
-                             Fmt::row_ptr(NMAT == 2 ? g.w1 : g.w0, arow, g.K, kg)};
-        // scales of group 0 of this lane's output rows 4kg..4kg+3 (group-major;
-        // with quad scales, of row 4kg + (lane & 3) alone: the lanes of a quad
-        // share kg)
-        const size_t srow = (size_t)e * nunits * g.N + row0 + 4 * kg +
-                            (Fmt::kQuadScales ? (lane & 3) : 0);
-        const float* sp[2] = {g.s0 ? g.s0 + srow : nullptr,
-                              NMAT == 2 && g.s1 ? g.s1 + srow : nullptr};
         const int nfull = has ? (u1 - u0) / U : 0;   // full batches of this wave
         const int tail_u = u0 + nfull * U;           // tail units [tail_u, u1)
-        for (int c0 = 0; c0 < m; c0 += 16) {
-            const int ntok = min(16, m - c0);        // distinct tokens of the chunk
-            // padding columns (beyond the expert's tokens) read token 0's row:
-            // an MFMA output column depends only on its own B column, and
-            // padding columns are never stored
-            const bool valid = col < ntok;
-            const int bcol = valid ? col : 0;
-            // the first weight batch needs only the expert and the row:
-            // request it before the token rows, whose addresses take two
-            // dependent loads (the first slab then waits for everything)
-            constexpr int kLoads = Fmt::template loads<NMAT, U>();
-            typename Fmt::template Batch<NMAT, U> A, B;
-            if (nfull > 0) Fmt::template load<NMAT, U>(A, wp, sp, g.N, u0);
-            // token rows this wave stages: tokens wave, wave + 4, ...
-            const uint16_t* tp[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int c = wave + kWaves * i;
-                const int qq = beg + c0 + (c < ntok ? c : 0);
-                const int brow = NMAT == 2 ? g.sorted_slot[qq] / g.top_k : qq;
-                tp[i] = g.b_src + (size_t)brow * g.b_pitch;
+        // the round in format F (tag: RoundFmt<F, read the second set>)
+        auto round = [&](auto tag) {
+            using F = typename decltype(tag)::Fmt;
+            constexpr bool kSecond = decltype(tag)::kFromSecond;
+            // scales of group 0 of this lane's output rows 4kg..4kg+3
+            // (group-major; with quad scales, of row 4kg + (lane & 3) alone:
+            // the lanes of a quad share kg)
+            const size_t srow = (size_t)e * nunits * g.N + row0 + 4 * kg +
+                                (F::kQuadScales ? (lane & 3) : 0);
+            const void* w0 = kSecond ? g.hw0 : g.w0;
+            const void* w1 = NMAT == 2 ? (kSecond ? g.hw1 : g.w1) : w0;
+            const float* s0 = kSecond ? g.hs0 : g.s0;
+            const float* s1 = kSecond ? g.hs1 : g.s1;
+            WeightSrc src;
+            src.w[0] = F::row_ptr(w0, arow, g.K, kg);
+            src.w[1] = F::row_ptr(w1, arow, g.K, kg);
+            src.s[0] = s0 ? s0 + srow : nullptr;
+            src.s[1] = NMAT == 2 && s1 ? s1 + srow : nullptr;
+            src.r[0] = src.r[1] = nullptr;
+            src.sr[0] = src.sr[1] = nullptr;
+            if constexpr (F::kResidual) {
+                src.r[0] = F::row_ptr(g.hw0, arow, g.K, kg);
+                src.r[1] = F::row_ptr(NMAT == 2 ? g.hw1 : g.hw0, arow, g.K, kg);
+                src.sr[0] = g.hs0 + srow;
+                src.sr[1] = NMAT == 2 ? g.hs1 + srow : nullptr;
             }
-            f32x4 acc[NMAT];
-#pragma unroll
-            for (int mm = 0; mm < NMAT; ++mm) acc[mm] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-            // Slab j holds, for each K part pp, its units [start(pp) + j*SPU,
-            // +SPU) at blocks [pp*SP, pp*SP + SP) of every token row.  One
-            // load instruction stages one token's whole slab row (1 KB): lane
-            // L fills block L/4 for K group L%4, so the row is read from
-            // global memory in contiguous runs of 1024/S bytes.
-            auto stage = [&](int j, int bsel) {
-                const int blk = lane >> 2;
-                const int kgl = lane & 3;
-                const int pp = blk / SP;
-                const int bb = blk - pp * SP;
-                const int p0 = min(nunits, pp * kpu);
-                const int p1 = min(nunits, p0 + kpu);
-                const int u = p0 + j * SPU + bb / Fmt::kBlocks;
-                const int off = u * 32 * Fmt::kBlocks + Fmt::block_offset(bb % Fmt::kBlocks, kgl);
-#pragma unroll
+            src.spitch = g.N;
+            for (int c0 = 0; c0 < m; c0 += 16) {
+                const int ntok = min(16, m - c0);        // distinct tokens of the chunk
+                // padding columns (beyond the expert's tokens) read token 0's row:
+                // an MFMA output column depends only on its own B column, and
+                // padding columns are never stored
+                const bool valid = col < ntok;
+                const int bcol = valid ? col : 0;
+                // the first weight batch needs only the expert and the row:
+                // request it before the token rows, whose addresses take two
+                // dependent loads (the first slab then waits for everything)
+                constexpr int kLoads = F::template loads<NMAT, U>();
+                typename F::template Batch<NMAT, U> A, B;
+                if (nfull > 0) F::template load<NMAT, U>(A, src, u0);
+                // token rows this wave stages: tokens wave, wave + 4, ...
+                const uint16_t* tp[4];
+    #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int c = wave + kWaves * i;
-                    if (c < ntok && u < p1)
-                        __builtin_amdgcn_global_load_lds((const void*)(tp[i] + off),
-                                                         (lds_void_ptr)&xs[bsel][tok_base(c)], 16,
-                                                         0, 0);
+                    const int qq = beg + c0 + (c < ntok ? c : 0);
+                    const int brow = NMAT == 2 ? g.sorted_slot[qq] / g.top_k : qq;
+                    tp[i] = g.b_src + (size_t)brow * g.b_pitch;
                 }
-            };
-            stage(0, 0);
-            // weight batches ping-pong between two register sets: batch bi
-            // lives in A when bi is even, in B when odd; the next batch is
-            // always requested before the current one is multiplied
-            int bi = 0;
-            for (int j = 0; j < nslab; ++j) {
-                // this wave's staging loads are done (only the batch
-                // prefetched for this slab may still be in flight; at slab
-                // 0, whose staging follows the first batch, everything)
-                if (j == 0)
-                    wait_vmcnt<0>();
-                else if (bi < nfull)
-                    wait_vmcnt<(kLoads < 63 ? kLoads : 63)>();
-                else
-                    wait_vmcnt<0>();
-                __syncthreads();
-                if (j + 1 < nslab) stage(j + 1, (j + 1) & 1);
-                const int slab_u0 = u0 + j * SPU;
-                // this lane's B fragments: token row bcol, K group kg, from the
-                // first block of this wave's K part
-                const u32x4* buf = &xs[j & 1][tok_base(bcol) + kp * SP * kBlockU4 + kg];
-                const int bend = min(nfull, (j + 1) * NB);
-                for (; bi < bend; ++bi) {
-                    const u32x4* bb = buf + (u0 + bi * U - slab_u0) * Fmt::kBlocks * kBlockU4;
-                    if ((bi & 1) == 0) {
-                        if (bi + 1 < nfull)
-                            Fmt::template load<NMAT, U>(B, wp, sp, g.N, u0 + (bi + 1) * U);
-                        Fmt::template mma<NMAT, U>(A, bb, acc);
-                    } else {
-                        if (bi + 1 < nfull)
-                            Fmt::template load<NMAT, U>(A, wp, sp, g.N, u0 + (bi + 1) * U);
-                        Fmt::template mma<NMAT, U>(B, bb, acc);
+                f32x4 acc[NMAT];
+    #pragma unroll
+                for (int mm = 0; mm < NMAT; ++mm) acc[mm] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+                // Slab j holds, for each K part pp, its units [start(pp) + j*SPU,
+                // +SPU) at blocks [pp*SP, pp*SP + SP) of every token row.  One
+                // load instruction stages one token's whole slab row (1 KB): lane
+                // L fills block L/4 for K group L%4, so the row is read from
+                // global memory in contiguous runs of 1024/S bytes.
+                auto stage = [&](int j, int bsel) {
+                    const int blk = lane >> 2;
+                    const int kgl = lane & 3;
+                    const int pp = blk / SP;
+                    const int bb = blk - pp * SP;
+                    const int p0 = min(nunits, pp * kpu);
+                    const int p1 = min(nunits, p0 + kpu);
+                    const int u = p0 + j * SPU + bb / F::kBlocks;
+                    const int off = u * 32 * F::kBlocks + F::block_offset(bb % F::kBlocks, kgl);
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int c = wave + kWaves * i;
+                        if (c < ntok && u < p1)
+                            __builtin_amdgcn_global_load_lds((const void*)(tp[i] + off),
+                                                             (lds_void_ptr)&xs[bsel][tok_base(c)], 16,
+                                                             0, 0);
                     }
-                }
-                if (has && tail_u < u1 && tail_u >= slab_u0 && tail_u < slab_u0 + SPU)
-                    for (int u = tail_u; u < u1; ++u) {
-                        typename Fmt::template Batch<NMAT, 1> t;
-                        Fmt::template load<NMAT, 1>(t, wp, sp, g.N, u);
-                        Fmt::template mma<NMAT, 1>(
-                            t, buf + (u - slab_u0) * Fmt::kBlocks * kBlockU4, acc);
+                };
+                stage(0, 0);
+                // weight batches ping-pong between two register sets: batch bi
+                // lives in A when bi is even, in B when odd; the next batch is
+                // always requested before the current one is multiplied
+                int bi = 0;
+                for (int j = 0; j < nslab; ++j) {
+                    // this wave's staging loads are done (only the batch
+                    // prefetched for this slab may still be in flight; at slab
+                    // 0, whose staging follows the first batch, everything)
+                    if (j == 0)
+                        wait_vmcnt<0>();
+                    else if (bi < nfull)
+                        wait_vmcnt<(kLoads < 63 ? kLoads : 63)>();
+                    else
+                        wait_vmcnt<0>();
+                    __syncthreads();
+                    if (j + 1 < nslab) stage(j + 1, (j + 1) & 1);
+                    const int slab_u0 = u0 + j * SPU;
+                    // this lane's B fragments: token row bcol, K group kg, from the
+                    // first block of this wave's K part
+                    const u32x4* buf = &xs[j & 1][tok_base(bcol) + kp * SP * kBlockU4 + kg];
+                    const int bend = min(nfull, (j + 1) * NB);
+                    for (; bi < bend; ++bi) {
+                        const u32x4* bb = buf + (u0 + bi * U - slab_u0) * F::kBlocks * kBlockU4;
+                        if ((bi & 1) == 0) {
+                            if (bi + 1 < nfull)
+                                F::template load<NMAT, U>(B, src, u0 + (bi + 1) * U);
+                            F::template mma<NMAT, U>(A, bb, acc);
+                        } else {
+                            if (bi + 1 < nfull)
+                                F::template load<NMAT, U>(A, src, u0 + (bi + 1) * U);
+                            F::template mma<NMAT, U>(B, bb, acc);
+                        }
                     }
-            }
-            __syncthreads();
-            if constexpr (S > 1) {
-                if (kp > 0) {
-#pragma unroll
-                    for (int mm = 0; mm < NMAT; ++mm)
-                        red[((wave - R) * NMAT + mm) * kWave + lane] = acc[mm];
+                    if (has && tail_u < u1 && tail_u >= slab_u0 && tail_u < slab_u0 + SPU)
+                        for (int u = tail_u; u < u1; ++u) {
+                            typename F::template Batch<NMAT, 1> t;
+                            F::template load<NMAT, 1>(t, src, u);
+                            F::template mma<NMAT, 1>(
+                                t, buf + (u - slab_u0) * F::kBlocks * kBlockU4, acc);
+                        }
                 }
                 __syncthreads();
-                if (kp == 0) {
-#pragma unroll
-                    for (int pp = 1; pp < S; ++pp)
-#pragma unroll
+                if constexpr (S > 1) {
+                    if (kp > 0) {
+    #pragma unroll
                         for (int mm = 0; mm < NMAT; ++mm)
-                            acc[mm] += red[(((pp - 1) * R + r) * NMAT + mm) * kWave + lane];
+                            red[((wave - R) * NMAT + mm) * kWave + lane] = acc[mm];
+                    }
+                    __syncthreads();
+                    if (kp == 0) {
+    #pragma unroll
+                        for (int pp = 1; pp < S; ++pp)
+    #pragma unroll
+                            for (int mm = 0; mm < NMAT; ++mm)
+                                acc[mm] += red[(((pp - 1) * R + r) * NMAT + mm) * kWave + lane];
+                    }
                 }
-            }
-            if (kp == 0 && has && valid) {
-                const size_t p = (size_t)beg + c0 + col;
-                if constexpr (NMAT == 2) {
-                    const f32x4 gv = acc[0], uv = acc[1];
-                    u32x2 packed;
-                    packed.x = (uint32_t)f32_to_bf16_bits(silu(gv.x) * uv.x) |
-                               ((uint32_t)f32_to_bf16_bits(silu(gv.y) * uv.y) << 16);
-                    packed.y = (uint32_t)f32_to_bf16_bits(silu(gv.z) * uv.z) |
-                               ((uint32_t)f32_to_bf16_bits(silu(gv.w) * uv.w) << 16);
-                    *reinterpret_cast<u32x2*>(g.h + p * g.N + row0 + kg * 4) = packed;
-                } else {
-                    const int slot = g.sorted_slot[p];
-                    *reinterpret_cast<f32x4*>(g.y + (size_t)slot * g.N + row0 + kg * 4) = acc[0];
+                if (kp == 0 && has && valid) {
+                    const size_t p = (size_t)beg + c0 + col;
+                    if constexpr (NMAT == 2) {
+                        const f32x4 gv = acc[0], uv = acc[1];
+                        u32x2 packed;
+                        packed.x = (uint32_t)f32_to_bf16_bits(silu(gv.x) * uv.x) |
+                                   ((uint32_t)f32_to_bf16_bits(silu(gv.y) * uv.y) << 16);
+                        packed.y = (uint32_t)f32_to_bf16_bits(silu(gv.z) * uv.z) |
+                                   ((uint32_t)f32_to_bf16_bits(silu(gv.w) * uv.w) << 16);
+                        *reinterpret_cast<u32x2*>(g.h + p * g.N + row0 + kg * 4) = packed;
+                    } else {
+                        const int slot = g.sorted_slot[p];
+                        *reinterpret_cast<f32x4*>(g.y + (size_t)slot * g.N + row0 + kg * 4) = acc[0];
+                    }
                 }
+                if constexpr (S > 1) __syncthreads();
             }
-            if constexpr (S > 1) __syncthreads();
+        };
+        if constexpr (IsMixed<Fmt>::value) {
+            if (g.critical[e])
+                round(RoundFmt<typename Fmt::HiFmt, Fmt::kHiReadsSecond>{});
+            else
+                round(RoundFmt<typename Fmt::LoFmt, false>{});
+        } else {
+            round(RoundFmt<Fmt, false>{});
         }
     }
 }
@@ -642,7 +806,9 @@ hipError_t launch_gemm(const ExpertGemm& g, int64_t max_active, int num_cu,
     return hipGetLastError();
 }
 
-template <class Fmt>
+// Fmt: the gate/up weight format; FmtDown: down's (the same but for the
+// residual split, whose down copies are not split).
+template <class Fmt, class FmtDown = Fmt>
 hipError_t launch_ffn(const uint16_t* x, const Routing& route, const FfnWeights& W,
                       uint16_t* out, const FfnShape& s, const Workspace& ws, int num_cu,
                       const StageEvents& ev, const SplitOverride& split, hipStream_t stream) {
@@ -664,6 +830,11 @@ hipError_t launch_ffn(const uint16_t* x, const Routing& route, const FfnWeights&
     gu.w1 = W.up;
     gu.s0 = W.s_gate;
     gu.s1 = W.s_up;
+    gu.hw0 = W.gate2;
+    gu.hw1 = W.up2;
+    gu.hs0 = W.s_gate2;
+    gu.hs1 = W.s_up2;
+    gu.critical = W.critical;
     gu.meta = ws.meta;
     gu.offsets = ws.offsets;
     gu.active = ws.active;
@@ -686,13 +857,17 @@ hipError_t launch_ffn(const uint16_t* x, const Routing& route, const FfnWeights&
     dn.w1 = nullptr;
     dn.s0 = W.s_down;
     dn.s1 = nullptr;
+    dn.hw0 = W.down2;
+    dn.hw1 = nullptr;
+    dn.hs0 = W.s_down2;
+    dn.hs1 = nullptr;
     dn.h = nullptr;
     dn.y = ws.y;
     dn.b_pitch = s.I;
     dn.N = s.H;
     dn.K = s.I;
     dn.split = split.down;
-    err = launch_gemm<Fmt, 1>(dn, max_active, num_cu, stream);
+    err = launch_gemm<FmtDown, 1>(dn, max_active, num_cu, stream);
     if (err == hipSuccess && tiled) err = launch_tiled_down(W, s, ws, num_cu, stream);
     if (err == hipSuccess) err = ev.mark(2, stream);
     if (err != hipSuccess) return err;
@@ -731,6 +906,13 @@ hipError_t launch_ffn_int8(const uint16_t* x, const Routing& route, const FfnWei
                            const StageEvents& ev, const SplitOverride& split,
                            hipStream_t stream) {
     return launch_ffn<Int8Weights>(x, route, W, out, s, ws, num_cu, ev, split, stream);
+}
+
+hipError_t launch_ffn_resplit(const uint16_t* x, const Routing& route, const FfnWeights& W,
+                           uint16_t* out, const FfnShape& s, const Workspace& ws, int num_cu,
+                           const StageEvents& ev, const SplitOverride& split,
+                           hipStream_t stream) {
+    return launch_ffn<ResidualGateUp, DualDown>(x, route, W, out, s, ws, num_cu, ev, split, stream);
 }
 
 }  // namespace moe

@@ -55,9 +55,18 @@ struct FfnWeights {
     const void* gate;
     const void* up;
     const void* down;
-    const float* s_gate;  // INT8 only
+    const float* s_gate;  // INT8 / INT4 only
     const float* s_up;
     const float* s_down;
+    // residual split only: W^R of gate and up, the high-precision down copy,
+    // their scales, and the per-expert precision flags
+    const void* gate2 = nullptr;
+    const void* up2 = nullptr;
+    const void* down2 = nullptr;
+    const float* s_gate2 = nullptr;
+    const float* s_up2 = nullptr;
+    const float* s_down2 = nullptr;
+    const uint8_t* critical = nullptr;
 };
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids,
@@ -85,6 +94,10 @@ hipError_t launch_ffn_int4(const uint16_t* x, const Routing& route, const FfnWei
                            hipStream_t stream);
 
 hipError_t launch_ffn_int8(const uint16_t* x, const Routing& route, const FfnWeights& W,
+                           uint16_t* out, const FfnShape& s, const Workspace& ws, int num_cu,
+                           const StageEvents& ev, const SplitOverride& split,
+                           hipStream_t stream);
+hipError_t launch_ffn_resplit(const uint16_t* x, const Routing& route, const FfnWeights& W,
                            uint16_t* out, const FfnShape& s, const Workspace& ws, int num_cu,
                            const StageEvents& ev, const SplitOverride& split,
                            hipStream_t stream);

@@ -329,6 +329,45 @@ int moe_ffn_forward_int4(const void* x, const int32_t* topk_ids, const float* to
     return err == hipSuccess ? MOE_FFN_OK : MOE_FFN_ERR_HIP;
 }
 
+int moe_ffn_forward_resplit(const void* x, const int32_t* topk_ids, const float* topk_w,
+                            const uint8_t* P_gate, const float* S_gate, const uint8_t* R_gate,
+                            const float* SR_gate, const uint8_t* P_up, const float* S_up,
+                            const uint8_t* R_up, const float* SR_up, const uint8_t* P_down_lo,
+                            const float* S_down_lo, const int8_t* Q_down_hi,
+                            const float* S_down_hi, const uint8_t* critical, int32_t group,
+                            void* out, int64_t T, int64_t H, int64_t I, int32_t E,
+                            int32_t top_k, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+    if (group != MOE_FFN_INT8_GROUP) return MOE_FFN_ERR_BAD_SHAPE;
+    moe_ffn_ws_layout L;
+    int rc = check_forward(x, topk_ids, topk_w, out, T, H, I, E, top_k, workspace,
+                           workspace_bytes, MOE_FFN_INT8_GROUP, &L);
+    if (rc != MOE_FFN_OK || T == 0) return rc;
+    const void* const tensors[] = {P_gate, S_gate, R_gate, SR_gate, P_up, S_up,
+                                   R_up, SR_up, P_down_lo, S_down_lo, Q_down_hi, S_down_hi};
+    for (const void* t : tensors) {
+        if (!t) return MOE_FFN_ERR_NULL_ARG;
+        if (!aligned16(t)) return MOE_FFN_ERR_MISALIGNED;
+    }
+    if (!critical) return MOE_FFN_ERR_NULL_ARG;
+    int ncu = 0;
+    if ((rc = num_cu(&ncu)) != MOE_FFN_OK) return rc;
+    const moe::FfnShape s{(int)T, (int)H, (int)I, E, top_k};
+    moe::FfnWeights W{P_gate, P_up, P_down_lo, S_gate, S_up, S_down_lo};
+    W.gate2 = R_gate;
+    W.up2 = R_up;
+    W.down2 = Q_down_hi;
+    W.s_gate2 = SR_gate;
+    W.s_up2 = SR_up;
+    W.s_down2 = S_down_hi;
+    W.critical = critical;
+    const moe::Routing route{nullptr, const_cast<int32_t*>(topk_ids), const_cast<float*>(topk_w)};
+    const hipError_t err = moe::launch_ffn_resplit(
+        static_cast<const uint16_t*>(x), route, W, static_cast<uint16_t*>(out), s,
+        carve(workspace, L), ncu, take_stage_events(), t_split, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? MOE_FFN_OK : MOE_FFN_ERR_HIP;
+}
+
 int moe_ffn_check_status(const void* workspace, void* stream, int64_t* n_dropped) {
     if (!workspace) return MOE_FFN_ERR_NULL_ARG;
     if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess)

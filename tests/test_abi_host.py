@@ -220,3 +220,30 @@ def test_attn_workspace_bytes():
     assert moe.moe_attn_decode_workspace_bytes(0, 8, 2, 64, 16) == 256
     assert moe.moe_attn_decode_workspace_bytes(1, 8, 2, 100, 16) == 0
     assert moe.moe_attn_decode_workspace_bytes(1, 8, 3, 64, 16) == 0
+
+
+def resplit(**kw):
+    """moe_ffn_forward_resplit with fake addresses (T=4, H=128, I=256, E=8,
+    k=2); keyword arguments replace single arguments by name."""
+    args = dict(x=A, ids=A + 0x100000, w=A + 0x200000, Pg=A + 0x1000000, Sg=A + 0x1100000,
+                Rg=A + 0x1200000, SRg=A + 0x1300000, Pu=A + 0x1400000, Su=A + 0x1500000,
+                Ru=A + 0x1600000, SRu=A + 0x1700000, Pd=A + 0x1800000, Sd=A + 0x1900000,
+                Qd=A + 0x1a00000, Sdh=A + 0x1b00000, crit=A + 0x1c00000, group=128,
+                out=A + 0x300000, T=4, H=128, I=256, E=8, k=2, ws=A + 0x4000000,
+                ws_bytes=1 << 30)
+    args.update(kw)
+    return moe.lib().moe_ffn_forward_resplit(*args.values(), None)
+
+
+def test_forward_resplit_host_validation():
+    assert resplit(group=64) == moe.MOE_FFN_ERR_BAD_SHAPE
+    assert resplit(H=96) == moe.MOE_FFN_ERR_BAD_SHAPE
+    assert resplit(I=160) == moe.MOE_FFN_ERR_BAD_SHAPE
+    assert resplit(crit=None) == moe.MOE_FFN_ERR_NULL_ARG
+    assert resplit(SRu=None) == moe.MOE_FFN_ERR_NULL_ARG
+    assert resplit(Qd=None) == moe.MOE_FFN_ERR_NULL_ARG
+    assert resplit(Rg=A + 0x1200008) == moe.MOE_FFN_ERR_MISALIGNED
+    assert resplit(Sdh=A + 0x1b00004) == moe.MOE_FFN_ERR_MISALIGNED
+    assert resplit(ws_bytes=1024) == moe.MOE_FFN_ERR_WORKSPACE
+    assert resplit(out=A + 0x40) == moe.MOE_FFN_ERR_ALIAS
+    assert resplit(T=0) == moe.MOE_FFN_OK

@@ -55,6 +55,7 @@ class Workload:
     zipf_s: float = 0.0
     int8: bool = False
     int4: bool = False
+    resplit: bool = False      # residual-split INT4 gate/up, INT4 / INT8 down copies
     group: int = 128
     seed: int = 0
 
@@ -74,6 +75,9 @@ def _registry() -> Dict[str, Workload]:
         w[f"mixtral8x7b_int4_m{m}"] = Workload(f"mixtral8x7b_int4_m{m}", H=4096,
                                                I=14336, E=8, k=2, T=4 * m,
                                                routing="forced", int4=True)
+        w[f"mixtral8x7b_resplit_m{m}"] = Workload(f"mixtral8x7b_resplit_m{m}", H=4096,
+                                                  I=14336, E=8, k=2, T=4 * m,
+                                                  routing="forced", resplit=True)
     w["deepseekv3_t16"] = Workload("deepseekv3_t16", H=7168, I=2048, E=256, k=8, T=16)
     w["deepseekv3_zipf_t16"] = Workload("deepseekv3_zipf_t16", H=7168, I=2048,
                                         E=256, k=8, T=16, routing="zipf", zipf_s=1.1)
@@ -279,9 +283,17 @@ def bits_to_bf16(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).view(torch.bfloat16)
 
 
-def weight_bytes_per_expert(wl: Workload) -> int:
-    """Bytes of one expert's three weight matrices (plus scales for INT8)."""
+def weight_bytes_per_expert(wl: Workload, critical: bool = True) -> int:
+    """Bytes of one expert's three weight matrices (plus scales for INT8 and
+    INT4).  Residual split: what one expert of the given precision reads
+    (critical: W^Q and W^R of gate/up and the INT8 down copy; otherwise W^Q
+    and the INT4 down copy)."""
     n = 3 * wl.H * wl.I
+    sc = (wl.H * wl.I // wl.group) * 4
+    if wl.resplit:
+        if critical:
+            return 2 * wl.H * wl.I + 4 * sc + wl.H * wl.I + sc
+        return n // 2 + 3 * sc
     if wl.int8:
         return n + 3 * (wl.H * wl.I // wl.group) * 4
     if wl.int4:
