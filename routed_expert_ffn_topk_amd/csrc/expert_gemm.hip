@@ -409,8 +409,9 @@ using DualDown = MixedWeights<Int4Weights, Int8Weights, true>;
 
 // Tuning per weight format and projection, measured on MI355X over the
 // Mixtral-8x7B, DeepSeek-V3, Qwen3-235B and Mixtral-8x22B expert shapes at
-// 1-16 tokens per expert (INT4: the Mixtral-8x7B shape): batch length U
-// (units) and resident workgroups per CU (LDS: 32 KB per workgroup).
+// 1-16 tokens per expert (INT4 and the residual split: the Mixtral-8x7B
+// shape): batch length U (units) and resident workgroups per CU (LDS: 32 KB
+// per workgroup).
 template <class Fmt, int NMAT>
 struct GemmTuning;
 template <>
@@ -441,11 +442,11 @@ struct GemmTuning<Int4Weights, 2> {
 template <>
 struct GemmTuning<ResidualGateUp, 2> {
     static constexpr int kBlocksPerCU = 2;
-    static constexpr int kBatch = 1;
+    static constexpr int kBatch = 2;
 };
 template <>
 struct GemmTuning<DualDown, 1> {
-    static constexpr int kBlocksPerCU = 3;
+    static constexpr int kBlocksPerCU = 2;
     static constexpr int kBatch = 2;
 };
 template <>
