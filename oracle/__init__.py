@@ -73,6 +73,10 @@ def lib() -> ctypes.CDLL:
             _u16p, _i32p, _f32p, _vpp, _vpp, _vpp, _vpp, _vpp, _vpp,
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
             ctypes.c_int32, ctypes.c_int32, _u16p, _f32p, _u16p, _f32p]
+        L.oracle_route_grouped.restype = ctypes.c_int
+        L.oracle_route_grouped.argtypes = [_f32p, _f32p, ctypes.c_int64, ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_float, _i32p, _f32p]
         L.oracle_moe_ffn_resplit.restype = ctypes.c_int
         L.oracle_moe_ffn_resplit.argtypes = [
             _u16p, _i32p, _f32p] + [_vpp] * 12 + [
@@ -129,6 +133,24 @@ def route_topk(logits: np.ndarray, k: int):
                                  _ptr(ids, ctypes.c_int32), _ptr(w, ctypes.c_float))
     if rc != 0:
         raise ValueError(f"oracle_route_topk failed ({rc})")
+    return ids, w
+
+
+def route_grouped(logits: np.ndarray, k: int, n_group: int, topk_group: int,
+                  bias: Optional[np.ndarray] = None, scale: float = 1.0):
+    """Grouped sigmoid router (see oracle_route_grouped): logits [T, E]
+    float32, optional selection bias [E] -> (ids [T, k] int32, w [T, k]
+    float32)."""
+    lg = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = lg.shape
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    ids = np.empty((T, k), dtype=np.int32)
+    w = np.empty((T, k), dtype=np.float32)
+    rc = lib().oracle_route_grouped(_ptr(lg, ctypes.c_float), _opt(b, ctypes.c_float), T, E,
+                                    n_group, topk_group, k, scale, _ptr(ids, ctypes.c_int32),
+                                    _ptr(w, ctypes.c_float))
+    if rc != 0:
+        raise ValueError(f"oracle_route_grouped failed ({rc})")
     return ids, w
 
 

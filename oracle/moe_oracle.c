@@ -38,7 +38,8 @@
  *
  * Readings where the pages are silent (each is listed in the design notes):
  *   - router: softmax over all experts, the k largest kept (ties -> lower
- *     expert id), weights renormalised over the k kept;
+ *     expert id), weights renormalised over the k kept; the grouped sigmoid
+ *     variant as stated at oracle_route_grouped;
  *   - h = RNE_bf16( silu(g) * u ) with g, u and silu(g) kept in FP32;
  *   - out[t] = RNE_bf16( sum_j w[t,j] * y_j ), summed in FP32 over ascending j,
  *     where y_j is the FP32 down-projection output (not rounded);
@@ -137,6 +138,77 @@ int oracle_route_topk(const float* logits, int64_t T, int32_t E, int32_t k,
     }
     free(chosen);
     free(p);
+    return ORACLE_OK;
+}
+
+/* Grouped sigmoid routing, the variant of the gate used by DeepSeek-V3
+ * (one of the models of HiNa-MoE's Table 3 and RapidMoE's evaluation; the
+ * pages name the model but do not spell out its gate).  For each token t:
+ *   s_e = 1 / (1 + exp(-l_e))                 (FP32)
+ *   c_e = s_e + bias_e                        (selection score; bias may be NULL = 0)
+ *   the E experts form n_group groups of G = E / n_group consecutive ids;
+ *   group score = the largest c in the group plus the second largest
+ *     (the largest alone when G = 1), added in that order;
+ *   keep the topk_group groups of highest score (ties -> lower group id);
+ *   choose k experts of the kept groups by descending c (ties -> lower id);
+ *   w_j = scale * s_{e_j} / (s_{e_0} + ... + s_{e_{k-1}}), the sum in
+ *     ascending j, then the division, then the multiplication (FP32).
+ * Slot j of token t holds the j-th choice.  Returns ORACLE_OK, or
+ * ORACLE_ERR_ARG for inconsistent sizes. */
+int oracle_route_grouped(const float* logits, const float* bias, int64_t T, int32_t E,
+                         int32_t n_group, int32_t topk_group, int32_t k, float scale,
+                         int32_t* topk_ids, float* topk_w) {
+    if (T < 0 || E <= 0 || n_group <= 0 || E % n_group != 0 || topk_group <= 0 ||
+        topk_group > n_group || k <= 0 || k > topk_group * (E / n_group))
+        return ORACLE_ERR_ARG;
+    const int32_t G = E / n_group;
+    float* s = (float*)malloc(sizeof(float) * (size_t)E);
+    float* c = (float*)malloc(sizeof(float) * (size_t)E);
+    float* gs = (float*)malloc(sizeof(float) * (size_t)n_group);
+    unsigned char* kept = (unsigned char*)malloc((size_t)n_group);
+    unsigned char* chosen = (unsigned char*)malloc((size_t)E);
+    if (!s || !c || !gs || !kept || !chosen) {
+        free(s); free(c); free(gs); free(kept); free(chosen);
+        return ORACLE_ERR_NOMEM;
+    }
+    for (int64_t t = 0; t < T; ++t) {
+        const float* l = logits + t * E;
+        for (int32_t e = 0; e < E; ++e) {
+            s[e] = 1.0f / (1.0f + expf(-l[e]));
+            c[e] = s[e] + (bias ? bias[e] : 0.0f);
+        }
+        for (int32_t g = 0; g < n_group; ++g) {
+            /* largest, then second largest, of the group's selection scores */
+            int32_t b1 = -1, b2 = -1;
+            for (int32_t e = g * G; e < (g + 1) * G; ++e)
+                if (b1 < 0 || c[e] > c[b1]) b1 = e;
+            for (int32_t e = g * G; e < (g + 1) * G; ++e)
+                if (e != b1 && (b2 < 0 || c[e] > c[b2])) b2 = e;
+            gs[g] = b2 < 0 ? c[b1] : c[b1] + c[b2];
+        }
+        memset(kept, 0, (size_t)n_group);
+        for (int32_t j = 0; j < topk_group; ++j) {
+            int32_t best = -1;
+            for (int32_t g = 0; g < n_group; ++g)
+                if (!kept[g] && (best < 0 || gs[g] > gs[best])) best = g;
+            kept[best] = 1;
+        }
+        memset(chosen, 0, (size_t)E);
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t best = -1;
+            for (int32_t e = 0; e < E; ++e) {
+                if (chosen[e] || !kept[e / G]) continue;
+                if (best < 0 || c[e] > c[best]) best = e;
+            }
+            chosen[best] = 1;
+            topk_ids[t * k + j] = best;
+        }
+        float sum = 0.0f;
+        for (int32_t j = 0; j < k; ++j) sum += s[topk_ids[t * k + j]];
+        for (int32_t j = 0; j < k; ++j)
+            topk_w[t * k + j] = s[topk_ids[t * k + j]] / sum * scale;
+    }
+    free(s); free(c); free(gs); free(kept); free(chosen);
     return ORACLE_OK;
 }
 

@@ -146,6 +146,42 @@ def test_int4_layer_graph_replays_match_eager():
     _replays_match(call, [out], other)
 
 
+def test_resplit_layer_graph_replays_match_eager():
+    need_gpu()
+    say("graph replay residual split")
+    rng = np.random.default_rng(7)
+    T, H, I, E, k = 12, 384, 256, 6, 2
+    x = workloads.bits_to_bf16(workloads.bf16_bits(
+        torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(torch.bfloat16))).cuda()
+    gm, p4 = workloads.scales_group_major, workloads.pack_int4
+    draw = lambda N, K: torch.from_numpy(  # noqa: E731
+        (rng.standard_normal((E, N, K)) * 0.05).astype(np.float32))
+    P = []
+    for N, K in ((I, H), (I, H)):
+        q, s, r, sr = workloads.quantize_residual_split(draw(N, K), 128, 7)
+        P += [p4(q).cuda(), gm(s).cuda(), p4(r).cuda(), gm(sr).cuda()]
+    wd = draw(H, I)
+    ql, sl = workloads.quantize_groupwise(wd, 128, 7)
+    qh, sh = workloads.quantize_groupwise(wd, 128, 127)
+    P += [p4(ql).cuda(), gm(sl).cuda(), qh.cuda(), gm(sh).cuda(),
+          torch.tensor([1, 0, 1, 1, 0, 0], dtype=torch.uint8).cuda()]
+    ids = torch.from_numpy(np.stack([rng.choice(E, size=k, replace=False)
+                                     for _ in range(T)]).astype(np.int32)).cuda()
+    w = torch.from_numpy(rng.uniform(0.05, 1.0, size=(T, k)).astype(np.float32)).cuda()
+    ws = moe.alloc_workspace(T, H, I, E, k)
+    out = torch.empty_like(x)
+
+    def call():
+        moe.moe_ffn_forward_resplit(x, ids, w, *P, out=out, workspace=ws,
+                                    stream=torch.cuda.current_stream())
+
+    def other():
+        moe.moe_ffn_forward_resplit(x, torch.flip(ids, dims=[1]).contiguous(), w, *P,
+                                    workspace=ws)
+
+    _replays_match(call, [out], other)
+
+
 def test_attn_graph_replays_match_eager():
     need_gpu()
     say("graph replay attention")

@@ -59,6 +59,15 @@ MUTANTS = {
         "const int8_t* qd = crit ? Qd_hi[e] : Qd_lo[e];\n            const float* sd = crit ? Sd_hi[e] : Sd_lo[e];",
         "const int8_t* qd = crit ? Qd_lo[e] : Qd_hi[e];\n            const float* sd = crit ? Sd_lo[e] : Sd_hi[e];"),
     "resplit_flag_by_slot": ("int crit = critical[e] != 0;", "int crit = critical[slot % E] != 0;"),
+    # grouped sigmoid router (pins in test_oracle_route_grouped_pins.py)
+    "grouped_group_score_max_only": ("gs[g] = b2 < 0 ? c[b1] : c[b1] + c[b2];", "gs[g] = c[b1];"),
+    "grouped_bias_in_weights": ("topk_w[t * k + j] = s[topk_ids[t * k + j]] / sum * scale;",
+                                "topk_w[t * k + j] = c[topk_ids[t * k + j]] / sum * scale;"),
+    "grouped_groups_not_masked": ("if (chosen[e] || !kept[e / G]) continue;",
+                                  "if (chosen[e]) continue;"),
+    "grouped_group_tie_break": ("if (!kept[g] && (best < 0 || gs[g] > gs[best])) best = g;",
+                                "if (!kept[g] && (best < 0 || gs[g] >= gs[best])) best = g;"),
+    "grouped_exp_not_sigmoid": ("s[e] = 1.0f / (1.0f + expf(-l[e]));", "s[e] = expf(l[e]);"),
 }
 
 
@@ -67,6 +76,8 @@ def pin_file(name: str) -> str:
         return "test_oracle_attn_pins.py"
     if name.startswith("resplit_"):
         return "test_oracle_resplit_pins.py"
+    if name.startswith("grouped_"):
+        return "test_oracle_route_grouped_pins.py"
     return "test_oracle_pins.py"
 
 
