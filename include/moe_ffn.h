@@ -122,6 +122,30 @@ int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t top_k,
                    int32_t* topk_ids, float* topk_w, void* stream);
 
 /*
+ * Grouped sigmoid router (the gate of DeepSeek-V3, one of the models in the
+ * pages' Table 3 and RapidMoE's evaluation; the pages name the model but do
+ * not spell out its gate).  For each token t, with l = logits[t]:
+ *   s_e = 1 / (1 + exp(-l_e)),  c_e = s_e + bias_e  (bias NULL: 0)   FP32
+ *   the E experts form n_group groups of E / n_group consecutive ids; a
+ *   group's score is its largest c plus its second largest (the largest
+ *   alone for groups of one);
+ *   the topk_group groups of highest score are kept (ties: lower group);
+ *   the top_k experts of the kept groups by descending c are chosen (ties:
+ *   lower id), slot j holding the j-th;
+ *   topk_w[t][j] = s_{e_j} / (sum over the chosen s, ascending j) * scale.
+ *   logits [T][E] float32, bias [E] float32 or NULL, device;
+ *   topk_ids [T][top_k] int32, topk_w [T][top_k] float32, device (written).
+ * Sizes: T >= 0 (0 is a no-op), 1 <= E <= MOE_FFN_MAX_EXPERTS, n_group in
+ * [1, 64] dividing E, 1 <= topk_group <= n_group, 1 <= top_k <= 64 and
+ * top_k <= topk_group * E / n_group.  Pointers 4-byte aligned.
+ * Errors: BAD_SHAPE, NULL_ARG, MISALIGNED, ALIAS (an output overlaps an input
+ * or the other output), HIP.  Asynchronous on `stream`.
+ */
+int moe_route_grouped(const float* logits, const float* bias, int64_t T, int32_t E,
+                      int32_t n_group, int32_t topk_group, int32_t top_k, float scale,
+                      int32_t* topk_ids, float* topk_w, void* stream);
+
+/*
  * Routed-expert FFN layer, BF16 weights (HiNa-MoE §4.1 FFN equation).
  *   x        [T][H] bf16, device: token activations.
  *   topk_ids [T][top_k] int32, device: expert of each slot.  Ids outside

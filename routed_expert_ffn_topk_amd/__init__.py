@@ -70,6 +70,9 @@ def lib() -> ctypes.CDLL:
         L.moe_ffn_forward_int4.restype = _c.c_int
         L.moe_ffn_forward_int4.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                                            _vp, _i64, _i64, _i64, _i32, _i32, _vp, _sz, _vp]
+        L.moe_route_grouped.restype = _c.c_int
+        L.moe_route_grouped.argtypes = [_vp, _vp, _i64, _i32, _i32, _i32, _i32, _c.c_float, _vp,
+                                        _vp, _vp]
         L.moe_ffn_forward_resplit.restype = _c.c_int
         L.moe_ffn_forward_resplit.argtypes = [_vp] * 16 + [_i32, _vp, _i64, _i64, _i64, _i32,
                                                            _i32, _vp, _sz, _vp]
@@ -282,6 +285,28 @@ def moe_ffn_forward_int4(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.
         T, H, I, E, top_k, _dev(workspace, "workspace", torch.uint8), workspace.numel(),
         _stream(stream)))
     return out
+
+
+def moe_route_grouped(logits: torch.Tensor, top_k: int, n_group: int, topk_group: int,
+                      bias: Optional[torch.Tensor] = None, scale: float = 1.0,
+                      topk_ids: Optional[torch.Tensor] = None,
+                      topk_w: Optional[torch.Tensor] = None, stream=None):
+    """Grouped sigmoid router: logits [T, E] float32 (device), optional
+    selection bias [E] -> (topk_ids [T, top_k] int32, topk_w [T, top_k]
+    float32)."""
+    T, E = logits.shape
+    if topk_ids is None:
+        topk_ids = torch.empty(T, top_k, dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty(T, top_k, dtype=torch.float32, device=logits.device)
+    if bias is not None and tuple(bias.shape) != (E,):
+        raise ValueError(f"bias must be [{E}], got {list(bias.shape)}")
+    _check("moe_route_grouped", lib().moe_route_grouped(
+        _dev(logits, "logits", torch.float32),
+        None if bias is None else _dev(bias, "bias", torch.float32), T, E, n_group,
+        topk_group, top_k, float(scale), _dev(topk_ids, "topk_ids", torch.int32),
+        _dev(topk_w, "topk_w", torch.float32), _stream(stream)))
+    return topk_ids, topk_w
 
 
 def moe_ffn_forward_resplit(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor,

@@ -71,6 +71,9 @@ struct FfnWeights {
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids,
                              float* w, hipStream_t stream);
+hipError_t launch_route_grouped(const float* logits, const float* bias, int T, int E,
+                               int n_group, int topk_group, int k, float scale, int32_t* ids,
+                               float* w, hipStream_t stream);
 
 // Gather index of ids [T][k]; experts with more than m_split slots are listed
 // for the tiled product (INT_MAX: none).

@@ -163,6 +163,32 @@ int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t top_k,
     return err == hipSuccess ? MOE_FFN_OK : MOE_FFN_ERR_HIP;
 }
 
+int moe_route_grouped(const float* logits, const float* bias, int64_t T, int32_t E,
+                      int32_t n_group, int32_t topk_group, int32_t top_k, float scale,
+                      int32_t* topk_ids, float* topk_w, void* stream) {
+    if (T < 0 || E < 1 || E > MOE_FFN_MAX_EXPERTS || n_group < 1 || n_group > 64 ||
+        E % n_group != 0 || topk_group < 1 || topk_group > n_group || top_k < 1 ||
+        top_k > 64 || top_k > topk_group * (E / n_group) ||
+        T * (int64_t)top_k >= ((int64_t)1 << 31) || T >= ((int64_t)1 << 31) / 4)
+        return MOE_FFN_ERR_BAD_SHAPE;
+    if (T == 0) return MOE_FFN_OK;
+    if (!logits || !topk_ids || !topk_w) return MOE_FFN_ERR_NULL_ARG;
+    if ((reinterpret_cast<uintptr_t>(logits) | reinterpret_cast<uintptr_t>(bias) |
+         reinterpret_cast<uintptr_t>(topk_ids) | reinterpret_cast<uintptr_t>(topk_w)) & 3u)
+        return MOE_FFN_ERR_MISALIGNED;
+    const size_t sb = (size_t)T * (size_t)top_k * 4;
+    const size_t lb = (size_t)T * (size_t)E * 4;
+    const size_t bb = (size_t)E * 4;
+    if (overlap(topk_ids, sb, topk_w, sb) || overlap(logits, lb, topk_ids, sb) ||
+        overlap(logits, lb, topk_w, sb) ||
+        (bias && (overlap(bias, bb, topk_ids, sb) || overlap(bias, bb, topk_w, sb))))
+        return MOE_FFN_ERR_ALIAS;
+    const hipError_t err =
+        moe::launch_route_grouped(logits, bias, (int)T, E, n_group, topk_group, top_k, scale,
+                                  topk_ids, topk_w, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? MOE_FFN_OK : MOE_FFN_ERR_HIP;
+}
+
 int moe_ffn_forward(const void* x, const int32_t* topk_ids, const float* topk_w,
                     const void* W_gate, const void* W_up, const void* W_down, void* out,
                     int64_t T, int64_t H, int64_t I, int32_t E, int32_t top_k,

@@ -4,6 +4,8 @@
 // permute:       the per-expert token lists that drive the gather of §4.1
 //                (each expert's routed tokens form one small matrix).
 // route_permute: both in one workgroup, for decode-sized batches.
+// route_grouped: the grouped sigmoid gate (selection bias, group-limited
+//                top-k, scaled weights).
 #include <cmath>
 
 #include "common.hpp"
@@ -106,6 +108,133 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
     int id;
     float wt;
     route_token_any(logits + (size_t)t * E, E, k, lane, &id, &wt);
+    if (lane < k) {
+        ids[(size_t)t * k + lane] = id;
+        w[(size_t)t * k + lane] = wt;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Grouped sigmoid routing (the gate of DeepSeek-V3, one of the models of the
+// pages' evaluation, whose gate they do not spell out): sigmoid scores s,
+// selection scores c = s + bias, the experts in n_group groups of G
+// consecutive ids scored by the sum of their two largest c, the topk_group
+// best groups kept, the k best experts of those by c, and weights
+// scale * s_j / sum_j s_j.  Ties go to the lower group and the lower id.
+// ---------------------------------------------------------------------------
+
+// One token with one wave.  Lane l holds experts l, l + 64, ...; the
+// selection scores also go to this wave's LDS row (cw), where lane g < n_group
+// reads its group's G scores.  Lane j < k returns the j-th choice.
+template <int PL>
+__device__ __forceinline__ void route_token_grouped(const float* __restrict__ l,
+                                                    const float* __restrict__ bias, int E,
+                                                    int n_group, int topk_group, int k,
+                                                    float scale, int lane, float* cw, int* id,
+                                                    float* wt) {
+    const int G = E / n_group;
+    float sv[PL];
+    int key[PL];
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+        const int e = lane + kWave * i;
+        sv[i] = 0.0f;
+        key[i] = INT_MIN;
+        if (e < E) {
+            sv[i] = 1.0f / (1.0f + expf(-l[e]));
+            const float c = sv[i] + (bias ? bias[e] : 0.0f);
+            key[i] = route_key(c);
+            cw[e] = c;
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // group scores: the largest selection score of the group plus the second
+    int gkey = INT_MIN;
+    if (lane < n_group) {
+        float b1 = -INFINITY, b2 = -INFINITY;
+        for (int e = lane * G; e < (lane + 1) * G; ++e) {
+            const float c = cw[e];
+            if (c > b1) {
+                b2 = b1;
+                b1 = c;
+            } else if (c > b2) {
+                b2 = c;
+            }
+        }
+        gkey = route_key(G > 1 ? b1 + b2 : b1);
+    }
+    // the topk_group best groups (uniform bit mask)
+    uint64_t kept = 0;
+    for (int j = 0; j < topk_group; ++j) {
+        const int K = wave_max_i32(gkey);
+        const int W = wave_min_i32(gkey == K ? lane : INT_MAX);
+        kept |= 1ull << W;
+        if (lane == W) gkey = INT_MIN;
+    }
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+        const int e = lane + kWave * i;
+        if (e < E && !((kept >> (e / G)) & 1ull)) key[i] = INT_MIN;
+    }
+    // k rounds over the kept experts: largest c, then lowest id
+    float my_s = 0.0f;
+    int my_e = -1;
+    for (int j = 0; j < k; ++j) {
+        int bk = INT_MIN, be = INT_MAX;
+        float bs = 0.0f;
+#pragma unroll
+        for (int i = 0; i < PL; ++i)
+            if (key[i] > bk) {
+                bk = key[i];
+                be = lane + kWave * i;
+                bs = sv[i];
+            }
+        const int K = wave_max_i32(bk);
+        const int W = wave_min_i32(bk == K ? be : INT_MAX);
+        const float sW = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bs), W & (kWave - 1)));
+        if (lane == j) {
+            my_e = W;
+            my_s = sW;
+        }
+#pragma unroll
+        for (int i = 0; i < PL; ++i)
+            if (lane + kWave * i == W) key[i] = INT_MIN;
+    }
+    // the sum of the chosen sigmoids in ascending slot order
+    float sum = 0.0f;
+    for (int j = 0; j < k; ++j)
+        sum += __builtin_bit_cast(float,
+                                  __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_s), j));
+    *id = lane < k ? my_e : -1;
+    *wt = lane < k ? my_s / sum * scale : 0.0f;
+}
+
+// Four tokens per 256-thread workgroup, one wave each.
+__global__ __launch_bounds__(256) void route_grouped_kernel(
+    const float* __restrict__ logits, const float* __restrict__ bias, int T, int E, int n_group,
+    int topk_group, int k, float scale, int32_t* __restrict__ ids, float* __restrict__ w) {
+    __shared__ float cs[4][kMaxExperts];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+    const int t = blockIdx.x * 4 + wv;
+    if (t >= T) return;
+    const float* l = logits + (size_t)t * E;
+    int id;
+    float wt;
+    if (E <= 64)
+        route_token_grouped<1>(l, bias, E, n_group, topk_group, k, scale, lane, cs[wv], &id, &wt);
+    else if (E <= 128)
+        route_token_grouped<2>(l, bias, E, n_group, topk_group, k, scale, lane, cs[wv], &id, &wt);
+    else if (E <= 256)
+        route_token_grouped<4>(l, bias, E, n_group, topk_group, k, scale, lane, cs[wv], &id, &wt);
+    else if (E <= 512)
+        route_token_grouped<8>(l, bias, E, n_group, topk_group, k, scale, lane, cs[wv], &id, &wt);
+    else
+        route_token_grouped<16>(l, bias, E, n_group, topk_group, k, scale, lane, cs[wv], &id,
+                                &wt);
     if (lane < k) {
         ids[(size_t)t * k + lane] = id;
         w[(size_t)t * k + lane] = wt;
@@ -374,6 +503,16 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
     const int grid = (T + tokens_per_block - 1) / tokens_per_block;
     hipLaunchKernelGGL(route_topk_kernel, dim3(grid), dim3(256), 0, stream, logits, T, E,
                        k, ids, w);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_grouped(const float* logits, const float* bias, int T, int E,
+                               int n_group, int topk_group, int k, float scale, int32_t* ids,
+                               float* w, hipStream_t stream) {
+    if (T == 0) return hipSuccess;
+    const int grid = (T + 3) / 4;
+    hipLaunchKernelGGL(route_grouped_kernel, dim3(grid), dim3(256), 0, stream, logits, bias, T,
+                       E, n_group, topk_group, k, scale, ids, w);
     return hipGetLastError();
 }
 

@@ -247,3 +247,25 @@ def test_forward_resplit_host_validation():
     assert resplit(ws_bytes=1024) == moe.MOE_FFN_ERR_WORKSPACE
     assert resplit(out=A + 0x40) == moe.MOE_FFN_ERR_ALIAS
     assert resplit(T=0) == moe.MOE_FFN_OK
+
+
+def test_route_grouped_host_validation():
+    L = moe.lib()
+
+    def call(T=4, E=256, ng=8, tg=4, k=8, lg=A, bias=None, ids=A + 0x100000, w=A + 0x200000):
+        return L.moe_route_grouped(lg, bias, T, E, ng, tg, k, 1.0, ids, w, None)
+
+    assert call(E=250) == moe.MOE_FFN_ERR_BAD_SHAPE          # groups do not divide E
+    assert call(ng=128, E=256) == moe.MOE_FFN_ERR_BAD_SHAPE   # more than 64 groups
+    assert call(tg=9) == moe.MOE_FFN_ERR_BAD_SHAPE
+    assert call(tg=0) == moe.MOE_FFN_ERR_BAD_SHAPE
+    assert call(tg=1, k=33) == moe.MOE_FFN_ERR_BAD_SHAPE      # more than one group holds
+    assert call(k=65, ng=1, tg=1) == moe.MOE_FFN_ERR_BAD_SHAPE
+    assert call(E=2048, ng=64) == moe.MOE_FFN_ERR_BAD_SHAPE
+    assert call(T=-1) == moe.MOE_FFN_ERR_BAD_SHAPE
+    assert call(T=0) == moe.MOE_FFN_OK
+    assert call(lg=None) == moe.MOE_FFN_ERR_NULL_ARG
+    assert call(bias=A + 0x300002) == moe.MOE_FFN_ERR_MISALIGNED
+    assert call(ids=A + 0x200010) == moe.MOE_FFN_ERR_ALIAS     # ids overlap w
+    assert call(ids=A + 0x40) == moe.MOE_FFN_ERR_ALIAS         # ids overlap logits
+    assert call(bias=A + 0x200000 - 512) == moe.MOE_FFN_ERR_ALIAS
