@@ -500,6 +500,21 @@ def main():
             torch.cuda.synchronize()
             per_layer[b["wl"].name]["us_route_then_layer"] = round(
                 e0.elapsed_time(e1) * 1e3 / reps, 1)
+            # the routers alone: the softmax gate, and (256 experts: DeepSeek-V3's
+            # grouping, 8 groups, 4 kept, scale 2.5) the grouped sigmoid gate
+            for key, route in (("us_route_topk", lambda: moe.moe_route_topk(
+                    b["lg"], b["wl"].k, topk_ids=rid, topk_w=rw, stream=stream)),
+                    ("us_route_grouped", lambda: moe.moe_route_grouped(
+                        b["lg"], b["wl"].k, 8, 4, scale=2.5, topk_ids=rid, topk_w=rw,
+                        stream=stream))):
+                if key == "us_route_grouped" and b["wl"].E != 256:
+                    continue
+                e0.record(stream)
+                for i in range(reps):
+                    route()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                per_layer[b["wl"].name][key] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
 
     # per-kernel durations from HIP events recorded on the launch stream
     # between the kernels of each call (stage 0 permute, 1 gate/up, 2 down,
