@@ -33,7 +33,6 @@ namespace moe {
 namespace {
 
 constexpr int kTileN = 128;                       // weight rows per block
-constexpr int kTileM = 128;                       // gathered rows per tile
 constexpr int kMaxLarge = 1024;                   // matches MOE_FFN_MAX_EXPERTS
 
 // An operand tile of one stage holds 128 rows of RW 16-byte words (K = 8 RW
@@ -74,9 +73,9 @@ struct TiledGemm {
 // (gate/up: the same rows of W_gate and W_up; down: kBlocks consecutive
 // 128-row blocks of W_down, so a tile covers 128 kBlocks output rows), waves
 // per workgroup arranged kWaveRows (along the weight rows) x kWaves /
-// kWaveRows (along the tokens), K per pipeline stage (32 or 64), stages in
-// flight, and resident workgroups per CU (LDS: kStages x (kBlocks + 1) x 128
-// rows x 2 kK bytes + 4 KB).
+// kWaveRows (along the tokens), gathered rows per tile (128 or 256), K per
+// pipeline stage (32 or 64), stages in flight, and resident workgroups per CU
+// (LDS: kStages x (128 kBlocks + kTokens) rows x 2 kK bytes + 4 KB).
 template <bool kDown>
 struct TileTuning;
 template <>
@@ -84,6 +83,7 @@ struct TileTuning<false> {
     static constexpr int kBlocks = 2;
     static constexpr int kWaves = 8;
     static constexpr int kWaveRows = 4;
+    static constexpr int kTokens = 128;
     static constexpr int kK = 32;
     static constexpr int kStages = 3;
     static constexpr int kBlocksPerCU = 2;
@@ -93,6 +93,7 @@ struct TileTuning<true> {
     static constexpr int kBlocks = 1;
     static constexpr int kWaves = 8;
     static constexpr int kWaveRows = 2;
+    static constexpr int kTokens = 128;
     static constexpr int kK = 32;
     static constexpr int kStages = 3;
     static constexpr int kBlocksPerCU = 3;
@@ -111,18 +112,25 @@ void expert_tile_kernel(const TiledGemm g) {
     constexpr int S = Tu::kStages;
     constexpr int kRows = kDown ? kTileN * NMAT : kTileN;   // output rows per tile
     static_assert(kDown || NMAT == 2, "gate/up tiles hold W_gate and W_up");
-    static_assert((W == 4 || W == 8) && W % WR == 0, "waves per workgroup");
+    constexpr int M = Tu::kTokens;                // gathered rows per tile
+    static_assert((W == 4 || W == 8 || W == 16) && W % WR == 0, "waves per workgroup");
     static_assert((KS == 32 || KS == 64) && S >= 2, "stage shape");
+    static_assert(M == 128 || M == 256, "tokens per tile");
     constexpr int RW = KS / 8;                    // 16-byte words of a row per stage
-    constexpr int kOperandWords = 128 * RW;       // one 128-row operand tile
+    constexpr int kOperandWords = 128 * RW;       // one 128-row weight block
     constexpr int RPI = kWave / RW;               // rows per staging load instruction
-    constexpr int IL = 128 / RPI / W;             // staging loads per wave and operand
+    // a stage's rows (NMAT weight blocks, then the M token rows) are staged
+    // by NCH load instructions of RPI rows each, IL per wave
+    constexpr int WCH = 128 / RPI;
+    constexpr int NCH = NMAT * WCH + M / RPI;
+    static_assert(NCH % W == 0, "whole staging loads per wave");
+    constexpr int IL = NCH / W;
     constexpr int RPW = kTileN / WR;              // weight rows per wave
-    constexpr int TPW = kTileM / (W / WR);        // tokens per wave
+    constexpr int TPW = M / (W / WR);             // tokens per wave
     constexpr int RB = RPW / 16;                  // 16-row blocks per wave
     constexpr int TB = TPW / 16;                  // 16-token blocks per wave
-    constexpr int kStageWords = (NMAT + 1) * kOperandWords;
-    constexpr int kLoads = IL * (NMAT + 1);       // load instructions per wave and stage
+    constexpr int kStageWords = (NMAT * 128 + M) * RW;
+    constexpr int kLoads = IL;                    // load instructions per wave and stage
     __shared__ u32x4 lds[S * kStageWords];
     __shared__ int pre[kMaxLarge + 1];
 
@@ -139,14 +147,14 @@ void expert_tile_kernel(const TiledGemm g) {
         int cnt = 0;
         for (int a = a0; a < a1; ++a) {
             const int e = g.large[a];
-            cnt += rt_n * ((g.offsets[e + 1] - g.offsets[e] + kTileM - 1) / kTileM);
+            cnt += rt_n * ((g.offsets[e + 1] - g.offsets[e] + M - 1) / M);
         }
         const int inc = wave_prefix_sum_i32(cnt);
         int b = inc - cnt;
         for (int a = a0; a < a1; ++a) {
             pre[a] = b;
             const int e = g.large[a];
-            b += rt_n * ((g.offsets[e + 1] - g.offsets[e] + kTileM - 1) / kTileM);
+            b += rt_n * ((g.offsets[e + 1] - g.offsets[e] + M - 1) / M);
         }
         if (lane == kWave - 1) pre[n_large] = inc;
     }
@@ -185,29 +193,31 @@ void expert_tile_kernel(const TiledGemm g) {
         const int e = g.large[lo];
         const int beg = g.offsets[e];
         const int m = g.offsets[e + 1] - beg;
-        const int mt_n = (m + kTileM - 1) / kTileM;
+        const int mt_n = (m + M - 1) / M;
         const int r = q - pre[lo];
         const int rt = r / mt_n;
         const int row0 = rt * kRows;
-        const int p0 = (r - rt * mt_n) * kTileM;
+        const int p0 = (r - rt * mt_n) * M;
 
         // per-lane source rows of the staging loads (rows past the matrix or
         // past the expert's tokens repeat a valid row; their results are
         // never stored)
-        const uint16_t* wsrc[NMAT][IL];
-        const uint16_t* bsrc[IL];
+        const uint16_t* src[IL];
 #pragma unroll
         for (int i = 0; i < IL; ++i) {
-            const int rr = RPI * (wave + W * i) + lane / RW;
-#pragma unroll
-            for (int mm = 0; mm < NMAT; ++mm) {
+            const int q = wave + W * i;               // this load's RPI rows of the stage
+            if (q < NMAT * WCH) {
+                const int mm = q / WCH;
+                const int rr = RPI * (q - mm * WCH) + lane / RW;
                 const int row = kDown ? row0 + kTileN * mm + rr : row0 + rr;
                 const size_t wrow = (size_t)e * g.N + min(row, g.N - 1);
-                wsrc[mm][i] = (kDown || mm == 0 ? g.w0 : g.w1) + wrow * g.K + cl * 8;
+                src[i] = (kDown || mm == 0 ? g.w0 : g.w1) + wrow * g.K + cl * 8;
+            } else {
+                const int rr = RPI * (q - NMAT * WCH) + lane / RW;
+                const int pp = beg + min(p0 + rr, m - 1);
+                const int brow = kDown ? pp : g.sorted_slot[pp] / g.top_k;
+                src[i] = g.b_src + (size_t)brow * g.b_pitch + cl * 8;
             }
-            const int pp = beg + min(p0 + rr, m - 1);
-            const int brow = kDown ? pp : g.sorted_slot[pp] / g.top_k;
-            bsrc[i] = g.b_src + (size_t)brow * g.b_pitch + cl * 8;
         }
         auto issue = [&](int s) {
             u32x4* buf = lds + (s % S) * kStageWords;
@@ -216,17 +226,10 @@ void expert_tile_kernel(const TiledGemm g) {
             // never used)
             if (KS > 32 && k0 + 8 * cl >= g.K) k0 -= 32;
 #pragma unroll
-            for (int i = 0; i < IL; ++i) {
-                const int dst = (wave + W * i) * kWave;
-#pragma unroll
-                for (int mm = 0; mm < NMAT; ++mm)
-                    __builtin_amdgcn_global_load_lds((const void*)(wsrc[mm][i] + k0),
-                                                     (lds_void_ptr)&buf[mm * kOperandWords + dst],
-                                                     16, 0, 0);
-                __builtin_amdgcn_global_load_lds((const void*)(bsrc[i] + k0),
-                                                 (lds_void_ptr)&buf[NMAT * kOperandWords + dst],
+            for (int i = 0; i < IL; ++i)
+                __builtin_amdgcn_global_load_lds((const void*)(src[i] + k0),
+                                                 (lds_void_ptr)&buf[(wave + W * i) * kWave],
                                                  16, 0, 0);
-            }
         };
 
         f32x4 acc[NMAT][RB][TB];
