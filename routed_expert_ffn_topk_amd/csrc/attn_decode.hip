@@ -238,19 +238,25 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(
 }
 
 // Merge of the splits of one query head: out = sum_s O_s e^(M_s - M) /
-// sum_s L_s e^(M_s - M), M = max_s M_s; an empty sequence gives zeros.  The
-// block's threads take the max over the splits together, then each sums
-// its head-dimension element over a subset of the splits (256 / d subsets),
-// merged through LDS.
+// sum_s L_s e^(M_s - M), M = max_s M_s; an empty sequence gives zeros.  A
+// block takes `cols` head-dimension elements of one query head (the whole
+// head, or 32 of them when there are many splits): its threads take the max
+// over the splits together, then each sums one element over a subset of the
+// splits (256 / cols subsets), merged through LDS.  Column blocks keep each
+// thread's chain of split loads short when a long sequence has many splits;
+// with few splits whole heads avoid recomputing the max per block.
 constexpr int kMergeThreads = 256;
+constexpr int kMergeManySplits = 64;
 
 __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
     const int32_t* __restrict__ lens, int h_q, int h_kv, int d, int max_len, int chunk,
-    int n_split, uint16_t* __restrict__ out) {
+    int n_split, int cols, uint16_t* __restrict__ out) {
     __shared__ float red[kMergeThreads];
     __shared__ float red_l[kMergeThreads];
-    const int h = blockIdx.x;
+    const int ncb = d / cols;                     // column blocks per head
+    const int h = blockIdx.x / ncb;
+    const int c0 = (blockIdx.x - h * ncb) * cols;
     const int b = blockIdx.y;
     const int tid = threadIdx.x;
     const int g = h_q / h_kv;
@@ -258,7 +264,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(
     const int n_valid = (min(max(lens[b], 0), max_len) + chunk - 1) / chunk;
     uint16_t* o_row = out + ((size_t)b * h_q + h) * d;
     if (n_valid == 0) {
-        if (tid < d) o_row[tid] = 0;
+        if (tid < cols) o_row[c0 + tid] = 0;
         return;
     }
     const size_t base = ((size_t)b * h_kv + j) * n_split * 16 + qq;
@@ -273,8 +279,8 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(
     }
     const float M = red[0];
     __syncthreads();
-    const int nsub = kMergeThreads / d;
-    const int sub = tid / d, c = tid - sub * d;
+    const int nsub = kMergeThreads / cols;
+    const int sub = tid / cols, c = c0 + (tid - sub * cols);
     float o = 0.0f, L = 0.0f;
     if (sub < nsub) {
         // eight splits per round, their loads issued together
@@ -308,8 +314,8 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(
     __syncthreads();
     if (sub == 0) {
         for (int k2 = 1; k2 < nsub; ++k2) {
-            o += red[k2 * d + c];
-            L += red_l[k2 * d + c];
+            o += red[k2 * cols + tid];
+            L += red_l[k2 * cols + tid];
         }
         o_row[c] = f32_to_bf16_bits(o / L);
     }
@@ -317,14 +323,16 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(
 
 }  // namespace
 
-// Positions per split: a power of two from 128 up, so that a launch has
-// about 2048 workgroups (eight per CU of a 256-CU MI355X; the partial results
-// stay small next to the KV bytes), at most 8192.  (4096 workgroups measured
-// no better, also with ragged lengths.)
+// Positions per split: a power of two from 256 up, so that a launch has
+// about 1024 workgroups (four per CU of a 256-CU MI355X; the partial results
+// stay small next to the KV bytes), at most 8192.  (Measured: about 2048
+// workgroups from 128 positions up were 1-4 % slower on long batches and
+// ragged lengths and 12 % slower on one long sequence, where each workgroup
+// then held a single tile per wave; 4096 no better.)
 int attn_chunk(int B, int h_kv, int max_len) {
     const long long positions = (long long)B * h_kv * max_len;
-    int chunk = kTilePos * kAttnWaves;
-    while (chunk < 8192 && positions / chunk > 2048) chunk *= 2;
+    int chunk = 2 * kTilePos * kAttnWaves;
+    while (chunk < 8192 && positions / chunk > 1024) chunk *= 2;
     return chunk;
 }
 
@@ -371,8 +379,10 @@ hipError_t launch_attn_decode(const uint16_t* q, const uint16_t* k, const uint16
     }
     hipError_t err = ev.mark(0, stream);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(attn_merge_kernel, dim3(h_q, B), dim3(kMergeThreads), 0, stream, part_o,
-                       part_ml, lens, h_q, h_kv, d, max_len, chunk, n_split, out);
+    const int cols = n_split >= kMergeManySplits ? 32 : d;
+    hipLaunchKernelGGL(attn_merge_kernel, dim3(h_q * (d / cols), B), dim3(kMergeThreads), 0,
+                       stream, part_o, part_ml, lens, h_q, h_kv, d, max_len, chunk, n_split,
+                       cols, out);
     err = hipGetLastError();
     return err == hipSuccess ? ev.mark(1, stream) : err;
 }
