@@ -267,7 +267,7 @@ struct Int4Weights {
     // instructions per group pair of the gate/up loop, 2-5 % faster layers)
     __device__ static uint32_t and_or(uint32_t x, uint32_t m, uint32_t b) {
         uint32_t r;
-        asm volatile("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(m), "v"(b));
+        asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(m), "v"(b));
         return r;
     }
     __device__ static u32x4 nibbles_to_bf16(uint32_t w) {
