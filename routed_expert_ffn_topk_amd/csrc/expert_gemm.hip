@@ -1,6 +1,6 @@
 // Routed-expert FFN kernels: the grouped expert product (gate/up with the
-// SiLU*up epilogue, and down), for BF16 and INT8 weights, and the weighted
-// combine.
+// SiLU*up epilogue, and down) for BF16, INT8, INT4 and residual-split INT4
+// weights, and the weighted combine.
 //
 // HiNa-MoE §4.1 (FFN equation, Fig. 5): each expert multiplies the small
 // matrix of its gathered tokens by W_gate and W_up, applies SiLU to the gate
@@ -12,9 +12,12 @@
 // row-major.  §4.2.1: BF16 operands, FP32 accumulation; the matrix unit is
 // used for every token count (16-column tiles padded with a real token row),
 // never a vector fallback.  §4.2.2: weights are streamed once, with no reuse.
-// §8.1 / Fig. 11: symmetric group-wise INT8 weights, dequantised in registers.
+// §8.1 / Fig. 11: symmetric group-wise INT8 weights, dequantised in registers;
+// INT4 the same way.  RapidMoE ("Residual-Split Representation"): INT4 W^Q
+// plus an INT4 residual W^R for the gate/up of critical experts, chosen per
+// expert within one launch.
 //
-// One kernel skeleton serves both projections and both weight formats.  Work
+// One kernel skeleton serves both projections and all weight formats.  Work
 // unit: a row block (16 output rows of one active expert, all its tokens).
 // The four waves of a workgroup form R row blocks x S K-parts (R * S = 4); a
 // round is R row blocks of one expert.  S is chosen on the device from the
