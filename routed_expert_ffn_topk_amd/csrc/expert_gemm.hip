@@ -265,18 +265,10 @@ struct Int4Weights {
                 d.s[i][m] = src.s[m][(size_t)(u + i) * src.spitch];
             }
     }
-    // (x & m) | b in one instruction: written out because the compiler emits
-    // the shifted forms below as shift, AND and OR (146 -> 115 VALU
-    // instructions per group pair of the gate/up loop, 2-5 % faster layers)
-    __device__ static uint32_t and_or(uint32_t x, uint32_t m, uint32_t b) {
-        uint32_t r;
-        asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(m), "v"(b));
-        return r;
-    }
     __device__ static u32x4 nibbles_to_bf16(uint32_t w) {
-        const uint32_t kMask = 0x000F000Fu, kBias = 0x43004300u;
-        return u32x4{and_or(w, kMask, kBias), and_or(w >> 4, kMask, kBias),
-                     and_or(w >> 8, kMask, kBias), and_or(w >> 12, kMask, kBias)};
+        constexpr uint32_t kMask = 0x000F000Fu, kBias = 0x43004300u;
+        return u32x4{(w & kMask) | kBias, ((w >> 4) & kMask) | kBias,
+                     ((w >> 8) & kMask) | kBias, ((w >> 12) & kMask) | kBias};
     }
     // token values (x0..x7) -> (x0, x4, x1, x5, x2, x6, x3, x7)
     __device__ static u32x4 interleave(u32x4 b) {
