@@ -61,6 +61,7 @@ def run_and_check(case, what):
     (517, 288, 256, 3, 2),     # ~345 tokens/expert: three token tiles, ragged; K = 288
     (129, 32, 32, 1, 1),       # K = 32 (one stage), N = 32 (a quarter row tile)
     (400, 64, 1024, 2, 2),     # long down K, short gate/up K
+    (1000, 96, 160, 2, 1),     # 500 tokens/expert: the register-staged gate/up; N = 160
 ])
 def test_tiled_layer_matches_oracle(T, H, I, E, k):
     need_gpu()
