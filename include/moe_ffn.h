@@ -79,8 +79,15 @@ extern "C" {
  *   h           bf16[S][I] SiLU(gate)*up of each gathered row, in
  *                          sorted_slot order (row p belongs to slot
  *                          sorted_slot[p])
- *   y           f32[S][H]  down-projection output of each slot, slot order
+ *   y           f32[P][S][H] down-projection output of each slot, slot
+ *                          order, P = y_parts.  With P > 1 (BF16 batches with
+ *                          few tiles of many tokens per expert: the K of the
+ *                          down product is split into P parts) the slots of
+ *                          experts listed in `large` hold partial sums in
+ *                          every plane, whose sum is their output; every other
+ *                          slot holds its output in plane 0.
  * After a forward call the regions hold these values (tests inspect them).
+ * y_parts is a count, not an offset; it depends on the sizes alone.
  */
 typedef struct moe_ffn_ws_layout {
     size_t total_bytes;
@@ -92,6 +99,7 @@ typedef struct moe_ffn_ws_layout {
     size_t sorted_slot;
     size_t h;
     size_t y;
+    size_t y_parts;
 } moe_ffn_ws_layout;
 
 /* Fill *layout for the given sizes.  Pure host computation (no HIP call).

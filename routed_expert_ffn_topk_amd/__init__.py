@@ -29,7 +29,7 @@ MOE_FFN_MAX_EXPERTS = 1024
 MOE_FFN_INT8_GROUP = 128
 
 LAYOUT_FIELDS = ("total_bytes", "meta", "counts", "offsets", "active", "large", "sorted_slot",
-                 "h", "y")
+                 "h", "y", "y_parts")
 
 
 class MoeFfnError(RuntimeError):

@@ -760,12 +760,17 @@ void expert_gemm_kernel(const ExpertGemm g) {
 // Combine: out[t][c] = bf16( sum_{j ascending} w[t][j] * y[t*k + j][c] ),
 // skipping slots whose expert id is out of range.  Eight columns per thread;
 // the transposed [row x token] tiles of the down kernel are already stored
-// token-major in y, so this writes plain row-major rows.
+// token-major in y, so this writes plain row-major rows.  The slots of
+// experts with more than large_min tokens have their y in `parts` planes of
+// K-part partial sums (the tiled down product), added first in plane order.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
                                                       const int32_t* __restrict__ ids,
                                                       const float* __restrict__ w,
                                                       uint16_t* __restrict__ out, int T,
-                                                      int H, int k, int E) {
+                                                      int H, int k, int E,
+                                                      const int32_t* __restrict__ counts,
+                                                      int large_min, int parts,
+                                                      size_t plane) {
     const int chunks = H / 8;
     const int idx = blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= T * chunks) return;
@@ -777,8 +782,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         const int e = ids[slot];
         if (e < 0 || e >= E) continue;
         const float wj = w[slot];
-        const f32x4 a = *reinterpret_cast<const f32x4*>(y + (size_t)slot * H + c);
-        const f32x4 b = *reinterpret_cast<const f32x4*>(y + (size_t)slot * H + c + 4);
+        const float* yp = y + (size_t)slot * H + c;
+        f32x4 a = *reinterpret_cast<const f32x4*>(yp);
+        f32x4 b = *reinterpret_cast<const f32x4*>(yp + 4);
+        if (parts > 1 && counts[e] > large_min)
+            for (int pt = 1; pt < parts; ++pt) {
+                a += *reinterpret_cast<const f32x4*>(yp + pt * plane);
+                b += *reinterpret_cast<const f32x4*>(yp + pt * plane + 4);
+            }
         acc[0] += wj * a.x; acc[1] += wj * a.y; acc[2] += wj * a.z; acc[3] += wj * a.w;
         acc[4] += wj * b.x; acc[5] += wj * b.y; acc[6] += wj * b.z; acc[7] += wj * b.w;
     }
@@ -875,7 +886,9 @@ hipError_t launch_ffn(const uint16_t* x, const Routing& route, const FfnWeights&
     if (err == hipSuccess && tiled) err = launch_tiled_down(W, s, ws, num_cu, stream);
     if (err == hipSuccess) err = ev.mark(2, stream);
     if (err != hipSuccess) return err;
-    err = launch_combine(ws.y, route.ids, route.w, out, s, stream);
+    err = launch_combine(ws.y, route.ids, route.w, out, s, ws.counts, m_split,
+                         tiled ? tiled_down_parts(s.T, s.H, s.I, s.E, s.k) : 1,
+                         (size_t)s.T * s.k * s.H, stream);
     if (err == hipSuccess) err = ev.mark(3, stream);
     return err;
 }
@@ -883,11 +896,12 @@ hipError_t launch_ffn(const uint16_t* x, const Routing& route, const FfnWeights&
 }  // namespace
 
 hipError_t launch_combine(const float* y, const int32_t* ids, const float* w,
-                          uint16_t* out, const FfnShape& s, hipStream_t stream) {
+                          uint16_t* out, const FfnShape& s, const int32_t* counts,
+                          int large_min, int parts, size_t plane, hipStream_t stream) {
     const int64_t n = (int64_t)s.T * (s.H / 8);
     const int grid = (int)((n + 255) / 256);
     hipLaunchKernelGGL(combine_kernel, dim3(grid), dim3(256), 0, stream, y, ids, w, out,
-                       s.T, s.H, s.k, s.E);
+                       s.T, s.H, s.k, s.E, counts, large_min, parts, plane);
     return hipGetLastError();
 }
 

@@ -25,6 +25,8 @@
 // small-m product's rounds (a contiguous slice per XCD, interleaved over its
 // workgroups): the token tiles that share a weight tile run at the same time
 // on one XCD, so the weight tile comes from HBM once and from L2 after that.
+#include <cmath>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -63,10 +65,13 @@ struct TiledGemm {
     const int32_t* large;
     const int32_t* sorted_slot;
     uint16_t* h;              // gate/up output, row p at p * N
-    float* y;                 // down output, slot s at s * N
+    float* y;                 // down output, slot s at s * N (+ y_plane per K part)
+    size_t y_plane;           // floats between the partial sums of two K parts
     int b_pitch;              // elements between B rows
     int N, K;
     int top_k;
+    int k_parts;              // K parts per tile (down; 1 for gate/up)
+    int part_stages;          // K stages of a part (the last part may have fewer)
 };
 
 // Per product (gate/up, down): weight blocks of 128 rows per tile
@@ -168,14 +173,14 @@ void expert_tile_kernel(const TiledGemm g) {
         int cnt = 0;
         for (int a = a0; a < a1; ++a) {
             const int e = g.large[a];
-            cnt += rt_n * ((g.offsets[e + 1] - g.offsets[e] + M - 1) / M);
+            cnt += rt_n * g.k_parts * ((g.offsets[e + 1] - g.offsets[e] + M - 1) / M);
         }
         const int inc = wave_prefix_sum_i32(cnt);
         int b = inc - cnt;
         for (int a = a0; a < a1; ++a) {
             pre[a] = b;
             const int e = g.large[a];
-            b += rt_n * ((g.offsets[e + 1] - g.offsets[e] + M - 1) / M);
+            b += rt_n * g.k_parts * ((g.offsets[e + 1] - g.offsets[e] + M - 1) / M);
         }
         if (lane == kWave - 1) pre[n_large] = inc;
     }
@@ -200,7 +205,7 @@ void expert_tile_kernel(const TiledGemm g) {
     const int cl = (lane % RW) ^ row_swizzle<RW>(lane / RW);
     // stages; K is a multiple of 32, so with 64 per stage the last one may
     // hold only its first half
-    const int nk = (g.K + KS - 1) / KS;
+    const int nk_all = (g.K + KS - 1) / KS;
 
     for (int q = qb + li; q < qe; q += per) {
         int lo = 0, hi = n_large - 1;                 // last a with pre[a] <= q
@@ -215,10 +220,19 @@ void expert_tile_kernel(const TiledGemm g) {
         const int beg = g.offsets[e];
         const int m = g.offsets[e + 1] - beg;
         const int mt_n = (m + M - 1) / M;
+        // tiles of an expert: (row tile, K part, token tile), token tiles
+        // fastest
         const int r = q - pre[lo];
-        const int rt = r / mt_n;
+        const int rt = r / (g.k_parts * mt_n);
+        const int r2 = r - rt * g.k_parts * mt_n;
+        const int kp = r2 / mt_n;
         const int row0 = rt * kRows;
-        const int p0 = (r - rt * mt_n) * M;
+        const int p0 = (r2 - kp * mt_n) * M;
+        // this part's stages, and the K left from its first (the last stage
+        // of the last part may be a half stage)
+        const int s0 = kp * g.part_stages;
+        const int nk = min(nk_all, s0 + g.part_stages) - s0;
+        const int kl = g.K - s0 * KS;
 
         // per-lane source rows of the staging loads (rows past the matrix or
         // past the expert's tokens repeat a valid row; their results are
@@ -232,18 +246,18 @@ void expert_tile_kernel(const TiledGemm g) {
                 const int rr = RPI * (q - mm * WCH) + lane / RW;
                 const int row = kDown ? row0 + kTileN * mm + rr : row0 + rr;
                 const size_t wrow = (size_t)e * g.N + min(row, g.N - 1);
-                src[i] = (kDown || mm == 0 ? g.w0 : g.w1) + wrow * g.K + cl * 8;
+                src[i] = (kDown || mm == 0 ? g.w0 : g.w1) + wrow * g.K + s0 * KS + cl * 8;
             } else {
                 const int rr = RPI * (q - NMAT * WCH) + lane / RW;
                 const int pp = beg + min(p0 + rr, m - 1);
                 const int brow = kDown ? pp : g.sorted_slot[pp] / g.top_k;
-                src[i] = g.b_src + (size_t)brow * g.b_pitch + cl * 8;
+                src[i] = g.b_src + (size_t)brow * g.b_pitch + s0 * KS + cl * 8;
             }
         }
         u32x4 rg[IL];
         auto load_regs = [&](int s) {
             int k0 = s * KS;
-            if (KS > 32 && k0 + 8 * cl >= g.K) k0 -= 32;
+            if (KS > 32 && k0 + 8 * cl >= kl) k0 -= 32;
 #pragma unroll
             for (int i = 0; i < IL; ++i) rg[i] = load16(src[i] + k0);
         };
@@ -257,7 +271,7 @@ void expert_tile_kernel(const TiledGemm g) {
             int k0 = s * KS;
             // the second half of a half stage re-reads the first (in bounds;
             // never used)
-            if (KS > 32 && k0 + 8 * cl >= g.K) k0 -= 32;
+            if (KS > 32 && k0 + 8 * cl >= kl) k0 -= 32;
 #pragma unroll
             for (int i = 0; i < IL; ++i)
                 __builtin_amdgcn_global_load_lds((const void*)(src[i] + k0),
@@ -306,7 +320,7 @@ void expert_tile_kernel(const TiledGemm g) {
             const u32x4* buf = lds + (s % S) * kStageWords;
 #pragma unroll
             for (int j = 0; j < KS / 32; ++j) {
-                if (j > 0 && s * KS + 32 * j >= g.K) break;      // half stage
+                if (j > 0 && s * KS + 32 * j >= kl) break;       // half stage
                 u32x4 af[NMAT][RB];
 #pragma unroll
                 for (int mm = 0; mm < NMAT; ++mm)
@@ -337,7 +351,7 @@ void expert_tile_kernel(const TiledGemm g) {
             const int p = p0 + TPW * wm + 16 * tb + col;
             if (p >= m) continue;
             if constexpr (kDown) {
-                float* yrow = g.y + (size_t)g.sorted_slot[beg + p] * g.N;
+                float* yrow = g.y + kp * g.y_plane + (size_t)g.sorted_slot[beg + p] * g.N;
 #pragma unroll
                 for (int mm = 0; mm < NMAT; ++mm)
 #pragma unroll
@@ -372,6 +386,16 @@ hipError_t launch_tile(const TiledGemm& g, int num_cu, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Workgroup slots of a full GPU for the down product, for the choice of its
+// K parts (a function of the sizes alone, since the workspace is sized from
+// them): 256 CUs at the down configuration's residency.
+constexpr int kNominalCUs = 256;
+constexpr int kMaxDownParts = 4;
+// nominal rates for the choice: the down product's (TFLOP/s) and HBM's for
+// the partial sums (TB/s, a write and a read)
+constexpr double kNominalTflops = 600.0;
+constexpr double kNominalTBs = 5.0;
+
 // Average tokens per expert from which gate/up takes the register-staged
 // configuration (measured: +9 % at 512 per expert, Mixtral-8x7B; -5 to +2 %
 // at 128, the Qwen3-235B and DeepSeek-V3 shapes).
@@ -394,6 +418,8 @@ hipError_t launch_tiled_gate_up(const uint16_t* x, const FfnWeights& W, const Ff
     g.N = s.I;
     g.K = s.H;
     g.top_k = s.k;
+    g.k_parts = 1;
+    g.part_stages = 1 << 30;
     const long long per_expert = (long long)s.T * s.k / s.E;
     return per_expert >= kRegStageMinTokens ? launch_tile<kGateUpReg>(g, num_cu, stream)
                                             : launch_tile<kGateUpLds>(g, num_cu, stream);
@@ -409,11 +435,49 @@ hipError_t launch_tiled_down(const FfnWeights& W, const FfnShape& s, const Works
     g.large = ws.large;
     g.sorted_slot = ws.sorted_slot;
     g.y = ws.y;
+    g.y_plane = (size_t)s.T * s.k * s.H;
     g.b_pitch = s.I;
     g.N = s.H;
     g.K = s.I;
     g.top_k = s.k;
+    g.k_parts = tiled_down_parts(s.T, s.H, s.I, s.E, s.k);
+    const int nk = (s.I + TileTuning<kDownLds>::kK - 1) / TileTuning<kDownLds>::kK;
+    g.part_stages = (nk + g.k_parts - 1) / g.k_parts;
     return launch_tile<kDownLds>(g, num_cu, stream);
+}
+
+// The down product's tiles are long (K = I) and few when a batch has few
+// experts (Mixtral-8x7B: 32 row tiles x ~36 token tiles at 2048 tokens,
+// against 768 resident workgroups): the last round of tiles leaves much of
+// the GPU idle.  Splitting K into parts multiplies the tiles; each part
+// writes its own FP32 partial sums of y, which the combine adds.  The part
+// count is chosen from the expected tile count (token tiles: T k / 128, plus
+// half a tile of padding per expert with more than 32 tokens): the rounds of
+// tiles it needs, in units of one round of full-K tiles at the product's
+// nominal rate, plus the time to write and read back each extra plane of
+// partial sums at a nominal HBM rate.
+int tiled_down_parts(int64_t T, int64_t H, int64_t I, int E, int k) {
+    if (T <= kTiledMinBatch) return 1;
+    const int64_t slots = T * k;
+    const int64_t large = slots / (kTiledMinTokens + 1) < E ? slots / (kTiledMinTokens + 1) : E;
+    const double tiles = (double)((H + kTileN - 1) / kTileN) *
+                         ((double)slots / TileTuning<kDownLds>::kTokens + 0.5 * (double)large);
+    const double wg = (double)kNominalCUs * TileTuning<kDownLds>::kBlocksPerCU;
+    const double round_us = wg * 2.0 * kTileN * TileTuning<kDownLds>::kTokens * (double)I /
+                            (kNominalTflops * 1e6);
+    const double plane_us = (double)slots * (double)H * 8.0 / (kNominalTBs * 1e6);
+    const int64_t nk = (I + TileTuning<kDownLds>::kK - 1) / TileTuning<kDownLds>::kK;
+    int best = 1;
+    double best_cost = 1e300;
+    for (int P = 1; P <= kMaxDownParts && P <= nk; P *= 2) {
+        if ((P - 1) * ((nk + P - 1) / P) >= nk) break;    // a part would be empty
+        const double cost = std::ceil(tiles * P / wg) / P * round_us + (P - 1) * plane_us;
+        if (cost < best_cost * (1.0 - 1e-9)) {
+            best = P;
+            best_cost = cost;
+        }
+    }
+    return best;
 }
 
 }  // namespace moe

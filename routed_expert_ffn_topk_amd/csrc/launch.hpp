@@ -117,9 +117,17 @@ hipError_t launch_tiled_down(const FfnWeights& W, const FfnShape& s, const Works
 constexpr int kTiledMinBatch = 64;
 constexpr int kTiledMinTokens = 32;
 
-// Weighted combine shared by both weight formats.
+// K parts of the tiled down product for these sizes (1, 2 or 4; a pure host
+// function): y holds this many planes of partial sums, [part][slot][H], of
+// which the slots of tiled experts fill every plane, the others the first.
+int tiled_down_parts(int64_t T, int64_t H, int64_t I, int E, int k);
+
+// Weighted combine shared by every weight format: y plane 0, plus planes 1 ..
+// parts - 1 (plane floats apart) for slots whose expert has more than
+// large_min tokens (counts).
 hipError_t launch_combine(const float* y, const int32_t* ids, const float* w,
-                          uint16_t* out, const FfnShape& s, hipStream_t stream);
+                          uint16_t* out, const FfnShape& s, const int32_t* counts,
+                          int large_min, int parts, size_t plane, hipStream_t stream);
 
 // Decode attention with grouped-query heads: workspace bytes, and the split
 // kernel + merge kernel on the caller's stream (sizes validated by the C ABI).

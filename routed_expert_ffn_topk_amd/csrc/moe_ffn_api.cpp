@@ -133,7 +133,8 @@ int moe_ffn_workspace_layout(int64_t T, int64_t H, int64_t I, int32_t E, int32_t
     layout->h = off;
     off += round_up(S * (size_t)I * sizeof(uint16_t));
     layout->y = off;
-    off += round_up(S * (size_t)H * sizeof(float));
+    layout->y_parts = (size_t)moe::tiled_down_parts(T, H, I, E, top_k);
+    off += round_up(layout->y_parts * S * (size_t)H * sizeof(float));
     layout->total_bytes = off;
     return MOE_FFN_OK;
 }

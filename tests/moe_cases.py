@@ -184,4 +184,7 @@ def read_workspace(ws: torch.Tensor, L: dict, T: int, H: int, I: int, E: int, k:
         "sorted_slot": i32(L["sorted_slot"], S),
         "h": b[L["h"]:L["h"] + S * I * 2].view(np.uint16).reshape(S, I).copy(),
         "y": b[L["y"]:L["y"] + S * H * 4].view(np.float32).reshape(S, H).copy(),
+        # every K-part plane of y (the tiled down product's partial sums)
+        "y_planes": b[L["y"]:L["y"] + L["y_parts"] * S * H * 4].view(np.float32)
+        .reshape(L["y_parts"], S, H).copy(),
     }

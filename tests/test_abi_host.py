@@ -48,7 +48,7 @@ def test_workspace_layout_regions_fit_and_align():
     regions = [("meta", 8 * 4), ("counts", E * 4), ("offsets", (E + 1) * 4),
                ("active", E * 4), ("large", E * 4), ("sorted_slot", T * k * 4),
                ("h", T * k * I * 2),
-               ("y", T * k * H * 4)]
+               ("y", L["y_parts"] * T * k * H * 4)]
     end = 0
     for name, size in regions:
         assert L[name] % 256 == 0
@@ -56,6 +56,23 @@ def test_workspace_layout_regions_fit_and_align():
         end = L[name] + size
     assert L["total_bytes"] >= end and L["total_bytes"] % 256 == 0
     assert moe.moe_ffn_workspace_bytes(T, H, I, E, k) == L["total_bytes"]
+
+
+def test_down_k_parts():
+    """y holds one plane per K part of the tiled down product: one for batches
+    of at most 64 tokens (no tiled product) and for shapes with many tiles
+    (Qwen3-235B, DeepSeek-V3 at 2048 / 4096 tokens), more for few long tiles
+    (Mixtral-8x7B prefill); the tiled parity cases run 1, 2 and 4 parts."""
+    parts = lambda *a: moe.moe_ffn_workspace_layout(*a)["y_parts"]  # noqa: E731
+    assert parts(64, 4096, 14336, 8, 2) == 1
+    assert parts(2048, 4096, 1536, 128, 8) == 1
+    assert parts(4096, 7168, 2048, 256, 8) == 1
+    assert parts(2048, 4096, 14336, 8, 2) == 2
+    assert parts(512, 4096, 14336, 8, 2) == 2
+    assert {parts(129, 32, 32, 1, 1), parts(1000, 96, 160, 2, 1),
+            parts(400, 64, 1024, 2, 2)} == {1, 2, 4}
+    # never more parts than K stages of 32
+    assert parts(65, 4096, 32, 8, 2) == 1 and parts(65, 4096, 64, 8, 2) <= 2
 
 
 @pytest.mark.parametrize("args", [(-1, 64, 64, 8, 2), (4, 0, 64, 8, 2), (4, 64, 64, 0, 1),

@@ -51,6 +51,13 @@ def run_and_check(case, what):
     keep &= case.ids.reshape(-1) < case.E
     assert (h[keep] == ref["h"][keep]).mean() >= 0.99
     assert_close_scaled(h[keep], ref["h"][keep], 1e-2, what="h")
+    # y of every slot: the sum of the K-part planes for tiled experts, plane 0
+    # for the others
+    flat = case.ids.reshape(-1)
+    tiled = np.zeros(flat.shape, bool)
+    tiled[keep] = r["counts"][flat[keep]] > 32
+    y = np.where(tiled[:, None], r["y_planes"].sum(0, dtype=np.float64), r["y_planes"][0])
+    assert_close_scaled(y[keep], ref["y"][keep], 1e-2, what="y")
     return r
 
 
@@ -68,6 +75,7 @@ def test_tiled_layer_matches_oracle(T, H, I, E, k):
     case = random_case(T * 7 + H + I + E, T, H, I, E, k, std=0.08)
     r = run_and_check(case, f"tiled T={T} H={H} I={I} E={E} k={k}")
     assert r["n_large"] >= 1
+
 
 
 def test_tiled_and_small_experts_in_one_call():
