@@ -763,6 +763,8 @@ void expert_gemm_kernel(const ExpertGemm g) {
 // token-major in y, so this writes plain row-major rows.  The slots of
 // experts with more than large_min tokens have their y in `parts` planes of
 // K-part partial sums (the tiled down product), added first in plane order.
+constexpr int kCombineBatch = 8;   // slots whose loads a thread issues together
+
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
                                                       const int32_t* __restrict__ ids,
                                                       const float* __restrict__ w,
@@ -777,21 +779,36 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     const int t = idx / chunks;
     const int c = (idx - t * chunks) * 8;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-        const int slot = t * k + j;
-        const int e = ids[slot];
-        if (e < 0 || e >= E) continue;
-        const float wj = w[slot];
-        const float* yp = y + (size_t)slot * H + c;
-        f32x4 a = *reinterpret_cast<const f32x4*>(yp);
-        f32x4 b = *reinterpret_cast<const f32x4*>(yp + 4);
-        if (parts > 1 && counts[e] > large_min)
-            for (int pt = 1; pt < parts; ++pt) {
-                a += *reinterpret_cast<const f32x4*>(yp + pt * plane);
-                b += *reinterpret_cast<const f32x4*>(yp + pt * plane + 4);
+    // slots in batches: every id, weight and y row of a batch is requested
+    // before any is used (slots past k re-read the last one; their values
+    // are not used), so a batch costs two memory latencies, not two per slot
+    for (int j0 = 0; j0 < k; j0 += kCombineBatch) {
+        int e[kCombineBatch];
+        float wj[kCombineBatch];
+        f32x4 a[kCombineBatch], b[kCombineBatch];
+#pragma unroll
+        for (int u = 0; u < kCombineBatch; ++u) {
+            const int slot = t * k + min(j0 + u, k - 1);
+            e[u] = ids[slot];
+            wj[u] = w[slot];
+            a[u] = *reinterpret_cast<const f32x4*>(y + (size_t)slot * H + c);
+            b[u] = *reinterpret_cast<const f32x4*>(y + (size_t)slot * H + c + 4);
+        }
+#pragma unroll
+        for (int u = 0; u < kCombineBatch; ++u) {
+            if (j0 + u >= k || e[u] < 0 || e[u] >= E) continue;
+            f32x4 av = a[u], bv = b[u];
+            if (parts > 1 && counts[e[u]] > large_min) {
+                const float* yp = y + (size_t)(t * k + j0 + u) * H + c;
+                for (int pt = 1; pt < parts; ++pt) {
+                    av += *reinterpret_cast<const f32x4*>(yp + pt * plane);
+                    bv += *reinterpret_cast<const f32x4*>(yp + pt * plane + 4);
+                }
             }
-        acc[0] += wj * a.x; acc[1] += wj * a.y; acc[2] += wj * a.z; acc[3] += wj * a.w;
-        acc[4] += wj * b.x; acc[5] += wj * b.y; acc[6] += wj * b.z; acc[7] += wj * b.w;
+            const float ww = wj[u];
+            acc[0] += ww * av.x; acc[1] += ww * av.y; acc[2] += ww * av.z; acc[3] += ww * av.w;
+            acc[4] += ww * bv.x; acc[5] += ww * bv.y; acc[6] += ww * bv.z; acc[7] += ww * bv.w;
+        }
     }
     u32x4 o;
     o.x = (uint32_t)f32_to_bf16_bits(acc[0]) | ((uint32_t)f32_to_bf16_bits(acc[1]) << 16);
