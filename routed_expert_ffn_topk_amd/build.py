@@ -15,8 +15,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_ffn.so")
-SOURCES = ["route_permute.hip", "expert_gemm.hip", "expert_tile.hip", "attn_decode.hip",
-           "read_probe.hip", "moe_ffn_api.cpp"]
+SOURCES = ["route_permute.hip", "expert_gemm.hip", "expert_tile.hip", "combine.hip",
+           "attn_decode.hip", "read_probe.hip", "moe_ffn_api.cpp"]
 ARCH = "gfx950"
 
 

@@ -14,17 +14,22 @@
 // MFMA 16x16x32 blocks per matrix) and 2 x 4 for down (64 x 32); eight
 // rather than four waves per tile keep more waves on each SIMD to cover the
 // per-stage barrier and load waits.  Per pipeline stage (K = 32) every
-// operand tile (128 rows x 32 K, 8 KB) is written to LDS by direct
-// global->LDS 16-byte loads, with the gather of the token rows folded into
-// the load addresses; three stages are in flight.  Rows are stored 64 bytes apart with their four 16-byte chunks
-// XOR-swizzled by bit 2 of the row, so that the MFMA fragment reads (eight
-// rows x two K chunks at a time) hit distinct LDS banks.
+// operand tile (128 rows x 32 K, 8 KB) goes to LDS, with the gather of the
+// token rows folded into the load addresses: either by direct global->LDS
+// 16-byte loads, three stages in flight, or (gate/up with 256 or more
+// tokens per expert on average) through registers loaded one stage ahead
+// and written to one of two LDS buffers.  Rows are stored 64 bytes apart
+// with their four 16-byte chunks XOR-swizzled by bit 2 of the row, so that
+// the MFMA fragment reads (eight rows x two K chunks at a time) hit distinct
+// LDS banks.
 //
 // Schedule: the tiles of all experts on the large list, ordered (expert, row
-// tile, token tile) with token tiles fastest, are dealt out per XCD like the
-// small-m product's rounds (a contiguous slice per XCD, interleaved over its
-// workgroups): the token tiles that share a weight tile run at the same time
-// on one XCD, so the weight tile comes from HBM once and from L2 after that.
+// tile, K part, token tile) with token tiles fastest, are dealt out per XCD
+// like the small-m product's rounds (a contiguous slice per XCD, interleaved
+// over its workgroups): the token tiles that share a weight tile run at the
+// same time on one XCD, so the weight tile comes from HBM once and from L2
+// after that.  Gate/up has one K part; down has 1, 2 or 4 (more when a batch
+// has few long tiles), each writing its own plane of FP32 partial sums of y.
 #include <cmath>
 
 #include "common.hpp"
