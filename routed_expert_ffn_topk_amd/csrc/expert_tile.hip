@@ -9,19 +9,18 @@
 // the reuse: a weight tile now serves up to 128 tokens, so both operands go
 // through LDS in tiles and the matrix unit, not HBM, sets the pace.
 //
-// Work unit: a tile of 128 weight rows x 128 gathered rows of one expert.
-// Eight waves split it, 4 x 2 for gate/up (32 rows x 64 tokens each, 2 x 4
-// MFMA 16x16x32 blocks per matrix) and 2 x 4 for down (64 x 32); eight
-// rather than four waves per tile keep more waves on each SIMD to cover the
-// per-stage barrier and load waits.  Per pipeline stage (K = 32) every
-// operand tile (128 rows x 32 K, 8 KB) goes to LDS, with the gather of the
-// token rows folded into the load addresses: either by direct global->LDS
-// 16-byte loads, three stages in flight, or (gate/up with 256 or more
-// tokens per expert on average) through registers loaded one stage ahead
-// and written to one of two LDS buffers.  Rows are stored 64 bytes apart
-// with their four 16-byte chunks XOR-swizzled by bit 2 of the row, so that
-// the MFMA fragment reads (eight rows x two K chunks at a time) hit distinct
-// LDS banks.
+// Work unit: a tile of 128 weight rows x 256 (or 128) gathered rows of one
+// expert, split among 8 or 16 waves, each computing 32 or 64 rows x 64
+// tokens with MFMA 16x16x32 blocks; many waves per SIMD cover the per-stage
+// barrier and load waits.  Per pipeline stage (K = 32) every operand tile
+// (rows x 32 K, 64 bytes a row) goes to LDS, with the gather of the token
+// rows folded into the load addresses: through registers loaded one stage
+// ahead and written to one of two LDS buffers (token rows past the expert's
+// last are not loaded), or, for the 128-row down tiles, by direct
+// global->LDS 16-byte loads with three stages in flight.  Rows are stored 64
+// bytes apart with their four 16-byte chunks XOR-swizzled by bit 2 of the
+// row, so that the MFMA fragment reads (eight rows x two K chunks at a time)
+// hit distinct LDS banks.
 //
 // Schedule: the tiles of all experts on the large list, ordered (expert, row
 // tile, K part, token tile) with token tiles fastest, are dealt out per XCD
@@ -86,29 +85,35 @@ struct TiledGemm {
 // kWaveRows (along the tokens), gathered rows per tile (128 or 256), K per
 // pipeline stage (32 or 64), stages in flight, and resident workgroups per CU
 // (LDS: kStages x (128 kBlocks + kTokens) rows x 2 kK bytes + 4 KB).
-// Gate/up has two configurations: stages staged straight into LDS, three in
-// flight, and (for batches with many tokens per expert) stages loaded into
-// registers one ahead and written to one of two LDS buffers.
-enum TileProduct : int { kGateUpLds = 0, kGateUpReg = 1, kDownLds = 2 };
+// Three configurations.  Gate/up: tiles of 256 gathered rows, sixteen waves
+// (4 x 4 of 32 rows x 64 tokens), stages loaded into registers one ahead and
+// written to one of two LDS buffers, one workgroup per CU; token rows past
+// the expert's last are not loaded, so an expert with few more than 128
+// tokens costs one weight staging, not two.  Down, with fewer than 256
+// tokens per expert on average: the same register staging with 256 gathered
+// rows in eight waves (2 x 4 of 64 rows x 64 tokens), two workgroups per CU.
+// Down with more: 128 gathered rows staged straight into LDS, three stages in
+// flight, three workgroups per CU.
+enum TileProduct : int { kGateUp = 0, kDownWide = 1, kDownLds = 2 };
 template <int P>
 struct TileTuning;
 template <>
-struct TileTuning<kGateUpLds> {
+struct TileTuning<kGateUp> {
     static constexpr int kBlocks = 2;
-    static constexpr int kWaves = 8;
+    static constexpr int kWaves = 16;
     static constexpr int kWaveRows = 4;
-    static constexpr int kTokens = 128;
+    static constexpr int kTokens = 256;
     static constexpr int kK = 32;
-    static constexpr int kStages = 3;
-    static constexpr bool kRegStage = false;
-    static constexpr int kBlocksPerCU = 2;
+    static constexpr int kStages = 2;
+    static constexpr bool kRegStage = true;
+    static constexpr int kBlocksPerCU = 1;
 };
 template <>
-struct TileTuning<kGateUpReg> {
-    static constexpr int kBlocks = 2;
+struct TileTuning<kDownWide> {
+    static constexpr int kBlocks = 1;
     static constexpr int kWaves = 8;
-    static constexpr int kWaveRows = 4;
-    static constexpr int kTokens = 128;
+    static constexpr int kWaveRows = 2;
+    static constexpr int kTokens = 256;
     static constexpr int kK = 32;
     static constexpr int kStages = 2;
     static constexpr bool kRegStage = true;
@@ -131,7 +136,7 @@ __global__ __launch_bounds__(TileTuning<P>::kWaves * kWave)
 __attribute__((amdgpu_waves_per_eu(TileTuning<P>::kBlocksPerCU * TileTuning<P>::kWaves / 4)))
 void expert_tile_kernel(const TiledGemm g) {
     using Tu = TileTuning<P>;
-    constexpr bool kDown = P == kDownLds;
+    constexpr bool kDown = P != kGateUp;
     constexpr int NMAT = Tu::kBlocks;             // weight blocks per tile
     constexpr int W = Tu::kWaves;
     constexpr int WR = Tu::kWaveRows;
@@ -259,12 +264,21 @@ void expert_tile_kernel(const TiledGemm g) {
                 src[i] = g.b_src + (size_t)brow * g.b_pitch + s0 * KS + cl * 8;
             }
         }
+        // register staging loads no token row past the expert's last (their
+        // MFMA columns are never stored)
+        bool live[IL];
+#pragma unroll
+        for (int i = 0; i < IL; ++i) {
+            const int q = wave + W * i;
+            live[i] = q < NMAT * WCH || p0 + RPI * (q - NMAT * WCH) + lane / RW < m;
+        }
         u32x4 rg[IL];
         auto load_regs = [&](int s) {
             int k0 = s * KS;
             if (KS > 32 && k0 + 8 * cl >= kl) k0 -= 32;
 #pragma unroll
-            for (int i = 0; i < IL; ++i) rg[i] = load16(src[i] + k0);
+            for (int i = 0; i < IL; ++i)
+                rg[i] = live[i] ? load16(src[i] + k0) : u32x4{0u, 0u, 0u, 0u};
         };
         auto store_regs = [&](int s) {
             u32x4* buf = lds + (s % S) * kStageWords;
@@ -401,10 +415,38 @@ constexpr int kMaxDownParts = 4;
 constexpr double kNominalTflops = 600.0;
 constexpr double kNominalTBs = 5.0;
 
-// Average tokens per expert from which gate/up takes the register-staged
-// configuration (measured: +9 % at 512 per expert, Mixtral-8x7B; -5 to +2 %
-// at 128, the Qwen3-235B and DeepSeek-V3 shapes).
-constexpr int kRegStageMinTokens = 256;
+// Average tokens per expert below which down takes the 256-row configuration
+// (measured: 10-13 % faster at ~128 per expert, Qwen3-235B, DeepSeek-V3 and
+// Mixtral-8x7B at 512 tokens; 5 % slower at 512 per expert, where the
+// 128-row tiles with their K in parts balance better).
+constexpr int kDownWideMaxTokens = 256;
+
+bool down_wide(int64_t T, int E, int k) { return T * k < (int64_t)kDownWideMaxTokens * E; }
+
+// K parts of the down product in configuration D (see tiled_down_parts).
+template <int D>
+int down_parts(int64_t T, int64_t H, int64_t I, int E, int k) {
+    using Tu = TileTuning<D>;
+    const int64_t slots = T * k;
+    const int64_t large = slots / (kTiledMinTokens + 1) < E ? slots / (kTiledMinTokens + 1) : E;
+    const double tiles = (double)((H + kTileN - 1) / kTileN) *
+                         ((double)slots / Tu::kTokens + 0.5 * (double)large);
+    const double wg = (double)kNominalCUs * Tu::kBlocksPerCU;
+    const double round_us = wg * 2.0 * kTileN * Tu::kTokens * (double)I / (kNominalTflops * 1e6);
+    const double plane_us = (double)slots * (double)H * 8.0 / (kNominalTBs * 1e6);
+    const int64_t nk = (I + Tu::kK - 1) / Tu::kK;
+    int best = 1;
+    double best_cost = 1e300;
+    for (int P = 1; P <= kMaxDownParts && P <= nk; P *= 2) {
+        if ((P - 1) * ((nk + P - 1) / P) >= nk) break;    // a part would be empty
+        const double cost = std::ceil(tiles * P / wg) / P * round_us + (P - 1) * plane_us;
+        if (cost < best_cost * (1.0 - 1e-9)) {
+            best = P;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
 
 }  // namespace
 
@@ -425,9 +467,7 @@ hipError_t launch_tiled_gate_up(const uint16_t* x, const FfnWeights& W, const Ff
     g.top_k = s.k;
     g.k_parts = 1;
     g.part_stages = 1 << 30;
-    const long long per_expert = (long long)s.T * s.k / s.E;
-    return per_expert >= kRegStageMinTokens ? launch_tile<kGateUpReg>(g, num_cu, stream)
-                                            : launch_tile<kGateUpLds>(g, num_cu, stream);
+    return launch_tile<kGateUp>(g, num_cu, stream);
 }
 
 hipError_t launch_tiled_down(const FfnWeights& W, const FfnShape& s, const Workspace& ws,
@@ -446,9 +486,11 @@ hipError_t launch_tiled_down(const FfnWeights& W, const FfnShape& s, const Works
     g.K = s.I;
     g.top_k = s.k;
     g.k_parts = tiled_down_parts(s.T, s.H, s.I, s.E, s.k);
+    static_assert(TileTuning<kDownWide>::kK == TileTuning<kDownLds>::kK, "one stage length");
     const int nk = (s.I + TileTuning<kDownLds>::kK - 1) / TileTuning<kDownLds>::kK;
     g.part_stages = (nk + g.k_parts - 1) / g.k_parts;
-    return launch_tile<kDownLds>(g, num_cu, stream);
+    return down_wide(s.T, s.E, s.k) ? launch_tile<kDownWide>(g, num_cu, stream)
+                                    : launch_tile<kDownLds>(g, num_cu, stream);
 }
 
 // The down product's tiles are long (K = I) and few when a batch has few
@@ -456,33 +498,16 @@ hipError_t launch_tiled_down(const FfnWeights& W, const FfnShape& s, const Works
 // against 768 resident workgroups): the last round of tiles leaves much of
 // the GPU idle.  Splitting K into parts multiplies the tiles; each part
 // writes its own FP32 partial sums of y, which the combine adds.  The part
-// count is chosen from the expected tile count (token tiles: T k / 128, plus
+// count is chosen from the expected tile count (token tiles: T k over the
+// gathered rows per tile of the down configuration the sizes select, plus
 // half a tile of padding per expert with more than 32 tokens): the rounds of
 // tiles it needs, in units of one round of full-K tiles at the product's
 // nominal rate, plus the time to write and read back each extra plane of
 // partial sums at a nominal HBM rate.
 int tiled_down_parts(int64_t T, int64_t H, int64_t I, int E, int k) {
     if (T <= kTiledMinBatch) return 1;
-    const int64_t slots = T * k;
-    const int64_t large = slots / (kTiledMinTokens + 1) < E ? slots / (kTiledMinTokens + 1) : E;
-    const double tiles = (double)((H + kTileN - 1) / kTileN) *
-                         ((double)slots / TileTuning<kDownLds>::kTokens + 0.5 * (double)large);
-    const double wg = (double)kNominalCUs * TileTuning<kDownLds>::kBlocksPerCU;
-    const double round_us = wg * 2.0 * kTileN * TileTuning<kDownLds>::kTokens * (double)I /
-                            (kNominalTflops * 1e6);
-    const double plane_us = (double)slots * (double)H * 8.0 / (kNominalTBs * 1e6);
-    const int64_t nk = (I + TileTuning<kDownLds>::kK - 1) / TileTuning<kDownLds>::kK;
-    int best = 1;
-    double best_cost = 1e300;
-    for (int P = 1; P <= kMaxDownParts && P <= nk; P *= 2) {
-        if ((P - 1) * ((nk + P - 1) / P) >= nk) break;    // a part would be empty
-        const double cost = std::ceil(tiles * P / wg) / P * round_us + (P - 1) * plane_us;
-        if (cost < best_cost * (1.0 - 1e-9)) {
-            best = P;
-            best_cost = cost;
-        }
-    }
-    return best;
+    return down_wide(T, E, k) ? down_parts<kDownWide>(T, H, I, E, k)
+                              : down_parts<kDownLds>(T, H, I, E, k);
 }
 
 }  // namespace moe
