@@ -6,18 +6,18 @@
 // the FFN equation of §4.1 and the BF16 operands with FP32 accumulation of
 // §4.2.1 are unchanged.  Weights stay in their row-major layout and only the
 // gathered rows are rearranged, as in the small-m product; what changes is
-// the reuse: a weight tile now serves up to 128 tokens, so both operands go
+// the reuse: a weight tile now serves up to 256 tokens, so both operands go
 // through LDS in tiles and the matrix unit, not HBM, sets the pace.
 //
-// Work unit: a tile of 128 weight rows x 256 (or 128) gathered rows of one
-// expert, split among 8 or 16 waves, each computing 32 or 64 rows x 64
-// tokens with MFMA 16x16x32 blocks; many waves per SIMD cover the per-stage
-// barrier and load waits.  Per pipeline stage (K = 32) every operand tile
-// (rows x 32 K, 64 bytes a row) goes to LDS, with the gather of the token
-// rows folded into the load addresses: through registers loaded one stage
-// ahead and written to one of two LDS buffers (token rows past the expert's
-// last are not loaded), or, for the 128-row down tiles, by direct
-// global->LDS 16-byte loads with three stages in flight.  Rows are stored 64
+// Work unit: a tile of two 128-row weight blocks (gate/up: W_gate and W_up;
+// down: two consecutive blocks of W_down) x 256 gathered rows of one
+// expert, split among sixteen waves, each computing 32 rows of each block x
+// 64 tokens with MFMA 16x16x32 blocks.  Per pipeline stage (K = 32) every
+// operand tile (rows x 32 K, 64 bytes a row) goes to LDS, with the gather of
+// the token rows folded into the load addresses: each wave loads its share
+// of the next stage into registers while the MFMAs consume the current one,
+// and writes it to the other of two LDS buffers after the step's barrier;
+// token rows past the expert's last are not loaded.  Rows are stored 64
 // bytes apart with their four 16-byte chunks XOR-swizzled by bit 2 of the
 // row, so that the MFMA fragment reads (eight rows x two K chunks at a time)
 // hit distinct LDS banks.
@@ -83,52 +83,21 @@ struct TiledGemm {
 // 128-row blocks of W_down, so a tile covers 128 kBlocks output rows), waves
 // per workgroup arranged kWaveRows (along the weight rows) x kWaves /
 // kWaveRows (along the tokens), gathered rows per tile (128 or 256), K per
-// pipeline stage (32 or 64), stages in flight, and resident workgroups per CU
-// (LDS: kStages x (128 kBlocks + kTokens) rows x 2 kK bytes + 4 KB).
-// Three configurations.  Gate/up: tiles of 256 gathered rows, sixteen waves
-// (4 x 4 of 32 rows x 64 tokens), stages loaded into registers one ahead and
-// written to one of two LDS buffers, one workgroup per CU; token rows past
-// the expert's last are not loaded, so an expert with few more than 128
-// tokens costs one weight staging, not two.  Down, with fewer than 256
-// tokens per expert on average: the same register staging with 256 gathered
-// rows in eight waves (2 x 4 of 64 rows x 64 tokens), two workgroups per CU.
-// Down with more: 128 gathered rows staged straight into LDS, three stages in
-// flight, three workgroups per CU.
-enum TileProduct : int { kGateUp = 0, kDownWide = 1, kDownLds = 2 };
+// pipeline stage (32 or 64) and resident workgroups per CU (LDS: two
+// buffers of (128 kBlocks + kTokens) rows x 2 kK bytes, + 4 KB).  Both
+// products use tiles of 256 gathered rows over sixteen waves, 4 x 4 of 32
+// rows (of each weight block) x 64 tokens, one workgroup per CU; down stacks
+// two blocks of W_down, so that its tiles have the two weight blocks of the
+// gate/up tiles.
+enum TileProduct : int { kGateUp = 0, kDownProd = 1 };
 template <int P>
-struct TileTuning;
-template <>
-struct TileTuning<kGateUp> {
+struct TileTuning {
     static constexpr int kBlocks = 2;
     static constexpr int kWaves = 16;
     static constexpr int kWaveRows = 4;
     static constexpr int kTokens = 256;
     static constexpr int kK = 32;
-    static constexpr int kStages = 2;
-    static constexpr bool kRegStage = true;
     static constexpr int kBlocksPerCU = 1;
-};
-template <>
-struct TileTuning<kDownWide> {
-    static constexpr int kBlocks = 1;
-    static constexpr int kWaves = 8;
-    static constexpr int kWaveRows = 2;
-    static constexpr int kTokens = 256;
-    static constexpr int kK = 32;
-    static constexpr int kStages = 2;
-    static constexpr bool kRegStage = true;
-    static constexpr int kBlocksPerCU = 2;
-};
-template <>
-struct TileTuning<kDownLds> {
-    static constexpr int kBlocks = 1;
-    static constexpr int kWaves = 8;
-    static constexpr int kWaveRows = 2;
-    static constexpr int kTokens = 128;
-    static constexpr int kK = 32;
-    static constexpr int kStages = 3;
-    static constexpr bool kRegStage = false;
-    static constexpr int kBlocksPerCU = 3;
 };
 
 template <int P>
@@ -141,16 +110,12 @@ void expert_tile_kernel(const TiledGemm g) {
     constexpr int W = Tu::kWaves;
     constexpr int WR = Tu::kWaveRows;
     constexpr int KS = Tu::kK;                    // K per stage
-    constexpr int S = Tu::kStages;
+    constexpr int S = 2;                          // LDS stage buffers
     constexpr int kRows = kDown ? kTileN * NMAT : kTileN;   // output rows per tile
     static_assert(kDown || NMAT == 2, "gate/up tiles hold W_gate and W_up");
     constexpr int M = Tu::kTokens;                // gathered rows per tile
     static_assert((W == 4 || W == 8 || W == 16) && W % WR == 0, "waves per workgroup");
-    static_assert((KS == 32 || KS == 64) && S >= 2, "stage shape");
-    // register staging: each stage's rows are loaded into registers one
-    // stage ahead and written to one of two LDS buffers after the barrier
-    constexpr bool kReg = Tu::kRegStage;
-    static_assert(!kReg || S == 2, "register staging uses two LDS buffers");
+    static_assert(KS == 32 || KS == 64, "stage shape");
     static_assert(M == 128 || M == 256, "tokens per tile");
     constexpr int RW = KS / 8;                    // 16-byte words of a row per stage
     constexpr int kOperandWords = 128 * RW;       // one 128-row weight block
@@ -166,7 +131,6 @@ void expert_tile_kernel(const TiledGemm g) {
     constexpr int RB = RPW / 16;                  // 16-row blocks per wave
     constexpr int TB = TPW / 16;                  // 16-token blocks per wave
     constexpr int kStageWords = (NMAT * 128 + M) * RW;
-    constexpr int kLoads = IL;                    // load instructions per wave and stage
     __shared__ u32x4 lds[S * kStageWords];
     __shared__ int pre[kMaxLarge + 1];
 
@@ -285,19 +249,6 @@ void expert_tile_kernel(const TiledGemm g) {
 #pragma unroll
             for (int i = 0; i < IL; ++i) buf[(wave + W * i) * kWave + lane] = rg[i];
         };
-        auto issue = [&](int s) {
-            u32x4* buf = lds + (s % S) * kStageWords;
-            int k0 = s * KS;
-            // the second half of a half stage re-reads the first (in bounds;
-            // never used)
-            if (KS > 32 && k0 + 8 * cl >= kl) k0 -= 32;
-#pragma unroll
-            for (int i = 0; i < IL; ++i)
-                __builtin_amdgcn_global_load_lds((const void*)(src[i] + k0),
-                                                 (lds_void_ptr)&buf[(wave + W * i) * kWave],
-                                                 16, 0, 0);
-        };
-
         f32x4 acc[NMAT][RB][TB];
 #pragma unroll
         for (int mm = 0; mm < NMAT; ++mm)
@@ -306,35 +257,19 @@ void expert_tile_kernel(const TiledGemm g) {
 #pragma unroll
                 for (int tb = 0; tb < TB; ++tb) acc[mm][rb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        if constexpr (kReg) {
-            load_regs(0);
-            store_regs(0);
-            if (nk > 1) load_regs(1);
-        } else {
-#pragma unroll
-            for (int s = 0; s < S - 1; ++s)
-                if (s < nk) issue(s);
-        }
+        // each wave loads its share of stage s + 1 into registers while the
+        // MFMAs consume stage s, and writes it to the other LDS buffer after
+        // the step's barrier
+        load_regs(0);
+        store_regs(0);
+        if (nk > 1) load_regs(1);
         for (int s = 0; s < nk; ++s) {
-            if constexpr (kReg) {
-                // stage s is in LDS and every wave is done with the other
-                // buffer; fill it with stage s + 1 and request stage s + 2
-                __syncthreads();
-                if (s + 1 < nk) {
-                    store_regs(s + 1);
-                    if (s + 2 < nk) load_regs(s + 2);
-                }
-            } else {
-                // this wave's loads of stage s are done (the next S - 2
-                // stages may still be in flight), then everyone's: the stage
-                // is complete in LDS and every wave has finished with the
-                // buffer stage s + S - 1 reuses
-                if (s + S - 2 < nk)
-                    wait_vmcnt<(S - 2) * kLoads>();
-                else
-                    wait_vmcnt<0>();
-                __syncthreads();
-                if (s + S - 1 < nk) issue(s + S - 1);
+            // stage s is in LDS and every wave is done with the other
+            // buffer; fill it with stage s + 1 and request stage s + 2
+            __syncthreads();
+            if (s + 1 < nk) {
+                store_regs(s + 1);
+                if (s + 2 < nk) load_regs(s + 2);
             }
             const u32x4* buf = lds + (s % S) * kStageWords;
 #pragma unroll
@@ -415,24 +350,17 @@ constexpr int kMaxDownParts = 4;
 constexpr double kNominalTflops = 600.0;
 constexpr double kNominalTBs = 5.0;
 
-// Average tokens per expert below which down takes the 256-row configuration
-// (measured: 10-13 % faster at ~128 per expert, Qwen3-235B, DeepSeek-V3 and
-// Mixtral-8x7B at 512 tokens; 5 % slower at 512 per expert, where the
-// 128-row tiles with their K in parts balance better).
-constexpr int kDownWideMaxTokens = 256;
-
-bool down_wide(int64_t T, int E, int k) { return T * k < (int64_t)kDownWideMaxTokens * E; }
-
 // K parts of the down product in configuration D (see tiled_down_parts).
 template <int D>
 int down_parts(int64_t T, int64_t H, int64_t I, int E, int k) {
     using Tu = TileTuning<D>;
     const int64_t slots = T * k;
     const int64_t large = slots / (kTiledMinTokens + 1) < E ? slots / (kTiledMinTokens + 1) : E;
-    const double tiles = (double)((H + kTileN - 1) / kTileN) *
+    constexpr int kRows = kTileN * Tu::kBlocks;   // output rows per tile
+    const double tiles = (double)((H + kRows - 1) / kRows) *
                          ((double)slots / Tu::kTokens + 0.5 * (double)large);
     const double wg = (double)kNominalCUs * Tu::kBlocksPerCU;
-    const double round_us = wg * 2.0 * kTileN * Tu::kTokens * (double)I / (kNominalTflops * 1e6);
+    const double round_us = wg * 2.0 * kRows * Tu::kTokens * (double)I / (kNominalTflops * 1e6);
     const double plane_us = (double)slots * (double)H * 8.0 / (kNominalTBs * 1e6);
     const int64_t nk = (I + Tu::kK - 1) / Tu::kK;
     int best = 1;
@@ -486,11 +414,9 @@ hipError_t launch_tiled_down(const FfnWeights& W, const FfnShape& s, const Works
     g.K = s.I;
     g.top_k = s.k;
     g.k_parts = tiled_down_parts(s.T, s.H, s.I, s.E, s.k);
-    static_assert(TileTuning<kDownWide>::kK == TileTuning<kDownLds>::kK, "one stage length");
-    const int nk = (s.I + TileTuning<kDownLds>::kK - 1) / TileTuning<kDownLds>::kK;
+    const int nk = (s.I + TileTuning<kDownProd>::kK - 1) / TileTuning<kDownProd>::kK;
     g.part_stages = (nk + g.k_parts - 1) / g.k_parts;
-    return down_wide(s.T, s.E, s.k) ? launch_tile<kDownWide>(g, num_cu, stream)
-                                    : launch_tile<kDownLds>(g, num_cu, stream);
+    return launch_tile<kDownProd>(g, num_cu, stream);
 }
 
 // The down product's tiles are long (K = I) and few when a batch has few
@@ -506,8 +432,7 @@ hipError_t launch_tiled_down(const FfnWeights& W, const FfnShape& s, const Works
 // partial sums at a nominal HBM rate.
 int tiled_down_parts(int64_t T, int64_t H, int64_t I, int E, int k) {
     if (T <= kTiledMinBatch) return 1;
-    return down_wide(T, E, k) ? down_parts<kDownWide>(T, H, I, E, k)
-                              : down_parts<kDownLds>(T, H, I, E, k);
+    return down_parts<kDownProd>(T, H, I, E, k);
 }
 
 }  // namespace moe

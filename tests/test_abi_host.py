@@ -67,7 +67,7 @@ def test_down_k_parts():
     assert parts(64, 4096, 14336, 8, 2) == 1
     assert parts(2048, 4096, 1536, 128, 8) == 1
     assert parts(4096, 7168, 2048, 256, 8) == 1
-    assert parts(2048, 4096, 14336, 8, 2) == 2
+    assert parts(2048, 4096, 14336, 8, 2) == 4
     assert parts(512, 4096, 14336, 8, 2) == 2
     assert {parts(129, 32, 32, 1, 1), parts(1000, 96, 160, 2, 1),
             parts(400, 64, 1024, 2, 2)} == {1, 2, 4}
