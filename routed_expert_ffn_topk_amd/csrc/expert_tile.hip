@@ -12,15 +12,15 @@
 // Work unit: a tile of two 128-row weight blocks (gate/up: W_gate and W_up;
 // down: two consecutive blocks of W_down) x 256 gathered rows of one
 // expert, split among sixteen waves, each computing 32 rows of each block x
-// 64 tokens with MFMA 16x16x32 blocks.  Per pipeline stage (K = 32) every
-// operand tile (rows x 32 K, 64 bytes a row) goes to LDS, with the gather of
+// 64 tokens with MFMA 16x16x32 blocks.  Per pipeline stage (K = 64) every
+// operand tile (rows x 64 K, 128 bytes a row) goes to LDS, with the gather of
 // the token rows folded into the load addresses: each wave loads its share
 // of the next stage into registers while the MFMAs consume the current one,
 // and writes it to the other of two LDS buffers after the step's barrier;
-// token rows past the expert's last are not loaded.  Rows are stored 64
-// bytes apart with their four 16-byte chunks XOR-swizzled by bit 2 of the
-// row, so that the MFMA fragment reads (eight rows x two K chunks at a time)
-// hit distinct LDS banks.
+// token rows past the expert's last are not loaded.  Rows are stored 128
+// bytes apart with their eight 16-byte chunks XOR-swizzled by bits 1-2 of
+// the row, so that the MFMA fragment reads (eight rows x two K chunks at a
+// time) hit distinct LDS banks.
 //
 // Schedule: the tiles of all experts on the large list, ordered (expert, row
 // tile, K part, token tile) with token tiles fastest, are dealt out per XCD
@@ -86,9 +86,9 @@ struct TiledGemm {
 // pipeline stage (32 or 64) and resident workgroups per CU (LDS: two
 // buffers of (128 kBlocks + kTokens) rows x 2 kK bytes, + 4 KB).  Both
 // products use tiles of 256 gathered rows over sixteen waves, 4 x 4 of 32
-// rows (of each weight block) x 64 tokens, one workgroup per CU; down stacks
-// two blocks of W_down, so that its tiles have the two weight blocks of the
-// gate/up tiles.
+// rows (of each weight block) x 64 tokens, K = 64 per stage (132 KB of
+// LDS), one workgroup per CU; down stacks two blocks of W_down, so that its
+// tiles have the two weight blocks of the gate/up tiles.
 enum TileProduct : int { kGateUp = 0, kDownProd = 1 };
 template <int P>
 struct TileTuning {
@@ -96,7 +96,7 @@ struct TileTuning {
     static constexpr int kWaves = 16;
     static constexpr int kWaveRows = 4;
     static constexpr int kTokens = 256;
-    static constexpr int kK = 32;
+    static constexpr int kK = 64;
     static constexpr int kBlocksPerCU = 1;
 };
 
