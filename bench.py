@@ -364,8 +364,8 @@ def main():
         print(json.dumps({"copy_probe_bytes": n, "copies": 5}), flush=True)
         return
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported: the MoE FFN layer runs on one "
-              "GPU only here (the sharding notes are in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py: --gpus {args.gpus} is not supported: the MoE FFN layer is measured "
+              "on one GPU only", file=sys.stderr)
         sys.exit(2)
 
     import workloads
