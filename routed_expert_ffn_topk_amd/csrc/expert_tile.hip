@@ -17,7 +17,8 @@
 // the token rows folded into the load addresses: each wave loads its share
 // of the next stage into registers while the MFMAs consume the current one,
 // and writes it to the other of two LDS buffers after the step's barrier;
-// token rows past the expert's last are not loaded.  Rows are stored 128
+// token rows past the expert's last are not loaded, and a wave whose 64
+// token columns all lie past it skips its multiplies.  Rows are stored 128
 // bytes apart with their eight 16-byte chunks XOR-swizzled by bits 1-2 of
 // the row, so that the MFMA fragment reads (eight rows x two K chunks at a
 // time) hit distinct LDS banks.
@@ -275,6 +276,9 @@ void expert_tile_kernel(const TiledGemm g) {
 #pragma unroll
             for (int j = 0; j < KS / 32; ++j) {
                 if (j > 0 && s * KS + 32 * j >= kl) break;       // half stage
+                // a wave whose token columns all lie past the expert's last
+                // token (the ragged last tile) has nothing to multiply
+                if (p0 + TPW * wm >= m) break;
                 u32x4 af[NMAT][RB];
 #pragma unroll
                 for (int mm = 0; mm < NMAT; ++mm)
