@@ -17,8 +17,8 @@
 // the token rows folded into the load addresses: each wave loads its share
 // of the next stage into registers while the MFMAs consume the current one,
 // and writes it to the other of two LDS buffers after the step's barrier;
-// token rows past the expert's last are not loaded, and a wave whose 64
-// token columns all lie past it skips its multiplies.  Rows are stored 128
+// token rows past the expert's last are not loaded, and the multiplies of
+// 16-token blocks that lie past it are skipped.  Rows are stored 128
 // bytes apart with their eight 16-byte chunks XOR-swizzled by bits 1-2 of
 // the row, so that the MFMA fragment reads (eight rows x two K chunks at a
 // time) hit distinct LDS banks.
@@ -288,6 +288,8 @@ void expert_tile_kernel(const TiledGemm g) {
                                          tile_word<RW>(RPW * wr + 16 * rb + col, 4 * j + kg)];
 #pragma unroll
                 for (int tb = 0; tb < TB; ++tb) {
+                    // and no 16-token block past the expert's last token
+                    if (p0 + TPW * wm + 16 * tb >= m) break;
                     const u32x4 bf = buf[NMAT * kOperandWords +
                                          tile_word<RW>(TPW * wm + 16 * tb + col, 4 * j + kg)];
 #pragma unroll
