@@ -412,10 +412,10 @@ def main():
         wlr = workloads.Workload(**{**wl0.__dict__, "seed": wl0.seed + r})
         if resplit:
             tens = workloads.gen_weights_resplit(wlr, dev)
-            p4, gm = workloads.pack_int4, workloads.scales_group_major
+            p4 = workloads.pack_int4
             Qg, Sg, Rg, SRg, Qu, Su, Ru, SRu, Qdl, Sdl, Qdh, Sdh = tens
-            sets.append((p4(Qg), gm(Sg), p4(Rg), gm(SRg), p4(Qu), gm(Su), p4(Ru), gm(SRu),
-                         p4(Qdl), gm(Sdl), Qdh, gm(Sdh), torch.from_numpy(crit).to(dev)))
+            sets.append((p4(Qg), Sg, p4(Rg), SRg, p4(Qu), Su, p4(Ru), SRu,
+                         p4(Qdl), Sdl, Qdh, Sdh, torch.from_numpy(crit).to(dev)))
             if r == 0:
                 host_rowmajor = tens
             else:
@@ -424,8 +424,7 @@ def main():
             gen = workloads.gen_weights_int8 if int8 else workloads.gen_weights_int4
             Qg, Sg, Qu, Su, Qd, Sd = gen(wlr, dev)
             store = (lambda q: q) if int8 else workloads.pack_int4  # noqa: E731
-            gm = workloads.scales_group_major
-            sets.append((store(Qg), gm(Sg), store(Qu), gm(Su), store(Qd), gm(Sd)))
+            sets.append((store(Qg), Sg, store(Qu), Su, store(Qd), Sd))
             if r == 0:
                 host_rowmajor = (Qg, Sg, Qu, Su, Qd, Sd)
             else:

@@ -216,15 +216,15 @@ int moe_ffn_forward_logits(const void* x, const float* logits, int32_t* topk_ids
  * float32 scale s(r, g) per group g of 128 consecutive K, and each dot
  * product is
  *   sum_g s(r, g) * (sum_{c in group g} v_c * q[r][c])   (FP32).
- * The int8 matrices are row-major like the BF16 ones; the scales are stored
- * group-major, s(r, g) at [e][g][r], so that one load returns the scales of
- * consecutive output rows:
- *   Q_gate, Q_up [E][I][H] int8 with S_gate, S_up [E][H/128][I] float32;
- *   Q_down [E][H][I] int8 with S_down [E][I/128][H] float32.
+ * Weights and scales are read in the layout a framework keeps them in
+ * (HiNa-MoE §3.1 and Table 1: no weight reformatting), row-major with the
+ * groups of a row contiguous:
+ *   Q_gate, Q_up [E][I][H] int8 with S_gate, S_up [E][I][H/128] float32;
+ *   Q_down [E][H][I] int8 with S_down [E][H][I/128] float32.
  * `group` is the scale group length along K; this library implements
  * group = MOE_FFN_INT8_GROUP (128) and returns MOE_FFN_ERR_BAD_SHAPE for any
- * other value.  Sizes: H and I multiples of 128.  Scale pointers must be
- * 16-byte aligned.
+ * other value.  Sizes: H and I multiples of 128.  Weight pointers 16-byte
+ * aligned, scale pointers 4-byte aligned.
  */
 int moe_ffn_forward_int8(const void* x, const int32_t* topk_ids,
                          const float* topk_w, const int8_t* Q_gate,
@@ -236,10 +236,12 @@ int moe_ffn_forward_int8(const void* x, const int32_t* topk_ids,
                          void* stream);
 
 /*
- * Decode attention with grouped-query heads (HiNa-MoE §6.1: in decoding the
- * h_q / h_kv query heads that share one KV head form a small block, and
- * scoring it against the head's keys, then weighting its values, are small
- * matrix products).
+ * Decode attention with grouped-query heads (HiNa-MoE §6.1, decode
+ * attention as small matrix products).  With grouped-query attention,
+ * g = h_q / h_kv consecutive query heads read the same KV head; during
+ * decoding each contributes one query row, so per KV head the scores are a
+ * g-row matrix times the head's keys, and the output that g-row softmax
+ * matrix times the head's values.
  *   q        [B][h_q][d] bf16, device: one query vector per sequence and
  *            query head.
  *   k_cache, v_cache [B][h_kv][max_len][d] bf16, device: the KV cache;
@@ -252,7 +254,9 @@ int moe_ffn_forward_int8(const void* x, const int32_t* topk_ids,
  *              out = RNE_bf16( sum_t softmax(s)_t * v_t )
  *            over t < seq_lens[b] (the softmax weights enter the value
  *            product as BF16); an empty sequence gives zeros.
- *   scale    the score scale (1/sqrt(d) for standard attention).
+ *   scale    the score scale; a value that is not positive (0, negative or
+ *            NaN) selects 1/sqrt(d), the scale of standard attention,
+ *            computed in double precision and rounded to float.
  *   workspace / workspace_bytes: at least
  *            moe_attn_decode_workspace_bytes(...) bytes, 256-byte aligned,
  *            device; contents on entry are ignored (per-split partial
@@ -283,10 +287,11 @@ size_t moe_attn_decode_workspace_bytes(int32_t B, int32_t h_q, int32_t h_kv,
  * [-8, 7] is accepted), stored two per byte as offset-binary nibbles
  * u = q + 8: K element 2i of a row in the low nibble of byte i, element
  * 2i + 1 in the high nibble.
- *   P_gate, P_up [E][I][H/2] uint8 with S_gate, S_up [E][H/128][I] float32;
- *   P_down [E][H][I/2] uint8 with S_down [E][I/128][H] float32
- * (scales group-major as for INT8).  `group` must be MOE_FFN_INT8_GROUP
- * (128).  Sizes: H and I multiples of 128.  Pointers 16-byte aligned.
+ *   P_gate, P_up [E][I][H/2] uint8 with S_gate, S_up [E][I][H/128] float32;
+ *   P_down [E][H][I/2] uint8 with S_down [E][H][I/128] float32
+ * (scales row-major as for INT8).  `group` must be MOE_FFN_INT8_GROUP
+ * (128).  Sizes: H and I multiples of 128.  Weight pointers 16-byte
+ * aligned, scale pointers 4-byte aligned.
  * Batches of any size take the small-m product (no tiled INT4 product).
  */
 int moe_ffn_forward_int4(const void* x, const int32_t* topk_ids,
@@ -316,15 +321,15 @@ int moe_ffn_forward_int4(const void* x, const int32_t* topk_ids,
  * caller's.
  *   P_gate, R_gate, P_up, R_up [E][I][H/2] uint8 (W^Q and W^R, the INT4
  *            nibble layout of moe_ffn_forward_int4) with S_gate, SR_gate,
- *            S_up, SR_up [E][H/128][I] float32 (group-major);
- *   P_down_lo [E][H][I/2] uint8 with S_down_lo [E][I/128][H] float32;
- *   Q_down_hi [E][H][I] int8 with S_down_hi [E][I/128][H] float32;
+ *            S_up, SR_up [E][I][H/128] float32 (row-major, as for INT8);
+ *   P_down_lo [E][H][I/2] uint8 with S_down_lo [E][H][I/128] float32;
+ *   Q_down_hi [E][H][I] int8 with S_down_hi [E][H][I/128] float32;
  *   critical [E] uint8, device.
  * Only the tensors an expert's precision needs are read: R_*, SR_* and the
  * high down copy of critical experts, the low down copy of the others.
  * `group` must be MOE_FFN_INT8_GROUP (128).  Sizes: H and I multiples of 128.
- * Weight and scale pointers 16-byte aligned.  Batches of any size take the
- * small-m product.  Errors as for moe_ffn_forward_int8 (NULL_ARG also for a
+ * Weight pointers 16-byte aligned, scale pointers 4-byte aligned.  Batches
+ * of any size take the small-m product.  Errors as for moe_ffn_forward_int8 (NULL_ARG also for a
  * null critical).
  */
 int moe_ffn_forward_resplit(const void* x, const int32_t* topk_ids,

@@ -123,6 +123,28 @@ def _dev(t: torch.Tensor, name: str, dtype) -> int:
     return t.data_ptr()
 
 
+def _check_shape(name: str, t: torch.Tensor, shape) -> None:
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {list(shape)}, got {list(t.shape)}")
+
+
+def _layer_args(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor,
+                out: Optional[torch.Tensor]) -> Tuple[int, int, int]:
+    """Sizes (T, H, top_k) of a layer call, after checking that x is [T, H],
+    topk_ids and topk_w are [T, top_k] and out (if given) is [T, H]: the
+    kernels index these tensors by those sizes."""
+    if x.dim() != 2:
+        raise ValueError(f"x must be [T, H], got {list(x.shape)}")
+    T, H = x.shape
+    if topk_ids.dim() != 2 or topk_ids.shape[0] != T:
+        raise ValueError(f"topk_ids must be [T, top_k] with T = {T}, got {list(topk_ids.shape)}")
+    top_k = topk_ids.shape[1]
+    _check_shape("topk_w", topk_w, (T, top_k))
+    if out is not None:
+        _check_shape("out", out, (T, H))
+    return T, H, top_k
+
+
 def moe_ffn_workspace_layout(T: int, H: int, I: int, E: int, top_k: int) -> dict:
     L = _Layout()
     _check("moe_ffn_workspace_layout", lib().moe_ffn_workspace_layout(T, H, I, E, top_k, _c.byref(L)))
@@ -150,6 +172,8 @@ def moe_route_topk(logits: torch.Tensor, top_k: int, topk_ids: Optional[torch.Te
         topk_ids = torch.empty(T, top_k, dtype=torch.int32, device=logits.device)
     if topk_w is None:
         topk_w = torch.empty(T, top_k, dtype=torch.float32, device=logits.device)
+    _check_shape("topk_ids", topk_ids, (T, top_k))
+    _check_shape("topk_w", topk_w, (T, top_k))
     _check("moe_route_topk", lib().moe_route_topk(
         _dev(logits, "logits", torch.float32), T, E, top_k,
         _dev(topk_ids, "topk_ids", torch.int32), _dev(topk_w, "topk_w", torch.float32),
@@ -162,9 +186,8 @@ def moe_ffn_forward(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tenso
                     out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                     stream=None) -> torch.Tensor:
     """Routed-expert FFN layer with BF16 weights; returns ``out`` [T, H] bf16."""
-    T, H = x.shape
+    T, H, top_k = _layer_args(x, topk_ids, topk_w, out)
     E, I, H2 = W_gate.shape
-    top_k = topk_ids.shape[1]
     if H2 != H or tuple(W_up.shape) != (E, I, H) or tuple(W_down.shape) != (E, H, I):
         raise ValueError("weight shapes must be W_gate/W_up [E,I,H], W_down [E,H,I]")
     if out is None:
@@ -190,10 +213,14 @@ def moe_ffn_forward_logits(x: torch.Tensor, logits: torch.Tensor, top_k: int,
     """Routed-expert FFN layer from router logits [T, E] float32 (BF16
     weights); returns (out [T, H] bf16, topk_ids [T, k] int32, topk_w [T, k]
     float32)."""
+    if x.dim() != 2:
+        raise ValueError(f"x must be [T, H], got {list(x.shape)}")
     T, H = x.shape
     E, I, H2 = W_gate.shape
     if tuple(logits.shape) != (T, E):
         raise ValueError(f"logits must be [T, E] = [{T}, {E}], got {list(logits.shape)}")
+    if out is not None:
+        _check_shape("out", out, (T, H))
     if H2 != H or tuple(W_up.shape) != (E, I, H) or tuple(W_down.shape) != (E, H, I):
         raise ValueError("weight shapes must be W_gate/W_up [E,I,H], W_down [E,H,I]")
     if out is None:
@@ -223,20 +250,19 @@ def moe_ffn_forward_int8(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.
                          workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Routed-expert FFN layer with INT8 group-quantised weights; returns ``out``.
 
-    Scales are group-major: S_gate/S_up [E, H/128, I], S_down [E, I/128, H]."""
-    T, H = x.shape
+    Scales are row-major, one per 128 K of a row: S_gate/S_up [E, I, H/128],
+    S_down [E, H, I/128] (the layout the quantiser produces)."""
+    T, H, top_k = _layer_args(x, topk_ids, topk_w, out)
     E, I, H2 = Q_gate.shape
-    top_k = topk_ids.shape[1]
-    if H2 != H or tuple(Q_down.shape) != (E, H, I):
+    if H2 != H:
         raise ValueError("weight shapes must be Q_gate/Q_up [E,I,H], Q_down [E,H,I]")
     G = 128
     if H % G or I % G:
         raise ValueError("H and I must be multiples of 128")
-    for name, S, shape in (("S_gate", S_gate, (E, H // G, I)), ("S_up", S_up, (E, H // G, I)),
-                           ("S_down", S_down, (E, I // G, H))):
-        if tuple(S.shape) != shape:
-            raise ValueError(f"{name} must be group-major {list(shape)} (scale of row r, "
-                             f"group g at [e][g][r]), got {list(S.shape)}")
+    for name, t, shape in (("Q_up", Q_up, (E, I, H)), ("Q_down", Q_down, (E, H, I)),
+                           ("S_gate", S_gate, (E, I, H // G)), ("S_up", S_up, (E, I, H // G)),
+                           ("S_down", S_down, (E, H, I // G))):
+        _check_shape(name, t, shape)
     if out is None:
         out = torch.empty_like(x)
     if workspace is None:
@@ -259,19 +285,16 @@ def moe_ffn_forward_int4(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.
                          workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Routed-expert FFN layer with INT4 group-quantised weights, two
     offset-binary nibbles per byte (P_gate/P_up [E, I, H/2], P_down [E, H, I/2]
-    uint8); scales group-major as for INT8.  Returns ``out``."""
-    T, H = x.shape
+    uint8); scales row-major as for INT8.  Returns ``out``."""
+    T, H, top_k = _layer_args(x, topk_ids, topk_w, out)
     E, I, H2 = P_gate.shape
-    top_k = topk_ids.shape[1]
-    if 2 * H2 != H or tuple(P_up.shape) != (E, I, H // 2) or tuple(P_down.shape) != (E, H, I // 2):
-        raise ValueError("packed weights must be P_gate/P_up [E,I,H/2], P_down [E,H,I/2]")
     G = 128
-    if H % G or I % G:
-        raise ValueError("H and I must be multiples of 128")
-    for name, S, shape in (("S_gate", S_gate, (E, H // G, I)), ("S_up", S_up, (E, H // G, I)),
-                           ("S_down", S_down, (E, I // G, H))):
-        if tuple(S.shape) != shape:
-            raise ValueError(f"{name} must be group-major {list(shape)}, got {list(S.shape)}")
+    if 2 * H2 != H or H % G or I % G:
+        raise ValueError("P_gate must be [E,I,H/2] with H and I multiples of 128")
+    for name, t, shape in (("P_up", P_up, (E, I, H // 2)), ("P_down", P_down, (E, H, I // 2)),
+                           ("S_gate", S_gate, (E, I, H // G)), ("S_up", S_up, (E, I, H // G)),
+                           ("S_down", S_down, (E, H, I // G))):
+        _check_shape(name, t, shape)
     if out is None:
         out = torch.empty_like(x)
     if workspace is None:
@@ -301,6 +324,8 @@ def moe_route_grouped(logits: torch.Tensor, top_k: int, n_group: int, topk_group
         topk_w = torch.empty(T, top_k, dtype=torch.float32, device=logits.device)
     if bias is not None and tuple(bias.shape) != (E,):
         raise ValueError(f"bias must be [{E}], got {list(bias.shape)}")
+    _check_shape("topk_ids", topk_ids, (T, top_k))
+    _check_shape("topk_w", topk_w, (T, top_k))
     _check("moe_route_grouped", lib().moe_route_grouped(
         _dev(logits, "logits", torch.float32),
         None if bias is None else _dev(bias, "bias", torch.float32), T, E, n_group,
@@ -319,21 +344,20 @@ def moe_ffn_forward_resplit(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: tor
                             workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Routed-expert FFN layer with residual-split weights: gate/up as INT4
     W^Q plus INT4 residual W^R (packed [E, I, H/2] uint8), down as an INT4
-    ([E, H, I/2] uint8) and an INT8 ([E, H, I] int8) copy, scales group-major;
+    ([E, H, I/2] uint8) and an INT8 ([E, H, I] int8) copy, scales row-major;
     experts with ``critical[e]`` (uint8 [E]) nonzero use W^Q + W^R and the
     INT8 down, the others W^Q and the INT4 down.  Returns ``out``."""
-    T, H = x.shape
+    T, H, top_k = _layer_args(x, topk_ids, topk_w, out)
     E, I, H2 = P_gate.shape
-    top_k = topk_ids.shape[1]
     G = 128
     if 2 * H2 != H or H % G or I % G:
         raise ValueError("P_gate must be [E,I,H/2] with H and I multiples of 128")
     shapes = {"R_gate": (R_gate, (E, I, H // 2)), "P_up": (P_up, (E, I, H // 2)),
               "R_up": (R_up, (E, I, H // 2)), "P_down_lo": (P_down_lo, (E, H, I // 2)),
-              "Q_down_hi": (Q_down_hi, (E, H, I)), "S_gate": (S_gate, (E, H // G, I)),
-              "SR_gate": (SR_gate, (E, H // G, I)), "S_up": (S_up, (E, H // G, I)),
-              "SR_up": (SR_up, (E, H // G, I)), "S_down_lo": (S_down_lo, (E, I // G, H)),
-              "S_down_hi": (S_down_hi, (E, I // G, H)), "critical": (critical, (E,))}
+              "Q_down_hi": (Q_down_hi, (E, H, I)), "S_gate": (S_gate, (E, I, H // G)),
+              "SR_gate": (SR_gate, (E, I, H // G)), "S_up": (S_up, (E, I, H // G)),
+              "SR_up": (SR_up, (E, I, H // G)), "S_down_lo": (S_down_lo, (E, H, I // G)),
+              "S_down_hi": (S_down_hi, (E, H, I // G)), "critical": (critical, (E,))}
     for name, (t, shape) in shapes.items():
         if tuple(t.shape) != shape:
             raise ValueError(f"{name} must be {list(shape)}, got {list(t.shape)}")
@@ -401,15 +425,16 @@ def moe_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
                     stream=None) -> torch.Tensor:
     """Decode attention with grouped-query heads: q [B, h_q, d], k_cache /
     v_cache [B, h_kv, max_len, d] (bf16), seq_lens [B] int32 -> out [B, h_q, d]
-    bf16.  ``scale`` defaults to 1/sqrt(d)."""
+    bf16.  ``scale`` defaults to 1/sqrt(d) (chosen by the library: None is
+    passed as 0)."""
     B, h_q, d = q.shape
     B2, h_kv, max_len, d2 = k_cache.shape
     if B2 != B or d2 != d or tuple(v_cache.shape) != tuple(k_cache.shape):
         raise ValueError("k_cache / v_cache must be [B, h_kv, max_len, d] matching q")
     if tuple(seq_lens.shape) != (B,):
         raise ValueError("seq_lens must be [B]")
-    if scale is None:
-        scale = 1.0 / float(d) ** 0.5
+    if out is not None:
+        _check_shape("out", out, (B, h_q, d))
     if out is None:
         out = torch.empty_like(q)
     if workspace is None:
@@ -420,6 +445,7 @@ def moe_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
     _check("moe_attn_decode", lib().moe_attn_decode(
         _dev(q, "q", torch.bfloat16), _dev(k_cache, "k_cache", torch.bfloat16),
         _dev(v_cache, "v_cache", torch.bfloat16), _dev(seq_lens, "seq_lens", torch.int32),
-        _dev(out, "out", torch.bfloat16), B, h_q, h_kv, d, max_len, float(scale),
+        _dev(out, "out", torch.bfloat16), B, h_q, h_kv, d, max_len,
+        0.0 if scale is None else float(scale),
         _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream)))
     return out

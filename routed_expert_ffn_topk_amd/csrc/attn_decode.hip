@@ -1,8 +1,10 @@
 // Decode attention with grouped-query heads as small matrix products.
 //
-// HiNa-MoE §6.1: in decoding, the h_q / h_kv query heads that share one KV
-// head form a small block, so scoring it against the KV head's l_seq x d
-// keys, and weighting the l_seq x d values, are matrix products with a small
+// HiNa-MoE §6.1 (decode attention as small matrix products): under
+// grouped-query attention g = h_q / h_kv consecutive query heads read one KV
+// head, and a decoding step has one query row per head, so each KV head's
+// scores are a g-row matrix times its l_seq x d keys and its output is the
+// g-row softmax matrix times its l_seq x d values: products with one small
 // operand.  The small operand (the query block) is laid out once for the
 // matrix unit and kept resident; the keys are read in their native row-major
 // layout, which is already the MFMA A operand (one key row per lane, 8

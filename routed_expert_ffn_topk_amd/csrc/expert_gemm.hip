@@ -87,20 +87,17 @@ struct ExpertGemm {
 //   INT8: one 128-wide scale group = four MFMAs per matrix, four LDS blocks.
 // ---------------------------------------------------------------------------
 
-// Per-lane weight and scale pointers of one round: this lane's weight row at
-// its K group, and the scales of group 0 of its output rows (group-major,
-// spitch floats between groups).  r / sr: the second set (residuals).
+// Per-lane weight pointers of one round: this lane's weight row at its K
+// group; r: the second set (residuals).  Scales are not read per lane: the
+// workgroup stages each slab's scales in LDS (see gemm_rounds).
 struct WeightSrc {
     const void* w[2];
-    const float* s[2];
     const void* r[2];
-    const float* sr[2];
-    int spitch;
 };
 
 struct Bf16Weights {
     static constexpr bool kResidual = false;
-    static constexpr bool kQuadScales = false;
+    static constexpr bool kScaled = false;
     static constexpr int kBlocks = 1;
     static constexpr float kBytesPerWeight = 2.0f;
     static constexpr int kUnitBytes = kWave * 16;       // weight bytes a wave loads per unit
@@ -125,9 +122,12 @@ struct Bf16Weights {
                 d.w[i][m] = load16(static_cast<const uint16_t*>(src.w[m]) + (u + i) * 32);
     }
     // bl: this lane's B fragment of the batch's first LDS block; block b of
-    // the batch at bl[b * kBlockU4]
-    template <int NMAT, int U>
-    __device__ static void mma(const Batch<NMAT, U>& d, const u32x4* bl, f32x4* acc) {
+    // the batch at bl[b * kBlockU4].  sl: scales in LDS (scaled formats):
+    // unit i of scale tensor t at sl[t * TS + 16 * i], the lane's four output
+    // rows 4kg .. 4kg + 3 as one aligned f32x4
+    template <int NMAT, int U, int TS>
+    __device__ static void mma(const Batch<NMAT, U>& d, const u32x4* bl, const float*,
+                               f32x4* acc) {
 #pragma unroll
         for (int i = 0; i < U; ++i) {
             const u32x4 bq = bl[i * kBlockU4];
@@ -159,31 +159,30 @@ __device__ __forceinline__ bf16x8 i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
 // use).  The group's FP32 partial tile is scaled by the per-row scale of each
 // of the lane's four output rows (4kg + j) and added to the accumulator:
 //   dot(row, v) = sum_g s[row][g] * (sum_{c in g} v_c * q[row][c]).
-// Scales are stored group-major, s[e][g][row]: the four output rows of a lane
-// are one aligned 16-byte load, and a wave's scales of one group sit in one
-// 64-byte segment (row-major scales would cost a cache line per row).
+// The scales come from the slab's scale table in LDS.
+__device__ __forceinline__ f32x4 lds_f32x4(const float* p) {
+    return *reinterpret_cast<const f32x4*>(p);
+}
+
 struct Int8Weights {
     static constexpr bool kResidual = false;
+    static constexpr bool kScaled = true;
     static constexpr int kBlocks = 4;
     static constexpr float kBytesPerWeight = 1.0f;
     static constexpr int kUnitBytes = kWave * 32;       // weight bytes a wave loads per unit
-    static constexpr bool kQuadScales = false;
     template <int NMAT, int U>
     struct Batch {
         u32x4 w[U][NMAT][2];
-        f32x4 s[U][NMAT];
     };
-    // two 16-byte weight loads and one 16-byte scale load per unit and matrix
+    // two 16-byte weight loads per unit and matrix
     template <int NMAT, int U>
-    static constexpr int loads() { return U * NMAT * 3; }
+    static constexpr int loads() { return U * NMAT * 2; }
     __device__ static int block_offset(int sub, int kg) {
         return (sub >> 1) * 64 + kg * 16 + (sub & 1) * 8;
     }
     __device__ static const void* row_ptr(const void* base, size_t row, int K, int kg) {
         return static_cast<const int8_t*>(base) + row * K + kg * 16;
     }
-    // a[m]: weight row at K offset 16*kg; sc[m]: scales of group 0 of the
-    // lane's output rows 4*kg..4*kg+3; spitch: floats between groups (N)
     template <int NMAT, int U>
     __device__ static void load(Batch<NMAT, U>& d, const WeightSrc& src, int u) {
 #pragma unroll
@@ -193,12 +192,11 @@ struct Int8Weights {
                 const int8_t* p = static_cast<const int8_t*>(src.w[m]) + (size_t)(u + i) * 128;
                 d.w[i][m][0] = load16(p);
                 d.w[i][m][1] = load16(p + 64);
-                d.s[i][m] = __builtin_bit_cast(
-                    f32x4, load16(src.s[m] + (size_t)(u + i) * src.spitch));
             }
     }
-    template <int NMAT, int U>
-    __device__ static void mma(const Batch<NMAT, U>& d, const u32x4* bl, f32x4* acc) {
+    template <int NMAT, int U, int TS>
+    __device__ static void mma(const Batch<NMAT, U>& d, const u32x4* bl, const float* sl,
+                               f32x4* acc) {
 #pragma unroll
         for (int i = 0; i < U; ++i) {
 #pragma unroll
@@ -212,7 +210,7 @@ struct Int8Weights {
                     part = mfma16x16x32(i8x8_to_bf16x8(w.z, w.w),
                                         as_bf16x8(bl[(4 * i + 2 * c + 1) * kBlockU4]), part);
                 }
-                acc[m] += d.s[i][m] * part;
+                acc[m] += lds_f32x4(sl + m * TS + 16 * i) * part;
             }
         }
     }
@@ -235,23 +233,17 @@ struct Int8Weights {
 // weight.
 struct Int4Weights {
     static constexpr bool kResidual = false;
+    static constexpr bool kScaled = true;
     static constexpr int kBlocks = 4;
     static constexpr float kBytesPerWeight = 0.5f;
     static constexpr int kUnitBytes = kWave * 16;       // weight bytes a wave loads per unit
-    // each lane loads the scale of one output row, 4kg + (lane & 3), with a
-    // 4-byte load, and the quad's four are gathered with DPP broadcasts: a
-    // 16-byte load of the lane's four rows would cost the load pipeline as
-    // much as the weights, and the registers saved let four workgroups share
-    // a CU
-    static constexpr bool kQuadScales = true;
     template <int NMAT, int U>
     struct Batch {
         u32x4 w[U][NMAT];
-        float s[U][NMAT];
     };
-    // one 16-byte weight load and one 4-byte scale load per unit and matrix
+    // one 16-byte weight load per unit and matrix
     template <int NMAT, int U>
-    static constexpr int loads() { return U * NMAT * 2; }
+    static constexpr int loads() { return U * NMAT; }
     __device__ static int block_offset(int sub, int kg) { return kg * 32 + sub * 8; }
     __device__ static const void* row_ptr(const void* base, size_t row, int K, int kg) {
         return static_cast<const uint8_t*>(base) + row * (size_t)(K / 2) + kg * 16;
@@ -261,10 +253,8 @@ struct Int4Weights {
 #pragma unroll
         for (int i = 0; i < U; ++i)
 #pragma unroll
-            for (int m = 0; m < NMAT; ++m) {
+            for (int m = 0; m < NMAT; ++m)
                 d.w[i][m] = load16(static_cast<const uint8_t*>(src.w[m]) + (size_t)(u + i) * 64);
-                d.s[i][m] = src.s[m][(size_t)(u + i) * src.spitch];
-            }
     }
     __device__ static u32x4 nibbles_to_bf16(uint32_t w) {
         constexpr uint32_t kMask = 0x000F000Fu, kBias = 0x43004300u;
@@ -276,8 +266,9 @@ struct Int4Weights {
         return u32x4{(b.x & 0xffffu) | (b.z << 16), (b.x >> 16) | (b.z & 0xffff0000u),
                      (b.y & 0xffffu) | (b.w << 16), (b.y >> 16) | (b.w & 0xffff0000u)};
     }
-    template <int NMAT, int U>
-    __device__ static void mma(const Batch<NMAT, U>& d, const u32x4* bl, f32x4* acc) {
+    template <int NMAT, int U, int TS>
+    __device__ static void mma(const Batch<NMAT, U>& d, const u32x4* bl, const float* sl,
+                               f32x4* acc) {
         const u32x4 k136 = {0x43084308u, 0x43084308u, 0x43084308u, 0x43084308u};  // BF16 136
 #pragma unroll
         for (int i = 0; i < U; ++i) {
@@ -296,7 +287,7 @@ struct Int4Weights {
                 for (int t = 0; t < 4; ++t)
                     part = mfma16x16x32(as_bf16x8(nibbles_to_bf16(words[t])), as_bf16x8(bx[t]),
                                         part);
-                acc[m] += quad_gather_f32(d.s[i][m]) * (part - corr);
+                acc[m] += lds_f32x4(sl + m * TS + 16 * i) * (part - corr);
             }
         }
     }
@@ -313,7 +304,7 @@ struct Int4Weights {
 //   acc += s_Q (sum (128 + u_Q) x - 136 sum x) + s_R (sum (128 + u_R) x - 136 sum x).
 struct Int4ResidualWeights {
     static constexpr bool kResidual = true;
-    static constexpr bool kQuadScales = true;
+    static constexpr bool kScaled = true;
     static constexpr int kBlocks = 4;
     static constexpr float kBytesPerWeight = 1.0f;
     static constexpr int kUnitBytes = 2 * kWave * 16;
@@ -321,11 +312,9 @@ struct Int4ResidualWeights {
     struct Batch {
         u32x4 w[U][NMAT];
         u32x4 r[U][NMAT];
-        float s[U][NMAT];
-        float sr[U][NMAT];
     };
     template <int NMAT, int U>
-    static constexpr int loads() { return U * NMAT * 4; }
+    static constexpr int loads() { return U * NMAT * 2; }
     __device__ static int block_offset(int sub, int kg) {
         return Int4Weights::block_offset(sub, kg);
     }
@@ -338,15 +327,15 @@ struct Int4ResidualWeights {
         for (int i = 0; i < U; ++i)
 #pragma unroll
             for (int m = 0; m < NMAT; ++m) {
-                const size_t wo = (size_t)(u + i) * 64, so = (size_t)(u + i) * src.spitch;
+                const size_t wo = (size_t)(u + i) * 64;
                 d.w[i][m] = load16(static_cast<const uint8_t*>(src.w[m]) + wo);
                 d.r[i][m] = load16(static_cast<const uint8_t*>(src.r[m]) + wo);
-                d.s[i][m] = src.s[m][so];
-                d.sr[i][m] = src.sr[m][so];
             }
     }
-    template <int NMAT, int U>
-    __device__ static void mma(const Batch<NMAT, U>& d, const u32x4* bl, f32x4* acc) {
+    // scale tensors: W^Q's of the NMAT matrices first, then W^R's
+    template <int NMAT, int U, int TS>
+    __device__ static void mma(const Batch<NMAT, U>& d, const u32x4* bl, const float* sl,
+                               f32x4* acc) {
         const u32x4 k136 = {0x43084308u, 0x43084308u, 0x43084308u, 0x43084308u};  // BF16 136
 #pragma unroll
         for (int i = 0; i < U; ++i) {
@@ -369,8 +358,8 @@ struct Int4ResidualWeights {
                     pr = mfma16x16x32(as_bf16x8(Int4Weights::nibbles_to_bf16(rw[t])),
                                       as_bf16x8(bx[t]), pr);
                 }
-                acc[m] += quad_gather_f32(d.s[i][m]) * (pq - corr) +
-                          quad_gather_f32(d.sr[i][m]) * (pr - corr);
+                acc[m] += lds_f32x4(sl + m * TS + 16 * i) * (pq - corr) +
+                          lds_f32x4(sl + (NMAT + m) * TS + 16 * i) * (pr - corr);
             }
         }
     }
@@ -390,6 +379,23 @@ struct MixedWeights {
     static constexpr float kBytesPerWeight = Hi::kBytesPerWeight;
     static constexpr int kUnitBytes = Hi::kUnitBytes;
 };
+
+// Scale tensors a round of format F reads (each staged per slab in LDS):
+// one per matrix, two per matrix for a residual format, none for BF16.
+template <class F, int NMAT>
+struct ScaleTensors {
+    static constexpr int value = F::kScaled ? NMAT * (F::kResidual ? 2 : 1) : 0;
+};
+template <class Lo, class Hi, bool b, int NMAT>
+struct ScaleTensors<MixedWeights<Lo, Hi, b>, NMAT> {
+    static constexpr int lo = ScaleTensors<Lo, NMAT>::value;
+    static constexpr int hi = ScaleTensors<Hi, NMAT>::value;
+    static constexpr int value = lo > hi ? lo : hi;
+};
+// Floats of one slab's scale table per tensor at K split S: R row blocks x S
+// K parts x (units per part and slab) x 16 rows = 256 / S (for 4-block units).
+constexpr int kScaleSlabFloats = 256;
+
 template <class F>
 struct IsMixed {
     static constexpr bool value = false;
@@ -414,49 +420,58 @@ using DualDown = MixedWeights<Int4Weights, Int8Weights, true>;
 // Tuning per weight format and projection, measured on MI355X over the
 // Mixtral-8x7B, DeepSeek-V3, Qwen3-235B and Mixtral-8x22B expert shapes at
 // 1-16 tokens per expert (INT4 and the residual split: the Mixtral-8x7B
-// shape): batch length U (units) and resident workgroups per CU (LDS: 32 KB
-// per workgroup).
+// shape): batch length U (units), resident workgroups per CU (LDS: 33-42 KB
+// per workgroup) and the weight batches held in registers (kDepth: 2, one
+// batch in flight while the other is multiplied, or 3, two in flight).
 template <class Fmt, int NMAT>
 struct GemmTuning;
 template <>
 struct GemmTuning<Bf16Weights, 2> {   // gate/up: two matrices per K step
     static constexpr int kBlocksPerCU = 4;
     static constexpr int kBatch = 2;
+    static constexpr int kDepth = 2;
 };
 template <>
 struct GemmTuning<Bf16Weights, 1> {   // down
     static constexpr int kBlocksPerCU = 3;
     static constexpr int kBatch = 8;
+    static constexpr int kDepth = 2;
 };
 template <>
 struct GemmTuning<Int8Weights, 2> {
     static constexpr int kBlocksPerCU = 3;
     static constexpr int kBatch = 1;
+    static constexpr int kDepth = 2;
 };
 template <>
 struct GemmTuning<Int8Weights, 1> {
     static constexpr int kBlocksPerCU = 3;
     static constexpr int kBatch = 2;
+    static constexpr int kDepth = 2;
 };
 template <>
 struct GemmTuning<Int4Weights, 2> {
     static constexpr int kBlocksPerCU = 4;
     static constexpr int kBatch = 1;
+    static constexpr int kDepth = 2;
 };
 template <>
 struct GemmTuning<ResidualGateUp, 2> {
     static constexpr int kBlocksPerCU = 2;
     static constexpr int kBatch = 2;
+    static constexpr int kDepth = 2;
 };
 template <>
 struct GemmTuning<DualDown, 1> {
     static constexpr int kBlocksPerCU = 2;
     static constexpr int kBatch = 2;
+    static constexpr int kDepth = 2;
 };
 template <>
 struct GemmTuning<Int4Weights, 1> {
     static constexpr int kBlocksPerCU = 2;
     static constexpr int kBatch = 4;
+    static constexpr int kDepth = 2;
 };
 
 // S: K-parts per row block; U: units per weight batch (divides the units of
@@ -467,14 +482,21 @@ struct GemmTuning<Int4Weights, 1> {
 // all active experts (expert-major) are dealt out per XCD: each XCD owns a
 // contiguous slice, and its workgroups take the slice's rounds interleaved
 // (an equal number each, +-1).
-template <class Fmt, int NMAT, int S, int U>
+template <class Fmt, int NMAT, int S, int U, int D>
 __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, int n_act, int grid,
-                                            u32x4 (*xs)[kSlabU4]) {
+                                            u32x4 (*xs)[kSlabU4], f32x4* sc) {
     constexpr int R = kWaves / S;              // row blocks per round
     constexpr int SP = kSlabBlocks / S;        // LDS blocks of each K part per slab
     constexpr int SPU = SP / Fmt::kBlocks;     // units of each K part per slab
     constexpr int NB = SPU / U;                // full batches per full slab
     static_assert(SPU >= 1 && SPU % U == 0, "batch must divide the slab part");
+    static_assert(D == 2 || D == 3, "two or three weight batches in registers");
+    // scale table of a slab (scaled formats): per tensor, [R][S][SPU][16 rows]
+    // floats, TS apart; two buffers (slabs alternate), SCB floats apart
+    constexpr int NSC = ScaleTensors<Fmt, NMAT>::value;
+    constexpr int TS = R * S * SPU * 16;
+    constexpr int SCB = NSC * kScaleSlabFloats;
+    static_assert(NSC == 0 || TS <= kScaleSlabFloats, "scale table fits its buffer");
     // after the slab loop the first slab buffer doubles as the K-part
     // reduction area (3 x NMAT x 1 KB <= 16 KB)
     f32x4* red = reinterpret_cast<f32x4*>(&xs[0][0]);
@@ -520,29 +542,32 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, int n_act, int 
         auto round = [&](auto tag) {
             using F = typename decltype(tag)::Fmt;
             constexpr bool kSecond = decltype(tag)::kFromSecond;
-            // scales of group 0 of this lane's output rows 4kg..4kg+3
-            // (group-major; with quad scales, of row 4kg + (lane & 3) alone:
-            // the lanes of a quad share kg)
-            const size_t srow = (size_t)e * nunits * g.N + row0 + 4 * kg +
-                                (F::kQuadScales ? (lane & 3) : 0);
+            constexpr int NSCF = ScaleTensors<F, NMAT>::value;
             const void* w0 = kSecond ? g.hw0 : g.w0;
             const void* w1 = NMAT == 2 ? (kSecond ? g.hw1 : g.w1) : w0;
-            const float* s0 = kSecond ? g.hs0 : g.s0;
-            const float* s1 = kSecond ? g.hs1 : g.s1;
             WeightSrc src;
             src.w[0] = F::row_ptr(w0, arow, g.K, kg);
             src.w[1] = F::row_ptr(w1, arow, g.K, kg);
-            src.s[0] = s0 ? s0 + srow : nullptr;
-            src.s[1] = NMAT == 2 && s1 ? s1 + srow : nullptr;
             src.r[0] = src.r[1] = nullptr;
-            src.sr[0] = src.sr[1] = nullptr;
             if constexpr (F::kResidual) {
                 src.r[0] = F::row_ptr(g.hw0, arow, g.K, kg);
                 src.r[1] = F::row_ptr(NMAT == 2 ? g.hw1 : g.hw0, arow, g.K, kg);
-                src.sr[0] = g.hs0 + srow;
-                src.sr[1] = NMAT == 2 ? g.hs1 + srow : nullptr;
             }
-            src.spitch = g.N;
+            // the expert's row-major scale tables [N][nunits], in the order
+            // the format's mma reads them: the matrices' (first or second
+            // set), then a residual format's second set
+            const float* stab[4] = {nullptr, nullptr, nullptr, nullptr};
+            if constexpr (NSCF > 0) {
+                const size_t eoff = (size_t)e * g.N * nunits;
+                const float* p0 = kSecond ? g.hs0 : g.s0;
+                const float* p1 = kSecond ? g.hs1 : g.s1;
+                stab[0] = p0 + eoff;
+                if (NMAT == 2) stab[1] = p1 + eoff;
+                if constexpr (F::kResidual) {
+                    stab[NMAT] = g.hs0 + eoff;
+                    if (NMAT == 2) stab[NMAT + 1] = g.hs1 + eoff;
+                }
+            }
             for (int c0 = 0; c0 < m; c0 += 16) {
                 const int ntok = min(16, m - c0);        // distinct tokens of the chunk
                 // padding columns (beyond the expert's tokens) read token 0's row:
@@ -554,7 +579,7 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, int n_act, int 
                 // request it before the token rows, whose addresses take two
                 // dependent loads (the first slab then waits for everything)
                 constexpr int kLoads = F::template loads<NMAT, U>();
-                typename F::template Batch<NMAT, U> A, B;
+                typename F::template Batch<NMAT, U> A, B, C;   // C: depth 3 only
                 if (nfull > 0) F::template load<NMAT, U>(A, src, u0);
                 // token rows this wave stages: tokens wave, wave + 4, ...
                 const uint16_t* tp[4];
@@ -574,6 +599,10 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, int n_act, int 
                 // load instruction stages one token's whole slab row (1 KB): lane
                 // L fills block L/4 for K group L%4, so the row is read from
                 // global memory in contiguous runs of 1024/S bytes.
+                // Scaled formats also stage the slab's scales: entry
+                // ((rr*S + pp)*SPU + jj)*16 + row of tensor t is the scale of
+                // row 16*(rb0 + rr) + row, unit start(pp) + j*SPU + jj; one
+                // 4-byte direct load per lane fills 64 consecutive entries.
                 auto stage = [&](int j, int bsel) {
                     const int blk = lane >> 2;
                     const int kgl = lane & 3;
@@ -591,47 +620,115 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, int n_act, int 
                                                              (lds_void_ptr)&xs[bsel][tok_base(c)], 16,
                                                              0, 0);
                     }
+                    if constexpr (NSCF > 0) {
+                        // wave w < TS / 64 fills entries [64w, 64w + 64) of
+                        // every tensor's table: one offset per lane serves
+                        // all tensors (they share the [N][nunits] shape)
+                        static_assert(TS % kWave == 0 && TS / kWave <= kWaves, "scale loads");
+                        if (wave < TS / kWave) {
+                            const int f = wave * kWave + lane;
+                            const int row = f & 15;
+                            const int qf = f >> 4;
+                            const int jj = qf % SPU;
+                            const int rp = qf / SPU;
+                            const int spp = rp % S;
+                            const int rb = rb0 + rp / S;
+                            const int q0 = min(nunits, spp * kpu);
+                            const int q1 = min(nunits, q0 + kpu);
+                            const int su = q0 + j * SPU + jj;
+                            const size_t off = (size_t)(rb * 16 + row) * nunits + su;
+                            float* dst = reinterpret_cast<float*>(sc) + bsel * SCB + wave * kWave;
+                            if (rb < nrb && su < q1) {
+    #pragma unroll
+                                for (int t = 0; t < NSCF; ++t)
+                                    __builtin_amdgcn_global_load_lds(
+                                        (const void*)(stab[t] + off), (lds_void_ptr)(dst + t * TS),
+                                        4, 0, 0);
+                            }
+                        }
+                    }
                 };
                 stage(0, 0);
-                // weight batches ping-pong between two register sets: batch bi
-                // lives in A when bi is even, in B when odd; the next batch is
-                // always requested before the current one is multiplied
+                // Weight batches rotate through D register sets: batch bi
+                // lives in set bi % D, and batch bi + D - 1 is requested just
+                // before batch bi is multiplied, so D - 1 batches are in flight.
+                // With D = 3 the second batch is requested after the first
+                // slab's staging loads.
+                if constexpr (D == 3)
+                    if (nfull > 1) F::template load<NMAT, U>(B, src, u0 + U);
+                // batch requests issued since the latest staging loads (D = 3)
+                int since = (D == 3 && nfull > 1) ? 1 : 0;
                 int bi = 0;
                 for (int j = 0; j < nslab; ++j) {
-                    // this wave's staging loads are done (only the batch
-                    // prefetched for this slab may still be in flight; at slab
-                    // 0, whose staging follows the first batch, everything)
-                    if (j == 0)
-                        wait_vmcnt<0>();
-                    else if (bi < nfull)
-                        wait_vmcnt<(kLoads < 63 ? kLoads : 63)>();
-                    else
-                        wait_vmcnt<0>();
+                    // this wave's staging loads are done; only batch requests
+                    // issued after them and not yet multiplied may still be in
+                    // flight (loads complete in issue order)
+                    if constexpr (D == 2) {
+                        if (j == 0)
+                            wait_vmcnt<0>();
+                        else if (bi < nfull)
+                            wait_vmcnt<(kLoads < 63 ? kLoads : 63)>();
+                        else
+                            wait_vmcnt<0>();
+                    } else {
+                        const int pend = min(since, min(D - 1, nfull - bi));
+                        if (pend >= 2)
+                            wait_vmcnt<(2 * kLoads < 63 ? 2 * kLoads : 63)>();
+                        else if (pend == 1)
+                            wait_vmcnt<(kLoads < 63 ? kLoads : 63)>();
+                        else
+                            wait_vmcnt<0>();
+                    }
                     __syncthreads();
-                    if (j + 1 < nslab) stage(j + 1, (j + 1) & 1);
+                    if (j + 1 < nslab) {
+                        stage(j + 1, (j + 1) & 1);
+                        since = 0;
+                    }
                     const int slab_u0 = u0 + j * SPU;
                     // this lane's B fragments: token row bcol, K group kg, from the
                     // first block of this wave's K part
                     const u32x4* buf = &xs[j & 1][tok_base(bcol) + kp * SP * kBlockU4 + kg];
+                    // this lane's scales: row block r, K part kp, unit 0 of the
+                    // slab, output rows 4kg .. 4kg + 3
+                    const float* sl = reinterpret_cast<const float*>(sc) + (j & 1) * SCB +
+                                      (r * S + kp) * SPU * 16 + 4 * kg;
                     const int bend = min(nfull, (j + 1) * NB);
                     for (; bi < bend; ++bi) {
-                        const u32x4* bb = buf + (u0 + bi * U - slab_u0) * F::kBlocks * kBlockU4;
-                        if ((bi & 1) == 0) {
-                            if (bi + 1 < nfull)
-                                F::template load<NMAT, U>(B, src, u0 + (bi + 1) * U);
-                            F::template mma<NMAT, U>(A, bb, acc);
+                        const int ub = u0 + bi * U - slab_u0;   // batch's first unit in the slab
+                        const u32x4* bb = buf + ub * F::kBlocks * kBlockU4;
+                        const float* sb = sl + 16 * ub;
+                        const int nx = bi + D - 1;              // batch requested now
+                        const int ux = u0 + nx * U;
+                        if constexpr (D == 2) {
+                            if ((bi & 1) == 0) {
+                                if (nx < nfull) F::template load<NMAT, U>(B, src, ux);
+                                F::template mma<NMAT, U, TS>(A, bb, sb, acc);
+                            } else {
+                                if (nx < nfull) F::template load<NMAT, U>(A, src, ux);
+                                F::template mma<NMAT, U, TS>(B, bb, sb, acc);
+                            }
                         } else {
-                            if (bi + 1 < nfull)
-                                F::template load<NMAT, U>(A, src, u0 + (bi + 1) * U);
-                            F::template mma<NMAT, U>(B, bb, acc);
+                            if (nx < nfull) ++since;
+                            const int ph = bi % 3;
+                            if (ph == 0) {
+                                if (nx < nfull) F::template load<NMAT, U>(C, src, ux);
+                                F::template mma<NMAT, U, TS>(A, bb, sb, acc);
+                            } else if (ph == 1) {
+                                if (nx < nfull) F::template load<NMAT, U>(A, src, ux);
+                                F::template mma<NMAT, U, TS>(B, bb, sb, acc);
+                            } else {
+                                if (nx < nfull) F::template load<NMAT, U>(B, src, ux);
+                                F::template mma<NMAT, U, TS>(C, bb, sb, acc);
+                            }
                         }
                     }
                     if (has && tail_u < u1 && tail_u >= slab_u0 && tail_u < slab_u0 + SPU)
                         for (int u = tail_u; u < u1; ++u) {
                             typename F::template Batch<NMAT, 1> t;
                             F::template load<NMAT, 1>(t, src, u);
-                            F::template mma<NMAT, 1>(
-                                t, buf + (u - slab_u0) * F::kBlocks * kBlockU4, acc);
+                            F::template mma<NMAT, 1, TS>(
+                                t, buf + (u - slab_u0) * F::kBlocks * kBlockU4,
+                                sl + 16 * (u - slab_u0), acc);
                         }
                 }
                 __syncthreads();
@@ -743,19 +840,28 @@ __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(GemmTuning<Fmt, NMAT>::kBlocksPerCU)))
 void expert_gemm_kernel(const ExpertGemm g) {
     constexpr int U = GemmTuning<Fmt, NMAT>::kBatch;
+    constexpr int D = GemmTuning<Fmt, NMAT>::kDepth;
     constexpr int units1 = kSlabBlocks / Fmt::kBlocks;   // units of a part per slab, S = 1
-    // K-slab buffers of the token tile, double-buffered
-    __shared__ u32x4 xs[2][kSlabU4];
+    // K-slab buffers of the token tile, double-buffered, followed (scaled
+    // formats) by the slabs' scale tables.  Both are filled by direct
+    // global->LDS loads and live in one LDS array: the compiler then leaves
+    // the waits for those loads to the kernel's own (vmcnt wait + barrier per
+    // slab), whereas with two arrays it waited for every outstanding load
+    // before each LDS read, which serialised the weight prefetch.
+    constexpr int kScF4 = ScaleTensors<Fmt, NMAT>::value * kScaleSlabFloats / 4 * 2;
+    __shared__ u32x4 lds[2 * kSlabU4 + kScF4];
+    u32x4 (*xs)[kSlabU4] = reinterpret_cast<u32x4 (*)[kSlabU4]>(lds);
+    f32x4* sc = reinterpret_cast<f32x4*>(lds + 2 * kSlabU4);
     const int n_act = g.meta[0];
     const int S = g.split ? g.split : choose_split<Fmt, NMAT, U>(g, n_act);
     const int G = busy_grid(rounds_for(n_act, g.N / 16, S));
     if ((int)blockIdx.x >= G) return;
     if (S == 1)
-        gemm_rounds<Fmt, NMAT, 1, cmin(U, units1)>(g, n_act, G, xs);
+        gemm_rounds<Fmt, NMAT, 1, cmin(U, units1), D>(g, n_act, G, xs, sc);
     else if (S == 2)
-        gemm_rounds<Fmt, NMAT, 2, cmin(U, units1 / 2)>(g, n_act, G, xs);
+        gemm_rounds<Fmt, NMAT, 2, cmin(U, units1 / 2), D>(g, n_act, G, xs, sc);
     else
-        gemm_rounds<Fmt, NMAT, 4, cmin(U, units1 / 4)>(g, n_act, G, xs);
+        gemm_rounds<Fmt, NMAT, 4, cmin(U, units1 / 4), D>(g, n_act, G, xs, sc);
 }
 
 // Grid of one grouped product: persistent, the resident workgroup count,

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cmath>
 #include <cstdint>
 
 #include "launch.hpp"
@@ -27,6 +28,7 @@ bool shape_ok(int64_t T, int64_t H, int64_t I, int32_t E, int32_t top_k) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 bool overlap(const void* a, size_t na, const void* b, size_t nb) {
     const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
@@ -259,8 +261,8 @@ int moe_ffn_forward_int8(const void* x, const int32_t* topk_ids, const float* to
                            workspace_bytes, MOE_FFN_INT8_GROUP, &L);
     if (rc != MOE_FFN_OK || T == 0) return rc;
     if (!Q_gate || !S_gate || !Q_up || !S_up || !Q_down || !S_down) return MOE_FFN_ERR_NULL_ARG;
-    if (!aligned16(Q_gate) || !aligned16(Q_up) || !aligned16(Q_down) || !aligned16(S_gate) ||
-        !aligned16(S_up) || !aligned16(S_down))
+    if (!aligned16(Q_gate) || !aligned16(Q_up) || !aligned16(Q_down) || !aligned4(S_gate) ||
+        !aligned4(S_up) || !aligned4(S_down))
         return MOE_FFN_ERR_MISALIGNED;
     int ncu = 0;
     if ((rc = num_cu(&ncu)) != MOE_FFN_OK) return rc;
@@ -323,6 +325,8 @@ int moe_attn_decode(const void* q, const void* k_cache, const void* v_cache,
                          overlap(workspace, wb, v_cache, kvb))) ||
         overlap(workspace, wb, q, qb) || overlap(workspace, wb, seq_lens, (size_t)B * 4))
         return MOE_FFN_ERR_ALIAS;
+    // the standard score scale unless the caller gives a positive one
+    if (!(scale > 0.f)) scale = (float)(1.0 / std::sqrt((double)d));
     const hipError_t err = moe::launch_attn_decode(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
         static_cast<const uint16_t*>(v_cache), seq_lens, static_cast<uint16_t*>(out), B, h_q,
@@ -342,8 +346,8 @@ int moe_ffn_forward_int4(const void* x, const int32_t* topk_ids, const float* to
                            workspace_bytes, MOE_FFN_INT8_GROUP, &L);
     if (rc != MOE_FFN_OK || T == 0) return rc;
     if (!P_gate || !S_gate || !P_up || !S_up || !P_down || !S_down) return MOE_FFN_ERR_NULL_ARG;
-    if (!aligned16(P_gate) || !aligned16(P_up) || !aligned16(P_down) || !aligned16(S_gate) ||
-        !aligned16(S_up) || !aligned16(S_down))
+    if (!aligned16(P_gate) || !aligned16(P_up) || !aligned16(P_down) || !aligned4(S_gate) ||
+        !aligned4(S_up) || !aligned4(S_down))
         return MOE_FFN_ERR_MISALIGNED;
     int ncu = 0;
     if ((rc = num_cu(&ncu)) != MOE_FFN_OK) return rc;
@@ -370,11 +374,15 @@ int moe_ffn_forward_resplit(const void* x, const int32_t* topk_ids, const float*
     int rc = check_forward(x, topk_ids, topk_w, out, T, H, I, E, top_k, workspace,
                            workspace_bytes, MOE_FFN_INT8_GROUP, &L);
     if (rc != MOE_FFN_OK || T == 0) return rc;
-    const void* const tensors[] = {P_gate, S_gate, R_gate, SR_gate, P_up, S_up,
-                                   R_up, SR_up, P_down_lo, S_down_lo, Q_down_hi, S_down_hi};
-    for (const void* t : tensors) {
+    const void* const weights[] = {P_gate, R_gate, P_up, R_up, P_down_lo, Q_down_hi};
+    const void* const scales[] = {S_gate, SR_gate, S_up, SR_up, S_down_lo, S_down_hi};
+    for (const void* t : weights) {
         if (!t) return MOE_FFN_ERR_NULL_ARG;
         if (!aligned16(t)) return MOE_FFN_ERR_MISALIGNED;
+    }
+    for (const void* t : scales) {
+        if (!t) return MOE_FFN_ERR_NULL_ARG;
+        if (!aligned4(t)) return MOE_FFN_ERR_MISALIGNED;
     }
     if (!critical) return MOE_FFN_ERR_NULL_ARG;
     int ncu = 0;

@@ -1,13 +1,20 @@
 """C ABI checks that need no GPU: symbols, workspace layout, host-side validation.
 
-Every call here returns before any HIP call (invalid arguments are rejected on
-the host), so fake, never-dereferenced device addresses are safe to pass.
+The validation tests pass fake, never-dereferenced device addresses.  Each of
+them expects the call to be rejected on the host; if a check were missing,
+the call would go on to launch kernels on those addresses.  So they run only
+in a child process in which no GPU is visible (``test_fake_address_calls``
+starts it; there a call that wrongly passes its checks fails to find a device
+and returns MOE_FFN_ERR_HIP), never in a process that can reach a GPU.
 """
 import ctypes
 import os
 import re
+import subprocess
+import sys
 
 import pytest
+import torch
 
 import routed_expert_ffn_topk_amd as moe
 
@@ -15,6 +22,28 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe_ffn.h")
 
 A = 0x7f0000000000  # fake, 256-byte aligned device address
+
+CHILD_ENV = "MOE_FFN_ABI_NO_GPU_CHILD"
+IN_CHILD = os.environ.get(CHILD_ENV) == "1"
+# fake-address tests: only in the child, and only if it really sees no GPU
+# (torch.cuda.device_count() counts devices without initialising one)
+fake = pytest.mark.skipif(not IN_CHILD or torch.cuda.device_count() > 0,
+                          reason="fake device addresses: run by test_fake_address_calls "
+                                 "in a child process with no visible GPU")
+
+
+@pytest.mark.skipif(IN_CHILD, reason="this is the child")
+def test_fake_address_calls():
+    """Run this file's fake-address tests in a child process that sees no GPU."""
+    env = dict(os.environ, **{CHILD_ENV: "1", "HIP_VISIBLE_DEVICES": "-1",
+                              "CUDA_VISIBLE_DEVICES": "-1", "ROCR_VISIBLE_DEVICES": "-1"})
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-p", "no:cacheprovider",
+                        "-m", "not gpu", "-rs", os.path.abspath(__file__)],
+                       env=env, cwd=ROOT, capture_output=True, text=True, timeout=600)
+    out = r.stdout[-6000:] + r.stderr[-2000:]
+    assert r.returncode == 0, out
+    # in the child only this launcher itself is skipped
+    assert "1 skipped" in out.splitlines()[-1], "fake-address tests skipped in the child:\n" + out
 
 
 def declared_functions():
@@ -93,6 +122,7 @@ def fwd(**kw):
                                      a["ws"], a["wsb"], None)
 
 
+@fake
 def test_forward_host_validation():
     assert fwd(T=0) == moe.MOE_FFN_OK                       # empty batch: no-op
     assert fwd(H=48) == moe.MOE_FFN_ERR_BAD_SHAPE            # H not a multiple of 32
@@ -121,6 +151,7 @@ def fwd_logits(**kw):
                                             a["k"], a["ws"], a["wsb"], None)
 
 
+@fake
 def test_forward_logits_host_validation():
     assert fwd_logits(T=0) == moe.MOE_FFN_OK
     assert fwd_logits(k=65, E=128) == moe.MOE_FFN_ERR_BAD_SHAPE    # router handles k <= 64
@@ -141,6 +172,7 @@ def test_forward_logits_host_validation():
     assert fwd_logits(out=A + 64) == moe.MOE_FFN_ERR_ALIAS
 
 
+@fake
 def test_forward_int8_requires_group_multiples():
     L = moe.lib()
     rc = L.moe_ffn_forward_int8(A, A + 0x100000, A + 0x200000, A + 0x1000000, A + 0x1800000,
@@ -153,6 +185,7 @@ def test_forward_int8_requires_group_multiples():
     assert rc == moe.MOE_FFN_ERR_NULL_ARG
 
 
+@fake
 @pytest.mark.parametrize("group", [0, 64, 256, -128])
 def test_forward_int8_rejects_other_groups(group):
     L = moe.lib()
@@ -163,6 +196,7 @@ def test_forward_int8_rejects_other_groups(group):
     assert rc == moe.MOE_FFN_ERR_BAD_SHAPE
 
 
+@fake
 def test_route_host_validation():
     L = moe.lib()
     assert L.moe_route_topk(A, 0, 8, 2, A + 0x1000, A + 0x2000, None) == moe.MOE_FFN_OK
@@ -173,6 +207,7 @@ def test_route_host_validation():
     assert L.moe_route_topk(A, 4, 8, 2, A + 0x1001, A + 0x2000, None) == moe.MOE_FFN_ERR_MISALIGNED
 
 
+@fake
 def test_read_probe_host_validation():
     L = moe.lib()
     assert L.moe_ffn_read_probe(None, 1 << 20, A + 0x100000, None) == moe.MOE_FFN_ERR_NULL_ARG
@@ -213,6 +248,7 @@ def attn(**kw):
                                      a["wsb"], None)
 
 
+@fake
 def test_attn_host_validation():
     assert attn(B=0) == moe.MOE_FFN_OK
     assert attn(d=96) == moe.MOE_FFN_ERR_BAD_SHAPE            # d in {64, 128, 256}
@@ -252,6 +288,7 @@ def resplit(**kw):
     return moe.lib().moe_ffn_forward_resplit(*args.values(), None)
 
 
+@fake
 def test_forward_resplit_host_validation():
     assert resplit(group=64) == moe.MOE_FFN_ERR_BAD_SHAPE
     assert resplit(H=96) == moe.MOE_FFN_ERR_BAD_SHAPE
@@ -260,12 +297,13 @@ def test_forward_resplit_host_validation():
     assert resplit(SRu=None) == moe.MOE_FFN_ERR_NULL_ARG
     assert resplit(Qd=None) == moe.MOE_FFN_ERR_NULL_ARG
     assert resplit(Rg=A + 0x1200008) == moe.MOE_FFN_ERR_MISALIGNED
-    assert resplit(Sdh=A + 0x1b00004) == moe.MOE_FFN_ERR_MISALIGNED
+    assert resplit(Sdh=A + 0x1b00002) == moe.MOE_FFN_ERR_MISALIGNED   # scales: 4 bytes
     assert resplit(ws_bytes=1024) == moe.MOE_FFN_ERR_WORKSPACE
     assert resplit(out=A + 0x40) == moe.MOE_FFN_ERR_ALIAS
     assert resplit(T=0) == moe.MOE_FFN_OK
 
 
+@fake
 def test_route_grouped_host_validation():
     L = moe.lib()
 
@@ -286,3 +324,93 @@ def test_route_grouped_host_validation():
     assert call(ids=A + 0x200010) == moe.MOE_FFN_ERR_ALIAS     # ids overlap w
     assert call(ids=A + 0x40) == moe.MOE_FFN_ERR_ALIAS         # ids overlap logits
     assert call(bias=A + 0x200000 - 512) == moe.MOE_FFN_ERR_ALIAS
+
+
+def _z(*shape, dtype=torch.bfloat16):
+    return torch.zeros(*shape, dtype=dtype)
+
+
+def _layer_inputs(T=4, H=128, I=256, E=8, k=2):
+    """CPU tensors of a small layer (the binding checks shapes before it
+    looks at devices, so none of these reach the library)."""
+    return dict(x=_z(T, H), ids=_z(T, k, dtype=torch.int32), w=_z(T, k, dtype=torch.float32),
+                T=T, H=H, I=I, E=E, k=k)
+
+
+BAD_ROUTING = [
+    ("ids_rows", lambda a: dict(ids=_z(a["T"] + 1, a["k"], dtype=torch.int32))),
+    ("ids_1d", lambda a: dict(ids=_z(a["T"] * a["k"], dtype=torch.int32))),
+    ("w_cols", lambda a: dict(w=_z(a["T"], a["k"] + 1, dtype=torch.float32))),
+    ("w_rows", lambda a: dict(w=_z(a["T"] - 1, a["k"], dtype=torch.float32))),
+    ("out", lambda a: dict(out=_z(a["T"], a["H"] + 32))),
+    ("x_3d", lambda a: dict(x=_z(1, a["T"], a["H"]))),
+]
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "int8", "int4", "resplit"])
+@pytest.mark.parametrize("bad", [b[0] for b in BAD_ROUTING])
+def test_binding_rejects_wrong_routing_and_out_shapes(fmt, bad):
+    """topk_ids / topk_w must be [T, top_k] and out [T, H]: the kernels index
+    them by those sizes, so the binding refuses anything else (ValueError)
+    before any library call."""
+    a = _layer_inputs()
+    a.update(dict(BAD_ROUTING)[bad](a))
+    E, I, H = a["E"], a["I"], a["H"]
+    G = 128
+    out = a.get("out")
+    with pytest.raises(ValueError):
+        if fmt == "bf16":
+            moe.moe_ffn_forward(a["x"], a["ids"], a["w"], _z(E, I, H), _z(E, I, H), _z(E, H, I),
+                                out=out)
+        elif fmt == "int8":
+            i8, f32 = torch.int8, torch.float32
+            moe.moe_ffn_forward_int8(a["x"], a["ids"], a["w"], _z(E, I, H, dtype=i8),
+                                     _z(E, I, H // G, dtype=f32), _z(E, I, H, dtype=i8),
+                                     _z(E, I, H // G, dtype=f32), _z(E, H, I, dtype=i8),
+                                     _z(E, H, I // G, dtype=f32), out=out)
+        elif fmt == "int4":
+            u8, f32 = torch.uint8, torch.float32
+            moe.moe_ffn_forward_int4(a["x"], a["ids"], a["w"], _z(E, I, H // 2, dtype=u8),
+                                     _z(E, I, H // G, dtype=f32), _z(E, I, H // 2, dtype=u8),
+                                     _z(E, I, H // G, dtype=f32), _z(E, H, I // 2, dtype=u8),
+                                     _z(E, H, I // G, dtype=f32), out=out)
+        else:
+            u8, f32 = torch.uint8, torch.float32
+            p, sg = _z(E, I, H // 2, dtype=u8), _z(E, I, H // G, dtype=f32)
+            moe.moe_ffn_forward_resplit(a["x"], a["ids"], a["w"], p, sg, p, sg, p, sg, p, sg,
+                                        _z(E, H, I // 2, dtype=u8), _z(E, H, I // G, dtype=f32),
+                                        _z(E, H, I, dtype=torch.int8),
+                                        _z(E, H, I // G, dtype=f32), _z(E, dtype=u8), out=out)
+
+
+@pytest.mark.parametrize("name", ["Q_up", "S_gate", "S_down"])
+def test_binding_rejects_wrong_int8_tensor_shapes(name):
+    """Every INT8 weight and scale tensor is checked against [E, N, K] and the
+    row-major scale shape [E, N, K/128]; a group-major table is refused."""
+    a = _layer_inputs()
+    E, I, H, G = a["E"], a["I"], a["H"], 128
+    i8, f32 = torch.int8, torch.float32
+    t = dict(Q_gate=_z(E, I, H, dtype=i8), S_gate=_z(E, I, H // G, dtype=f32),
+             Q_up=_z(E, I, H, dtype=i8), S_up=_z(E, I, H // G, dtype=f32),
+             Q_down=_z(E, H, I, dtype=i8), S_down=_z(E, H, I // G, dtype=f32))
+    t[name] = {"Q_up": _z(E, I + 16, H, dtype=i8), "S_gate": _z(E, H // G, I, dtype=f32),
+               "S_down": _z(E, I // G, H, dtype=f32)}[name]
+    with pytest.raises(ValueError):
+        moe.moe_ffn_forward_int8(a["x"], a["ids"], a["w"], t["Q_gate"], t["S_gate"], t["Q_up"],
+                                 t["S_up"], t["Q_down"], t["S_down"])
+
+
+def test_binding_rejects_wrong_router_and_attention_outputs():
+    with pytest.raises(ValueError):
+        moe.moe_route_topk(_z(4, 8, dtype=torch.float32), 2,
+                           topk_ids=_z(4, 3, dtype=torch.int32))
+    with pytest.raises(ValueError):
+        moe.moe_route_grouped(_z(4, 256, dtype=torch.float32), 8, 8, 4,
+                              topk_w=_z(5, 8, dtype=torch.float32))
+    with pytest.raises(ValueError):
+        moe.moe_ffn_forward_logits(_z(4, 128), _z(4, 8, dtype=torch.float32), 2,
+                                   _z(8, 256, 128), _z(8, 256, 128), _z(8, 128, 256),
+                                   out=_z(4, 64))
+    with pytest.raises(ValueError):
+        moe.moe_attn_decode(_z(2, 8, 128), _z(2, 2, 64, 128), _z(2, 2, 64, 128),
+                            _z(2, dtype=torch.int32), out=_z(2, 8, 64))

@@ -62,6 +62,24 @@ def test_attn_matches_oracle(B, h_q, h_kv, d, max_len, lens):
             assert_close_scaled(got[b], ref[b], 2e-2, what=f"sequence {b}")
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_attn_default_scale_chosen_by_the_library(d):
+    """A score scale that is not positive (0, negative, NaN) selects 1/sqrt(d)
+    inside the library: the output equals, bit for bit, a call that passes
+    1/sqrt(d) (rounded from double to float) explicitly."""
+    need_gpu()
+    rng = np.random.default_rng(d)
+    B, h_q, h_kv, L = 2, 8, 2, 300
+    q = rnd_bits(rng, (B, h_q, d))
+    k = rnd_bits(rng, (B, h_kv, L, d))
+    v = rnd_bits(rng, (B, h_kv, L, d))
+    lens = np.array([300, 77], np.int32)
+    say(f"attn default scale d={d}")
+    explicit = run(q, k, v, lens, scale=float(np.float32(1.0 / np.sqrt(d))))
+    for s in (None, 0.0, -1.0, float("nan")):
+        assert np.array_equal(run(q, k, v, lens, scale=s), explicit), f"scale={s}"
+
+
 def test_attn_other_scale_and_clamped_lengths():
     need_gpu()
     rng = np.random.default_rng(77)

@@ -40,9 +40,8 @@ def run_both(x, ids, w, Q, E):
     Qg, Sg, Qu, Su, Qd, Sd = Q
     I = Qg.shape[1]
     k = ids.shape[1]
-    gm = workloads.scales_group_major
-    dev = [t.cuda() for t in (workloads.pack_int4(Qg), gm(Sg), workloads.pack_int4(Qu), gm(Su),
-                              workloads.pack_int4(Qd), gm(Sd))]
+    dev = [t.cuda() for t in (workloads.pack_int4(Qg), Sg, workloads.pack_int4(Qu), Su,
+                              workloads.pack_int4(Qd), Sd)]
     ws = moe.alloc_workspace(T, H, I, E, k)
     out = moe.moe_ffn_forward_int4(workloads.bits_to_bf16(x).cuda(), torch.from_numpy(ids).cuda(),
                                    torch.from_numpy(w).cuda(), *dev, workspace=ws)
@@ -104,12 +103,11 @@ def test_int4_full_size_sampled_rows(m):
     xb = workloads.bf16_bits(workloads.gen_x(wl))
     ids, w = oracle.route_topk(workloads.gen_logits(wl).numpy(), wl.k)
     Qg, Sg, Qu, Su, Qd, Sd = workloads.gen_weights_int4(wl, "cuda")
-    gm = workloads.scales_group_major
     ws = moe.alloc_workspace(wl.T, wl.H, wl.I, wl.E, wl.k)
     out = moe.moe_ffn_forward_int4(workloads.bits_to_bf16(xb).cuda(), torch.from_numpy(ids).cuda(),
-                                   torch.from_numpy(w).cuda(), workloads.pack_int4(Qg), gm(Sg),
-                                   workloads.pack_int4(Qu), gm(Su), workloads.pack_int4(Qd),
-                                   gm(Sd), workspace=ws)
+                                   torch.from_numpy(w).cuda(), workloads.pack_int4(Qg), Sg,
+                                   workloads.pack_int4(Qu), Su, workloads.pack_int4(Qd),
+                                   Sd, workspace=ws)
     torch.cuda.synchronize()
     got = workloads.bf16_bits(out)
     rows = np.array(sorted({0, wl.T - 1, wl.T // 2}))

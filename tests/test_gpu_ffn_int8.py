@@ -31,9 +31,7 @@ def run_both(x, ids, w, Q, E):
     Qg, Sg, Qu, Su, Qd, Sd = Q
     I = Qg.shape[1]
     k = ids.shape[1]
-    dev = [t.cuda() for t in (Qg, workloads.scales_group_major(Sg), Qu,
-                              workloads.scales_group_major(Su), Qd,
-                              workloads.scales_group_major(Sd))]
+    dev = [t.cuda() for t in (Qg, Sg, Qu, Su, Qd, Sd)]
     ws = moe.alloc_workspace(T, H, I, E, k)
     out = moe.moe_ffn_forward_int8(workloads.bits_to_bf16(x).cuda(), torch.from_numpy(ids).cuda(),
                                    torch.from_numpy(w).cuda(), *dev, workspace=ws)

@@ -43,11 +43,10 @@ def resplit_case(seed, T, H, I, E, k, std=0.05, ids=None, crit=None):
 
 
 def device_args(t, crit):
-    gm = workloads.scales_group_major
     p4 = workloads.pack_int4
-    return [a.cuda() for a in (p4(t["Qg"]), gm(t["Sg"]), p4(t["Rg"]), gm(t["SRg"]),
-                               p4(t["Qu"]), gm(t["Su"]), p4(t["Ru"]), gm(t["SRu"]),
-                               p4(t["Qd_lo"]), gm(t["Sd_lo"]), t["Qd_hi"], gm(t["Sd_hi"]),
+    return [a.cuda() for a in (p4(t["Qg"]), t["Sg"], p4(t["Rg"]), t["SRg"],
+                               p4(t["Qu"]), t["Su"], p4(t["Ru"]), t["SRu"],
+                               p4(t["Qd_lo"]), t["Sd_lo"], t["Qd_hi"], t["Sd_hi"],
                                torch.from_numpy(crit))]
 
 
@@ -101,7 +100,6 @@ def test_resplit_without_critical_experts_is_the_int4_layer():
     need_gpu()
     E = 6
     x, ids, w, t, crit = resplit_case(70, 9, 384, 256, E, 2, crit=[0] * E)
-    gm = workloads.scales_group_major
     p4 = workloads.pack_int4
     for split in (1, 2, 4):
         moe.moe_ffn_set_split(split, split)
@@ -110,9 +108,9 @@ def test_resplit_without_critical_experts_is_the_int4_layer():
             a = run_gpu(x, ids, w, t, crit)
             b = moe.moe_ffn_forward_int4(
                 workloads.bits_to_bf16(x).cuda(), torch.from_numpy(ids).cuda(),
-                torch.from_numpy(w).cuda(), p4(t["Qg"]).cuda(), gm(t["Sg"]).cuda(),
-                p4(t["Qu"]).cuda(), gm(t["Su"]).cuda(), p4(t["Qd_lo"]).cuda(),
-                gm(t["Sd_lo"]).cuda())
+                torch.from_numpy(w).cuda(), p4(t["Qg"]).cuda(), t["Sg"].cuda(),
+                p4(t["Qu"]).cuda(), t["Su"].cuda(), p4(t["Qd_lo"]).cuda(),
+                t["Sd_lo"].cuda())
             torch.cuda.synchronize()
         finally:
             moe.moe_ffn_set_split(0, 0)

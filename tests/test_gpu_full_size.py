@@ -14,7 +14,8 @@ from moe_cases import (TOL_BF16, TOL_INT8, assert_close, check_lists, need_gpu,
 
 pytestmark = pytest.mark.gpu
 
-FULL = ["mixtral8x7b_m1", "mixtral8x7b_m16", "deepseekv3_t16", "deepseekv3_zipf_t16",
+FULL = ["mixtral8x7b_m1", "mixtral8x7b_m2", "mixtral8x7b_m4", "mixtral8x7b_m8",
+        "mixtral8x7b_m16", "deepseekv3_t16", "deepseekv3_zipf_t16",
         "mixtral8x22b_t1", "mixtral8x22b_t4", "mixtral8x22b_t16", "qwen3_235b_t1",
         "qwen3_235b_t4", "qwen3_235b_t16",
         # prefill-sized batches: the tiled product takes the experts
@@ -51,7 +52,7 @@ def test_full_size_bf16_sampled_rows(name):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("m", [1, 16])
+@pytest.mark.parametrize("m", [1, 2, 4, 8, 16])
 def test_full_size_int8_sampled_rows(m):
     need_gpu()
     name = f"mixtral8x7b_int8_m{m}"
@@ -62,9 +63,8 @@ def test_full_size_int8_sampled_rows(m):
     Q = workloads.gen_weights_int8(wl, "cuda")
     ws = moe.alloc_workspace(wl.T, wl.H, wl.I, wl.E, wl.k)
     Qg, Sg, Qu, Su, Qd, Sd = Q
-    gm = workloads.scales_group_major
     out = moe.moe_ffn_forward_int8(workloads.bits_to_bf16(xb).cuda(), torch.from_numpy(ids).cuda(),
-                                   torch.from_numpy(w).cuda(), Qg, gm(Sg), Qu, gm(Su), Qd, gm(Sd),
+                                   torch.from_numpy(w).cuda(), Qg, Sg, Qu, Su, Qd, Sd,
                                    workspace=ws)
     torch.cuda.synchronize()
     got = workloads.bf16_bits(out)

@@ -69,12 +69,11 @@ def test_int8_layer_graph_replays_match_eager():
     T, H, I, E, k = 16, 512, 384, 8, 2
     x = workloads.bits_to_bf16(workloads.bf16_bits(
         torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(torch.bfloat16))).cuda()
-    gm = workloads.scales_group_major
     Q = []
     for N, K in ((I, H), (I, H), (H, I)):
         q, sc = workloads.quantize_groupwise(
             torch.from_numpy((rng.standard_normal((E, N, K)) * 0.05).astype(np.float32)))
-        Q += [q.cuda(), gm(sc).cuda()]
+        Q += [q.cuda(), sc.cuda()]
     ids = torch.from_numpy(np.stack([rng.choice(E, size=k, replace=False)
                                      for _ in range(T)]).astype(np.int32)).cuda()
     w = torch.from_numpy(rng.uniform(0.05, 1.0, size=(T, k)).astype(np.float32)).cuda()
@@ -124,12 +123,11 @@ def test_int4_layer_graph_replays_match_eager():
     T, H, I, E, k = 16, 512, 384, 8, 2
     x = workloads.bits_to_bf16(workloads.bf16_bits(
         torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(torch.bfloat16))).cuda()
-    gm = workloads.scales_group_major
     P = []
     for N, K in ((I, H), (I, H), (H, I)):
         q, sc = workloads.quantize_groupwise(
             torch.from_numpy((rng.standard_normal((E, N, K)) * 0.05).astype(np.float32)), 128, 7)
-        P += [workloads.pack_int4(q).cuda(), gm(sc).cuda()]
+        P += [workloads.pack_int4(q).cuda(), sc.cuda()]
     ids = torch.from_numpy(np.stack([rng.choice(E, size=k, replace=False)
                                      for _ in range(T)]).astype(np.int32)).cuda()
     w = torch.from_numpy(rng.uniform(0.05, 1.0, size=(T, k)).astype(np.float32)).cuda()
@@ -153,17 +151,17 @@ def test_resplit_layer_graph_replays_match_eager():
     T, H, I, E, k = 12, 384, 256, 6, 2
     x = workloads.bits_to_bf16(workloads.bf16_bits(
         torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(torch.bfloat16))).cuda()
-    gm, p4 = workloads.scales_group_major, workloads.pack_int4
+    p4 = workloads.pack_int4
     draw = lambda N, K: torch.from_numpy(  # noqa: E731
         (rng.standard_normal((E, N, K)) * 0.05).astype(np.float32))
     P = []
     for N, K in ((I, H), (I, H)):
         q, s, r, sr = workloads.quantize_residual_split(draw(N, K), 128, 7)
-        P += [p4(q).cuda(), gm(s).cuda(), p4(r).cuda(), gm(sr).cuda()]
+        P += [p4(q).cuda(), s.cuda(), p4(r).cuda(), sr.cuda()]
     wd = draw(H, I)
     ql, sl = workloads.quantize_groupwise(wd, 128, 7)
     qh, sh = workloads.quantize_groupwise(wd, 128, 127)
-    P += [p4(ql).cuda(), gm(sl).cuda(), qh.cuda(), gm(sh).cuda(),
+    P += [p4(ql).cuda(), sl.cuda(), qh.cuda(), sh.cuda(),
           torch.tensor([1, 0, 1, 1, 0, 0], dtype=torch.uint8).cuda()]
     ids = torch.from_numpy(np.stack([rng.choice(E, size=k, replace=False)
                                      for _ in range(T)]).astype(np.int32)).cuda()

@@ -74,8 +74,7 @@ def test_int8_every_split_matches_oracle(T, H, I, E, k):
     Qg, Sg, Qu, Su, Qd, Sd = Q
     ref = oracle.moe_ffn_int8(x, ids, w, Qg.numpy(), Sg.numpy(), Qu.numpy(), Su.numpy(),
                               Qd.numpy(), Sd.numpy(), E=E)
-    gm = workloads.scales_group_major
-    dev = [t.cuda() for t in (Qg, gm(Sg), Qu, gm(Su), Qd, gm(Sd))]
+    dev = [t.cuda() for t in (Qg, Sg, Qu, Su, Qd, Sd)]
     xd = workloads.bits_to_bf16(x).cuda()
     idd, wd = torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda()
     for gu, dn in SPLITS:

@@ -175,12 +175,6 @@ def quantize_groupwise(w: torch.Tensor, group: int = 128, qmax: int = 127):
     return q.to(torch.int8).reshape(*lead, K), s.contiguous()
 
 
-def scales_group_major(s: torch.Tensor) -> torch.Tensor:
-    """Row-major group scales [..., N, K/group] -> group-major [..., K/group, N]
-    (the scale layout of the INT8 HIP path).  A layout change only."""
-    return s.transpose(-1, -2).contiguous()
-
-
 def gen_weights_int8(wl: Workload, device="cpu", experts: Optional[list] = None):
     """INT8 expert weights with per-group scales:
     (Qg [E,I,H], Sg [E,I,H/g], Qu, Su, Qd [E,H,I], Sd [E,H,I/g])."""
@@ -302,8 +296,8 @@ def weight_bytes_per_expert(wl: Workload, critical: bool = True) -> int:
 
 
 # --------------------------------------------------------------------------
-# Decode attention with grouped-query heads (HiNa-MoE §6.1): the query heads
-# that share one KV head form a small block; the KV cache holds, per sequence
+# Decode attention with grouped-query heads (HiNa-MoE §6.1): g = h_q / h_kv
+# consecutive query heads read the same KV head; the KV cache holds, per sequence
 # and KV head, a [max_len][d] matrix of which the first len positions are
 # valid.  Head layouts of the models the pages decode with (Qwen3-30B-A3B:
 # 32 query heads over 4 KV heads; Mixtral-8x7B: 32 over 8; Qwen2-57B-A14B:
