@@ -184,6 +184,36 @@ int moe_ffn_forward(const void* x, const int32_t* topk_ids, const float* topk_w,
                     int32_t top_k, void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/* Workspace bytes the library holds, per GPU, for moe_ffn_forward_noalloc. */
+#define MOE_FFN_NOALLOC_WORKSPACE_BYTES ((size_t)32 << 20)
+
+/*
+ * moe_ffn_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The workspace is a device array of
+ * MOE_FFN_NOALLOC_WORKSPACE_BYTES (32 MiB) that the library holds on every GPU
+ * it runs on until the process ends; its address is looked up once per
+ * device, on the first call made with that device current.  The call itself
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ * Arguments and result: as moe_ffn_forward (x, topk_ids, topk_w, W_gate,
+ * W_up, W_down, out and the sizes mean the same, the caller owns them).
+ * The array's contents on entry are ignored (every region a call reads is
+ * written earlier in the same call), so no clearing is needed between calls.
+ * All calls on one GPU share the array: calls that may overlap on one GPU
+ * (different streams or threads without ordering) race and give undefined
+ * results; calls ordered on one stream are safe.  Slots with ids outside
+ * [0, E) are dropped as in moe_ffn_forward, but their count is not reported
+ * (moe_ffn_check_status needs a caller workspace).
+ * Errors: as moe_ffn_forward, and MOE_FFN_ERR_WORKSPACE when these sizes need
+ * more than MOE_FFN_NOALLOC_WORKSPACE_BYTES (moe_ffn_workspace_bytes gives the
+ * need; decode-sized batches need a few MiB), MOE_FFN_ERR_HIP if the array's
+ * address cannot be obtained.
+ */
+int moe_ffn_forward_noalloc(const void* x, const int32_t* topk_ids, const float* topk_w,
+                            const void* W_gate, const void* W_up, const void* W_down,
+                            void* out, int64_t T, int64_t H, int64_t I, int32_t E,
+                            int32_t top_k, void* stream);
+
 /*
  * Routed-expert FFN layer from router logits, BF16 weights: the top-k gate
  * (HiNa-MoE §2.1 / Fig. 2) followed by the layer of moe_ffn_forward

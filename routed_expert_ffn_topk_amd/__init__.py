@@ -27,6 +27,7 @@ MOE_FFN_ERR_HIP = -6
 MOE_FFN_ERR_BAD_IDS = -7
 MOE_FFN_MAX_EXPERTS = 1024
 MOE_FFN_INT8_GROUP = 128
+MOE_FFN_NOALLOC_WORKSPACE_BYTES = 32 << 20
 
 LAYOUT_FIELDS = ("total_bytes", "meta", "counts", "offsets", "active", "large", "sorted_slot",
                  "h", "y", "y_parts")
@@ -64,6 +65,9 @@ def lib() -> ctypes.CDLL:
         L.moe_ffn_forward.restype = _c.c_int
         L.moe_ffn_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
                                       _i32, _i32, _vp, _sz, _vp]
+        L.moe_ffn_forward_noalloc.restype = _c.c_int
+        L.moe_ffn_forward_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
+                                              _i32, _i32, _vp]
         L.moe_ffn_forward_logits.restype = _c.c_int
         L.moe_ffn_forward_logits.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64,
                                              _i64, _i32, _i32, _vp, _sz, _vp]
@@ -200,6 +204,24 @@ def moe_ffn_forward(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tenso
         _dev(W_up, "W_up", torch.bfloat16), _dev(W_down, "W_down", torch.bfloat16),
         _dev(out, "out", torch.bfloat16), T, H, I, E, top_k,
         _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream)))
+    return out
+
+
+def moe_ffn_forward_noalloc(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor,
+                            W_gate: torch.Tensor, W_up: torch.Tensor, W_down: torch.Tensor,
+                            out: torch.Tensor, stream=None) -> torch.Tensor:
+    """moe_ffn_forward with the library's own per-GPU workspace (no workspace
+    argument; the C call allocates nothing, and ``out`` is the caller's).
+    Calls that may overlap on one GPU race on that workspace."""
+    T, H, top_k = _layer_args(x, topk_ids, topk_w, out)
+    E, I, H2 = W_gate.shape
+    if H2 != H or tuple(W_up.shape) != (E, I, H) or tuple(W_down.shape) != (E, H, I):
+        raise ValueError("weight shapes must be W_gate/W_up [E,I,H], W_down [E,H,I]")
+    _check("moe_ffn_forward_noalloc", lib().moe_ffn_forward_noalloc(
+        _dev(x, "x", torch.bfloat16), _dev(topk_ids, "topk_ids", torch.int32),
+        _dev(topk_w, "topk_w", torch.float32), _dev(W_gate, "W_gate", torch.bfloat16),
+        _dev(W_up, "W_up", torch.bfloat16), _dev(W_down, "W_down", torch.bfloat16),
+        _dev(out, "out", torch.bfloat16), T, H, I, E, top_k, _stream(stream)))
     return out
 
 

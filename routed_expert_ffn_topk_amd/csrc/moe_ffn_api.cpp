@@ -8,6 +8,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "launch.hpp"
 
@@ -107,6 +108,34 @@ int check_forward(const void* x, const int32_t* ids, const float* w, const void*
     if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return MOE_FFN_ERR_MISALIGNED;
     if (overlap(workspace, L->total_bytes, out, xb) || overlap(workspace, L->total_bytes, x, xb))
         return MOE_FFN_ERR_ALIAS;
+    return MOE_FFN_OK;
+}
+
+// Workspace of moe_ffn_forward_noalloc: a device array the library holds on
+// every GPU it runs on, until the process ends.  In host code `scratch` only
+// names the symbol; its device address (one per GPU) comes from
+// hipGetSymbolAddress, and only that address is ever passed to kernels.
+static __device__ __align__(256) unsigned char scratch[MOE_FFN_NOALLOC_WORKSPACE_BYTES];
+
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and cached.
+int scratch_address(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_FFN_ERR_HIP;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+                return MOE_FFN_ERR_HIP;
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
     return MOE_FFN_OK;
 }
 
@@ -212,6 +241,25 @@ int moe_ffn_forward(const void* x, const int32_t* topk_ids, const float* topk_w,
         static_cast<const uint16_t*>(x), route, W, static_cast<uint16_t*>(out), s,
         carve(workspace, L), ncu, take_stage_events(), t_split, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? MOE_FFN_OK : MOE_FFN_ERR_HIP;
+}
+
+int moe_ffn_forward_noalloc(const void* x, const int32_t* topk_ids, const float* topk_w,
+                            const void* W_gate, const void* W_up, const void* W_down, void* out,
+                            int64_t T, int64_t H, int64_t I, int32_t E, int32_t top_k,
+                            void* stream) {
+    if (!shape_ok(T, H, I, E, top_k) || H % 32 != 0 || I % 32 != 0) return MOE_FFN_ERR_BAD_SHAPE;
+    if (T == 0) return MOE_FFN_OK;
+    moe_ffn_ws_layout L;
+    if (moe_ffn_workspace_layout(T, H, I, E, top_k, &L) != MOE_FFN_OK) return MOE_FFN_ERR_BAD_SHAPE;
+    if (L.total_bytes > MOE_FFN_NOALLOC_WORKSPACE_BYTES) return MOE_FFN_ERR_WORKSPACE;
+    // every other check (pointers, alignment, overlaps) is moe_ffn_forward's;
+    // the workspace argument is the library's array
+    void* ws = nullptr;
+    if (!x || !topk_ids || !topk_w || !out || !W_gate || !W_up || !W_down)
+        return MOE_FFN_ERR_NULL_ARG;
+    if (const int rc = scratch_address(&ws); rc != MOE_FFN_OK) return rc;
+    return moe_ffn_forward(x, topk_ids, topk_w, W_gate, W_up, W_down, out, T, H, I, E, top_k, ws,
+                           MOE_FFN_NOALLOC_WORKSPACE_BYTES, stream);
 }
 
 int moe_ffn_forward_logits(const void* x, const float* logits, int32_t* topk_ids,

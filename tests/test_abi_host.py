@@ -151,6 +151,40 @@ def fwd_logits(**kw):
                                             a["k"], a["ws"], a["wsb"], None)
 
 
+def fwd_noalloc(**kw):
+    a = dict(x=A, ids=A + 0x100000, w=A + 0x200000, wg=A + 0x1000000, wu=A + 0x2000000,
+             wd=A + 0x3000000, out=A + 0x300000, T=4, H=64, I=96, E=8, k=2)
+    a.update(kw)
+    return moe.lib().moe_ffn_forward_noalloc(a["x"], a["ids"], a["w"], a["wg"], a["wu"],
+                                             a["wd"], a["out"], a["T"], a["H"], a["I"], a["E"],
+                                             a["k"], None)
+
+
+@fake
+def test_forward_noalloc_host_validation():
+    """The no-allocation entry point refuses sizes whose workspace exceeds the
+    array it holds (before any device call), and otherwise checks as
+    moe_ffn_forward does."""
+    big = dict(T=4096, H=4096, I=14336, E=8, k=2)
+    assert moe.moe_ffn_workspace_bytes(4096, 4096, 14336, 8, 2) > moe.MOE_FFN_NOALLOC_WORKSPACE_BYTES
+    assert fwd_noalloc(**big) == moe.MOE_FFN_ERR_WORKSPACE
+    assert fwd_noalloc(T=0) == moe.MOE_FFN_OK
+    assert fwd_noalloc(H=48) == moe.MOE_FFN_ERR_BAD_SHAPE
+    assert fwd_noalloc(k=9) == moe.MOE_FFN_ERR_BAD_SHAPE
+    assert fwd_noalloc(x=None) == moe.MOE_FFN_ERR_NULL_ARG
+    assert fwd_noalloc(wd=None) == moe.MOE_FFN_ERR_NULL_ARG
+
+
+def test_noalloc_limit_matches_header():
+    text = open(HEADER).read()
+    assert "#define MOE_FFN_NOALLOC_WORKSPACE_BYTES ((size_t)32 << 20)" in text
+    assert moe.MOE_FFN_NOALLOC_WORKSPACE_BYTES == 32 << 20
+    # decode-sized batches of every workload shape fit
+    for T, H, I, E, k in [(64, 4096, 14336, 8, 2), (16, 7168, 2048, 256, 8),
+                          (16, 6144, 16384, 8, 2), (16, 4096, 1536, 128, 8)]:
+        assert moe.moe_ffn_workspace_bytes(T, H, I, E, k) <= moe.MOE_FFN_NOALLOC_WORKSPACE_BYTES
+
+
 @fake
 def test_forward_logits_host_validation():
     assert fwd_logits(T=0) == moe.MOE_FFN_OK
