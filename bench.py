@@ -176,7 +176,7 @@ def read_ceiling(stream, nbytes=4 << 30, reps=10) -> float:
     return nbytes / (best * 1e-6) / 1e9
 
 
-def cpu_baseline(wl, host_weights, logits_cpu, x_cpu, reps=3, critical=None):
+def cpu_baseline(wl, host_weights, logits_cpu, x_cpu, reps=5, critical=None):
     """The CPU oracle on a bounded token sample of one layer of the workload:
     the leading tokens, as many as fit CPU_SAMPLE_MACS multiply-adds and
     CPU_SAMPLE_BYTES of expert weights copied to the host."""
@@ -215,17 +215,93 @@ def cpu_baseline(wl, host_weights, logits_cpu, x_cpu, reps=3, critical=None):
               if wl.resplit else len(need) * expert_bytes(wl))
     sample_bytes = wbytes + 2 * n * wl.H * 2 + n * wl.k * 8
     return {"value": round(sample_bytes / t / 1e9, 3), "unit": "GB/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
-            "us_per_layer": round(t * 1e6, 1),
+            "cores": oracle.num_threads(), "kind": "oracle", "cpu_model": cpu_model(),
+            "us_per_layer": round(t * 1e6, 1), "runs": reps,
+            "tiny_single_thread": tiny_single_thread(),
             "sample": f"{wl.name}: the first {n} of {wl.T} tokens ({len(need)} experts), "
                       f"median of {reps} runs, plain C oracle (FP32 accumulation, per-token "
                       f"loops, {'residual-split INT4/INT8' if wl.resplit else 'INT8' if wl.int8 else 'INT4' if wl.int4 else 'BF16'} weights)"}
 
 
+def per_call_us(call, n, stream):
+    """GPU microseconds of each of n back-to-back calls: an event is recorded
+    on the launch stream before the first call and after every call, with one
+    synchronisation at the end (the host enqueues ahead of the GPU)."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    ev[0].record(stream)
+    for i in range(n):
+        call(i)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(n)]
+
+
+def call_stats(us):
+    """Median and geometric mean (the pages' summary statistic) of per-call
+    times, with the spread."""
+    return {"calls": len(us), "median": round(statistics.median(us), 2),
+            "geomean": round(math.exp(statistics.mean(math.log(u) for u in us)), 2),
+            "min": round(min(us), 2), "max": round(max(us), 2)}
+
+
+def launch_gap_us(stream, n=2000):
+    """Dispatch gap between back-to-back kernels on the stream: GPU time of a
+    chain of n empty kernels (the library's launch probe) divided by n."""
+    import torch
+
+    import routed_expert_ffn_topk_amd as moe
+    moe.moe_ffn_launch_probe(100, stream)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    moe.moe_ffn_launch_probe(n, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return round(e0.elapsed_time(e1) * 1e3 / n, 3)
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (lscpu), or the platform's processor string."""
+    import platform
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+        for ln in out.splitlines():
+            if ln.strip().startswith("Model name:"):
+                return ln.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    return platform.processor() or "unknown"
+
+
+def tiny_single_thread(reps=100):
+    """The oracle on the Tiny layer (hidden 256, intermediate 512, 8 experts,
+    top-2, 16 tokens) on one thread, median of reps runs."""
+    import oracle
+    import workloads
+    wl = workloads.WORKLOADS["tiny"]
+    xb = workloads.bf16_bits(workloads.gen_x(wl))
+    ids, w = oracle.route_topk(workloads.gen_logits(wl).numpy(), wl.k)
+    W = [workloads.bf16_bits(t) for t in workloads.gen_weights(wl, "cpu")]
+    threads = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        used = oracle.num_threads()
+        times = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            oracle.moe_ffn_bf16(xb, ids, w, W[0], W[1], W[2], E=wl.E)
+            times.append(time.perf_counter() - t0)
+    finally:
+        oracle.set_num_threads(threads)
+    return {"us": round(statistics.median(times) * 1e6, 1), "threads": used, "runs": reps}
+
+
 ATTN_METRIC = "decode GQA attention: KV-stream GB/s (% HBM peak) and µs per call, BF16"
 
 
-def cpu_baseline_attn(wl, q, k_host, v_host, lens, reps=3):
+def cpu_baseline_attn(wl, q, k_host, v_host, lens, reps=5):
     """The CPU oracle on a bounded sample of the same attention batch: the
     leading sequences whose KV positions total at most 2^23 (a few seconds of
     CPU work), median of `reps` runs, in the same GB/s unit."""
@@ -244,7 +320,8 @@ def cpu_baseline_attn(wl, q, k_host, v_host, lens, reps=3):
     t = statistics.median(times)
     nbytes = pos * wl.h_kv * wl.d * 4 + 2 * n * wl.h_q * wl.d * 2
     return {"value": round(nbytes / t / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "us_per_call": round(t * 1e6, 1),
+            "kind": "oracle", "cpu_model": cpu_model(), "us_per_call": round(t * 1e6, 1),
+            "runs": reps,
             "sample": f"{wl.name}: the first {n} of {wl.B} sequences ({pos} KV positions), "
                       f"median of {reps} runs, plain C oracle (FP32 scores, softmax and "
                       f"value sums, BF16 inputs)"}
@@ -293,6 +370,7 @@ def run_attn(args):
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / args.steps
     call_bytes = kv_bytes + 2 * wl.B * wl.h_q * wl.d * 2
+    per_call = call_stats(per_call_us(call, max(100, args.calls), stream))
     value = n_sets * call_bytes / (ms_per_step * 1e-3) / 1e9
     # per-kernel durations from HIP events on the launch stream: split kernel
     # (the dominant one: every K and V byte), then the merge of the splits
@@ -320,6 +398,7 @@ def run_attn(args):
                    "head_dim": wl.d, "max_len": wl.max_len, "lengths": wl.lens,
                    "kv_positions": int(lens.sum()), "kv_sets": n_sets,
                    "us_per_call": round(ms_per_step * 1e3 / n_sets, 1),
+                   "per_call_us": per_call, "launch_gap_us": launch_gap_us(stream),
                    "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
                    "pct_measured_read_ceiling": round(100 * value / ceiling, 1),
                    "device": torch.cuda.get_device_name(dev)},
@@ -349,6 +428,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calls", type=int, default=100,
+                    help="calls per layer timed one by one for the median / geometric mean")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB, 5 times "
                          "(calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE), then exit")
@@ -515,6 +596,18 @@ def main():
                 torch.cuda.synchronize()
                 per_layer[b["wl"].name][key] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
 
+    # per-call statistics: every layer timed call by call, at least 100 calls
+    ncalls = max(100, args.calls)
+    for b in batches:
+        us = per_call_us(lambda i, b=b: layer(b, i % n_sets), ncalls, stream)
+        per_layer[b["wl"].name]["per_call_us"] = call_stats(us)
+    names_l = [b["wl"].name for b in batches]
+    m1 = next((n for n in names_l if n.endswith("_m1")), None)
+    m16 = next((n for n in names_l if n.endswith("_m16")), None)
+    m16_over_m1 = (round(per_layer[m16]["per_call_us"]["median"] /
+                         per_layer[m1]["per_call_us"]["median"], 3) if m1 and m16 else None)
+    gap = launch_gap_us(stream)
+
     # per-kernel durations from HIP events recorded on the launch stream
     # between the kernels of each call (stage 0 permute, 1 gate/up, 2 down,
     # 3 combine)
@@ -587,6 +680,7 @@ def main():
                    "TFLOPs": round(sum(layer_flops(b["wl"]) for b in batches) * n_sets /
                                    (ms_per_step * 1e-3) / 1e12, 1),
                    "pct_measured_read_ceiling": round(100 * value / ceiling, 1),
+                   "us_m16_over_m1": m16_over_m1, "launch_gap_us": gap,
                    "per_layer": per_layer, "device": torch.cuda.get_device_name(dev)},
         "roofline": roofline,
     }

@@ -420,6 +420,15 @@ int moe_ffn_set_split(int32_t gate_up_split, int32_t down_split);
  */
 int moe_ffn_read_probe(const void* buf, size_t bytes, void* sink, void* stream);
 
+/*
+ * Measurement helper: the dispatch gap between back-to-back kernels.
+ * Enqueues n launches of an empty one-wave kernel on `stream`; the GPU time
+ * of the chain divided by n is the fixed cost one more kernel adds to a layer
+ * (the floor under the four launches of a forward call).  n in [0, 10^6].
+ * Returns MOE_FFN_OK, MOE_FFN_ERR_BAD_SHAPE or MOE_FFN_ERR_HIP.
+ */
+int moe_ffn_launch_probe(int32_t n, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

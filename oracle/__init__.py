@@ -43,6 +43,8 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(path)
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_num_threads.argtypes = []
+        L.oracle_set_num_threads.restype = None
+        L.oracle_set_num_threads.argtypes = [ctypes.c_int]
         L.oracle_bf16_to_f32.restype = ctypes.c_float
         L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
         L.oracle_f32_to_bf16.restype = ctypes.c_uint16
@@ -89,6 +91,12 @@ def lib() -> ctypes.CDLL:
 def num_threads() -> int:
     """OpenMP threads the oracle's loops use."""
     return int(lib().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Set the OpenMP threads of the oracle's loops (results do not depend on
+    it: only independent outputs are split between threads)."""
+    lib().oracle_set_num_threads(int(n))
 
 
 def _ptr(a: np.ndarray, ctype):

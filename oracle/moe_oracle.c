@@ -68,6 +68,12 @@
 /* Threads the OpenMP loops below will use (reported with CPU timings). */
 int oracle_num_threads(void) { return omp_get_max_threads(); }
 
+/* Set that thread count (n >= 1); used to time a single-thread run.  The
+ * results do not depend on it: the loops split only independent outputs. */
+void oracle_set_num_threads(int n) {
+    if (n >= 1) omp_set_num_threads(n);
+}
+
 /* ---------------------------------------------------------------------- */
 /* BF16 <-> FP32.  BF16 is the upper half of an IEEE binary32 word.        */
 /* ---------------------------------------------------------------------- */

@@ -96,6 +96,8 @@ def lib() -> ctypes.CDLL:
         L.moe_ffn_set_stage_events.argtypes = [_c.POINTER(_vp), _i32]
         L.moe_ffn_set_split.restype = _c.c_int
         L.moe_ffn_set_split.argtypes = [_i32, _i32]
+        L.moe_ffn_launch_probe.restype = _c.c_int
+        L.moe_ffn_launch_probe.argtypes = [_i32, _vp]
         L.moe_ffn_read_probe.restype = _c.c_int
         L.moe_ffn_read_probe.argtypes = [_vp, _sz, _vp, _vp]
         _lib = L
@@ -425,6 +427,12 @@ def moe_ffn_read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> No
         raise ValueError("sink must be a device int32 tensor")
     _check("moe_ffn_read_probe", lib().moe_ffn_read_probe(
         buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(), _stream(stream)))
+
+
+def moe_ffn_launch_probe(n: int, stream=None) -> None:
+    """Measurement helper: enqueue n launches of an empty kernel (the
+    launch-gap probe)."""
+    _check("moe_ffn_launch_probe", lib().moe_ffn_launch_probe(n, _stream(stream)))
 
 
 def moe_ffn_set_stage_events(events) -> None:

@@ -143,4 +143,7 @@ hipError_t launch_attn_decode(const uint16_t* q, const uint16_t* k, const uint16
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int num_cu,
                              hipStream_t stream);
 
+// n launches of an empty one-wave kernel on stream (launch-gap probe).
+hipError_t launch_empty_chain(int n, hipStream_t stream);
+
 }  // namespace moe

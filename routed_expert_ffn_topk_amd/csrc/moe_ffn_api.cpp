@@ -475,6 +475,13 @@ int moe_ffn_read_probe(const void* buf, size_t bytes, void* sink, void* stream) 
                : MOE_FFN_ERR_HIP;
 }
 
+int moe_ffn_launch_probe(int32_t n, void* stream) {
+    if (n < 0 || n > 1000000) return MOE_FFN_ERR_BAD_SHAPE;
+    return moe::launch_empty_chain(n, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? MOE_FFN_OK
+               : MOE_FFN_ERR_HIP;
+}
+
 int moe_ffn_set_split(int32_t gate_up_split, int32_t down_split) {
     auto ok = [](int32_t v) { return v == 0 || v == 1 || v == 2 || v == 4; };
     if (!ok(gate_up_split) || !ok(down_split)) return MOE_FFN_ERR_BAD_SHAPE;

@@ -1,4 +1,4 @@
-// HBM read-bandwidth probe: the streaming-read ceiling the expert products are
+// Measurement helpers.  HBM read-bandwidth probe: the streaming-read ceiling the expert products are
 // measured against (the GPU analogue of the STREAM bandwidth the HiNa-MoE
 // evaluation quotes for its CPUs, Table 2).  Every byte of the buffer is read
 // once with 16-byte non-temporal loads, grid-stride, eight loads in flight per
@@ -36,7 +36,21 @@ __global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(const u32x4* 
     if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9E3779B9u) *sink = 1u;
 }
 
+// An empty kernel: a chain of launches measures the dispatch gap between
+// back-to-back kernels on a stream (the fixed cost each of a layer's kernels
+// adds).
+__global__ __launch_bounds__(64) void empty_kernel() {}
+
 }  // namespace
+
+hipError_t launch_empty_chain(int n, hipStream_t stream) {
+    for (int i = 0; i < n; ++i) {
+        hipLaunchKernelGGL(empty_kernel, dim3(1), dim3(64), 0, stream);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
+}
 
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int num_cu,
                              hipStream_t stream) {

@@ -241,6 +241,12 @@ def test_route_host_validation():
     assert L.moe_route_topk(A, 4, 8, 2, A + 0x1001, A + 0x2000, None) == moe.MOE_FFN_ERR_MISALIGNED
 
 
+def test_launch_probe_rejects_bad_counts():
+    # rejected before any device call; no address involved
+    assert moe.lib().moe_ffn_launch_probe(-1, None) == moe.MOE_FFN_ERR_BAD_SHAPE
+    assert moe.lib().moe_ffn_launch_probe(1000001, None) == moe.MOE_FFN_ERR_BAD_SHAPE
+
+
 @fake
 def test_read_probe_host_validation():
     L = moe.lib()
