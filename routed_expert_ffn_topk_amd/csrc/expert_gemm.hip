@@ -420,58 +420,59 @@ using DualDown = MixedWeights<Int4Weights, Int8Weights, true>;
 // Tuning per weight format and projection, measured on MI355X over the
 // Mixtral-8x7B, DeepSeek-V3, Qwen3-235B and Mixtral-8x22B expert shapes at
 // 1-16 tokens per expert (INT4 and the residual split: the Mixtral-8x7B
-// shape): batch length U (units), resident workgroups per CU (LDS: 33-42 KB
-// per workgroup) and the weight batches held in registers (kDepth: 2, one
-// batch in flight while the other is multiplied, or 3, two in flight).
+// shape): batch length U (units), resident workgroups per CU, and the
+// deepest slab (kMaxDepth: a slab row of a chunk with few tokens covers up
+// to this many times 512 K; scaled formats hold that many times the slab's
+// scale table in LDS, which the workgroups per CU must fit).
 template <class Fmt, int NMAT>
 struct GemmTuning;
 template <>
 struct GemmTuning<Bf16Weights, 2> {   // gate/up: two matrices per K step
     static constexpr int kBlocksPerCU = 4;
     static constexpr int kBatch = 2;
-    static constexpr int kDepth = 2;
+    static constexpr int kMaxDepth = 16;
 };
 template <>
 struct GemmTuning<Bf16Weights, 1> {   // down
     static constexpr int kBlocksPerCU = 3;
     static constexpr int kBatch = 8;
-    static constexpr int kDepth = 2;
+    static constexpr int kMaxDepth = 16;
 };
 template <>
 struct GemmTuning<Int8Weights, 2> {
     static constexpr int kBlocksPerCU = 3;
     static constexpr int kBatch = 1;
-    static constexpr int kDepth = 2;
+    static constexpr int kMaxDepth = 4;
 };
 template <>
 struct GemmTuning<Int8Weights, 1> {
     static constexpr int kBlocksPerCU = 3;
     static constexpr int kBatch = 2;
-    static constexpr int kDepth = 2;
+    static constexpr int kMaxDepth = 8;
 };
 template <>
 struct GemmTuning<Int4Weights, 2> {
     static constexpr int kBlocksPerCU = 4;
     static constexpr int kBatch = 1;
-    static constexpr int kDepth = 2;
+    static constexpr int kMaxDepth = 1;
 };
 template <>
 struct GemmTuning<ResidualGateUp, 2> {
     static constexpr int kBlocksPerCU = 2;
     static constexpr int kBatch = 2;
-    static constexpr int kDepth = 2;
+    static constexpr int kMaxDepth = 4;
 };
 template <>
 struct GemmTuning<DualDown, 1> {
     static constexpr int kBlocksPerCU = 2;
     static constexpr int kBatch = 2;
-    static constexpr int kDepth = 2;
+    static constexpr int kMaxDepth = 16;
 };
 template <>
 struct GemmTuning<Int4Weights, 1> {
     static constexpr int kBlocksPerCU = 2;
     static constexpr int kBatch = 4;
-    static constexpr int kDepth = 2;
+    static constexpr int kMaxDepth = 16;
 };
 
 // S: K-parts per row block; U: units per weight batch (divides the units of
@@ -482,21 +483,24 @@ struct GemmTuning<Int4Weights, 1> {
 // all active experts (expert-major) are dealt out per XCD: each XCD owns a
 // contiguous slice, and its workgroups take the slice's rounds interleaved
 // (an equal number each, +-1).
-template <class Fmt, int NMAT, int S, int U, int D>
+template <class Fmt, int NMAT, int S, int U, int FMAX>
 __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, int n_act, int grid,
                                             u32x4 (*xs)[kSlabU4], f32x4* sc) {
     constexpr int R = kWaves / S;              // row blocks per round
-    constexpr int SP = kSlabBlocks / S;        // LDS blocks of each K part per slab
-    constexpr int SPU = SP / Fmt::kBlocks;     // units of each K part per slab
-    constexpr int NB = SPU / U;                // full batches per full slab
+    constexpr int SP = kSlabBlocks / S;        // LDS blocks of each K part per slab (depth 1)
+    constexpr int SPU = SP / Fmt::kBlocks;     // units of each K part per slab (depth 1)
+    constexpr int NB = SPU / U;                // full batches per slab (depth 1)
     static_assert(SPU >= 1 && SPU % U == 0, "batch must divide the slab part");
-    static_assert(D == 2 || D == 3, "two or three weight batches in registers");
-    // scale table of a slab (scaled formats): per tensor, [R][S][SPU][16 rows]
-    // floats, TS apart; two buffers (slabs alternate), SCB floats apart
+    static_assert(FMAX >= 1 && FMAX <= 16 && (FMAX & (FMAX - 1)) == 0, "slab depth");
+    constexpr int LOG_SP = SP == 16 ? 4 : SP == 8 ? 3 : 2;
+    static_assert((1 << LOG_SP) == SP, "power-of-two slab parts");
+    // scale table of a slab (scaled formats): per tensor, [R][S][SPU*F][16
+    // rows] floats in a region of TS floats (sized for depth FMAX); two
+    // buffers (slabs alternate), SCB floats apart
     constexpr int NSC = ScaleTensors<Fmt, NMAT>::value;
-    constexpr int TS = R * S * SPU * 16;
-    constexpr int SCB = NSC * kScaleSlabFloats;
-    static_assert(NSC == 0 || TS <= kScaleSlabFloats, "scale table fits its buffer");
+    constexpr int TS = R * S * SPU * 16 * FMAX;
+    constexpr int SCB = NSC * TS;
+    static_assert(NSC == 0 || TS <= kScaleSlabFloats * FMAX, "scale table fits its buffer");
     // after the slab loop the first slab buffer doubles as the K-part
     // reduction area (3 x NMAT x 1 KB <= 16 KB)
     f32x4* red = reinterpret_cast<f32x4*>(&xs[0][0]);
@@ -513,7 +517,6 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, int n_act, int 
     const int kpu = (nunits + S - 1) / S;      // units per K part
     const int u0 = min(nunits, kp * kpu);
     const int u1 = min(nunits, u0 + kpu);
-    const int nslab = (kpu + SPU - 1) / SPU;
 
     // this workgroup's rounds: every per-th round of its XCD's slice, from
     // its index li in the XCD.  The XCD's workgroups work on neighbouring
@@ -570,6 +573,17 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, int n_act, int 
             }
             for (int c0 = 0; c0 < m; c0 += 16) {
                 const int ntok = min(16, m - c0);        // distinct tokens of the chunk
+                // Slab depth: a slab buffer holds 16 token rows of 512 K; a
+                // chunk of ntok <= 16 / 2^d tokens gives each of its rows
+                // 2^d times that K (up to FMAX), so a round crosses 2^d times
+                // fewer slab barriers.
+                const int dl = min(ntok <= 1 ? 4 : ntok <= 2 ? 3 : ntok <= 4 ? 2 : ntok <= 8 ? 1 : 0,
+                                   FMAX == 16 ? 4 : FMAX == 8 ? 3 : FMAX == 4 ? 2 : FMAX == 2 ? 1 : 0);
+                const int dep = 1 << dl;
+                const int spu = SPU << dl;               // units of each K part per slab
+                const int nb = NB << dl;                 // full batches per full slab
+                const int tpitch = kTokRowU4 * dep + 2;  // LDS words between token rows
+                const int nslab = (kpu + spu - 1) / spu;
                 // padding columns (beyond the expert's tokens) read token 0's row:
                 // an MFMA output column depends only on its own B column, and
                 // padding columns are never stored
@@ -579,13 +593,15 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, int n_act, int 
                 // request it before the token rows, whose addresses take two
                 // dependent loads (the first slab then waits for everything)
                 constexpr int kLoads = F::template loads<NMAT, U>();
-                typename F::template Batch<NMAT, U> A, B, C;   // C: depth 3 only
+                typename F::template Batch<NMAT, U> A, B;
                 if (nfull > 0) F::template load<NMAT, U>(A, src, u0);
-                // token rows this wave stages: tokens wave, wave + 4, ...
+                // staging loads this wave issues per slab: ii = wave, wave + 4,
+                // ... of the chunk's ntok * dep loads; load ii stages 512 K of
+                // token ii >> dl, the (ii & (dep - 1))-th of the token's slab row
                 const uint16_t* tp[4];
     #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int c = wave + kWaves * i;
+                    const int c = (wave + kWaves * i) >> dl;
                     const int qq = beg + c0 + (c < ntok ? c : 0);
                     const int brow = NMAT == 2 ? g.sorted_slot[qq] / g.top_k : qq;
                     tp[i] = g.b_src + (size_t)brow * g.b_pitch;
@@ -594,135 +610,105 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, int n_act, int 
     #pragma unroll
                 for (int mm = 0; mm < NMAT; ++mm) acc[mm] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-                // Slab j holds, for each K part pp, its units [start(pp) + j*SPU,
-                // +SPU) at blocks [pp*SP, pp*SP + SP) of every token row.  One
-                // load instruction stages one token's whole slab row (1 KB): lane
-                // L fills block L/4 for K group L%4, so the row is read from
-                // global memory in contiguous runs of 1024/S bytes.
+                // Slab j holds, for each K part pp, its units [start(pp) + j*spu,
+                // +spu) at blocks [pp*SP*dep, (pp+1)*SP*dep) of every token row.
+                // One load instruction stages 16 blocks (1 KB) of one token's
+                // slab row: lane L fills block 16i + L/4 for K group L%4, so the
+                // row is read from global memory in contiguous runs.
                 // Scaled formats also stage the slab's scales: entry
-                // ((rr*S + pp)*SPU + jj)*16 + row of tensor t is the scale of
-                // row 16*(rb0 + rr) + row, unit start(pp) + j*SPU + jj; one
+                // ((rr*S + pp)*spu + jj)*16 + row of tensor t is the scale of
+                // row 16*(rb0 + rr) + row, unit start(pp) + j*spu + jj; one
                 // 4-byte direct load per lane fills 64 consecutive entries.
                 auto stage = [&](int j, int bsel) {
-                    const int blk = lane >> 2;
                     const int kgl = lane & 3;
-                    const int pp = blk / SP;
-                    const int bb = blk - pp * SP;
-                    const int p0 = min(nunits, pp * kpu);
-                    const int p1 = min(nunits, p0 + kpu);
-                    const int u = p0 + j * SPU + bb / F::kBlocks;
-                    const int off = u * 32 * F::kBlocks + F::block_offset(bb % F::kBlocks, kgl);
     #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int c = wave + kWaves * i;
+                        const int ii = wave + kWaves * i;
+                        const int c = ii >> dl;
+                        const int blk = ((ii & (dep - 1)) << 4) + (lane >> 2);
+                        const int pp = blk >> (LOG_SP + dl);
+                        const int bb = blk - (pp << (LOG_SP + dl));
+                        const int p0 = min(nunits, pp * kpu);
+                        const int p1 = min(nunits, p0 + kpu);
+                        const int u = p0 + j * spu + bb / F::kBlocks;
+                        const int off =
+                            u * 32 * F::kBlocks + F::block_offset(bb % F::kBlocks, kgl);
                         if (c < ntok && u < p1)
-                            __builtin_amdgcn_global_load_lds((const void*)(tp[i] + off),
-                                                             (lds_void_ptr)&xs[bsel][tok_base(c)], 16,
-                                                             0, 0);
+                            __builtin_amdgcn_global_load_lds(
+                                (const void*)(tp[i] + off),
+                                (lds_void_ptr)&xs[bsel][c * tpitch + ((ii & (dep - 1)) << 6)], 16,
+                                0, 0);
                     }
                     if constexpr (NSCF > 0) {
-                        // wave w < TS / 64 fills entries [64w, 64w + 64) of
-                        // every tensor's table: one offset per lane serves
-                        // all tensors (they share the [N][nunits] shape)
-                        static_assert(TS % kWave == 0 && TS / kWave <= kWaves, "scale loads");
-                        if (wave < TS / kWave) {
-                            const int f = wave * kWave + lane;
+                        // load k (64 entries of every tensor's table) by wave
+                        // k % 4: one offset per lane serves all tensors (they
+                        // share the [N][nunits] shape)
+                        const int nld = (R * S * 16 * spu) / kWave;
+                        float* sbuf = reinterpret_cast<float*>(sc) + bsel * SCB;
+                        for (int k = wave; k < nld; k += kWaves) {
+                            const int f = k * kWave + lane;
                             const int row = f & 15;
                             const int qf = f >> 4;
-                            const int jj = qf % SPU;
-                            const int rp = qf / SPU;
+                            const int jj = qf % spu;
+                            const int rp = qf / spu;
                             const int spp = rp % S;
                             const int rb = rb0 + rp / S;
                             const int q0 = min(nunits, spp * kpu);
                             const int q1 = min(nunits, q0 + kpu);
-                            const int su = q0 + j * SPU + jj;
-                            const size_t off = (size_t)(rb * 16 + row) * nunits + su;
-                            float* dst = reinterpret_cast<float*>(sc) + bsel * SCB + wave * kWave;
+                            const int su = q0 + j * spu + jj;
+                            const size_t soff = (size_t)(rb * 16 + row) * nunits + su;
                             if (rb < nrb && su < q1) {
     #pragma unroll
                                 for (int t = 0; t < NSCF; ++t)
                                     __builtin_amdgcn_global_load_lds(
-                                        (const void*)(stab[t] + off), (lds_void_ptr)(dst + t * TS),
-                                        4, 0, 0);
+                                        (const void*)(stab[t] + soff),
+                                        (lds_void_ptr)(sbuf + t * TS + k * kWave), 4, 0, 0);
                             }
                         }
                     }
                 };
                 stage(0, 0);
-                // Weight batches rotate through D register sets: batch bi
-                // lives in set bi % D, and batch bi + D - 1 is requested just
-                // before batch bi is multiplied, so D - 1 batches are in flight.
-                // With D = 3 the second batch is requested after the first
-                // slab's staging loads.
-                if constexpr (D == 3)
-                    if (nfull > 1) F::template load<NMAT, U>(B, src, u0 + U);
-                // batch requests issued since the latest staging loads (D = 3)
-                int since = (D == 3 && nfull > 1) ? 1 : 0;
+                // weight batches ping-pong between two register sets: batch bi
+                // lives in A when bi is even, in B when odd; the next batch is
+                // always requested before the current one is multiplied
                 int bi = 0;
                 for (int j = 0; j < nslab; ++j) {
-                    // this wave's staging loads are done; only batch requests
-                    // issued after them and not yet multiplied may still be in
-                    // flight (loads complete in issue order)
-                    if constexpr (D == 2) {
-                        if (j == 0)
-                            wait_vmcnt<0>();
-                        else if (bi < nfull)
-                            wait_vmcnt<(kLoads < 63 ? kLoads : 63)>();
-                        else
-                            wait_vmcnt<0>();
-                    } else {
-                        const int pend = min(since, min(D - 1, nfull - bi));
-                        if (pend >= 2)
-                            wait_vmcnt<(2 * kLoads < 63 ? 2 * kLoads : 63)>();
-                        else if (pend == 1)
-                            wait_vmcnt<(kLoads < 63 ? kLoads : 63)>();
-                        else
-                            wait_vmcnt<0>();
-                    }
+                    // this wave's staging loads are done (only the batch
+                    // prefetched for this slab may still be in flight; at slab
+                    // 0, whose staging follows the first batch, everything)
+                    if (j == 0)
+                        wait_vmcnt<0>();
+                    else if (bi < nfull)
+                        wait_vmcnt<(kLoads < 63 ? kLoads : 63)>();
+                    else
+                        wait_vmcnt<0>();
                     __syncthreads();
-                    if (j + 1 < nslab) {
-                        stage(j + 1, (j + 1) & 1);
-                        since = 0;
-                    }
-                    const int slab_u0 = u0 + j * SPU;
+                    if (j + 1 < nslab) stage(j + 1, (j + 1) & 1);
+                    const int slab_u0 = u0 + j * spu;
                     // this lane's B fragments: token row bcol, K group kg, from the
                     // first block of this wave's K part
-                    const u32x4* buf = &xs[j & 1][tok_base(bcol) + kp * SP * kBlockU4 + kg];
+                    const u32x4* buf =
+                        &xs[j & 1][bcol * tpitch + ((kp * SP * kBlockU4) << dl) + kg];
                     // this lane's scales: row block r, K part kp, unit 0 of the
                     // slab, output rows 4kg .. 4kg + 3
                     const float* sl = reinterpret_cast<const float*>(sc) + (j & 1) * SCB +
-                                      (r * S + kp) * SPU * 16 + 4 * kg;
-                    const int bend = min(nfull, (j + 1) * NB);
+                                      (r * S + kp) * spu * 16 + 4 * kg;
+                    const int bend = min(nfull, (j + 1) * nb);
                     for (; bi < bend; ++bi) {
                         const int ub = u0 + bi * U - slab_u0;   // batch's first unit in the slab
                         const u32x4* bb = buf + ub * F::kBlocks * kBlockU4;
                         const float* sb = sl + 16 * ub;
-                        const int nx = bi + D - 1;              // batch requested now
-                        const int ux = u0 + nx * U;
-                        if constexpr (D == 2) {
-                            if ((bi & 1) == 0) {
-                                if (nx < nfull) F::template load<NMAT, U>(B, src, ux);
-                                F::template mma<NMAT, U, TS>(A, bb, sb, acc);
-                            } else {
-                                if (nx < nfull) F::template load<NMAT, U>(A, src, ux);
-                                F::template mma<NMAT, U, TS>(B, bb, sb, acc);
-                            }
+                        if ((bi & 1) == 0) {
+                            if (bi + 1 < nfull)
+                                F::template load<NMAT, U>(B, src, u0 + (bi + 1) * U);
+                            F::template mma<NMAT, U, TS>(A, bb, sb, acc);
                         } else {
-                            if (nx < nfull) ++since;
-                            const int ph = bi % 3;
-                            if (ph == 0) {
-                                if (nx < nfull) F::template load<NMAT, U>(C, src, ux);
-                                F::template mma<NMAT, U, TS>(A, bb, sb, acc);
-                            } else if (ph == 1) {
-                                if (nx < nfull) F::template load<NMAT, U>(A, src, ux);
-                                F::template mma<NMAT, U, TS>(B, bb, sb, acc);
-                            } else {
-                                if (nx < nfull) F::template load<NMAT, U>(B, src, ux);
-                                F::template mma<NMAT, U, TS>(C, bb, sb, acc);
-                            }
+                            if (bi + 1 < nfull)
+                                F::template load<NMAT, U>(A, src, u0 + (bi + 1) * U);
+                            F::template mma<NMAT, U, TS>(B, bb, sb, acc);
                         }
                     }
-                    if (has && tail_u < u1 && tail_u >= slab_u0 && tail_u < slab_u0 + SPU)
+                    if (has && tail_u < u1 && tail_u >= slab_u0 && tail_u < slab_u0 + spu)
                         for (int u = tail_u; u < u1; ++u) {
                             typename F::template Batch<NMAT, 1> t;
                             F::template load<NMAT, 1>(t, src, u);
@@ -840,7 +826,7 @@ __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(GemmTuning<Fmt, NMAT>::kBlocksPerCU)))
 void expert_gemm_kernel(const ExpertGemm g) {
     constexpr int U = GemmTuning<Fmt, NMAT>::kBatch;
-    constexpr int D = GemmTuning<Fmt, NMAT>::kDepth;
+    constexpr int FMAX = GemmTuning<Fmt, NMAT>::kMaxDepth;
     constexpr int units1 = kSlabBlocks / Fmt::kBlocks;   // units of a part per slab, S = 1
     // K-slab buffers of the token tile, double-buffered, followed (scaled
     // formats) by the slabs' scale tables.  Both are filled by direct
@@ -848,7 +834,8 @@ void expert_gemm_kernel(const ExpertGemm g) {
     // the waits for those loads to the kernel's own (vmcnt wait + barrier per
     // slab), whereas with two arrays it waited for every outstanding load
     // before each LDS read, which serialised the weight prefetch.
-    constexpr int kScF4 = ScaleTensors<Fmt, NMAT>::value * kScaleSlabFloats / 4 * 2;
+    constexpr int kScF4 =
+        ScaleTensors<Fmt, NMAT>::value * kScaleSlabFloats * GemmTuning<Fmt, NMAT>::kMaxDepth / 4 * 2;
     __shared__ u32x4 lds[2 * kSlabU4 + kScF4];
     u32x4 (*xs)[kSlabU4] = reinterpret_cast<u32x4 (*)[kSlabU4]>(lds);
     f32x4* sc = reinterpret_cast<f32x4*>(lds + 2 * kSlabU4);
@@ -857,11 +844,11 @@ void expert_gemm_kernel(const ExpertGemm g) {
     const int G = busy_grid(rounds_for(n_act, g.N / 16, S));
     if ((int)blockIdx.x >= G) return;
     if (S == 1)
-        gemm_rounds<Fmt, NMAT, 1, cmin(U, units1), D>(g, n_act, G, xs, sc);
+        gemm_rounds<Fmt, NMAT, 1, cmin(U, units1), FMAX>(g, n_act, G, xs, sc);
     else if (S == 2)
-        gemm_rounds<Fmt, NMAT, 2, cmin(U, units1 / 2), D>(g, n_act, G, xs, sc);
+        gemm_rounds<Fmt, NMAT, 2, cmin(U, units1 / 2), FMAX>(g, n_act, G, xs, sc);
     else
-        gemm_rounds<Fmt, NMAT, 4, cmin(U, units1 / 4), D>(g, n_act, G, xs, sc);
+        gemm_rounds<Fmt, NMAT, 4, cmin(U, units1 / 4), FMAX>(g, n_act, G, xs, sc);
 }
 
 // Grid of one grouped product: persistent, the resident workgroup count,
