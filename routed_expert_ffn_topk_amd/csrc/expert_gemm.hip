@@ -34,6 +34,8 @@
 // the token rows, which are padded so the reads are free of bank conflicts.
 // Weights stream through registers in batches with the next batch always in
 // flight, also across slab barriers.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -423,7 +425,9 @@ using DualDown = MixedWeights<Int4Weights, Int8Weights, true>;
 // shape): batch length U (units), resident workgroups per CU, and the
 // deepest slab (kMaxDepth: a slab row of a chunk with few tokens covers up
 // to this many times 512 K; scaled formats hold that many times the slab's
-// scale table in LDS, which the workgroups per CU must fit).
+// scale table in LDS, which the workgroups per CU must fit), and the batch
+// of the wide chunks (kWideBatch units, 0 = none: chunks of up to 32 tokens
+// use two B tiles per weight batch; BF16 only).
 template <class Fmt, int NMAT>
 struct GemmTuning;
 template <>
@@ -431,48 +435,56 @@ struct GemmTuning<Bf16Weights, 2> {   // gate/up: two matrices per K step
     static constexpr int kBlocksPerCU = 4;
     static constexpr int kBatch = 2;
     static constexpr int kMaxDepth = 16;
+    static constexpr int kWideBatch = 1;
 };
 template <>
 struct GemmTuning<Bf16Weights, 1> {   // down
     static constexpr int kBlocksPerCU = 3;
     static constexpr int kBatch = 8;
     static constexpr int kMaxDepth = 16;
+    static constexpr int kWideBatch = 4;
 };
 template <>
 struct GemmTuning<Int8Weights, 2> {
     static constexpr int kBlocksPerCU = 3;
     static constexpr int kBatch = 1;
     static constexpr int kMaxDepth = 4;
+    static constexpr int kWideBatch = 0;
 };
 template <>
 struct GemmTuning<Int8Weights, 1> {
     static constexpr int kBlocksPerCU = 3;
     static constexpr int kBatch = 2;
     static constexpr int kMaxDepth = 8;
+    static constexpr int kWideBatch = 0;
 };
 template <>
 struct GemmTuning<Int4Weights, 2> {
     static constexpr int kBlocksPerCU = 4;
     static constexpr int kBatch = 1;
     static constexpr int kMaxDepth = 1;
+    static constexpr int kWideBatch = 0;
 };
 template <>
 struct GemmTuning<ResidualGateUp, 2> {
     static constexpr int kBlocksPerCU = 2;
     static constexpr int kBatch = 2;
     static constexpr int kMaxDepth = 4;
+    static constexpr int kWideBatch = 0;
 };
 template <>
 struct GemmTuning<DualDown, 1> {
     static constexpr int kBlocksPerCU = 2;
     static constexpr int kBatch = 2;
     static constexpr int kMaxDepth = 16;
+    static constexpr int kWideBatch = 0;
 };
 template <>
 struct GemmTuning<Int4Weights, 1> {
     static constexpr int kBlocksPerCU = 2;
     static constexpr int kBatch = 4;
     static constexpr int kMaxDepth = 16;
+    static constexpr int kWideBatch = 0;
 };
 
 // S: K-parts per row block; U: units per weight batch (divides the units of
@@ -483,7 +495,7 @@ struct GemmTuning<Int4Weights, 1> {
 // all active experts (expert-major) are dealt out per XCD: each XCD owns a
 // contiguous slice, and its workgroups take the slice's rounds interleaved
 // (an equal number each, +-1).
-template <class Fmt, int NMAT, int S, int U, int FMAX>
+template <class Fmt, int NMAT, int S, int U, int FMAX, int UW>
 __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, int n_act, int grid,
                                             u32x4 (*xs)[kSlabU4], f32x4* sc) {
     constexpr int R = kWaves / S;              // row blocks per round
@@ -492,6 +504,8 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, int n_act, int 
     constexpr int NB = SPU / U;                // full batches per slab (depth 1)
     static_assert(SPU >= 1 && SPU % U == 0, "batch must divide the slab part");
     static_assert(FMAX >= 1 && FMAX <= 16 && (FMAX & (FMAX - 1)) == 0, "slab depth");
+    // wide (32-token) chunks: UW units per weight batch, 0 = none
+    constexpr bool kWide = UW > 0 && Fmt::kBlocks == 1 && SPU % (2 * (UW > 0 ? UW : 1)) == 0;
     constexpr int LOG_SP = SP == 16 ? 4 : SP == 8 ? 3 : 2;
     static_assert((1 << LOG_SP) == SP, "power-of-two slab parts");
     // scale table of a slab (scaled formats): per tensor, [R][S][SPU*F][16
@@ -571,7 +585,245 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, int n_act, int 
                     if (NMAT == 2) stab[NMAT + 1] = g.hs1 + eoff;
                 }
             }
-            for (int c0 = 0; c0 < m; c0 += 16) {
+            // wide chunk: 17-32 tokens, two 16-column B tiles per weight batch
+            auto chunk_wide = [&](int c0) __attribute__((always_inline)) {
+              if constexpr (kWide && NSCF == 0 && F::kBlocks == 1) {
+                constexpr int NC = 2;
+                constexpr int UC = UW > 0 ? UW : 1;          // units per weight batch
+                static_assert(NC == 1 || (NSCF == 0 && F::kBlocks == 1 && SPU % (2 * UC) == 0),
+                              "wide chunks: BF16 weights, half slabs of whole batches");
+                const int ntok = min(16 * NC, m - c0);        // distinct tokens of the chunk
+                // Slab depth (NC = 1): a slab buffer holds 16 token rows of
+                // 512 K; a chunk of ntok <= 16 / 2^d tokens gives each of its
+                // rows 2^d times that K (up to FMAX), so a round crosses 2^d
+                // times fewer slab barriers.  NC = 2: 32 rows of 256 K.
+                const int dl = NC == 2 ? 0
+                                       : min(ntok <= 1 ? 4 : ntok <= 2 ? 3 : ntok <= 4 ? 2
+                                                                  : ntok <= 8 ? 1 : 0,
+                                             FMAX == 16 ? 4 : FMAX == 8 ? 3 : FMAX == 4 ? 2
+                                                                : FMAX == 2 ? 1 : 0);
+                const int dep = 1 << dl;
+                constexpr int SPUC = NC == 1 ? SPU : SPU / 2;    // units per part and slab (depth 1)
+                constexpr int SPC = NC == 1 ? SP : SP / 2;       // blocks per part and slab (depth 1)
+                constexpr int LOG_SPC = NC == 1 ? LOG_SP : LOG_SP - 1;
+                const int spu = SPUC << dl;              // units of each K part per slab
+                const int nb = (SPUC / UC) << dl;        // full batches per full slab
+                const int tpitch = (kTokRowU4 / NC) * dep + 2;   // LDS words between token rows
+                const int nslab = (kpu + spu - 1) / spu;
+                const int nfull = has ? (u1 - u0) / UC : 0;   // full batches of this wave
+                const int tail_u = u0 + nfull * UC;           // tail units [tail_u, u1)
+                // padding columns (beyond the expert's tokens) read token 0's row:
+                // an MFMA output column depends only on its own B column, and
+                // padding columns are never stored
+                bool valid[NC];
+                int bcol[NC];
+    #pragma unroll
+                for (int hh = 0; hh < NC; ++hh) {
+                    valid[hh] = 16 * hh + col < ntok;
+                    bcol[hh] = valid[hh] ? 16 * hh + col : 0;
+                }
+                // the first weight batch needs only the expert and the row:
+                // request it before the token rows, whose addresses take two
+                // dependent loads (the first slab then waits for everything)
+                constexpr int kLoads = F::template loads<NMAT, UC>();
+                typename F::template Batch<NMAT, UC> A, B;
+                if (nfull > 0) F::template load<NMAT, UC>(A, src, u0);
+                // staging loads this wave issues per slab: ii = wave, wave + 4,
+                // ...; NC = 1: of the chunk's ntok * dep loads, load ii stages
+                // 512 K of token ii >> dl, the (ii & (dep - 1))-th of the
+                // token's slab row; NC = 2: load ii stages token ii's 256 K
+                constexpr int NL = 4 * NC;
+                // (element offsets of the rows, 32-bit: B rows are at most
+                // a few times 10^7 elements apart)
+                uint32_t tp[NL];
+    #pragma unroll
+                for (int i = 0; i < NL; ++i) {
+                    const int c = (wave + kWaves * i) >> dl;
+                    const int qq = beg + c0 + (c < ntok ? c : 0);
+                    const int brow = NMAT == 2 ? g.sorted_slot[qq] / g.top_k : qq;
+                    tp[i] = (uint32_t)brow * (uint32_t)g.b_pitch;
+                }
+                f32x4 acc[NC][NMAT];
+    #pragma unroll
+                for (int hh = 0; hh < NC; ++hh)
+    #pragma unroll
+                    for (int mm = 0; mm < NMAT; ++mm) acc[hh][mm] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+                // Slab j holds, for each K part pp, its units [start(pp) + j*spu,
+                // +spu) at blocks [pp*SPC*dep, (pp+1)*SPC*dep) of every token row.
+                // One load instruction stages 16 blocks (1 KB; NC = 2: 8 blocks
+                // from lanes 0-31) of one token's slab row: lane L fills block
+                // 16i + L/4 for K group L%4, so the row is read from global
+                // memory in contiguous runs.
+                // Scaled formats also stage the slab's scales: entry
+                // ((rr*S + pp)*spu + jj)*16 + row of tensor t is the scale of
+                // row 16*(rb0 + rr) + row, unit start(pp) + j*spu + jj; one
+                // 4-byte direct load per lane fills 64 consecutive entries.
+                auto stage = [&](int j, int bsel) {
+                    const int kgl = lane & 3;
+    #pragma unroll
+                    for (int i = 0; i < NL; ++i) {
+                        const int ii = wave + kWaves * i;
+                        const int c = ii >> dl;
+                        const int blk = ((ii & (dep - 1)) << 4) + (lane >> 2);
+                        const int pp = blk >> (LOG_SPC + dl);
+                        const int bb = blk - (pp << (LOG_SPC + dl));
+                        const int p0 = min(nunits, pp * kpu);
+                        const int p1 = min(nunits, p0 + kpu);
+                        const int u = p0 + j * spu + bb / F::kBlocks;
+                        const int off =
+                            u * 32 * F::kBlocks + F::block_offset(bb % F::kBlocks, kgl);
+                        if (c < ntok && u < p1 && (NC == 1 || lane < 32))
+                            __builtin_amdgcn_global_load_lds(
+                                (const void*)(g.b_src + tp[i] + off),
+                                (lds_void_ptr)&xs[bsel][c * tpitch + ((ii & (dep - 1)) << 6)], 16,
+                                0, 0);
+                    }
+                    if constexpr (NSCF > 0) {
+                        // load k (64 entries of every tensor's table) by wave
+                        // k % 4: one offset per lane serves all tensors (they
+                        // share the [N][nunits] shape)
+                        const int nld = (R * S * 16 * spu) / kWave;
+                        float* sbuf = reinterpret_cast<float*>(sc) + bsel * SCB;
+                        for (int k = wave; k < nld; k += kWaves) {
+                            const int f = k * kWave + lane;
+                            const int row = f & 15;
+                            const int qf = f >> 4;
+                            const int jj = qf % spu;
+                            const int rp = qf / spu;
+                            const int spp = rp % S;
+                            const int rb = rb0 + rp / S;
+                            const int q0 = min(nunits, spp * kpu);
+                            const int q1 = min(nunits, q0 + kpu);
+                            const int su = q0 + j * spu + jj;
+                            const size_t soff = (size_t)(rb * 16 + row) * nunits + su;
+                            if (rb < nrb && su < q1) {
+    #pragma unroll
+                                for (int t = 0; t < NSCF; ++t)
+                                    __builtin_amdgcn_global_load_lds(
+                                        (const void*)(stab[t] + soff),
+                                        (lds_void_ptr)(sbuf + t * TS + k * kWave), 4, 0, 0);
+                            }
+                        }
+                    }
+                };
+                stage(0, 0);
+                // weight batches ping-pong between two register sets: batch bi
+                // lives in A when bi is even, in B when odd; the next batch is
+                // always requested before the current one is multiplied
+                int bi = 0;
+                for (int j = 0; j < nslab; ++j) {
+                    // this wave's staging loads are done (only the batch
+                    // prefetched for this slab may still be in flight; at slab
+                    // 0, whose staging follows the first batch, everything)
+                    if (j == 0)
+                        wait_vmcnt<0>();
+                    else if (bi < nfull)
+                        wait_vmcnt<(kLoads < 63 ? kLoads : 63)>();
+                    else
+                        wait_vmcnt<0>();
+                    __syncthreads();
+                    if (j + 1 < nslab) stage(j + 1, (j + 1) & 1);
+                    const int slab_u0 = u0 + j * spu;
+                    // this lane's B fragments: token row bcol, K group kg, from the
+                    // first block of this wave's K part
+                    const u32x4* buf[NC];
+    #pragma unroll
+                    for (int hh = 0; hh < NC; ++hh)
+                        buf[hh] = &xs[j & 1][bcol[hh] * tpitch + ((kp * SPC * kBlockU4) << dl) + kg];
+                    // this lane's scales: row block r, K part kp, unit 0 of the
+                    // slab, output rows 4kg .. 4kg + 3
+                    const float* sl = reinterpret_cast<const float*>(sc) + (j & 1) * SCB +
+                                      (r * S + kp) * spu * 16 + 4 * kg;
+                    const int bend = min(nfull, (j + 1) * nb);
+                    for (; bi < bend; ++bi) {
+                        const int ub = u0 + bi * UC - slab_u0;   // batch's first unit in the slab
+                        const float* sb = sl + 16 * ub;
+                        // the B pointers before the next batch's loads (computing
+                        // them after those loads made the compiler keep far more
+                        // registers live in the quantised gate/up kernels)
+                        const u32x4* bb[NC];
+    #pragma unroll
+                        for (int hh = 0; hh < NC; ++hh) bb[hh] = buf[hh] + ub * F::kBlocks * kBlockU4;
+                        if ((bi & 1) == 0) {
+                            if (bi + 1 < nfull)
+                                F::template load<NMAT, UC>(B, src, u0 + (bi + 1) * UC);
+                            F::template mma<NMAT, UC, TS>(A, bb[0], sb, acc[0]);
+                            if constexpr (NC == 2) F::template mma<NMAT, UC, TS>(A, bb[1], sb, acc[1]);
+                        } else {
+                            if (bi + 1 < nfull)
+                                F::template load<NMAT, UC>(A, src, u0 + (bi + 1) * UC);
+                            F::template mma<NMAT, UC, TS>(B, bb[0], sb, acc[0]);
+                            if constexpr (NC == 2) F::template mma<NMAT, UC, TS>(B, bb[1], sb, acc[1]);
+                        }
+                    }
+                    if (has && tail_u < u1 && tail_u >= slab_u0 && tail_u < slab_u0 + spu)
+                        for (int u = tail_u; u < u1; ++u) {
+                            typename F::template Batch<NMAT, 1> t;
+                            F::template load<NMAT, 1>(t, src, u);
+    #pragma unroll
+                            for (int hh = 0; hh < NC; ++hh)
+                                F::template mma<NMAT, 1, TS>(
+                                    t, buf[hh] + (u - slab_u0) * F::kBlocks * kBlockU4,
+                                    sl + 16 * (u - slab_u0), acc[hh]);
+                        }
+                }
+                __syncthreads();
+                if constexpr (S > 1) {
+                    if (kp > 0) {
+    #pragma unroll
+                        for (int hh = 0; hh < NC; ++hh)
+    #pragma unroll
+                            for (int mm = 0; mm < NMAT; ++mm)
+                                red[(((wave - R) * NC + hh) * NMAT + mm) * kWave + lane] =
+                                    acc[hh][mm];
+                    }
+                    __syncthreads();
+                    if (kp == 0) {
+    #pragma unroll
+                        for (int pp = 1; pp < S; ++pp)
+    #pragma unroll
+                            for (int hh = 0; hh < NC; ++hh)
+    #pragma unroll
+                                for (int mm = 0; mm < NMAT; ++mm)
+                                    acc[hh][mm] +=
+                                        red[((((pp - 1) * R + r) * NC + hh) * NMAT + mm) * kWave +
+                                            lane];
+                    }
+                }
+    #pragma unroll
+                for (int hh = 0; hh < NC; ++hh) {
+                    if (kp == 0 && has && valid[hh]) {
+                        const size_t p = (size_t)beg + c0 + 16 * hh + col;
+                        if constexpr (NMAT == 2) {
+                            const f32x4 gv = acc[hh][0], uv = acc[hh][1];
+                            u32x2 packed;
+                            packed.x = (uint32_t)f32_to_bf16_bits(silu(gv.x) * uv.x) |
+                                       ((uint32_t)f32_to_bf16_bits(silu(gv.y) * uv.y) << 16);
+                            packed.y = (uint32_t)f32_to_bf16_bits(silu(gv.z) * uv.z) |
+                                       ((uint32_t)f32_to_bf16_bits(silu(gv.w) * uv.w) << 16);
+                            *reinterpret_cast<u32x2*>(g.h + p * g.N + row0 + kg * 4) = packed;
+                        } else {
+                            const int slot = g.sorted_slot[p];
+                            *reinterpret_cast<f32x4*>(g.y + (size_t)slot * g.N + row0 + kg * 4) =
+                                acc[hh][0];
+                        }
+                    }
+                }
+                if constexpr (S > 1) __syncthreads();
+              }
+            };
+            // an expert with 17-32 tokens: one wide chunk (BF16 weights at
+            // splits whose slab parts hold whole wide batches); otherwise
+            // chunks of 16
+            bool wide_done = false;
+            if constexpr (kWide && NSCF == 0 && F::kBlocks == 1) {
+                if (m > 16 && m <= 32) {
+                    chunk_wide(0);
+                    wide_done = true;
+                }
+            }
+            for (int c0 = 0; c0 < m && !wide_done;) {
                 const int ntok = min(16, m - c0);        // distinct tokens of the chunk
                 // Slab depth: a slab buffer holds 16 token rows of 512 K; a
                 // chunk of ntok <= 16 / 2^d tokens gives each of its rows
@@ -749,6 +1001,7 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, int n_act, int 
                     }
                 }
                 if constexpr (S > 1) __syncthreads();
+                            c0 += 16;
             }
         };
         if constexpr (IsMixed<Fmt>::value) {
@@ -821,12 +1074,16 @@ __device__ __forceinline__ int choose_split(const ExpertGemm& g, int n_act) {
 // NMAT = 1: down, epilogue y[slot][row] = acc (FP32, slot = sorted_slot[p]).
 // One kernel holds the three K splits; the split is uniform over the launch
 // (read from the device-side active-expert count, or forced by g.split).
-template <class Fmt, int NMAT>
+// WIDE: the kernel also holds the wide (17-32 token) chunk path; launched
+// only when an expert can receive more than 16 slots (the extra path costs
+// registers, which the narrow path of small batches would otherwise pay for).
+template <class Fmt, int NMAT, bool WIDE>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(GemmTuning<Fmt, NMAT>::kBlocksPerCU)))
 void expert_gemm_kernel(const ExpertGemm g) {
     constexpr int U = GemmTuning<Fmt, NMAT>::kBatch;
     constexpr int FMAX = GemmTuning<Fmt, NMAT>::kMaxDepth;
+    constexpr int UW = WIDE ? GemmTuning<Fmt, NMAT>::kWideBatch : 0;
     constexpr int units1 = kSlabBlocks / Fmt::kBlocks;   // units of a part per slab, S = 1
     // K-slab buffers of the token tile, double-buffered, followed (scaled
     // formats) by the slabs' scale tables.  Both are filled by direct
@@ -844,11 +1101,11 @@ void expert_gemm_kernel(const ExpertGemm g) {
     const int G = busy_grid(rounds_for(n_act, g.N / 16, S));
     if ((int)blockIdx.x >= G) return;
     if (S == 1)
-        gemm_rounds<Fmt, NMAT, 1, cmin(U, units1), FMAX>(g, n_act, G, xs, sc);
+        gemm_rounds<Fmt, NMAT, 1, cmin(U, units1), FMAX, cmin(UW, units1 / 2)>(g, n_act, G, xs, sc);
     else if (S == 2)
-        gemm_rounds<Fmt, NMAT, 2, cmin(U, units1 / 2), FMAX>(g, n_act, G, xs, sc);
+        gemm_rounds<Fmt, NMAT, 2, cmin(U, units1 / 2), FMAX, cmin(UW, units1 / 4)>(g, n_act, G, xs, sc);
     else
-        gemm_rounds<Fmt, NMAT, 4, cmin(U, units1 / 4), FMAX>(g, n_act, G, xs, sc);
+        gemm_rounds<Fmt, NMAT, 4, cmin(U, units1 / 4), FMAX, cmin(UW, units1 / 8)>(g, n_act, G, xs, sc);
 }
 
 // Grid of one grouped product: persistent, the resident workgroup count,
@@ -863,11 +1120,20 @@ int gemm_grid(int64_t max_active, int N, int num_cu, int blocks_per_cu) {
     return (int)grid;
 }
 
+// wide: some expert may receive more than 16 slots (T * k > 16)
 template <class Fmt, int NMAT>
-hipError_t launch_gemm(const ExpertGemm& g, int64_t max_active, int num_cu,
+hipError_t launch_gemm(const ExpertGemm& g, int64_t max_active, int num_cu, bool wide,
                        hipStream_t stream) {
     const int grid = gemm_grid(max_active, g.N, num_cu, GemmTuning<Fmt, NMAT>::kBlocksPerCU);
-    hipLaunchKernelGGL((expert_gemm_kernel<Fmt, NMAT>), dim3(grid), dim3(kThreads), 0, stream, g);
+    if constexpr (GemmTuning<Fmt, NMAT>::kWideBatch > 0) {
+        if (wide) {
+            hipLaunchKernelGGL((expert_gemm_kernel<Fmt, NMAT, true>), dim3(grid), dim3(kThreads),
+                               0, stream, g);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((expert_gemm_kernel<Fmt, NMAT, false>), dim3(grid), dim3(kThreads), 0,
+                       stream, g);
     return hipGetLastError();
 }
 
@@ -911,7 +1177,9 @@ hipError_t launch_ffn(const uint16_t* x, const Routing& route, const FfnWeights&
     gu.K = s.H;
     gu.top_k = s.k;
     gu.split = split.gate_up;
-    err = launch_gemm<Fmt, 2>(gu, max_active, num_cu, stream);
+    // an expert can receive more than 16 slots only if the batch has more
+    const bool wide = (int64_t)s.T * s.k > 16;
+    err = launch_gemm<Fmt, 2>(gu, max_active, num_cu, wide, stream);
     if (err == hipSuccess && tiled) err = launch_tiled_gate_up(x, W, s, ws, num_cu, stream);
     if (err == hipSuccess) err = ev.mark(1, stream);
     if (err != hipSuccess) return err;
@@ -932,7 +1200,7 @@ hipError_t launch_ffn(const uint16_t* x, const Routing& route, const FfnWeights&
     dn.N = s.H;
     dn.K = s.I;
     dn.split = split.down;
-    err = launch_gemm<FmtDown, 1>(dn, max_active, num_cu, stream);
+    err = launch_gemm<FmtDown, 1>(dn, max_active, num_cu, wide, stream);
     if (err == hipSuccess && tiled) err = launch_tiled_down(W, s, ws, num_cu, stream);
     if (err == hipSuccess) err = ev.mark(2, stream);
     if (err != hipSuccess) return err;

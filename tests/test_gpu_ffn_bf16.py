@@ -97,6 +97,34 @@ def test_bf16_more_than_16_tokens_per_expert(T, E):
     check_h(case, ws, ref["h"])
 
 
+@pytest.mark.parametrize("counts,k,H,I", [
+    ([17, 32], 1, 128, 96),            # one wide chunk each, ragged and full
+    ([17, 24, 32, 16, 1], 1, 256, 160),  # wide and narrow experts in one launch
+    ([31, 18, 25, 20], 1, 512, 1024),  # several slabs per part
+    ([24, 24, 24], 2, 128, 160),       # two slots per token
+])
+def test_bf16_17_to_32_tokens_per_expert(counts, k, H, I):
+    """Experts with 17-32 tokens take one wide chunk: each weight batch
+    multiplies two 16-column token tiles, so the weights stream once."""
+    need_gpu()
+    E = len(counts)
+    rng = np.random.default_rng(sum(counts) + H)
+    if k == 1:
+        ids = rng.permutation(np.repeat(np.arange(E), counts)).astype(np.int32)[:, None]
+    else:   # token t picks experts t mod E and (t + 1) mod E
+        T = sum(counts) // k
+        ids = np.stack([np.arange(T) % E, (np.arange(T) + 1) % E], axis=1).astype(np.int32)
+        assert np.bincount(ids.reshape(-1), minlength=E).tolist() == counts
+    T = ids.shape[0]
+    case = random_case(T + H + I, T, H, I, E, k, std=0.08, ids=ids)
+    say(f"bf16 17-32 tokens/expert counts={counts} k={k} H={H} I={I}")
+    out, ws = run(case)
+    ref = case.oracle(aux=True)
+    assert_close(out, ref["out"], TOL_BF16)
+    assert_close_scaled(out, ref["out"], 1e-2)
+    check_h(case, ws, ref["h"])
+
+
 def test_bf16_duplicate_and_dropped_ids():
     need_gpu()
     T, E, k = 12, 5, 3

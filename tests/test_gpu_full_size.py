@@ -15,7 +15,7 @@ from moe_cases import (TOL_BF16, TOL_INT8, assert_close, check_lists, need_gpu,
 pytestmark = pytest.mark.gpu
 
 FULL = ["mixtral8x7b_m1", "mixtral8x7b_m2", "mixtral8x7b_m4", "mixtral8x7b_m8",
-        "mixtral8x7b_m16", "deepseekv3_t16", "deepseekv3_zipf_t16",
+        "mixtral8x7b_m16", "mixtral8x7b_t64", "deepseekv3_t16", "deepseekv3_zipf_t16",
         "mixtral8x22b_t1", "mixtral8x22b_t4", "mixtral8x22b_t16", "qwen3_235b_t1",
         "qwen3_235b_t4", "qwen3_235b_t16",
         # prefill-sized batches: the tiled product takes the experts

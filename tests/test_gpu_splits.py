@@ -27,7 +27,8 @@ def _restore_device_choice():
 @pytest.mark.parametrize("T,H,I,E,k", [
     (13, 320, 288, 6, 3),      # K steps 10 / 9: parts 3,3,3,1 and 3,3,3,0 at S = 4
     (16, 1024, 512, 8, 2),     # several LDS slabs per part
-    (40, 128, 96, 2, 1),       # 20 tokens per expert: two token chunks
+    (40, 128, 96, 2, 1),       # 20 tokens per expert: one wide chunk
+    (56, 256, 160, 2, 1),      # 28 tokens per expert: one wide chunk, several slabs
 ])
 def test_bf16_every_split_matches_oracle(T, H, I, E, k):
     need_gpu()

@@ -86,6 +86,9 @@ def _registry() -> Dict[str, Workload]:
                                            E=8, k=2, T=T)
         w[f"qwen3_235b_t{T}"] = Workload(f"qwen3_235b_t{T}", H=4096, I=1536,
                                          E=128, k=8, T=T)
+    # the largest decode batch of the small-m product at the Mixtral-8x7B
+    # shape with N(0,1) router logits: about 16 tokens per expert, some 17-32
+    w["mixtral8x7b_t64"] = Workload("mixtral8x7b_t64", H=4096, I=14336, E=8, k=2, T=64)
     # prefill-sized batches (many tokens per expert) at the same expert shapes
     for T in (512, 2048):
         w[f"mixtral8x7b_t{T}"] = Workload(f"mixtral8x7b_t{T}", H=4096, I=14336,
