@@ -460,9 +460,9 @@ struct GemmTuning<Int8Weights, 1> {
 };
 template <>
 struct GemmTuning<Int4Weights, 2> {
-    static constexpr int kBlocksPerCU = 4;
-    static constexpr int kBatch = 1;
-    static constexpr int kMaxDepth = 1;
+    static constexpr int kBlocksPerCU = 3;
+    static constexpr int kBatch = 2;
+    static constexpr int kMaxDepth = 4;
     static constexpr int kWideBatch = 0;
 };
 template <>
