@@ -37,6 +37,7 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "gather_index.hpp"
 #include "launch.hpp"
 
 namespace moe {
@@ -81,6 +82,22 @@ struct ExpertGemm {
     int N, K;                 // rows per expert matrix, reduction length
     int top_k;                // gate/up: B row of gathered row p is token sorted_slot[p] / top_k
     int split;                // K parts per row block (1, 2 or 4); 0 = chosen on the device
+    // gate/up launched with the gather index built in its prologue: the
+    // slots' expert ids [n_slots] (topk_ids), the expert count, and where
+    // workgroup 0 publishes the index; meta/offsets/active/sorted_slot above
+    // are then not read
+    const int32_t* ids;
+    int n_slots;
+    int E;
+    IndexOut ix_out;
+};
+
+// Where a launch reads the gather index: the workspace, or the LDS copy its
+// prologue built.
+struct IndexView {
+    const int32_t* offsets;
+    const int32_t* active;
+    const int32_t* sorted_slot;
 };
 
 // ---------------------------------------------------------------------------
@@ -496,7 +513,8 @@ struct GemmTuning<Int4Weights, 1> {
 // contiguous slice, and its workgroups take the slice's rounds interleaved
 // (an equal number each, +-1).
 template <class Fmt, int NMAT, int S, int U, int FMAX, int UW>
-__device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, int n_act, int grid,
+__device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView ix, int n_act,
+                                            int grid,
                                             u32x4 (*xs)[kSlabU4], f32x4* sc) {
     constexpr int R = kWaves / S;              // row blocks per round
     constexpr int SP = kSlabBlocks / S;        // LDS blocks of each K part per slab (depth 1)
@@ -546,9 +564,9 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, int n_act, int 
     for (int q = qb + li; q < qe; q += per) {
         const int a = q / rpe;                   // active expert of the round
         const int rb0 = (q - a * rpe) * R;       // its first row block
-        const int e = g.active[a];
-        const int beg = g.offsets[e];
-        const int m = g.offsets[e + 1] - beg;
+        const int e = ix.active[a];
+        const int beg = ix.offsets[e];
+        const int m = ix.offsets[e + 1] - beg;
         const int my = rb0 + r;
         const bool has = my < nrb;
         const int row0 = (has ? my : 0) * 16;
@@ -640,7 +658,7 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, int n_act, int 
                 for (int i = 0; i < NL; ++i) {
                     const int c = (wave + kWaves * i) >> dl;
                     const int qq = beg + c0 + (c < ntok ? c : 0);
-                    const int brow = NMAT == 2 ? g.sorted_slot[qq] / g.top_k : qq;
+                    const int brow = NMAT == 2 ? ix.sorted_slot[qq] / g.top_k : qq;
                     tp[i] = (uint32_t)brow * (uint32_t)g.b_pitch;
                 }
                 f32x4 acc[NC][NMAT];
@@ -804,7 +822,7 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, int n_act, int 
                                        ((uint32_t)f32_to_bf16_bits(silu(gv.w) * uv.w) << 16);
                             *reinterpret_cast<u32x2*>(g.h + p * g.N + row0 + kg * 4) = packed;
                         } else {
-                            const int slot = g.sorted_slot[p];
+                            const int slot = ix.sorted_slot[p];
                             *reinterpret_cast<f32x4*>(g.y + (size_t)slot * g.N + row0 + kg * 4) =
                                 acc[hh][0];
                         }
@@ -855,7 +873,7 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, int n_act, int 
                 for (int i = 0; i < 4; ++i) {
                     const int c = (wave + kWaves * i) >> dl;
                     const int qq = beg + c0 + (c < ntok ? c : 0);
-                    const int brow = NMAT == 2 ? g.sorted_slot[qq] / g.top_k : qq;
+                    const int brow = NMAT == 2 ? ix.sorted_slot[qq] / g.top_k : qq;
                     tp[i] = g.b_src + (size_t)brow * g.b_pitch;
                 }
                 f32x4 acc[NMAT];
@@ -996,7 +1014,7 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, int n_act, int 
                                    ((uint32_t)f32_to_bf16_bits(silu(gv.w) * uv.w) << 16);
                         *reinterpret_cast<u32x2*>(g.h + p * g.N + row0 + kg * 4) = packed;
                     } else {
-                        const int slot = g.sorted_slot[p];
+                        const int slot = ix.sorted_slot[p];
                         *reinterpret_cast<f32x4*>(g.y + (size_t)slot * g.N + row0 + kg * 4) = acc[0];
                     }
                 }
@@ -1077,7 +1095,11 @@ __device__ __forceinline__ int choose_split(const ExpertGemm& g, int n_act) {
 // WIDE: the kernel also holds the wide (17-32 token) chunk path; launched
 // only when an expert can receive more than 16 slots (the extra path costs
 // registers, which the narrow path of small batches would otherwise pay for).
-template <class Fmt, int NMAT, bool WIDE>
+// FUSED (gate/up, decode-sized batches): every workgroup first builds the
+// gather index from the routing ids into LDS and reads it from there;
+// workgroup 0 also publishes it for the down product.  One launch fewer per
+// layer, and the rounds' expert and token lookups become LDS reads.
+template <class Fmt, int NMAT, bool WIDE, bool FUSED>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(GemmTuning<Fmt, NMAT>::kBlocksPerCU)))
 void expert_gemm_kernel(const ExpertGemm g) {
@@ -1093,19 +1115,37 @@ void expert_gemm_kernel(const ExpertGemm g) {
     // before each LDS read, which serialised the weight prefetch.
     constexpr int kScF4 =
         ScaleTensors<Fmt, NMAT>::value * kScaleSlabFloats * GemmTuning<Fmt, NMAT>::kMaxDepth / 4 * 2;
-    __shared__ u32x4 lds[2 * kSlabU4 + kScF4];
+    // (FUSED: the LDS copy of the gather index at the end, in the same array)
+    static_assert(!FUSED || NMAT == 2, "the index is built by the gate/up product");
+    static_assert(kFxScratchInts * 4 <= (int)sizeof(u32x4) * kSlabU4, "index scratch fits a slab");
+    constexpr int kIxF4 = FUSED ? kFxInts / 4 : 0;
+    __shared__ u32x4 lds[2 * kSlabU4 + kScF4 + kIxF4];
     u32x4 (*xs)[kSlabU4] = reinterpret_cast<u32x4 (*)[kSlabU4]>(lds);
     f32x4* sc = reinterpret_cast<f32x4*>(lds + 2 * kSlabU4);
-    const int n_act = g.meta[0];
+    int n_act;
+    IndexView ix;
+    if constexpr (FUSED) {
+        // scratch in the first slab buffer, free before the first round
+        int* ixl = reinterpret_cast<int*>(lds + 2 * kSlabU4 + kScF4);
+        n_act = build_index_lds<kThreads>(g.ids, g.n_slots, g.E, reinterpret_cast<int*>(lds),
+                                          ixl, blockIdx.x == 0, g.ix_out);
+        ix = IndexView{ixl + kFxOffsets, ixl + kFxActive, ixl + kFxSorted};
+    } else {
+        n_act = g.meta[0];
+        ix = IndexView{g.offsets, g.active, g.sorted_slot};
+    }
     const int S = g.split ? g.split : choose_split<Fmt, NMAT, U>(g, n_act);
     const int G = busy_grid(rounds_for(n_act, g.N / 16, S));
     if ((int)blockIdx.x >= G) return;
     if (S == 1)
-        gemm_rounds<Fmt, NMAT, 1, cmin(U, units1), FMAX, cmin(UW, units1 / 2)>(g, n_act, G, xs, sc);
+        gemm_rounds<Fmt, NMAT, 1, cmin(U, units1), FMAX, cmin(UW, units1 / 2)>(g, ix, n_act, G,
+                                                                              xs, sc);
     else if (S == 2)
-        gemm_rounds<Fmt, NMAT, 2, cmin(U, units1 / 2), FMAX, cmin(UW, units1 / 4)>(g, n_act, G, xs, sc);
+        gemm_rounds<Fmt, NMAT, 2, cmin(U, units1 / 2), FMAX, cmin(UW, units1 / 4)>(g, ix, n_act,
+                                                                                  G, xs, sc);
     else
-        gemm_rounds<Fmt, NMAT, 4, cmin(U, units1 / 4), FMAX, cmin(UW, units1 / 8)>(g, n_act, G, xs, sc);
+        gemm_rounds<Fmt, NMAT, 4, cmin(U, units1 / 4), FMAX, cmin(UW, units1 / 8)>(g, ix, n_act,
+                                                                                  G, xs, sc);
 }
 
 // Grid of one grouped product: persistent, the resident workgroup count,
@@ -1120,21 +1160,30 @@ int gemm_grid(int64_t max_active, int N, int num_cu, int blocks_per_cu) {
     return (int)grid;
 }
 
-// wide: some expert may receive more than 16 slots (T * k > 16)
+template <class Fmt, int NMAT, bool FUSED>
+hipError_t launch_gemm_as(const ExpertGemm& g, int grid, bool wide, hipStream_t stream) {
+    if constexpr (GemmTuning<Fmt, NMAT>::kWideBatch > 0) {
+        if (wide) {
+            hipLaunchKernelGGL((expert_gemm_kernel<Fmt, NMAT, true, FUSED>), dim3(grid),
+                               dim3(kThreads), 0, stream, g);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((expert_gemm_kernel<Fmt, NMAT, false, FUSED>), dim3(grid), dim3(kThreads),
+                       0, stream, g);
+    return hipGetLastError();
+}
+
+// wide: some expert may receive more than 16 slots (T * k > 16); g.ids set:
+// the gate/up launch that builds the gather index itself
 template <class Fmt, int NMAT>
 hipError_t launch_gemm(const ExpertGemm& g, int64_t max_active, int num_cu, bool wide,
                        hipStream_t stream) {
     const int grid = gemm_grid(max_active, g.N, num_cu, GemmTuning<Fmt, NMAT>::kBlocksPerCU);
-    if constexpr (GemmTuning<Fmt, NMAT>::kWideBatch > 0) {
-        if (wide) {
-            hipLaunchKernelGGL((expert_gemm_kernel<Fmt, NMAT, true>), dim3(grid), dim3(kThreads),
-                               0, stream, g);
-            return hipGetLastError();
-        }
+    if constexpr (NMAT == 2) {
+        if (g.ids) return launch_gemm_as<Fmt, NMAT, true>(g, grid, wide, stream);
     }
-    hipLaunchKernelGGL((expert_gemm_kernel<Fmt, NMAT, false>), dim3(grid), dim3(kThreads), 0,
-                       stream, g);
-    return hipGetLastError();
+    return launch_gemm_as<Fmt, NMAT, false>(g, grid, wide, stream);
 }
 
 // Fmt: the gate/up weight format; FmtDown: down's (the same but for the
@@ -1147,9 +1196,16 @@ hipError_t launch_ffn(const uint16_t* x, const Routing& route, const FfnWeights&
     // large enough that an expert can have more than kTiledMinTokens)
     const bool tiled = Fmt::kBytesPerWeight == 2.0f && s.T > kTiledMinBatch;
     const int m_split = tiled ? kTiledMinTokens : INT_MAX;
-    hipError_t err =
-        route.logits ? launch_route_permute(route.logits, route.ids, route.w, s, ws, m_split, stream)
-                     : launch_permute(route.ids, s, ws, m_split, stream);
+    // decode-sized batches from given ids: the gate/up product builds the
+    // gather index in its prologue (no separate index launch)
+    const int64_t n_slots = (int64_t)s.T * s.k;
+    const bool fused = !route.logits && !tiled && n_slots >= 1 && n_slots <= kFusedMaxSlots &&
+                       s.E <= kFusedMaxExperts;
+    hipError_t err = hipSuccess;
+    if (route.logits)
+        err = launch_route_permute(route.logits, route.ids, route.w, s, ws, m_split, stream);
+    else if (!fused)
+        err = launch_permute(route.ids, s, ws, m_split, stream);
     if (err == hipSuccess) err = ev.mark(0, stream);
     if (err != hipSuccess) return err;
     // upper bound of active experts: every slot could name a different one
@@ -1177,6 +1233,12 @@ hipError_t launch_ffn(const uint16_t* x, const Routing& route, const FfnWeights&
     gu.K = s.H;
     gu.top_k = s.k;
     gu.split = split.gate_up;
+    if (fused) {
+        gu.ids = route.ids;
+        gu.n_slots = (int)n_slots;
+        gu.E = s.E;
+        gu.ix_out = IndexOut{ws.meta, ws.counts, ws.offsets, ws.active, ws.sorted_slot};
+    }
     // an expert can receive more than 16 slots only if the batch has more
     const bool wide = (int64_t)s.T * s.k > 16;
     err = launch_gemm<Fmt, 2>(gu, max_active, num_cu, wide, stream);
@@ -1200,6 +1262,7 @@ hipError_t launch_ffn(const uint16_t* x, const Routing& route, const FfnWeights&
     dn.N = s.H;
     dn.K = s.I;
     dn.split = split.down;
+    dn.ids = nullptr;
     err = launch_gemm<FmtDown, 1>(dn, max_active, num_cu, wide, stream);
     if (err == hipSuccess && tiled) err = launch_tiled_down(W, s, ws, num_cu, stream);
     if (err == hipSuccess) err = ev.mark(2, stream);

@@ -9,13 +9,13 @@
 #include <cmath>
 
 #include "common.hpp"
+#include "gather_index.hpp"
 #include "launch.hpp"
 
 namespace moe {
 
 namespace {
 
-constexpr int kMaxExperts = 1024;          // matches MOE_FFN_MAX_EXPERTS
 // The fused router + gather index: batches of at most this many tokens and
 // slots (16 waves route up to four tokens each; one wave places the slots),
 // with the logits staged in LDS when the batch's T*E fits.
@@ -241,116 +241,6 @@ __global__ __launch_bounds__(256) void route_grouped_kernel(
     }
 }
 
-// ---------------------------------------------------------------------------
-// Gather index: stable counting sort of the n slots by expert.  Writes
-// counts, offsets (exclusive prefix), the ascending lists of active experts
-// (split by token count between the small-m and the tiled product), and
-// sorted_slot (expert-major, slot order within an expert).  Slots with ids
-// outside [0, E) are left out and counted in meta[1].
-// ---------------------------------------------------------------------------
-
-// The experts' offsets (exclusive scan of cnt[]) and lists, by wave 0 alone
-// (each lane owns a run of up to 16 consecutive experts).  Experts with more
-// than m_split slots go to the large list (the tiled product), the other
-// active ones to the active list (the small-m product).  base[] receives the
-// offsets.
-__device__ __forceinline__ void scan_experts(const int* cnt, int E, int m_split, int nbad,
-                                             int* base, int32_t* __restrict__ meta,
-                                             int32_t* __restrict__ counts,
-                                             int32_t* __restrict__ offsets,
-                                             int32_t* __restrict__ active,
-                                             int32_t* __restrict__ large) {
-    const int lane = threadIdx.x;
-    const int per = (E + kWave - 1) / kWave;
-    const int e0 = min(E, lane * per), e1 = min(E, e0 + per);
-    int lc = 0, la = 0, ll = 0;
-    for (int e = e0; e < e1; ++e) {
-        lc += cnt[e];
-        la += cnt[e] > 0 && cnt[e] <= m_split;
-        ll += cnt[e] > m_split;
-    }
-    const int ic = wave_prefix_sum_i32(lc);
-    const int ia = wave_prefix_sum_i32(la);
-    const int il = wave_prefix_sum_i32(ll);
-    int bc = ic - lc, ba = ia - la, bl = il - ll;
-    for (int e = e0; e < e1; ++e) {
-        base[e] = bc;
-        offsets[e] = bc;
-        counts[e] = cnt[e];
-        if (cnt[e] > m_split)
-            large[bl++] = e;
-        else if (cnt[e] > 0)
-            active[ba++] = e;
-        bc += cnt[e];
-    }
-    if (lane == kWave - 1) {
-        offsets[E] = ic;
-        meta[0] = ia;
-        meta[1] = nbad;
-        meta[2] = il;
-    }
-}
-
-// Per-expert counts of the n slots (all NT threads), then scan_experts.
-// Ends with a barrier.
-template <int NT, class Ids>
-__device__ __forceinline__ void count_and_scan(Ids ids, int n, int E, int m_split, int* cnt,
-                                               int* base, int* nbad, int32_t* __restrict__ meta,
-                                               int32_t* __restrict__ counts,
-                                               int32_t* __restrict__ offsets,
-                                               int32_t* __restrict__ active,
-                                               int32_t* __restrict__ large) {
-    const int tid = threadIdx.x;
-    for (int e = tid; e < E; e += NT) cnt[e] = 0;
-    if (tid == 0) *nbad = 0;
-    __syncthreads();
-    for (int s = tid; s < n; s += NT) {
-        const int e = ids(s);
-        if (e >= 0 && e < E)
-            atomicAdd(&cnt[e], 1);
-        else
-            atomicAdd(nbad, 1);
-    }
-    __syncthreads();
-    if (tid < kWave) scan_experts(cnt, E, m_split, *nbad, base, meta, counts, offsets, active, large);
-    __syncthreads();
-}
-
-// Stable scatter of slots [s0, s1) by one wave, 64 at a time (the next
-// chunk's ids are requested before this one is placed): a slot's place is
-// run[e] (its expert's offset plus the slots of that expert placed before
-// this chunk) plus the lanes below it in this chunk with the same expert.
-// Lanes with equal ids are found bit by bit with ballots; the last lane of
-// each group advances run[e] (LDS operations of one wave complete in order).
-template <class Ids>
-__device__ __forceinline__ void scatter_range(Ids ids, int s0, int s1, int E, int* run,
-                                              int32_t* __restrict__ sorted_slot) {
-    const int lane = threadIdx.x & (kWave - 1);
-    int e_next = s0 + lane < s1 ? ids(s0 + lane) : -1;
-    for (int c0 = s0; c0 < s1; c0 += kWave) {
-        const int s = c0 + lane;
-        const int e = e_next;
-        const int sn = s + kWave;
-        e_next = sn < s1 ? ids(sn) : -1;
-        const bool ok = s < s1 && e >= 0 && e < E;
-        const int key = ok ? e : kMaxExperts;   // every dropped slot in one group
-        unsigned long long eq = ~0ull;
-#pragma unroll
-        for (int b = 0; b < 11; ++b) {          // ids < 2048
-            const bool bit = (key >> b) & 1;
-            const unsigned long long m = __ballot(bit);
-            eq &= bit ? m : ~m;
-        }
-        const int below = __builtin_amdgcn_mbcnt_hi(
-            (unsigned)(eq >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)eq, 0u));
-        const int group = __popcll(eq);
-        int pos = 0;
-        if (ok) pos = run[e] + below;
-        if (ok) sorted_slot[pos] = s;
-        if (ok && below == group - 1) run[e] = pos + 1;
-    }
-}
-
 // Batches up to this many slots: ids staged in LDS, counted by the 256
 // threads of permute_kernel, placed by one wave.  Larger batches
 // (permute_large_kernel, 16 waves): every wave counts, then places, a
@@ -360,15 +250,6 @@ constexpr int kOneWaveSlots = 512;
 constexpr int kPermThreads = 256;
 constexpr int kPermLargeThreads = 1024;
 constexpr int kPermWaves = kPermLargeThreads / kWave;
-
-struct GlobalIds {
-    const int32_t* p;
-    __device__ int operator()(int s) const { return p[s]; }
-};
-struct LdsIds {
-    const int* p;
-    __device__ int operator()(int s) const { return p[s]; }
-};
 
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     const int32_t* __restrict__ ids, int n, int E, int m_split, int32_t* __restrict__ meta,

@@ -60,7 +60,12 @@ def test_route_empty_batch():
                                        # one expert for every slot, two experts, all
                                        # slots dropped, several chunks of 256 slots
                                        (512, 1, 1, 0), (256, 2, 2, 0), (128, 64, 4, 7),
-                                       (171, 64, 3, 2), (4, 8, 2, 8)])
+                                       (171, 64, 3, 2), (4, 8, 2, 8),
+                                       # the gate/up product builds the index itself up
+                                       # to 256 slots over 256 experts: both limits
+                                       # exactly, and one past each
+                                       (32, 256, 8, 0), (32, 256, 8, 4), (257, 8, 1, 0),
+                                       (8, 257, 4, 1)])
 def test_gather_index_matches_oracle(T, E, k, bad):
     need_gpu()
     rng = np.random.default_rng(T + 7 * E + bad)
@@ -143,8 +148,9 @@ def test_forward_logits_matches_oracle(T, H, I, E, k, kind):
 
 @pytest.mark.parametrize("name", ["tiny", "deepseekv3_zipf_t16", "qwen3_235b_t4"])
 def test_forward_logits_equals_two_step_layer(name):
-    """The logits entry point gives bit-identical output to moe_route_topk
-    followed by moe_ffn_forward (same kernels after the gather index)."""
+    """The logits entry point (router and gather index in one kernel) gives
+    bit-identical output to moe_route_topk followed by moe_ffn_forward, whose
+    gate/up product builds the gather index itself at these batch sizes."""
     need_gpu()
     wl = workloads.WORKLOADS[name]
     if wl.H > 1024:    # the real expert shapes, shrunk: routing is what differs here
