@@ -28,7 +28,9 @@
 // like the small-m product's rounds (a contiguous slice per XCD, interleaved
 // over its workgroups): the token tiles that share a weight tile run at the
 // same time on one XCD, so the weight tile comes from HBM once and from L2
-// after that.  Gate/up has one K part; down has 1, 2 or 4 (more when a batch
+// after that; an expert's tokens are split evenly over its token tiles (in
+// 16-token blocks), so that those tiles take equally long and stay in step.
+// Gate/up has one K part; down has 1, 2 or 4 (more when a batch
 // has few long tiles), each writing its own plane of FP32 partial sums of y.
 #include <cmath>
 
@@ -138,7 +140,7 @@ void expert_tile_kernel(const TiledGemm g) {
     const int n_large = g.meta[2];
     if (n_large <= 0) return;
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int rt_n = (g.N + kRows - 1) / kRows;       // row tiles per expert
 
     // tiles before large expert a: pre[a] (wave 0, one run of experts per lane)
@@ -202,7 +204,24 @@ void expert_tile_kernel(const TiledGemm g) {
         const int r2 = r - rt * g.k_parts * mt_n;
         const int kp = r2 / mt_n;
         const int row0 = rt * kRows;
-        const int p0 = (r2 - kp * mt_n) * M;
+        // the expert's 16-token blocks are split evenly over its mt_n token
+        // tiles (at most M / 16 each, at least one), so the token tiles of
+        // one weight tile do the same work and stay in step on the XCD: the
+        // weight tile is read from HBM once and from L2 by the others.  (With
+        // M tokens per tile but the last, a short last tile finished early
+        // and then read its weight tiles alone.)
+        const int nbe = (m + 15) >> 4;
+        const int mt = r2 - kp * mt_n;                // token tile
+        const int p0 = 16 * ((mt * nbe) / mt_n);
+        const int pend = min(m, 16 * (((mt + 1) * nbe) / mt_n));   // tokens [p0, pend)
+        // the tile's 16-token blocks, TB per wave in wave order: wave wm
+        // takes blocks [bs, bs + nbw).  (Dealing them evenly to the waves
+        // was 2-7 % slower on tiles of 100-160 tokens: every wave with a
+        // block reads the weight fragments of each stage from LDS, and the
+        // LDS reads set the pace.)
+        const int nblk = (pend - p0 + 15) >> 4;
+        const int bs = TB * wm;
+        const int nbw = min(TB, max(0, nblk - bs));
         // this part's stages, and the K left from its first (the last stage
         // of the last part may be a half stage)
         const int s0 = kp * g.part_stages;
@@ -224,7 +243,7 @@ void expert_tile_kernel(const TiledGemm g) {
                 src[i] = (kDown || mm == 0 ? g.w0 : g.w1) + wrow * g.K + s0 * KS + cl * 8;
             } else {
                 const int rr = RPI * (q - NMAT * WCH) + lane / RW;
-                const int pp = beg + min(p0 + rr, m - 1);
+                const int pp = beg + min(p0 + rr, pend - 1);
                 const int brow = kDown ? pp : g.sorted_slot[pp] / g.top_k;
                 src[i] = g.b_src + (size_t)brow * g.b_pitch + s0 * KS + cl * 8;
             }
@@ -235,7 +254,7 @@ void expert_tile_kernel(const TiledGemm g) {
 #pragma unroll
         for (int i = 0; i < IL; ++i) {
             const int q = wave + W * i;
-            live[i] = q < NMAT * WCH || p0 + RPI * (q - NMAT * WCH) + lane / RW < m;
+            live[i] = q < NMAT * WCH || p0 + RPI * (q - NMAT * WCH) + lane / RW < pend;
         }
         u32x4 rg[IL];
         auto load_regs = [&](int s) {
@@ -273,12 +292,11 @@ void expert_tile_kernel(const TiledGemm g) {
                 if (s + 2 < nk) load_regs(s + 2);
             }
             const u32x4* buf = lds + (s % S) * kStageWords;
-#pragma unroll
             for (int j = 0; j < KS / 32; ++j) {
                 if (j > 0 && s * KS + 32 * j >= kl) break;       // half stage
-                // a wave whose token columns all lie past the expert's last
-                // token (the ragged last tile) has nothing to multiply
-                if (p0 + TPW * wm >= m) break;
+                // a wave with no token block of this tile has nothing to
+                // multiply
+                if (nbw == 0) break;
                 u32x4 af[NMAT][RB];
 #pragma unroll
                 for (int mm = 0; mm < NMAT; ++mm)
@@ -288,10 +306,11 @@ void expert_tile_kernel(const TiledGemm g) {
                                          tile_word<RW>(RPW * wr + 16 * rb + col, 4 * j + kg)];
 #pragma unroll
                 for (int tb = 0; tb < TB; ++tb) {
-                    // and no 16-token block past the expert's last token
-                    if (p0 + TPW * wm + 16 * tb >= m) break;
+                    // only the wave's own token blocks (a uniform test: nbw
+                    // is fixed per tile and wave)
+                    if (tb >= nbw) break;
                     const u32x4 bf = buf[NMAT * kOperandWords +
-                                         tile_word<RW>(TPW * wm + 16 * tb + col, 4 * j + kg)];
+                                         tile_word<RW>(16 * (bs + tb) + col, 4 * j + kg)];
 #pragma unroll
                     for (int mm = 0; mm < NMAT; ++mm)
 #pragma unroll
@@ -308,8 +327,8 @@ void expert_tile_kernel(const TiledGemm g) {
         // epilogue: lane holds rows n .. n+3 of token column p for each block
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
-            const int p = p0 + TPW * wm + 16 * tb + col;
-            if (p >= m) continue;
+            const int p = p0 + 16 * (bs + tb) + col;
+            if (tb >= nbw || p >= pend) continue;
             if constexpr (kDown) {
                 float* yrow = g.y + kp * g.y_plane + (size_t)g.sorted_slot[beg + p] * g.N;
 #pragma unroll
