@@ -445,7 +445,11 @@ using DualDown = MixedWeights<Int4Weights, Int8Weights, true>;
 // scale table in LDS, which the workgroups per CU must fit), and the batch
 // of the wide chunks (kWideBatch units, 0 = none: chunks of up to 32 tokens
 // use two B tiles per weight batch; BF16 only).
-template <class Fmt, int NMAT>
+// The three grouped products: down (one matrix), gate/up (W_gate and W_up
+// per K step), and down as two half-height matrices (the two halves of
+// W_down's rows share each token fragment).
+enum GemmProj : int { kDown = 1, kGateUp = 2, kDownPair = 3 };
+template <class Fmt, int PROJ>
 struct GemmTuning;
 template <>
 struct GemmTuning<Bf16Weights, 2> {   // gate/up: two matrices per K step
@@ -497,10 +501,10 @@ struct GemmTuning<DualDown, 1> {
     static constexpr int kWideBatch = 0;
 };
 template <>
-struct GemmTuning<Int4Weights, 1> {
+struct GemmTuning<Int4Weights, kDownPair> {
     static constexpr int kBlocksPerCU = 2;
-    static constexpr int kBatch = 4;
-    static constexpr int kMaxDepth = 16;
+    static constexpr int kBatch = 2;
+    static constexpr int kMaxDepth = 8;
     static constexpr int kWideBatch = 0;
 };
 
@@ -512,11 +516,17 @@ struct GemmTuning<Int4Weights, 1> {
 // all active experts (expert-major) are dealt out per XCD: each XCD owns a
 // contiguous slice, and its workgroups take the slice's rounds interleaved
 // (an equal number each, +-1).
-template <class Fmt, int NMAT, int S, int U, int FMAX, int UW>
+// PAIR (down, NMAT = 2): the two "matrices" are the two halves of W_down's
+// rows (g.N = H / 2 rows each, the second half at g.w1 / g.s1), so that one
+// token fragment feeds both, as W_gate and W_up share it in gate/up.
+template <class Fmt, int NMAT, int S, int U, int FMAX, int UW, bool PAIR>
 __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView ix, int n_act,
                                             int grid,
                                             u32x4 (*xs)[kSlabU4], f32x4* sc) {
     constexpr int R = kWaves / S;              // row blocks per round
+    constexpr bool kIsGateUp = NMAT == 2 && !PAIR;
+    static_assert(!PAIR || NMAT == 2, "a pair is two matrices");
+    const int erows = PAIR ? 2 * g.N : g.N;    // weight rows per expert, output row pitch
     constexpr int SP = kSlabBlocks / S;        // LDS blocks of each K part per slab (depth 1)
     constexpr int SPU = SP / Fmt::kBlocks;     // units of each K part per slab (depth 1)
     constexpr int NB = SPU / U;                // full batches per slab (depth 1)
@@ -570,7 +580,7 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
         const int my = rb0 + r;
         const bool has = my < nrb;
         const int row0 = (has ? my : 0) * 16;
-        const size_t arow = (size_t)e * g.N + row0 + col;   // this lane's weight row
+        const size_t arow = (size_t)e * erows + row0 + col;   // this lane's weight row
         const int nfull = has ? (u1 - u0) / U : 0;   // full batches of this wave
         const int tail_u = u0 + nfull * U;           // tail units [tail_u, u1)
         // the round in format F (tag: RoundFmt<F, read the second set>)
@@ -593,7 +603,7 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
             // set), then a residual format's second set
             const float* stab[4] = {nullptr, nullptr, nullptr, nullptr};
             if constexpr (NSCF > 0) {
-                const size_t eoff = (size_t)e * g.N * nunits;
+                const size_t eoff = (size_t)e * erows * nunits;
                 const float* p0 = kSecond ? g.hs0 : g.s0;
                 const float* p1 = kSecond ? g.hs1 : g.s1;
                 stab[0] = p0 + eoff;
@@ -658,7 +668,7 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                 for (int i = 0; i < NL; ++i) {
                     const int c = (wave + kWaves * i) >> dl;
                     const int qq = beg + c0 + (c < ntok ? c : 0);
-                    const int brow = NMAT == 2 ? ix.sorted_slot[qq] / g.top_k : qq;
+                    const int brow = kIsGateUp ? ix.sorted_slot[qq] / g.top_k : qq;
                     tp[i] = (uint32_t)brow * (uint32_t)g.b_pitch;
                 }
                 f32x4 acc[NC][NMAT];
@@ -813,7 +823,7 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                 for (int hh = 0; hh < NC; ++hh) {
                     if (kp == 0 && has && valid[hh]) {
                         const size_t p = (size_t)beg + c0 + 16 * hh + col;
-                        if constexpr (NMAT == 2) {
+                        if constexpr (kIsGateUp) {
                             const f32x4 gv = acc[hh][0], uv = acc[hh][1];
                             u32x2 packed;
                             packed.x = (uint32_t)f32_to_bf16_bits(silu(gv.x) * uv.x) |
@@ -823,8 +833,10 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                             *reinterpret_cast<u32x2*>(g.h + p * g.N + row0 + kg * 4) = packed;
                         } else {
                             const int slot = ix.sorted_slot[p];
-                            *reinterpret_cast<f32x4*>(g.y + (size_t)slot * g.N + row0 + kg * 4) =
-                                acc[hh][0];
+    #pragma unroll
+                            for (int mm = 0; mm < NMAT; ++mm)
+                                *reinterpret_cast<f32x4*>(g.y + (size_t)slot * erows + mm * g.N +
+                                                          row0 + kg * 4) = acc[hh][mm];
                         }
                     }
                 }
@@ -873,7 +885,7 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                 for (int i = 0; i < 4; ++i) {
                     const int c = (wave + kWaves * i) >> dl;
                     const int qq = beg + c0 + (c < ntok ? c : 0);
-                    const int brow = NMAT == 2 ? ix.sorted_slot[qq] / g.top_k : qq;
+                    const int brow = kIsGateUp ? ix.sorted_slot[qq] / g.top_k : qq;
                     tp[i] = g.b_src + (size_t)brow * g.b_pitch;
                 }
                 f32x4 acc[NMAT];
@@ -1005,7 +1017,7 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                 }
                 if (kp == 0 && has && valid) {
                     const size_t p = (size_t)beg + c0 + col;
-                    if constexpr (NMAT == 2) {
+                    if constexpr (kIsGateUp) {
                         const f32x4 gv = acc[0], uv = acc[1];
                         u32x2 packed;
                         packed.x = (uint32_t)f32_to_bf16_bits(silu(gv.x) * uv.x) |
@@ -1015,7 +1027,10 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                         *reinterpret_cast<u32x2*>(g.h + p * g.N + row0 + kg * 4) = packed;
                     } else {
                         const int slot = ix.sorted_slot[p];
-                        *reinterpret_cast<f32x4*>(g.y + (size_t)slot * g.N + row0 + kg * 4) = acc[0];
+    #pragma unroll
+                        for (int mm = 0; mm < NMAT; ++mm)
+                            *reinterpret_cast<f32x4*>(g.y + (size_t)slot * erows + mm * g.N +
+                                                      row0 + kg * 4) = acc[mm];
                     }
                 }
                 if constexpr (S > 1) __syncthreads();
@@ -1099,13 +1114,17 @@ __device__ __forceinline__ int choose_split(const ExpertGemm& g, int n_act) {
 // gather index from the routing ids into LDS and reads it from there;
 // workgroup 0 also publishes it for the down product.  One launch fewer per
 // layer, and the rounds' expert and token lookups become LDS reads.
-template <class Fmt, int NMAT, bool WIDE, bool FUSED>
+// PROJ: kDown, kGateUp or kDownPair (down as two half-height matrices).
+template <class Fmt, int PROJ, bool WIDE, bool FUSED>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(GemmTuning<Fmt, NMAT>::kBlocksPerCU)))
+__attribute__((amdgpu_waves_per_eu(GemmTuning<Fmt, PROJ>::kBlocksPerCU)))
 void expert_gemm_kernel(const ExpertGemm g) {
-    constexpr int U = GemmTuning<Fmt, NMAT>::kBatch;
-    constexpr int FMAX = GemmTuning<Fmt, NMAT>::kMaxDepth;
-    constexpr int UW = WIDE ? GemmTuning<Fmt, NMAT>::kWideBatch : 0;
+    constexpr int NMAT = PROJ == kDown ? 1 : 2;
+    constexpr bool PAIR = PROJ == kDownPair;
+    using Tune = GemmTuning<Fmt, PROJ>;
+    constexpr int U = Tune::kBatch;
+    constexpr int FMAX = Tune::kMaxDepth;
+    constexpr int UW = WIDE ? Tune::kWideBatch : 0;
     constexpr int units1 = kSlabBlocks / Fmt::kBlocks;   // units of a part per slab, S = 1
     // K-slab buffers of the token tile, double-buffered, followed (scaled
     // formats) by the slabs' scale tables.  Both are filled by direct
@@ -1114,9 +1133,9 @@ void expert_gemm_kernel(const ExpertGemm g) {
     // slab), whereas with two arrays it waited for every outstanding load
     // before each LDS read, which serialised the weight prefetch.
     constexpr int kScF4 =
-        ScaleTensors<Fmt, NMAT>::value * kScaleSlabFloats * GemmTuning<Fmt, NMAT>::kMaxDepth / 4 * 2;
+        ScaleTensors<Fmt, NMAT>::value * kScaleSlabFloats * Tune::kMaxDepth / 4 * 2;
     // (FUSED: the LDS copy of the gather index at the end, in the same array)
-    static_assert(!FUSED || NMAT == 2, "the index is built by the gate/up product");
+    static_assert(!FUSED || PROJ == kGateUp, "the index is built by the gate/up product");
     static_assert(kFxScratchInts * 4 <= (int)sizeof(u32x4) * kSlabU4, "index scratch fits a slab");
     constexpr int kIxF4 = FUSED ? kFxInts / 4 : 0;
     __shared__ u32x4 lds[2 * kSlabU4 + kScF4 + kIxF4];
@@ -1138,14 +1157,14 @@ void expert_gemm_kernel(const ExpertGemm g) {
     const int G = busy_grid(rounds_for(n_act, g.N / 16, S));
     if ((int)blockIdx.x >= G) return;
     if (S == 1)
-        gemm_rounds<Fmt, NMAT, 1, cmin(U, units1), FMAX, cmin(UW, units1 / 2)>(g, ix, n_act, G,
-                                                                              xs, sc);
+        gemm_rounds<Fmt, NMAT, 1, cmin(U, units1), FMAX, cmin(UW, units1 / 2), PAIR>(
+            g, ix, n_act, G, xs, sc);
     else if (S == 2)
-        gemm_rounds<Fmt, NMAT, 2, cmin(U, units1 / 2), FMAX, cmin(UW, units1 / 4)>(g, ix, n_act,
-                                                                                  G, xs, sc);
+        gemm_rounds<Fmt, NMAT, 2, cmin(U, units1 / 2), FMAX, cmin(UW, units1 / 4), PAIR>(
+            g, ix, n_act, G, xs, sc);
     else
-        gemm_rounds<Fmt, NMAT, 4, cmin(U, units1 / 4), FMAX, cmin(UW, units1 / 8)>(g, ix, n_act,
-                                                                                  G, xs, sc);
+        gemm_rounds<Fmt, NMAT, 4, cmin(U, units1 / 4), FMAX, cmin(UW, units1 / 8), PAIR>(
+            g, ix, n_act, G, xs, sc);
 }
 
 // Grid of one grouped product: persistent, the resident workgroup count,
@@ -1160,31 +1179,42 @@ int gemm_grid(int64_t max_active, int N, int num_cu, int blocks_per_cu) {
     return (int)grid;
 }
 
-template <class Fmt, int NMAT, bool FUSED>
+template <class Fmt, int PROJ, bool FUSED>
 hipError_t launch_gemm_as(const ExpertGemm& g, int grid, bool wide, hipStream_t stream) {
-    if constexpr (GemmTuning<Fmt, NMAT>::kWideBatch > 0) {
+    if constexpr (GemmTuning<Fmt, PROJ>::kWideBatch > 0) {
         if (wide) {
-            hipLaunchKernelGGL((expert_gemm_kernel<Fmt, NMAT, true, FUSED>), dim3(grid),
+            hipLaunchKernelGGL((expert_gemm_kernel<Fmt, PROJ, true, FUSED>), dim3(grid),
                                dim3(kThreads), 0, stream, g);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((expert_gemm_kernel<Fmt, NMAT, false, FUSED>), dim3(grid), dim3(kThreads),
+    hipLaunchKernelGGL((expert_gemm_kernel<Fmt, PROJ, false, FUSED>), dim3(grid), dim3(kThreads),
                        0, stream, g);
     return hipGetLastError();
 }
 
 // wide: some expert may receive more than 16 slots (T * k > 16); g.ids set:
 // the gate/up launch that builds the gather index itself
-template <class Fmt, int NMAT>
+template <class Fmt, int PROJ>
 hipError_t launch_gemm(const ExpertGemm& g, int64_t max_active, int num_cu, bool wide,
                        hipStream_t stream) {
-    const int grid = gemm_grid(max_active, g.N, num_cu, GemmTuning<Fmt, NMAT>::kBlocksPerCU);
-    if constexpr (NMAT == 2) {
-        if (g.ids) return launch_gemm_as<Fmt, NMAT, true>(g, grid, wide, stream);
+    const int grid = gemm_grid(max_active, g.N, num_cu, GemmTuning<Fmt, PROJ>::kBlocksPerCU);
+    if constexpr (PROJ == kGateUp) {
+        if (g.ids) return launch_gemm_as<Fmt, PROJ, true>(g, grid, wide, stream);
     }
-    return launch_gemm_as<Fmt, NMAT, false>(g, grid, wide, stream);
+    return launch_gemm_as<Fmt, PROJ, false>(g, grid, wide, stream);
 }
+
+// INT4 down runs as two half-height matrices: its units move 1 KB of
+// weights per 16 rows, so the token fragment reads and staging are a larger
+// share than in the other formats, and a pair shares them (measured: INT4
+// down -15 % at one token per expert; INT8, BF16 and the two-copy down were
+// not faster as pairs).
+template <class Fmt>
+struct PairedDown : std::false_type {};
+template <>
+struct PairedDown<Int4Weights> : std::true_type {};
+
 
 // Fmt: the gate/up weight format; FmtDown: down's (the same but for the
 // residual split, whose down copies are not split).
@@ -1241,7 +1271,7 @@ hipError_t launch_ffn(const uint16_t* x, const Routing& route, const FfnWeights&
     }
     // an expert can receive more than 16 slots only if the batch has more
     const bool wide = (int64_t)s.T * s.k > 16;
-    err = launch_gemm<Fmt, 2>(gu, max_active, num_cu, wide, stream);
+    err = launch_gemm<Fmt, kGateUp>(gu, max_active, num_cu, wide, stream);
     if (err == hipSuccess && tiled) err = launch_tiled_gate_up(x, W, s, ws, num_cu, stream);
     if (err == hipSuccess) err = ev.mark(1, stream);
     if (err != hipSuccess) return err;
@@ -1263,7 +1293,19 @@ hipError_t launch_ffn(const uint16_t* x, const Routing& route, const FfnWeights&
     dn.K = s.I;
     dn.split = split.down;
     dn.ids = nullptr;
-    err = launch_gemm<FmtDown, 1>(dn, max_active, num_cu, wide, stream);
+    // formats whose down product runs as two half-height matrices (the
+    // halves of W_down's rows, each H / 2 rows, a whole number of 16-row
+    // blocks: the quantised entry points take H a multiple of 128)
+    if constexpr (PairedDown<FmtDown>::value) {
+        static_assert(std::is_same_v<FmtDown, Int4Weights>, "paired down: INT4 rows");
+        const size_t rows = (size_t)(s.H / 2);
+        dn.N = s.H / 2;
+        dn.w1 = static_cast<const uint8_t*>(W.down) + rows * (size_t)s.I / 2;   // two per byte
+        dn.s1 = W.s_down + rows * (s.I / 128);
+        err = launch_gemm<FmtDown, kDownPair>(dn, max_active, num_cu, wide, stream);
+    } else {
+        err = launch_gemm<FmtDown, kDown>(dn, max_active, num_cu, wide, stream);
+    }
     if (err == hipSuccess && tiled) err = launch_tiled_down(W, s, ws, num_cu, stream);
     if (err == hipSuccess) err = ev.mark(2, stream);
     if (err != hipSuccess) return err;
