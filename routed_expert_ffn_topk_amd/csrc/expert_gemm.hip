@@ -117,6 +117,9 @@ struct WeightSrc {
 struct Bf16Weights {
     static constexpr bool kResidual = false;
     static constexpr bool kScaled = false;
+    // weight batches double-buffered as pairs with fixed register roles
+    // (measured 3-10 % slower for BF16 than the parity-switched loop)
+    static constexpr bool kFixedRolePipeline = false;
     static constexpr int kBlocks = 1;
     static constexpr float kBytesPerWeight = 2.0f;
     static constexpr int kUnitBytes = kWave * 16;       // weight bytes a wave loads per unit
@@ -186,6 +189,7 @@ __device__ __forceinline__ f32x4 lds_f32x4(const float* p) {
 struct Int8Weights {
     static constexpr bool kResidual = false;
     static constexpr bool kScaled = true;
+    static constexpr bool kFixedRolePipeline = true;
     static constexpr int kBlocks = 4;
     static constexpr float kBytesPerWeight = 1.0f;
     static constexpr int kUnitBytes = kWave * 32;       // weight bytes a wave loads per unit
@@ -253,6 +257,7 @@ struct Int8Weights {
 struct Int4Weights {
     static constexpr bool kResidual = false;
     static constexpr bool kScaled = true;
+    static constexpr bool kFixedRolePipeline = true;
     static constexpr int kBlocks = 4;
     static constexpr float kBytesPerWeight = 0.5f;
     static constexpr int kUnitBytes = kWave * 16;       // weight bytes a wave loads per unit
@@ -324,6 +329,7 @@ struct Int4Weights {
 struct Int4ResidualWeights {
     static constexpr bool kResidual = true;
     static constexpr bool kScaled = true;
+    static constexpr bool kFixedRolePipeline = true;
     static constexpr int kBlocks = 4;
     static constexpr float kBytesPerWeight = 1.0f;
     static constexpr int kUnitBytes = 2 * kWave * 16;
@@ -976,18 +982,42 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                     const float* sl = reinterpret_cast<const float*>(sc) + (j & 1) * SCB +
                                       (r * S + kp) * spu * 16 + 4 * kg;
                     const int bend = min(nfull, (j + 1) * nb);
-                    for (; bi < bend; ++bi) {
-                        const int ub = u0 + bi * U - slab_u0;   // batch's first unit in the slab
-                        const u32x4* bb = buf + ub * F::kBlocks * kBlockU4;
-                        const float* sb = sl + 16 * ub;
-                        if ((bi & 1) == 0) {
-                            if (bi + 1 < nfull)
-                                F::template load<NMAT, U>(B, src, u0 + (bi + 1) * U);
-                            F::template mma<NMAT, U, TS>(A, bb, sb, acc);
-                        } else {
-                            if (bi + 1 < nfull)
-                                F::template load<NMAT, U>(A, src, u0 + (bi + 1) * U);
-                            F::template mma<NMAT, U, TS>(B, bb, sb, acc);
+                    if constexpr (F::kFixedRolePipeline) {
+                        // one batch: request the next one into nxt (after the
+                        // last batch, the last again: an unconditional request
+                        // keeps the number of loads in flight fixed, so the
+                        // compiler waits for cur only), then multiply cur.
+                        // Pairs of batches with fixed roles keep the two
+                        // register sets apart (with the parity test below
+                        // inside the loop the compiler copies between them,
+                        // and the copy waits for the batch just requested).
+                        auto step = [&](auto& cur, auto& nxt, int b) __attribute__((always_inline)) {
+                            const int ub = u0 + b * U - slab_u0;   // batch's first unit in the slab
+                            const u32x4* bb = buf + ub * F::kBlocks * kBlockU4;
+                            const float* sb = sl + 16 * ub;
+                            F::template load<NMAT, U>(nxt, src, u0 + min(b + 1, nfull - 1) * U);
+                            F::template mma<NMAT, U, TS>(cur, bb, sb, acc);
+                        };
+                        if (bi < bend && (bi & 1)) step(B, A, bi++);
+                        for (; bi + 1 < bend; bi += 2) {
+                            step(A, B, bi);
+                            step(B, A, bi + 1);
+                        }
+                        if (bi < bend) step(A, B, bi++);
+                    } else {
+                        for (; bi < bend; ++bi) {
+                            const int ub = u0 + bi * U - slab_u0;   // batch's first unit in the slab
+                            const u32x4* bb = buf + ub * F::kBlocks * kBlockU4;
+                            const float* sb = sl + 16 * ub;
+                            if ((bi & 1) == 0) {
+                                if (bi + 1 < nfull)
+                                    F::template load<NMAT, U>(B, src, u0 + (bi + 1) * U);
+                                F::template mma<NMAT, U, TS>(A, bb, sb, acc);
+                            } else {
+                                if (bi + 1 < nfull)
+                                    F::template load<NMAT, U>(A, src, u0 + (bi + 1) * U);
+                                F::template mma<NMAT, U, TS>(B, bb, sb, acc);
+                            }
                         }
                     }
                     if (has && tail_u < u1 && tail_u >= slab_u0 && tail_u < slab_u0 + spu)
