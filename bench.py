@@ -609,9 +609,12 @@ def main():
     gap = launch_gap_us(stream)
 
     # per-kernel durations from HIP events recorded on the launch stream
-    # between the kernels of each call (stage 0 permute, 1 gate/up, 2 down,
-    # 3 combine)
-    names = ("permute", "gateup", "down", "combine")
+    # between the kernels of each call (stage 0 the gather-index kernel, 1
+    # gate/up, 2 down, 3 combine).  Batches of up to 256 slots from given ids
+    # have no index kernel (gate/up builds the index in its prologue): their
+    # stage 0 is two events back to back, which measures the events' own
+    # overhead, and is reported as "index" all the same.
+    names = ("index", "gateup", "down", "combine")
     dur = {n: [] for n in names}
     dur_l = {b["wl"].name: {n: [] for n in names} for b in batches}
     gu_bytes = []
