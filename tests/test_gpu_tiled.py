@@ -65,7 +65,7 @@ def run_and_check(case, what):
     (65, 128, 256, 2, 1),      # smallest tiled batch: two experts of ~32 tokens
     (130, 256, 384, 4, 2),     # ~65 tokens/expert: one full, one partial token tile
     (300, 256, 320, 8, 2),     # I = 320: the last gate/up row tile is half full
-    (517, 288, 256, 3, 2),     # ~345 tokens/expert: three token tiles, ragged; K = 288
+    (517, 288, 256, 3, 2),     # ~345 tokens/expert: two token tiles, ragged; K = 288
     (129, 32, 32, 1, 1),       # K = 32 (one stage), N = 32 (a quarter row tile)
     (400, 64, 1024, 2, 2),     # long down K, short gate/up K
     (1000, 96, 160, 2, 1),     # 500 tokens/expert: the register-staged gate/up; N = 160
@@ -100,6 +100,21 @@ def test_tiled_duplicate_and_dropped_ids():
     case = random_case(6, T, H, I, E, k, std=0.08, ids=ids)
     r = run_and_check(case, "tiled dup/drop")
     assert r["n_dropped"] == 20 and r["n_large"] >= 1
+
+
+def test_tiled_even_token_tiles():
+    """Experts of 257, 513 and 530 tokens: their 16-token blocks are split
+    evenly over 2, 3 and 3 token tiles (8 + 9, 11 + 11 + 11 and 11 + 11 + 12
+    blocks), the last tile ending inside a block; next to a small-m expert
+    and an idle one."""
+    need_gpu()
+    counts = [257, 0, 513, 20, 530]
+    ids = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(counts)])
+    ids = np.random.default_rng(4).permutation(ids).reshape(-1, 1)
+    T, H, I, E, k = ids.shape[0], 64, 96, len(counts), 1
+    case = random_case(21, T, H, I, E, k, std=0.08, ids=ids)
+    r = run_and_check(case, "tiled even token tiles 257/513/530")
+    assert r["n_large"] == 3 and r["n_active"] == 1
 
 
 def test_tiled_one_expert_many_tokens():
