@@ -1101,13 +1101,14 @@ __device__ __forceinline__ int busy_grid(int Q) {
 // bytes in flight, two weight batches, over the load latency) and its share
 // of an effective HBM rate among the 4 * G_S busy waves; each LDS slab adds a
 // fixed cost (barrier, staging wait).  Constants fitted to forced-split
-// measurements on MI355X over the Mixtral-8x7B/8x22B, DeepSeek-V3 and
-// Qwen3-235B expert shapes at 2..103 active experts and 1..16 tokens per
-// expert (the choice costs 0.8 % on average against the fastest split, at
-// most 4.4 %).
+// measurements on MI355X of the current kernels over the Mixtral-8x7B/8x22B,
+// DeepSeek-V3 and Qwen3-235B expert shapes (BF16, INT8, INT4, residual
+// split) at 2..103 active experts and 1..16 tokens per expert: the choice
+// costs 0.11 % on average against the fastest split, at most 1.7 % (the
+// earlier constants, 4 us and 1 us, cost 0.31 % and up to 4.2 %).
 constexpr float kHbmBytesPerUs = 8.0e6f;   // effective HBM rate shared by busy waves
-constexpr float kLoadLatencyUs = 4.0f;     // loaded-memory latency of a batch
-constexpr float kSlabUs = 1.0f;            // fixed cost per slab
+constexpr float kLoadLatencyUs = 5.0f;     // loaded-memory latency of a batch
+constexpr float kSlabUs = 4.0f;            // fixed cost per slab
 template <class Fmt, int NMAT, int U>
 __device__ __forceinline__ int choose_split(const ExpertGemm& g, int n_act) {
     constexpr int units1 = kSlabBlocks / Fmt::kBlocks;
