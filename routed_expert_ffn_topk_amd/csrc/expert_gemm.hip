@@ -542,11 +542,11 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
     constexpr bool kWide = UW > 0 && Fmt::kBlocks == 1 && SPU % (2 * (UW > 0 ? UW : 1)) == 0;
     constexpr int LOG_SP = SP == 16 ? 4 : SP == 8 ? 3 : 2;
     static_assert((1 << LOG_SP) == SP, "power-of-two slab parts");
-    // scale table of a slab (scaled formats): per tensor, [R][S][SPU*F][16
-    // rows] floats in a region of TS floats (sized for depth FMAX); two
-    // buffers (slabs alternate), SCB floats apart
+    // scale table of a group of slabs (scaled formats): per tensor,
+    // [R][S][units][16 rows] floats in a region of TS floats (the units of
+    // one slab at depth FMAX); two buffers (groups alternate), SCB floats apart
     constexpr int NSC = ScaleTensors<Fmt, NMAT>::value;
-    constexpr int TS = R * S * SPU * 16 * FMAX;
+    constexpr int TS = R * S * SPU * FMAX * 16;
     constexpr int SCB = NSC * TS;
     static_assert(NSC == 0 || TS <= kScaleSlabFloats * FMAX, "scale table fits its buffer");
     // after the slab loop the first slab buffer doubles as the K-part
@@ -870,6 +870,20 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                 const int dep = 1 << dl;
                 const int spu = SPU << dl;               // units of each K part per slab
                 const int nb = NB << dl;                 // full batches per full slab
+                // Scaled formats stage the scales of P slabs at a time into
+                // the table sized for the deepest slab: a row's scales for
+                // those slabs are contiguous, so each of its scale lines is
+                // fetched once or twice per round instead of by every slab
+                // (a round's slabs are microseconds apart and L2 drops the
+                // line in between: +18 % reads for INT8 gate/up at 16 tokens
+                // per expert, +23 % INT4).  Gate/up takes P = FMAX / 2^d;
+                // down at most two (its long K makes a full group a burst of
+                // up to 16 loads per wave, measured 6 % slower for INT4 at 8
+                // tokens per expert).
+                constexpr int kLogF = FMAX == 16 ? 4 : FMAX == 8 ? 3 : FMAX == 4 ? 2 : FMAX == 2 ? 1 : 0;
+                const int logP = kIsGateUp ? kLogF - dl : min(1, kLogF - dl);
+                const int P = 1 << logP;
+                const int GU = P * spu;                  // units of each K part per scale group
                 const int tpitch = kTokRowU4 * dep + 2;  // LDS words between token rows
                 const int nslab = (kpu + spu - 1) / spu;
                 // padding columns (beyond the expert's tokens) read token 0's row:
@@ -903,10 +917,11 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                 // One load instruction stages 16 blocks (1 KB) of one token's
                 // slab row: lane L fills block 16i + L/4 for K group L%4, so the
                 // row is read from global memory in contiguous runs.
-                // Scaled formats also stage the slab's scales: entry
-                // ((rr*S + pp)*spu + jj)*16 + row of tensor t is the scale of
-                // row 16*(rb0 + rr) + row, unit start(pp) + j*spu + jj; one
-                // 4-byte direct load per lane fills 64 consecutive entries.
+                // Scaled formats also stage the scales of a group of slabs:
+                // entry ((rr*S + pp)*GU + jj)*16 + row of tensor t in group
+                // G is the scale of row 16*(rb0 + rr) + row, unit start(pp) +
+                // G*GU + jj; one 4-byte direct load per lane fills 64
+                // consecutive entries.
                 auto stage = [&](int j, int bsel) {
                     const int kgl = lane & 3;
     #pragma unroll
@@ -928,29 +943,35 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                                 0, 0);
                     }
                     if constexpr (NSCF > 0) {
-                        // load k (64 entries of every tensor's table) by wave
-                        // k % 4: one offset per lane serves all tensors (they
-                        // share the [N][nunits] shape)
-                        const int nld = (R * S * 16 * spu) / kWave;
-                        float* sbuf = reinterpret_cast<float*>(sc) + bsel * SCB;
-                        for (int k = wave; k < nld; k += kWaves) {
-                            const int f = k * kWave + lane;
-                            const int row = f & 15;
-                            const int qf = f >> 4;
-                            const int jj = qf % spu;
-                            const int rp = qf / spu;
-                            const int spp = rp % S;
-                            const int rb = rb0 + rp / S;
-                            const int q0 = min(nunits, spp * kpu);
-                            const int q1 = min(nunits, q0 + kpu);
-                            const int su = q0 + j * spu + jj;
-                            const size_t soff = (size_t)(rb * 16 + row) * nunits + su;
-                            if (rb < nrb && su < q1) {
+                        // scale group G (slabs [G*P, (G+1)*P)) goes with the
+                        // staging of slab (G-1)*P + 1 (group 0 with slab 0)
+                        // into scale buffer G & 1, which group G - 1 is then
+                        // done with.  Load k (64 entries of every tensor's
+                        // table) by wave k % 4: one offset per lane serves all
+                        // tensors (they share the [N][nunits] shape).
+                        if (j == 0 || ((j - 1) & (P - 1)) == 0) {
+                            const int G = j == 0 ? 0 : ((j - 1) >> logP) + 1;
+                            const int nld = (R * S * 16 * GU) / kWave;
+                            float* sbuf = reinterpret_cast<float*>(sc) + (G & 1) * SCB;
+                            for (int k = wave; k < nld; k += kWaves) {
+                                const int f = k * kWave + lane;
+                                const int row = f & 15;
+                                const int qf = f >> 4;
+                                const int jj = qf % GU;
+                                const int rp = qf / GU;
+                                const int spp = rp % S;
+                                const int rb = rb0 + rp / S;
+                                const int q0 = min(nunits, spp * kpu);
+                                const int q1 = min(nunits, q0 + kpu);
+                                const int su = q0 + G * GU + jj;
+                                const size_t soff = (size_t)(rb * 16 + row) * nunits + su;
+                                if (rb < nrb && su < q1) {
     #pragma unroll
-                                for (int t = 0; t < NSCF; ++t)
-                                    __builtin_amdgcn_global_load_lds(
-                                        (const void*)(stab[t] + soff),
-                                        (lds_void_ptr)(sbuf + t * TS + k * kWave), 4, 0, 0);
+                                    for (int t = 0; t < NSCF; ++t)
+                                        __builtin_amdgcn_global_load_lds(
+                                            (const void*)(stab[t] + soff),
+                                            (lds_void_ptr)(sbuf + t * TS + k * kWave), 4, 0, 0);
+                                }
                             }
                         }
                     }
@@ -978,9 +999,9 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                     const u32x4* buf =
                         &xs[j & 1][bcol * tpitch + ((kp * SP * kBlockU4) << dl) + kg];
                     // this lane's scales: row block r, K part kp, unit 0 of the
-                    // slab, output rows 4kg .. 4kg + 3
-                    const float* sl = reinterpret_cast<const float*>(sc) + (j & 1) * SCB +
-                                      (r * S + kp) * spu * 16 + 4 * kg;
+                    // slab (slab j & (P - 1) of its group), output rows 4kg .. 4kg + 3
+                    const float* sl = reinterpret_cast<const float*>(sc) + ((j >> logP) & 1) * SCB +
+                                      ((r * S + kp) * GU + (j & (P - 1)) * spu) * 16 + 4 * kg;
                     const int bend = min(nfull, (j + 1) * nb);
                     if constexpr (F::kFixedRolePipeline) {
                         // one batch: request the next one into nxt (after the
