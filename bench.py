@@ -69,7 +69,7 @@ def suite_layers(name: str):
         return [workloads.WORKLOADS[f"mixtral8x7b_int4_m{m}"] for m in MS]
     if name == "mixtral8x7b_resplit_forced_m1-16":
         return [workloads.WORKLOADS[f"mixtral8x7b_resplit_m{m}"] for m in MS]
-    if name in workloads.WORKLOADS and name != "tiny":
+    if name in workloads.WORKLOADS:
         return [workloads.WORKLOADS[name]]
     raise SystemExit(f"bench.py: unknown workload {name!r}")
 
