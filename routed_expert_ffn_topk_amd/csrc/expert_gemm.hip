@@ -876,12 +876,12 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                 // fetched once or twice per round instead of by every slab
                 // (a round's slabs are microseconds apart and L2 drops the
                 // line in between: +18 % reads for INT8 gate/up at 16 tokens
-                // per expert, +23 % INT4).  Gate/up takes P = FMAX / 2^d;
-                // down at most two (its long K makes a full group a burst of
-                // up to 16 loads per wave, measured 6 % slower for INT4 at 8
-                // tokens per expert).
+                // per expert, +23 % INT4).  P = FMAX / 2^d, but at most two
+                // for INT4 down as a pair (its two matrices' tables make a
+                // full group a burst of up to 16 loads per wave, measured 6 %
+                // slower at 8 tokens per expert).
                 constexpr int kLogF = FMAX == 16 ? 4 : FMAX == 8 ? 3 : FMAX == 4 ? 2 : FMAX == 2 ? 1 : 0;
-                const int logP = kIsGateUp ? kLogF - dl : min(1, kLogF - dl);
+                const int logP = PAIR ? min(1, kLogF - dl) : kLogF - dl;
                 const int P = 1 << logP;
                 const int GU = P * spu;                  // units of each K part per scale group
                 const int tpitch = kTokRowU4 * dep + 2;  // LDS words between token rows
