@@ -108,7 +108,7 @@ struct IndexView {
 
 // Per-lane weight pointers of one round: this lane's weight row at its K
 // group; r: the second set (residuals).  Scales are not read per lane: the
-// workgroup stages each slab's scales in LDS (see gemm_rounds).
+// workgroup stages the scales of groups of slabs in LDS (see gemm_rounds).
 struct WeightSrc {
     const void* w[2];
     const void* r[2];
@@ -181,7 +181,7 @@ __device__ __forceinline__ bf16x8 i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
 // use).  The group's FP32 partial tile is scaled by the per-row scale of each
 // of the lane's four output rows (4kg + j) and added to the accumulator:
 //   dot(row, v) = sum_g s[row][g] * (sum_{c in g} v_c * q[row][c]).
-// The scales come from the slab's scale table in LDS.
+// The scales come from the scale table of the slab's group in LDS.
 __device__ __forceinline__ f32x4 lds_f32x4(const float* p) {
     return *reinterpret_cast<const f32x4*>(p);
 }
@@ -405,7 +405,7 @@ struct MixedWeights {
     static constexpr int kUnitBytes = Hi::kUnitBytes;
 };
 
-// Scale tensors a round of format F reads (each staged per slab in LDS):
+// Scale tensors a round of format F reads (each staged in LDS per group of slabs):
 // one per matrix, two per matrix for a residual format, none for BF16.
 template <class F, int NMAT>
 struct ScaleTensors {
