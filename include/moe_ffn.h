@@ -374,6 +374,20 @@ int moe_ffn_forward_resplit(const void* x, const int32_t* topk_ids,
                             int64_t I, int32_t E, int32_t top_k, void* workspace,
                             size_t workspace_bytes, void* stream);
 
+/* Device bounds checks (debug build).  libmoe_ffn_debug.so is the same
+ * library compiled with -DMOE_FFN_DEVICE_CHECKS: before its kernels' global
+ * accesses (weight rows, gathered token rows, h and y rows) an index outside
+ * its buffer is recorded and the access skipped or redirected to row 0, so a
+ * bad index shows up here instead of as a memory fault.  This call waits for
+ * the device, then writes to *where the first failed check since the last
+ * call, as (source file number) * 100000 + source line (files: 1
+ * route_permute, 2 expert_gemm, 3 expert_tile, 4 combine, 5 attn_decode), or
+ * 0 if none, and clears the record.  Returns 1 for the debug build, 0 for
+ * the release build (whose kernels carry no checks: *where is always 0), or
+ * MOE_FFN_ERR_NULL_ARG / MOE_FFN_ERR_HIP.  A debugging aid for the callers
+ * and tests of this library, not one of the pages' operations. */
+int moe_ffn_device_check(int32_t* where);
+
 /* Wait for `stream`, then read the workspace meta written by the last forward
  * call: MOE_FFN_ERR_BAD_IDS if it dropped slots with out-of-range ids,
  * MOE_FFN_OK otherwise (MOE_FFN_ERR_HIP if the wait or the read fails).  If

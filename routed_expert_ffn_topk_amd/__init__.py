@@ -15,7 +15,10 @@ from typing import Optional, Tuple
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe_ffn.so")
+# MOE_FFN_DEBUG=1 loads the debug build, whose kernels check their indices
+# (moe_ffn_device_check)
+LIB_PATH = os.path.join(_HERE, "libmoe_ffn_debug.so" if os.environ.get("MOE_FFN_DEBUG", "0") not in
+                        ("", "0") else "libmoe_ffn.so")
 
 MOE_FFN_OK = 0
 MOE_FFN_ERR_NULL_ARG = -1
@@ -90,6 +93,8 @@ def lib() -> ctypes.CDLL:
                                            _vp, _i64, _i64, _i64, _i32, _i32, _vp, _sz, _vp]
         L.moe_ffn_check_status.restype = _c.c_int
         L.moe_ffn_check_status.argtypes = [_vp, _vp, _c.POINTER(_i64)]
+        L.moe_ffn_device_check.restype = _c.c_int
+        L.moe_ffn_device_check.argtypes = [_c.POINTER(_i32)]
         L.moe_ffn_status_string.restype = _c.c_char_p
         L.moe_ffn_status_string.argtypes = [_c.c_int]
         L.moe_ffn_set_stage_events.restype = _c.c_int
@@ -408,6 +413,17 @@ def moe_ffn_check_status(workspace: torch.Tensor, stream=None) -> Tuple[int, int
     code = lib().moe_ffn_check_status(_dev(workspace, "workspace", torch.uint8),
                                       _stream(stream), _c.byref(n))
     return code, int(n.value)
+
+
+def moe_ffn_device_check() -> Tuple[bool, int]:
+    """Wait for the device; return (the library is the debug build, the first
+    failed device bounds check since the last call as file * 100000 + line,
+    or 0), clearing the record."""
+    where = _i32(0)
+    code = lib().moe_ffn_device_check(_c.byref(where))
+    if code < 0:
+        raise MoeFfnError("moe_ffn_device_check", code)
+    return bool(code), int(where.value)
 
 
 def moe_ffn_set_split(gate_up: int = 0, down: int = 0) -> None:

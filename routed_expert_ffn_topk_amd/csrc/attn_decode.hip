@@ -389,4 +389,6 @@ hipError_t launch_attn_decode(const uint16_t* q, const uint16_t* k, const uint16
     return err == hipSuccess ? ev.mark(1, stream) : err;
 }
 
+MOE_DEVICE_CHECK_READER(attn_decode)
+
 }  // namespace moe

@@ -98,4 +98,6 @@ hipError_t launch_combine(const float* y, const int32_t* ids, const float* w,
     return hipGetLastError();
 }
 
+MOE_DEVICE_CHECK_READER(combine)
+
 }  // namespace moe

@@ -62,6 +62,44 @@ constexpr int kXcds = 8;
 // LDS address space (destination of the direct global->LDS loads).
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
+// ---------------------------------------------------------------------------
+// Device bounds checks of the debug build (compiled with
+// -DMOE_FFN_DEVICE_CHECKS: libmoe_ffn_debug.so).  MOE_IN_BOUNDS(cond) guards
+// an index before a global access: in the debug build a false condition
+// records the source line in this translation unit's check word (the first
+// failing line wins, a vector atomic) and yields false, and the caller then
+// skips the access or substitutes a valid index, so a bad index becomes a
+// report (moe_ffn_device_check) rather than a memory fault.  Release builds
+// compile the guards away (the condition is not even evaluated).
+// ---------------------------------------------------------------------------
+#ifdef MOE_FFN_DEVICE_CHECKS
+namespace {
+__device__ int g_check_line;
+}
+__device__ __forceinline__ bool check_bound(bool ok, int line) {
+    if (!ok) atomicCAS(&g_check_line, 0, line);
+    return ok;
+}
+#define MOE_IN_BOUNDS(cond) ::moe::check_bound((cond), __LINE__)
+// Host side: the first failing line of this translation unit since the last
+// read (0: none), cleared by the read.
+#define MOE_DEVICE_CHECK_READER(name)                                               \
+    hipError_t device_check_##name(int* line) {                                     \
+        hipError_t e = hipMemcpyFromSymbol(line, HIP_SYMBOL(g_check_line), sizeof(int)); \
+        const int zero = 0;                                                         \
+        if (e == hipSuccess)                                                        \
+            e = hipMemcpyToSymbol(HIP_SYMBOL(g_check_line), &zero, sizeof(int));    \
+        return e;                                                                   \
+    }
+#else
+#define MOE_IN_BOUNDS(cond) true
+#define MOE_DEVICE_CHECK_READER(name)                                               \
+    hipError_t device_check_##name(int* line) {                                     \
+        *line = 0;                                                                  \
+        return hipSuccess;                                                          \
+    }
+#endif
+
 // Wait until at most N vector-memory loads of this wave are outstanding
 // (loads complete in issue order), leaving LDS and export counters alone.
 template <int N>

@@ -79,6 +79,8 @@ struct ExpertGemm {
     uint16_t* h;              // gate/up output, row p at p * N
     float* y;                 // down output, slot s at s * N
     int b_pitch;              // elements between B rows
+    int b_rows;               // B rows (x: T; h: T * top_k), for the debug build's checks
+    int slots;                // T * top_k: rows of h and y
     int N, K;                 // rows per expert matrix, reduction length
     int top_k;                // gate/up: B row of gathered row p is token sorted_slot[p] / top_k
     int split;                // K parts per row block (1, 2 or 4); 0 = chosen on the device
@@ -586,7 +588,11 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
         const int my = rb0 + r;
         const bool has = my < nrb;
         const int row0 = (has ? my : 0) * 16;
-        const size_t arow = (size_t)e * erows + row0 + col;   // this lane's weight row
+        // this lane's weight row (debug build: row 0 if the expert or row is
+        // out of range)
+        const size_t arow = MOE_IN_BOUNDS(e >= 0 && e < g.E && row0 + col < erows)
+                                ? (size_t)e * erows + row0 + col
+                                : 0;
         const int nfull = has ? (u1 - u0) / U : 0;   // full batches of this wave
         const int tail_u = u0 + nfull * U;           // tail units [tail_u, u1)
         // the round in format F (tag: RoundFmt<F, read the second set>)
@@ -674,7 +680,8 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                 for (int i = 0; i < NL; ++i) {
                     const int c = (wave + kWaves * i) >> dl;
                     const int qq = beg + c0 + (c < ntok ? c : 0);
-                    const int brow = kIsGateUp ? ix.sorted_slot[qq] / g.top_k : qq;
+                    const int b0 = kIsGateUp ? ix.sorted_slot[qq] / g.top_k : qq;
+                    const int brow = MOE_IN_BOUNDS(b0 >= 0 && b0 < g.b_rows) ? b0 : 0;
                     tp[i] = (uint32_t)brow * (uint32_t)g.b_pitch;
                 }
                 f32x4 acc[NC][NMAT];
@@ -827,8 +834,8 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                 }
     #pragma unroll
                 for (int hh = 0; hh < NC; ++hh) {
-                    if (kp == 0 && has && valid[hh]) {
-                        const size_t p = (size_t)beg + c0 + 16 * hh + col;
+                    const size_t p = (size_t)beg + c0 + 16 * hh + col;
+                    if (kp == 0 && has && valid[hh] && MOE_IN_BOUNDS(p < (size_t)g.slots)) {
                         if constexpr (kIsGateUp) {
                             const f32x4 gv = acc[hh][0], uv = acc[hh][1];
                             u32x2 packed;
@@ -839,6 +846,7 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                             *reinterpret_cast<u32x2*>(g.h + p * g.N + row0 + kg * 4) = packed;
                         } else {
                             const int slot = ix.sorted_slot[p];
+                            if (MOE_IN_BOUNDS(slot >= 0 && slot < g.slots))
     #pragma unroll
                             for (int mm = 0; mm < NMAT; ++mm)
                                 *reinterpret_cast<f32x4*>(g.y + (size_t)slot * erows + mm * g.N +
@@ -905,7 +913,8 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                 for (int i = 0; i < 4; ++i) {
                     const int c = (wave + kWaves * i) >> dl;
                     const int qq = beg + c0 + (c < ntok ? c : 0);
-                    const int brow = kIsGateUp ? ix.sorted_slot[qq] / g.top_k : qq;
+                    const int b0 = kIsGateUp ? ix.sorted_slot[qq] / g.top_k : qq;
+                    const int brow = MOE_IN_BOUNDS(b0 >= 0 && b0 < g.b_rows) ? b0 : 0;
                     tp[i] = g.b_src + (size_t)brow * g.b_pitch;
                 }
                 f32x4 acc[NMAT];
@@ -1066,8 +1075,8 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                                 acc[mm] += red[(((pp - 1) * R + r) * NMAT + mm) * kWave + lane];
                     }
                 }
-                if (kp == 0 && has && valid) {
-                    const size_t p = (size_t)beg + c0 + col;
+                const size_t p = (size_t)beg + c0 + col;
+                if (kp == 0 && has && valid && MOE_IN_BOUNDS(p < (size_t)g.slots)) {
                     if constexpr (kIsGateUp) {
                         const f32x4 gv = acc[0], uv = acc[1];
                         u32x2 packed;
@@ -1078,6 +1087,7 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                         *reinterpret_cast<u32x2*>(g.h + p * g.N + row0 + kg * 4) = packed;
                     } else {
                         const int slot = ix.sorted_slot[p];
+                        if (MOE_IN_BOUNDS(slot >= 0 && slot < g.slots))
     #pragma unroll
                         for (int mm = 0; mm < NMAT; ++mm)
                             *reinterpret_cast<f32x4*>(g.y + (size_t)slot * erows + mm * g.N +
@@ -1311,14 +1321,16 @@ hipError_t launch_ffn(const uint16_t* x, const Routing& route, const FfnWeights&
     gu.h = ws.h;
     gu.y = nullptr;
     gu.b_pitch = s.H;
+    gu.b_rows = s.T;
+    gu.slots = s.T * s.k;
     gu.N = s.I;
     gu.K = s.H;
     gu.top_k = s.k;
     gu.split = split.gate_up;
+    gu.E = s.E;
     if (fused) {
         gu.ids = route.ids;
         gu.n_slots = (int)n_slots;
-        gu.E = s.E;
         gu.ix_out = IndexOut{ws.meta, ws.counts, ws.offsets, ws.active, ws.sorted_slot};
     }
     // an expert can receive more than 16 slots only if the batch has more
@@ -1341,6 +1353,7 @@ hipError_t launch_ffn(const uint16_t* x, const Routing& route, const FfnWeights&
     dn.h = nullptr;
     dn.y = ws.y;
     dn.b_pitch = s.I;
+    dn.b_rows = s.T * s.k;
     dn.N = s.H;
     dn.K = s.I;
     dn.split = split.down;
@@ -1390,6 +1403,8 @@ hipError_t launch_ffn_int8(const uint16_t* x, const Routing& route, const FfnWei
                            hipStream_t stream) {
     return launch_ffn<Int8Weights>(x, route, W, out, s, ws, num_cu, ev, split, stream);
 }
+
+MOE_DEVICE_CHECK_READER(expert_gemm)
 
 hipError_t launch_ffn_resplit(const uint16_t* x, const Routing& route, const FfnWeights& W,
                            uint16_t* out, const FfnShape& s, const Workspace& ws, int num_cu,

@@ -75,6 +75,8 @@ struct TiledGemm {
     float* y;                 // down output, slot s at s * N (+ y_plane per K part)
     size_t y_plane;           // floats between the partial sums of two K parts
     int b_pitch;              // elements between B rows
+    int b_rows;               // B rows (x: T; h: T * top_k), for the debug build's checks
+    int slots;                // T * top_k: rows of h and y
     int N, K;
     int top_k;
     int k_parts;              // K parts per tile (down; 1 for gate/up)
@@ -244,7 +246,8 @@ void expert_tile_kernel(const TiledGemm g) {
             } else {
                 const int rr = RPI * (q - NMAT * WCH) + lane / RW;
                 const int pp = beg + min(p0 + rr, pend - 1);
-                const int brow = kDown ? pp : g.sorted_slot[pp] / g.top_k;
+                const int b0 = kDown ? pp : g.sorted_slot[pp] / g.top_k;
+                const int brow = MOE_IN_BOUNDS(b0 >= 0 && b0 < g.b_rows) ? b0 : 0;
                 src[i] = g.b_src + (size_t)brow * g.b_pitch + s0 * KS + cl * 8;
             }
         }
@@ -329,8 +332,11 @@ void expert_tile_kernel(const TiledGemm g) {
         for (int tb = 0; tb < TB; ++tb) {
             const int p = p0 + 16 * (bs + tb) + col;
             if (tb >= nbw || p >= pend) continue;
+            if (!MOE_IN_BOUNDS(beg + p < g.slots)) continue;
             if constexpr (kDown) {
-                float* yrow = g.y + kp * g.y_plane + (size_t)g.sorted_slot[beg + p] * g.N;
+                const int slot = g.sorted_slot[beg + p];
+                if (!MOE_IN_BOUNDS(slot >= 0 && slot < g.slots)) continue;
+                float* yrow = g.y + kp * g.y_plane + (size_t)slot * g.N;
 #pragma unroll
                 for (int mm = 0; mm < NMAT; ++mm)
 #pragma unroll
@@ -415,6 +421,8 @@ hipError_t launch_tiled_gate_up(const uint16_t* x, const FfnWeights& W, const Ff
     g.sorted_slot = ws.sorted_slot;
     g.h = ws.h;
     g.b_pitch = s.H;
+    g.b_rows = s.T;
+    g.slots = s.T * s.k;
     g.N = s.I;
     g.K = s.H;
     g.top_k = s.k;
@@ -435,6 +443,8 @@ hipError_t launch_tiled_down(const FfnWeights& W, const FfnShape& s, const Works
     g.y = ws.y;
     g.y_plane = (size_t)s.T * s.k * s.H;
     g.b_pitch = s.I;
+    g.b_rows = s.T * s.k;
+    g.slots = s.T * s.k;
     g.N = s.H;
     g.K = s.I;
     g.top_k = s.k;
@@ -455,6 +465,8 @@ hipError_t launch_tiled_down(const FfnWeights& W, const FfnShape& s, const Works
 // tiles it needs, in units of one round of full-K tiles at the product's
 // nominal rate, plus the time to write and read back each extra plane of
 // partial sums at a nominal HBM rate.
+MOE_DEVICE_CHECK_READER(expert_tile)
+
 int tiled_down_parts(int64_t T, int64_t H, int64_t I, int E, int k) {
     if (T <= kTiledMinBatch) return 1;
     return down_parts<kDownProd>(T, H, I, E, k);

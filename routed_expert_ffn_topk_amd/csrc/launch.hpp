@@ -146,4 +146,13 @@ hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int 
 // n launches of an empty one-wave kernel on stream (launch-gap probe).
 hipError_t launch_empty_chain(int n, hipStream_t stream);
 
+// Debug build (-DMOE_FFN_DEVICE_CHECKS): the first device bounds check that
+// failed in each translation unit since the last read (0: none), cleared by
+// the read; release builds report 0.
+hipError_t device_check_route_permute(int* line);
+hipError_t device_check_expert_gemm(int* line);
+hipError_t device_check_expert_tile(int* line);
+hipError_t device_check_combine(int* line);
+hipError_t device_check_attn_decode(int* line);
+
 }  // namespace moe

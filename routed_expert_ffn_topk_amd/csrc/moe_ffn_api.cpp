@@ -499,6 +499,26 @@ int moe_ffn_set_stage_events(void* const* events, int32_t n_events) {
     return MOE_FFN_OK;
 }
 
+int moe_ffn_device_check(int32_t* where) {
+    if (!where) return MOE_FFN_ERR_NULL_ARG;
+    *where = 0;
+    if (hipDeviceSynchronize() != hipSuccess) return MOE_FFN_ERR_HIP;
+    // translation units in a fixed order; the first that reports wins
+    hipError_t (*const readers[])(int*) = {moe::device_check_route_permute, moe::device_check_expert_gemm,
+                                           moe::device_check_expert_tile, moe::device_check_combine,
+                                           moe::device_check_attn_decode};
+    for (int i = 0; i < (int)(sizeof(readers) / sizeof(readers[0])); ++i) {
+        int line = 0;
+        if (readers[i](&line) != hipSuccess) return MOE_FFN_ERR_HIP;
+        if (line != 0 && *where == 0) *where = (i + 1) * 100000 + line;
+    }
+#ifdef MOE_FFN_DEVICE_CHECKS
+    return 1;
+#else
+    return 0;
+#endif
+}
+
 const char* moe_ffn_status_string(int status) {
     switch (status) {
         case MOE_FFN_OK: return "ok";

@@ -426,4 +426,6 @@ hipError_t launch_permute(const int32_t* ids, const FfnShape& s, const Workspace
     return hipGetLastError();
 }
 
+MOE_DEVICE_CHECK_READER(route_permute)
+
 }  // namespace moe

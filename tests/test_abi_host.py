@@ -59,9 +59,12 @@ def test_library_exports_every_declared_symbol():
     assert {"moe_ffn_forward", "moe_ffn_forward_int8", "moe_ffn_forward_logits", "moe_route_topk",
             "moe_ffn_workspace_bytes", "moe_ffn_workspace_layout", "moe_ffn_check_status",
             "moe_ffn_status_string"} <= set(names)
-    L = ctypes.CDLL(moe.LIB_PATH)
-    for n in names:
-        assert hasattr(L, n), n
+    assert "moe_ffn_device_check" in names
+    here = os.path.dirname(moe.__file__)
+    for path in (os.path.join(here, "libmoe_ffn.so"), os.path.join(here, "libmoe_ffn_debug.so")):
+        L = ctypes.CDLL(path)
+        for n in names:
+            assert hasattr(L, n), (path, n)
 
 
 def test_status_strings():
