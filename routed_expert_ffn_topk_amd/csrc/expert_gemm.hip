@@ -452,7 +452,10 @@ using DualDown = MixedWeights<Int4Weights, Int8Weights, true>;
 // to this many times 512 K; scaled formats hold that many times the slab's
 // scale table in LDS, which the workgroups per CU must fit), and the batch
 // of the wide chunks (kWideBatch units, 0 = none: chunks of up to 32 tokens
-// use two B tiles per weight batch; BF16 only).
+// use two B tiles per weight batch; BF16 only), and kEarlyBatch: the
+// quantised pipeline requests a slab's second batch before the slab's
+// barrier (measured: INT8 down 3-4 % faster at 4-16 tokens per expert; INT8
+// and INT4 gate/up, INT4 down and the two-copy down not faster or slower).
 // The three grouped products: down (one matrix), gate/up (W_gate and W_up
 // per K step), and down as two half-height matrices (the two halves of
 // W_down's rows share each token fragment).
@@ -465,6 +468,7 @@ struct GemmTuning<Bf16Weights, 2> {   // gate/up: two matrices per K step
     static constexpr int kBatch = 2;
     static constexpr int kMaxDepth = 16;
     static constexpr int kWideBatch = 1;
+    static constexpr bool kEarlyBatch = false;
 };
 template <>
 struct GemmTuning<Bf16Weights, 1> {   // down
@@ -472,6 +476,7 @@ struct GemmTuning<Bf16Weights, 1> {   // down
     static constexpr int kBatch = 8;
     static constexpr int kMaxDepth = 16;
     static constexpr int kWideBatch = 4;
+    static constexpr bool kEarlyBatch = false;
 };
 template <>
 struct GemmTuning<Int8Weights, 2> {   // (3, 1, 4) before the scales were staged per group: 2-3 % slower
@@ -479,6 +484,7 @@ struct GemmTuning<Int8Weights, 2> {   // (3, 1, 4) before the scales were staged
     static constexpr int kBatch = 2;
     static constexpr int kMaxDepth = 8;
     static constexpr int kWideBatch = 0;
+    static constexpr bool kEarlyBatch = false;
 };
 template <>
 struct GemmTuning<Int8Weights, 1> {
@@ -486,6 +492,7 @@ struct GemmTuning<Int8Weights, 1> {
     static constexpr int kBatch = 2;
     static constexpr int kMaxDepth = 8;
     static constexpr int kWideBatch = 0;
+    static constexpr bool kEarlyBatch = true;
 };
 template <>
 struct GemmTuning<Int4Weights, 2> {
@@ -493,6 +500,7 @@ struct GemmTuning<Int4Weights, 2> {
     static constexpr int kBatch = 2;
     static constexpr int kMaxDepth = 4;
     static constexpr int kWideBatch = 0;
+    static constexpr bool kEarlyBatch = false;
 };
 template <>
 struct GemmTuning<ResidualGateUp, 2> {
@@ -500,6 +508,7 @@ struct GemmTuning<ResidualGateUp, 2> {
     static constexpr int kBatch = 2;
     static constexpr int kMaxDepth = 4;
     static constexpr int kWideBatch = 0;
+    static constexpr bool kEarlyBatch = false;
 };
 template <>
 struct GemmTuning<DualDown, 1> {
@@ -507,6 +516,7 @@ struct GemmTuning<DualDown, 1> {
     static constexpr int kBatch = 2;
     static constexpr int kMaxDepth = 16;
     static constexpr int kWideBatch = 0;
+    static constexpr bool kEarlyBatch = false;
 };
 template <>
 struct GemmTuning<Int4Weights, kDownPair> {
@@ -514,6 +524,7 @@ struct GemmTuning<Int4Weights, kDownPair> {
     static constexpr int kBatch = 2;
     static constexpr int kMaxDepth = 8;
     static constexpr int kWideBatch = 0;
+    static constexpr bool kEarlyBatch = false;
 };
 
 // S: K-parts per row block; U: units per weight batch (divides the units of
@@ -527,7 +538,7 @@ struct GemmTuning<Int4Weights, kDownPair> {
 // PAIR (down, NMAT = 2): the two "matrices" are the two halves of W_down's
 // rows (g.N = H / 2 rows each, the second half at g.w1 / g.s1), so that one
 // token fragment feeds both, as W_gate and W_up share it in gate/up.
-template <class Fmt, int NMAT, int S, int U, int FMAX, int UW, bool PAIR>
+template <class Fmt, int NMAT, int S, int U, int FMAX, int UW, bool PAIR, bool EARLY>
 __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView ix, int n_act,
                                             int grid,
                                             u32x4 (*xs)[kSlabU4], f32x4* sc) {
@@ -991,15 +1002,45 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                 // always requested before the current one is multiplied
                 int bi = 0;
                 for (int j = 0; j < nslab; ++j) {
-                    // this wave's staging loads are done (only the batch
-                    // prefetched for this slab may still be in flight; at slab
-                    // 0, whose staging follows the first batch, everything)
-                    if (j == 0)
-                        wait_vmcnt<0>();
-                    else if (bi < nfull)
-                        wait_vmcnt<(kLoads < 63 ? kLoads : 63)>();
-                    else
-                        wait_vmcnt<0>();
+                    const int bend = min(nfull, (j + 1) * nb);
+                    if constexpr (F::kFixedRolePipeline && EARLY) {
+                        // The slab's first batch requests the one after it
+                        // here, before the barrier: the register set it fills
+                        // was multiplied by the previous slab's last batch, so
+                        // two batches are in flight while the waves meet at
+                        // the barrier instead of one (a quantised slab holds
+                        // only a few batches per wave).  Then this wave's
+                        // staging loads of slab j are done once no more than
+                        // the loads issued after them are outstanding: the
+                        // previous slab's batch requests (nb - 1 of them, the
+                        // last one this slab's first batch) and the request
+                        // here.  At slab 0 the staging follows the first batch
+                        // and precedes the request.
+                        if (bi < bend) {
+                            const int un = u0 + min(bi + 1, nfull - 1) * U;
+                            if (bi & 1)
+                                F::template load<NMAT, U>(A, src, un);
+                            else
+                                F::template load<NMAT, U>(B, src, un);
+                            if (j == 0 || nb < 2)
+                                wait_vmcnt<(kLoads < 63 ? kLoads : 63)>();
+                            else
+                                wait_vmcnt<(2 * kLoads < 63 ? 2 * kLoads : 63)>();
+                        } else {
+                            wait_vmcnt<0>();
+                        }
+                    } else {
+                        // this wave's staging loads are done (only the batch
+                        // prefetched for this slab may still be in flight; at
+                        // slab 0, whose staging follows the first batch,
+                        // everything)
+                        if (j == 0)
+                            wait_vmcnt<0>();
+                        else if (bi < nfull)
+                            wait_vmcnt<(kLoads < 63 ? kLoads : 63)>();
+                        else
+                            wait_vmcnt<0>();
+                    }
                     __syncthreads();
                     if (j + 1 < nslab) stage(j + 1, (j + 1) & 1);
                     const int slab_u0 = u0 + j * spu;
@@ -1011,7 +1052,6 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                     // slab (slab j & (P - 1) of its group), output rows 4kg .. 4kg + 3
                     const float* sl = reinterpret_cast<const float*>(sc) + ((j >> logP) & 1) * SCB +
                                       ((r * S + kp) * GU + (j & (P - 1)) * spu) * 16 + 4 * kg;
-                    const int bend = min(nfull, (j + 1) * nb);
                     if constexpr (F::kFixedRolePipeline) {
                         // one batch: request the next one into nxt (after the
                         // last batch, the last again: an unconditional request
@@ -1021,13 +1061,23 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                         // register sets apart (with the parity test below
                         // inside the loop the compiler copies between them,
                         // and the copy waits for the batch just requested).
-                        auto step = [&](auto& cur, auto& nxt, int b) __attribute__((always_inline)) {
+                        auto mult = [&](auto& cur, int b) __attribute__((always_inline)) {
                             const int ub = u0 + b * U - slab_u0;   // batch's first unit in the slab
-                            const u32x4* bb = buf + ub * F::kBlocks * kBlockU4;
-                            const float* sb = sl + 16 * ub;
-                            F::template load<NMAT, U>(nxt, src, u0 + min(b + 1, nfull - 1) * U);
-                            F::template mma<NMAT, U, TS>(cur, bb, sb, acc);
+                            F::template mma<NMAT, U, TS>(cur, buf + ub * F::kBlocks * kBlockU4,
+                                                         sl + 16 * ub, acc);
                         };
+                        auto step = [&](auto& cur, auto& nxt, int b) __attribute__((always_inline)) {
+                            F::template load<NMAT, U>(nxt, src, u0 + min(b + 1, nfull - 1) * U);
+                            mult(cur, b);
+                        };
+                        // the slab's first batch (its request was issued above)
+                        if (EARLY && bi < bend) {
+                            if (bi & 1)
+                                mult(B, bi);
+                            else
+                                mult(A, bi);
+                            ++bi;
+                        }
                         if (bi < bend && (bi & 1)) step(B, A, bi++);
                         for (; bi + 1 < bend; bi += 2) {
                             step(A, B, bi);
@@ -1187,6 +1237,7 @@ void expert_gemm_kernel(const ExpertGemm g) {
     constexpr int U = Tune::kBatch;
     constexpr int FMAX = Tune::kMaxDepth;
     constexpr int UW = WIDE ? Tune::kWideBatch : 0;
+    constexpr bool EARLY = Tune::kEarlyBatch;
     constexpr int units1 = kSlabBlocks / Fmt::kBlocks;   // units of a part per slab, S = 1
     // K-slab buffers of the token tile, double-buffered, followed (scaled
     // formats) by the slabs' scale tables.  Both are filled by direct
@@ -1219,13 +1270,13 @@ void expert_gemm_kernel(const ExpertGemm g) {
     const int G = busy_grid(rounds_for(n_act, g.N / 16, S));
     if ((int)blockIdx.x >= G) return;
     if (S == 1)
-        gemm_rounds<Fmt, NMAT, 1, cmin(U, units1), FMAX, cmin(UW, units1 / 2), PAIR>(
+        gemm_rounds<Fmt, NMAT, 1, cmin(U, units1), FMAX, cmin(UW, units1 / 2), PAIR, EARLY>(
             g, ix, n_act, G, xs, sc);
     else if (S == 2)
-        gemm_rounds<Fmt, NMAT, 2, cmin(U, units1 / 2), FMAX, cmin(UW, units1 / 4), PAIR>(
+        gemm_rounds<Fmt, NMAT, 2, cmin(U, units1 / 2), FMAX, cmin(UW, units1 / 4), PAIR, EARLY>(
             g, ix, n_act, G, xs, sc);
     else
-        gemm_rounds<Fmt, NMAT, 4, cmin(U, units1 / 4), FMAX, cmin(UW, units1 / 8), PAIR>(
+        gemm_rounds<Fmt, NMAT, 4, cmin(U, units1 / 4), FMAX, cmin(UW, units1 / 8), PAIR, EARLY>(
             g, ix, n_act, G, xs, sc);
 }
 
