@@ -684,8 +684,9 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                 // 512 K of token ii >> dl, the (ii & (dep - 1))-th of the
                 // token's slab row; NC = 2: load ii stages token ii's 256 K
                 constexpr int NL = 4 * NC;
-                // (element offsets of the rows, 32-bit: B rows are at most
-                // a few times 10^7 elements apart)
+                // the loads' B rows (below 2^31; each load forms the row's
+                // 64-bit element offset, since rows x pitch can exceed 2^32
+                // in large batches)
                 uint32_t tp[NL];
     #pragma unroll
                 for (int i = 0; i < NL; ++i) {
@@ -693,7 +694,7 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                     const int qq = beg + c0 + (c < ntok ? c : 0);
                     const int b0 = kIsGateUp ? ix.sorted_slot[qq] / g.top_k : qq;
                     const int brow = MOE_IN_BOUNDS(b0 >= 0 && b0 < g.b_rows) ? b0 : 0;
-                    tp[i] = (uint32_t)brow * (uint32_t)g.b_pitch;
+                    tp[i] = (uint32_t)brow;
                 }
                 f32x4 acc[NC][NMAT];
     #pragma unroll
@@ -727,7 +728,7 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                             u * 32 * F::kBlocks + F::block_offset(bb % F::kBlocks, kgl);
                         if (c < ntok && u < p1 && (NC == 1 || lane < 32))
                             __builtin_amdgcn_global_load_lds(
-                                (const void*)(g.b_src + tp[i] + off),
+                                (const void*)(g.b_src + (size_t)tp[i] * (size_t)g.b_pitch + off),
                                 (lds_void_ptr)&xs[bsel][c * tpitch + ((ii & (dep - 1)) << 6)], 16,
                                 0, 0);
                     }
