@@ -28,11 +28,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       const int32_t* __restrict__ counts,
                                                       int large_min, int parts,
                                                       size_t plane) {
+    // (the thread index in 64 bits: T * H / 8 passes 2^31 for batches of a
+    // few million tokens)
     const int chunks = H / 8;
-    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= T * chunks) return;
-    const int t = idx / chunks;
-    const int c = (idx - t * chunks) * 8;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (int64_t)T * chunks) return;
+    const int t = (int)(idx / chunks);
+    const int c = (int)(idx - (int64_t)t * chunks) * 8;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     // slots in batches of B: every id, weight and y row of a batch is
     // requested before any is used (slots past k re-read the last one; their

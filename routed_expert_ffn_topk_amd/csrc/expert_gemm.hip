@@ -692,7 +692,8 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                 for (int i = 0; i < NL; ++i) {
                     const int c = (wave + kWaves * i) >> dl;
                     const int qq = beg + c0 + (c < ntok ? c : 0);
-                    const int b0 = kIsGateUp ? ix.sorted_slot[qq] / g.top_k : qq;
+                    const bool qin = MOE_IN_BOUNDS(qq >= 0 && qq < g.slots);
+                    const int b0 = kIsGateUp ? (qin ? ix.sorted_slot[qq] / g.top_k : 0) : qq;
                     const int brow = MOE_IN_BOUNDS(b0 >= 0 && b0 < g.b_rows) ? b0 : 0;
                     tp[i] = (uint32_t)brow;
                 }
@@ -925,7 +926,8 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                 for (int i = 0; i < 4; ++i) {
                     const int c = (wave + kWaves * i) >> dl;
                     const int qq = beg + c0 + (c < ntok ? c : 0);
-                    const int b0 = kIsGateUp ? ix.sorted_slot[qq] / g.top_k : qq;
+                    const bool qin = MOE_IN_BOUNDS(qq >= 0 && qq < g.slots);
+                    const int b0 = kIsGateUp ? (qin ? ix.sorted_slot[qq] / g.top_k : 0) : qq;
                     const int brow = MOE_IN_BOUNDS(b0 >= 0 && b0 < g.b_rows) ? b0 : 0;
                     tp[i] = g.b_src + (size_t)brow * g.b_pitch;
                 }

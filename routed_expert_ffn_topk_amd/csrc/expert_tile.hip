@@ -214,8 +214,10 @@ void expert_tile_kernel(const TiledGemm g) {
         // and then read its weight tiles alone.)
         const int nbe = (m + 15) >> 4;
         const int mt = r2 - kp * mt_n;                // token tile
-        const int p0 = 16 * ((mt * nbe) / mt_n);
-        const int pend = min(m, 16 * (((mt + 1) * nbe) / mt_n));   // tokens [p0, pend)
+        // (the products in 64 bits: mt * nbe grows as m^2 / 4096 and passes
+        // 2^31 once an expert has about three million tokens)
+        const int p0 = 16 * (int)(((int64_t)mt * nbe) / mt_n);
+        const int pend = min(m, 16 * (int)(((int64_t)(mt + 1) * nbe) / mt_n));   // tokens [p0, pend)
         // the tile's 16-token blocks, TB per wave in wave order: wave wm
         // takes blocks [bs, bs + nbw).  (Dealing them evenly to the waves
         // was 2-7 % slower on tiles of 100-160 tokens: every wave with a
@@ -246,7 +248,9 @@ void expert_tile_kernel(const TiledGemm g) {
             } else {
                 const int rr = RPI * (q - NMAT * WCH) + lane / RW;
                 const int pp = beg + min(p0 + rr, pend - 1);
-                const int b0 = kDown ? pp : g.sorted_slot[pp] / g.top_k;
+                // (debug build: the gathered row itself is checked too)
+                const bool pin = MOE_IN_BOUNDS(pp >= 0 && pp < g.slots);
+                const int b0 = kDown ? pp : (pin ? g.sorted_slot[pp] / g.top_k : 0);
                 const int brow = MOE_IN_BOUNDS(b0 >= 0 && b0 < g.b_rows) ? b0 : 0;
                 src[i] = g.b_src + (size_t)brow * g.b_pitch + s0 * KS + cl * 8;
             }

@@ -64,3 +64,42 @@ def test_rows_past_element_2_32(H, I):
     assert_close(got, ref, TOL_BF16, what=f"H={H} I={I} rows {rows.tolist()}")
     del x, out
     torch.cuda.empty_cache()
+
+
+def test_combine_past_2_31_outputs():
+    """2^22 + 64 tokens of hidden 4096: the combine's flat index over T * H / 8
+    output chunks passes 2^31 (x and out are 34 GB each, the FP32 per-slot
+    rows 69 GB); the last 20 tokens again form one wide chunk of expert 1."""
+    need_gpu()
+    T2, H, I = (1 << 22) + 64, 4096, 32
+    need = 2 * T2 * H * 2 + T2 * H * 4 + (8 << 30)
+    free, _ = torch.cuda.mem_get_info()
+    if free < need:
+        pytest.skip(f"needs {need >> 30} GiB of free device memory, {free >> 30} free")
+    say(f"combine past 2^31 outputs: T={T2} H={H} I={I} E={E} top-1")
+    assert T2 * (H // 8) > 1 << 31
+    rng = np.random.default_rng(8)
+    Wg = [bf16_weights(rng, (I, H)) for _ in range(E)]
+    Wu = [bf16_weights(rng, (I, H)) for _ in range(E)]
+    Wd = [bf16_weights(rng, (H, I)) for _ in range(E)]
+    dev = lambda W: torch.stack([workloads.bits_to_bf16(w) for w in W]).cuda()  # noqa: E731
+    ids = np.zeros((T2, 1), dtype=np.int32)
+    ids[T2 - TAIL:] = 1
+    w = rng.uniform(0.5, 1.0, size=(T2, 1)).astype(np.float32)
+    gen = torch.Generator(device="cuda").manual_seed(12)
+    x = torch.empty(T2, H, dtype=torch.bfloat16, device="cuda")
+    step = 1 << 16
+    for a in range(0, T2, step):
+        b = min(T2, a + step)
+        x[a:b] = torch.randn(b - a, H, device="cuda", generator=gen).to(torch.bfloat16)
+    out = moe.moe_ffn_forward(x, torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda(),
+                              dev(Wg), dev(Wu), dev(Wd))
+    torch.cuda.synchronize()
+    rows = np.array([0, 1 << 21, (1 << 22) - 1, T2 - TAIL - 1] + list(range(T2 - TAIL, T2)))
+    idx = torch.from_numpy(rows).cuda()
+    got = workloads.bf16_bits(out.index_select(0, idx).cpu())
+    xb = workloads.bf16_bits(x.index_select(0, idx).cpu())
+    ref = oracle.moe_ffn_bf16(xb, ids[rows], w[rows], Wg, Wu, Wd, E=E)
+    assert_close(got, ref, TOL_BF16, what=f"T={T2} rows {rows.tolist()}")
+    del x, out
+    torch.cuda.empty_cache()
