@@ -45,6 +45,7 @@ def run_both(x, ids, w, Q, E):
 @pytest.mark.parametrize("T,H,I,E,k", [
     (16, 256, 512, 8, 2), (5, 384, 640, 4, 2), (1, 128, 128, 1, 1), (13, 512, 256, 16, 4),
     (40, 128, 256, 2, 1), (16, 1024, 384, 64, 8), (24, 128, 256, 1024, 4),
+    (150, 128, 256, 2, 1),     # ~75 tokens per expert: several 16-token chunks each
 ])
 def test_int8_layer_matches_oracle(T, H, I, E, k):
     need_gpu()
