@@ -27,6 +27,12 @@ TAIL = 20           # expert 1's tokens: one wide chunk of the small-m product
 E = 2
 
 
+def need_free(nbytes: int):
+    free, _ = torch.cuda.mem_get_info()
+    if free < nbytes:
+        pytest.skip(f"needs {nbytes >> 30} GiB of free device memory, {free >> 30} free")
+
+
 def bf16_weights(rng, shape, std=0.05):
     return workloads.bf16_bits(torch.from_numpy(
         (rng.standard_normal(shape) * std).astype(np.float32)).to(torch.bfloat16))
@@ -35,6 +41,8 @@ def bf16_weights(rng, shape, std=0.05):
 @pytest.mark.parametrize("H,I", [(4096, 32), (32, 4096)])
 def test_rows_past_element_2_32(H, I):
     need_gpu()
+    # x, out, the FP32 per-slot rows and h, with room to spare
+    need_free(T * H * 2 * 2 + T * H * 4 + T * I * 2 + (4 << 30))
     say(f"rows past element 2^32: T={T} H={H} I={I} E={E} top-1")
     assert (T - TAIL) * max(H, I) > 1 << 32
     rng = np.random.default_rng(7)
@@ -72,10 +80,7 @@ def test_combine_past_2_31_outputs():
     rows 69 GB); the last 20 tokens again form one wide chunk of expert 1."""
     need_gpu()
     T2, H, I = (1 << 22) + 64, 4096, 32
-    need = 2 * T2 * H * 2 + T2 * H * 4 + (8 << 30)
-    free, _ = torch.cuda.mem_get_info()
-    if free < need:
-        pytest.skip(f"needs {need >> 30} GiB of free device memory, {free >> 30} free")
+    need_free(2 * T2 * H * 2 + T2 * H * 4 + (8 << 30))
     say(f"combine past 2^31 outputs: T={T2} H={H} I={I} E={E} top-1")
     assert T2 * (H // 8) > 1 << 31
     rng = np.random.default_rng(8)
