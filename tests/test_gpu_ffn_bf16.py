@@ -73,6 +73,9 @@ def test_tiny_workload_matches_oracle_and_golden():
     (16, 512, 256, 256, 8),    # many experts, most with one token
     (1, 128, 128, 1, 1),       # single expert
     (33, 128, 96, 2, 1),       # ~16 tokens per expert, ragged token tile
+    (32, 64, 96, 256, 8),      # 256 slots over 256 experts: the most the gate/up prologue indexes
+    (33, 64, 96, 256, 8),      # 264 slots: one past it, the separate index kernel
+    (32, 64, 96, 257, 8),      # 257 experts: likewise
     (16, 64, 96, 300, 8),      # more than 256 experts: the separate index kernel
     (40, 64, 96, 1024, 8),     # the most experts the library takes
     (200, 64, 64, 1024, 4),    # 800 slots: the many-slot index kernel; tiled batch size

@@ -104,6 +104,10 @@ def test_gather_index_matches_oracle(T, E, k, bad):
     (64, 32, 64, 64, 64, "normal"),      # k = 64: every lane of the wave chooses
     (5, 64, 64, 1024, 8, "masked"),
     (9, 32, 32, 1, 1, "normal"),
+    (64, 32, 64, 256, 8, "normal"),      # 512 slots, 16384 logits: router and index in one
+                                         # kernel at both of its limits (logits staged in LDS)
+    (64, 32, 64, 257, 8, "normal"),      # 16448 logits: past the LDS staging of the logits
+    (65, 32, 64, 16, 8, "normal"),       # 65 tokens: past the one-kernel router and index
     (512, 32, 64, 64, 8, "normal"),      # 4096 slots: the largest fused batch
     (600, 32, 64, 64, 8, "ties"),        # 4800 slots: router kernel, then the sort
 ])
