@@ -56,6 +56,18 @@ constexpr int kTokRowU4 = kSlabBlocks * kBlockU4;   // one token's slab row (1 K
 // banks (measured: no LDS bank conflicts).
 __device__ __forceinline__ int tok_base(int c) { return c * (kTokRowU4 + 2); }
 constexpr int kSlabU4 = 16 * (kTokRowU4 + 2);     // slab buffer of 16 token rows
+// Scale tables in LDS (scaled formats), per row block and K part of a round,
+// in one of two layouts; either way the four output rows 4kg .. 4kg + 3 of a
+// lane form one aligned f32x4 per unit.
+//  * rows: [unit][16 rows].  A 64-lane staging load of 4-byte entries reads
+//    4 units of 16 rows (16 cache lines of the row-major [N][K/128] table);
+//    the four row quads a wave reads at once lie in 64 contiguous bytes.
+//  * quads: [row quad][unit][4 rows].  A staging load reads 16 units of 4
+//    rows (4 cache lines); the four row quads lie 16 x (units per group)
+//    bytes apart, which shares LDS banks from 16 units up.
+// Floats between consecutive units of a row quad:
+constexpr int kScaleUnitStrideRows = 16;
+constexpr int kScaleUnitStrideQuads = 4;
 
 // One grouped expert product: for every active expert e and gathered row p
 // of e, out[p][n] = sum_k W[e][n][k] * B[p][k].
@@ -147,9 +159,9 @@ struct Bf16Weights {
     }
     // bl: this lane's B fragment of the batch's first LDS block; block b of
     // the batch at bl[b * kBlockU4].  sl: scales in LDS (scaled formats):
-    // unit i of scale tensor t at sl[t * TS + 16 * i], the lane's four output
+    // unit i of scale tensor t at sl[t * TS + SU * i], the lane's four output
     // rows 4kg .. 4kg + 3 as one aligned f32x4
-    template <int NMAT, int U, int TS>
+    template <int NMAT, int U, int TS, int SU>
     __device__ static void mma(const Batch<NMAT, U>& d, const u32x4* bl, const float*,
                                f32x4* acc) {
 #pragma unroll
@@ -219,7 +231,7 @@ struct Int8Weights {
                 d.w[i][m][1] = load16(p + 64);
             }
     }
-    template <int NMAT, int U, int TS>
+    template <int NMAT, int U, int TS, int SU>
     __device__ static void mma(const Batch<NMAT, U>& d, const u32x4* bl, const float* sl,
                                f32x4* acc) {
 #pragma unroll
@@ -235,7 +247,7 @@ struct Int8Weights {
                     part = mfma16x16x32(i8x8_to_bf16x8(w.z, w.w),
                                         as_bf16x8(bl[(4 * i + 2 * c + 1) * kBlockU4]), part);
                 }
-                acc[m] += lds_f32x4(sl + m * TS + 16 * i) * part;
+                acc[m] += lds_f32x4(sl + m * TS + SU * i) * part;
             }
         }
     }
@@ -292,7 +304,7 @@ struct Int4Weights {
         return u32x4{(b.x & 0xffffu) | (b.z << 16), (b.x >> 16) | (b.z & 0xffff0000u),
                      (b.y & 0xffffu) | (b.w << 16), (b.y >> 16) | (b.w & 0xffff0000u)};
     }
-    template <int NMAT, int U, int TS>
+    template <int NMAT, int U, int TS, int SU>
     __device__ static void mma(const Batch<NMAT, U>& d, const u32x4* bl, const float* sl,
                                f32x4* acc) {
         const u32x4 k136 = {0x43084308u, 0x43084308u, 0x43084308u, 0x43084308u};  // BF16 136
@@ -313,7 +325,7 @@ struct Int4Weights {
                 for (int t = 0; t < 4; ++t)
                     part = mfma16x16x32(as_bf16x8(nibbles_to_bf16(words[t])), as_bf16x8(bx[t]),
                                         part);
-                acc[m] += lds_f32x4(sl + m * TS + 16 * i) * (part - corr);
+                acc[m] += lds_f32x4(sl + m * TS + SU * i) * (part - corr);
             }
         }
     }
@@ -360,7 +372,7 @@ struct Int4ResidualWeights {
             }
     }
     // scale tensors: W^Q's of the NMAT matrices first, then W^R's
-    template <int NMAT, int U, int TS>
+    template <int NMAT, int U, int TS, int SU>
     __device__ static void mma(const Batch<NMAT, U>& d, const u32x4* bl, const float* sl,
                                f32x4* acc) {
         const u32x4 k136 = {0x43084308u, 0x43084308u, 0x43084308u, 0x43084308u};  // BF16 136
@@ -385,8 +397,8 @@ struct Int4ResidualWeights {
                     pr = mfma16x16x32(as_bf16x8(Int4Weights::nibbles_to_bf16(rw[t])),
                                       as_bf16x8(bx[t]), pr);
                 }
-                acc[m] += lds_f32x4(sl + m * TS + 16 * i) * (pq - corr) +
-                          lds_f32x4(sl + (NMAT + m) * TS + 16 * i) * (pr - corr);
+                acc[m] += lds_f32x4(sl + m * TS + SU * i) * (pq - corr) +
+                          lds_f32x4(sl + (NMAT + m) * TS + SU * i) * (pr - corr);
             }
         }
     }
@@ -469,6 +481,7 @@ struct GemmTuning<Bf16Weights, 2> {   // gate/up: two matrices per K step
     static constexpr int kMaxDepth = 16;
     static constexpr int kWideBatch = 1;
     static constexpr bool kEarlyBatch = false;
+    static constexpr bool kScaleQuads = false;
 };
 template <>
 struct GemmTuning<Bf16Weights, 1> {   // down
@@ -477,6 +490,7 @@ struct GemmTuning<Bf16Weights, 1> {   // down
     static constexpr int kMaxDepth = 16;
     static constexpr int kWideBatch = 4;
     static constexpr bool kEarlyBatch = false;
+    static constexpr bool kScaleQuads = false;
 };
 template <>
 struct GemmTuning<Int8Weights, 2> {   // (3, 1, 4) before the scales were staged per group: 2-3 % slower
@@ -485,6 +499,7 @@ struct GemmTuning<Int8Weights, 2> {   // (3, 1, 4) before the scales were staged
     static constexpr int kMaxDepth = 8;
     static constexpr int kWideBatch = 0;
     static constexpr bool kEarlyBatch = false;
+    static constexpr bool kScaleQuads = true;
 };
 template <>
 struct GemmTuning<Int8Weights, 1> {
@@ -493,6 +508,7 @@ struct GemmTuning<Int8Weights, 1> {
     static constexpr int kMaxDepth = 8;
     static constexpr int kWideBatch = 0;
     static constexpr bool kEarlyBatch = true;
+    static constexpr bool kScaleQuads = true;
 };
 template <>
 struct GemmTuning<Int4Weights, 2> {
@@ -501,6 +517,7 @@ struct GemmTuning<Int4Weights, 2> {
     static constexpr int kMaxDepth = 4;
     static constexpr int kWideBatch = 0;
     static constexpr bool kEarlyBatch = false;
+    static constexpr bool kScaleQuads = true;
 };
 template <>
 struct GemmTuning<ResidualGateUp, 2> {
@@ -509,6 +526,7 @@ struct GemmTuning<ResidualGateUp, 2> {
     static constexpr int kMaxDepth = 4;
     static constexpr int kWideBatch = 0;
     static constexpr bool kEarlyBatch = false;
+    static constexpr bool kScaleQuads = true;
 };
 template <>
 struct GemmTuning<DualDown, 1> {
@@ -517,6 +535,7 @@ struct GemmTuning<DualDown, 1> {
     static constexpr int kMaxDepth = 16;
     static constexpr int kWideBatch = 0;
     static constexpr bool kEarlyBatch = false;
+    static constexpr bool kScaleQuads = true;
 };
 template <>
 struct GemmTuning<Int4Weights, kDownPair> {
@@ -525,8 +544,12 @@ struct GemmTuning<Int4Weights, kDownPair> {
     static constexpr int kMaxDepth = 8;
     static constexpr int kWideBatch = 0;
     static constexpr bool kEarlyBatch = false;
+    static constexpr bool kScaleQuads = false;
 };
 
+// kScaleQuads picks the scale table's LDS layout (quads or rows, above):
+// quads measured 1-2 % faster for INT8, 5 % for INT4 gate/up and 4-9 % for
+// the residual split's gate/up, and 10-15 % slower for INT4 down as a pair.
 // S: K-parts per row block; U: units per weight batch (divides the units of
 // one K part in a slab).
 // A round is R row blocks of one expert (R = 4 / S), processed by the four
@@ -538,7 +561,7 @@ struct GemmTuning<Int4Weights, kDownPair> {
 // PAIR (down, NMAT = 2): the two "matrices" are the two halves of W_down's
 // rows (g.N = H / 2 rows each, the second half at g.w1 / g.s1), so that one
 // token fragment feeds both, as W_gate and W_up share it in gate/up.
-template <class Fmt, int NMAT, int S, int U, int FMAX, int UW, bool PAIR, bool EARLY>
+template <class Fmt, int NMAT, int S, int U, int FMAX, int UW, bool PAIR, bool EARLY, bool QUADS>
 __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView ix, int n_act,
                                             int grid,
                                             u32x4 (*xs)[kSlabU4], f32x4* sc) {
@@ -562,6 +585,8 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
     constexpr int TS = R * S * SPU * FMAX * 16;
     constexpr int SCB = NSC * TS;
     static_assert(NSC == 0 || TS <= kScaleSlabFloats * FMAX, "scale table fits its buffer");
+    // the scale table's layout and its floats between consecutive units
+    constexpr int SU = QUADS ? kScaleUnitStrideQuads : kScaleUnitStrideRows;
     // after the slab loop the first slab buffer doubles as the K-part
     // reduction area (3 x NMAT x 1 KB <= 16 KB)
     f32x4* red = reinterpret_cast<f32x4*>(&xs[0][0]);
@@ -709,10 +734,6 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                 // from lanes 0-31) of one token's slab row: lane L fills block
                 // 16i + L/4 for K group L%4, so the row is read from global
                 // memory in contiguous runs.
-                // Scaled formats also stage the slab's scales: entry
-                // ((rr*S + pp)*spu + jj)*16 + row of tensor t is the scale of
-                // row 16*(rb0 + rr) + row, unit start(pp) + j*spu + jj; one
-                // 4-byte direct load per lane fills 64 consecutive entries.
                 auto stage = [&](int j, int bsel) {
                     const int kgl = lane & 3;
     #pragma unroll
@@ -732,33 +753,6 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                                 (const void*)(g.b_src + (size_t)tp[i] * (size_t)g.b_pitch + off),
                                 (lds_void_ptr)&xs[bsel][c * tpitch + ((ii & (dep - 1)) << 6)], 16,
                                 0, 0);
-                    }
-                    if constexpr (NSCF > 0) {
-                        // load k (64 entries of every tensor's table) by wave
-                        // k % 4: one offset per lane serves all tensors (they
-                        // share the [N][nunits] shape)
-                        const int nld = (R * S * 16 * spu) / kWave;
-                        float* sbuf = reinterpret_cast<float*>(sc) + bsel * SCB;
-                        for (int k = wave; k < nld; k += kWaves) {
-                            const int f = k * kWave + lane;
-                            const int row = f & 15;
-                            const int qf = f >> 4;
-                            const int jj = qf % spu;
-                            const int rp = qf / spu;
-                            const int spp = rp % S;
-                            const int rb = rb0 + rp / S;
-                            const int q0 = min(nunits, spp * kpu);
-                            const int q1 = min(nunits, q0 + kpu);
-                            const int su = q0 + j * spu + jj;
-                            const size_t soff = (size_t)(rb * 16 + row) * nunits + su;
-                            if (rb < nrb && su < q1) {
-    #pragma unroll
-                                for (int t = 0; t < NSCF; ++t)
-                                    __builtin_amdgcn_global_load_lds(
-                                        (const void*)(stab[t] + soff),
-                                        (lds_void_ptr)(sbuf + t * TS + k * kWave), 4, 0, 0);
-                            }
-                        }
                     }
                 };
                 stage(0, 0);
@@ -785,14 +779,11 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
     #pragma unroll
                     for (int hh = 0; hh < NC; ++hh)
                         buf[hh] = &xs[j & 1][bcol[hh] * tpitch + ((kp * SPC * kBlockU4) << dl) + kg];
-                    // this lane's scales: row block r, K part kp, unit 0 of the
-                    // slab, output rows 4kg .. 4kg + 3
-                    const float* sl = reinterpret_cast<const float*>(sc) + (j & 1) * SCB +
-                                      (r * S + kp) * spu * 16 + 4 * kg;
+                    // unscaled weights: the formats' mma takes no scales
+                    const float* sb = nullptr;
                     const int bend = min(nfull, (j + 1) * nb);
                     for (; bi < bend; ++bi) {
                         const int ub = u0 + bi * UC - slab_u0;   // batch's first unit in the slab
-                        const float* sb = sl + 16 * ub;
                         // the B pointers before the next batch's loads (computing
                         // them after those loads made the compiler keep far more
                         // registers live in the quantised gate/up kernels)
@@ -802,13 +793,13 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                         if ((bi & 1) == 0) {
                             if (bi + 1 < nfull)
                                 F::template load<NMAT, UC>(B, src, u0 + (bi + 1) * UC);
-                            F::template mma<NMAT, UC, TS>(A, bb[0], sb, acc[0]);
-                            if constexpr (NC == 2) F::template mma<NMAT, UC, TS>(A, bb[1], sb, acc[1]);
+                            F::template mma<NMAT, UC, TS, SU>(A, bb[0], sb, acc[0]);
+                            if constexpr (NC == 2) F::template mma<NMAT, UC, TS, SU>(A, bb[1], sb, acc[1]);
                         } else {
                             if (bi + 1 < nfull)
                                 F::template load<NMAT, UC>(A, src, u0 + (bi + 1) * UC);
-                            F::template mma<NMAT, UC, TS>(B, bb[0], sb, acc[0]);
-                            if constexpr (NC == 2) F::template mma<NMAT, UC, TS>(B, bb[1], sb, acc[1]);
+                            F::template mma<NMAT, UC, TS, SU>(B, bb[0], sb, acc[0]);
+                            if constexpr (NC == 2) F::template mma<NMAT, UC, TS, SU>(B, bb[1], sb, acc[1]);
                         }
                     }
                     if (has && tail_u < u1 && tail_u >= slab_u0 && tail_u < slab_u0 + spu)
@@ -817,9 +808,9 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                             F::template load<NMAT, 1>(t, src, u);
     #pragma unroll
                             for (int hh = 0; hh < NC; ++hh)
-                                F::template mma<NMAT, 1, TS>(
-                                    t, buf[hh] + (u - slab_u0) * F::kBlocks * kBlockU4,
-                                    sl + 16 * (u - slab_u0), acc[hh]);
+                                F::template mma<NMAT, 1, TS, SU>(
+                                    t, buf[hh] + (u - slab_u0) * F::kBlocks * kBlockU4, sb,
+                                    acc[hh]);
                         }
                 }
                 __syncthreads();
@@ -941,10 +932,11 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                 // slab row: lane L fills block 16i + L/4 for K group L%4, so the
                 // row is read from global memory in contiguous runs.
                 // Scaled formats also stage the scales of a group of slabs:
-                // entry ((rr*S + pp)*GU + jj)*16 + row of tensor t in group
-                // G is the scale of row 16*(rb0 + rr) + row, unit start(pp) +
-                // G*GU + jj; one 4-byte direct load per lane fills 64
-                // consecutive entries.
+                // the scale of row 16*(rb0 + rr) + 4*rq + t, unit start(pp) +
+                // G*GU + jj in group G is entry ((rr*S + pp)*GU + jj)*16 +
+                // 4*rq + t (rows) or (((rr*S + pp)*4 + rq)*GU + jj)*4 + t
+                // (quads) of its tensor's table; one 4-byte direct load per
+                // lane fills 64 consecutive entries.
                 auto stage = [&](int j, int bsel) {
                     const int kgl = lane & 3;
     #pragma unroll
@@ -978,10 +970,10 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                             float* sbuf = reinterpret_cast<float*>(sc) + (G & 1) * SCB;
                             for (int k = wave; k < nld; k += kWaves) {
                                 const int f = k * kWave + lane;
-                                const int row = f & 15;
-                                const int qf = f >> 4;
+                                const int qf = QUADS ? f >> 2 : f >> 4;
                                 const int jj = qf % GU;
-                                const int rp = qf / GU;
+                                const int rp = QUADS ? (qf / GU) >> 2 : qf / GU;
+                                const int row = QUADS ? 4 * ((qf / GU) & 3) + (f & 3) : f & 15;
                                 const int spp = rp % S;
                                 const int rb = rb0 + rp / S;
                                 const int q0 = min(nunits, spp * kpu);
@@ -1053,8 +1045,10 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                         &xs[j & 1][bcol * tpitch + ((kp * SP * kBlockU4) << dl) + kg];
                     // this lane's scales: row block r, K part kp, unit 0 of the
                     // slab (slab j & (P - 1) of its group), output rows 4kg .. 4kg + 3
-                    const float* sl = reinterpret_cast<const float*>(sc) + ((j >> logP) & 1) * SCB +
-                                      ((r * S + kp) * GU + (j & (P - 1)) * spu) * 16 + 4 * kg;
+                    const float* sl =
+                        reinterpret_cast<const float*>(sc) + ((j >> logP) & 1) * SCB +
+                        (QUADS ? (((r * S + kp) * 4 + kg) * GU + (j & (P - 1)) * spu) * SU
+                               : ((r * S + kp) * GU + (j & (P - 1)) * spu) * SU + 4 * kg);
                     if constexpr (F::kFixedRolePipeline) {
                         // one batch: request the next one into nxt (after the
                         // last batch, the last again: an unconditional request
@@ -1066,8 +1060,8 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                         // and the copy waits for the batch just requested).
                         auto mult = [&](auto& cur, int b) __attribute__((always_inline)) {
                             const int ub = u0 + b * U - slab_u0;   // batch's first unit in the slab
-                            F::template mma<NMAT, U, TS>(cur, buf + ub * F::kBlocks * kBlockU4,
-                                                         sl + 16 * ub, acc);
+                            F::template mma<NMAT, U, TS, SU>(cur, buf + ub * F::kBlocks * kBlockU4,
+                                                         sl + SU * ub, acc);
                         };
                         auto step = [&](auto& cur, auto& nxt, int b) __attribute__((always_inline)) {
                             F::template load<NMAT, U>(nxt, src, u0 + min(b + 1, nfull - 1) * U);
@@ -1091,15 +1085,15 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                         for (; bi < bend; ++bi) {
                             const int ub = u0 + bi * U - slab_u0;   // batch's first unit in the slab
                             const u32x4* bb = buf + ub * F::kBlocks * kBlockU4;
-                            const float* sb = sl + 16 * ub;
+                            const float* sb = sl + SU * ub;
                             if ((bi & 1) == 0) {
                                 if (bi + 1 < nfull)
                                     F::template load<NMAT, U>(B, src, u0 + (bi + 1) * U);
-                                F::template mma<NMAT, U, TS>(A, bb, sb, acc);
+                                F::template mma<NMAT, U, TS, SU>(A, bb, sb, acc);
                             } else {
                                 if (bi + 1 < nfull)
                                     F::template load<NMAT, U>(A, src, u0 + (bi + 1) * U);
-                                F::template mma<NMAT, U, TS>(B, bb, sb, acc);
+                                F::template mma<NMAT, U, TS, SU>(B, bb, sb, acc);
                             }
                         }
                     }
@@ -1107,9 +1101,9 @@ __device__ __forceinline__ void gemm_rounds(const ExpertGemm& g, const IndexView
                         for (int u = tail_u; u < u1; ++u) {
                             typename F::template Batch<NMAT, 1> t;
                             F::template load<NMAT, 1>(t, src, u);
-                            F::template mma<NMAT, 1, TS>(
+                            F::template mma<NMAT, 1, TS, SU>(
                                 t, buf + (u - slab_u0) * F::kBlocks * kBlockU4,
-                                sl + 16 * (u - slab_u0), acc);
+                                sl + SU * (u - slab_u0), acc);
                         }
                 }
                 __syncthreads();
@@ -1241,6 +1235,7 @@ void expert_gemm_kernel(const ExpertGemm g) {
     constexpr int FMAX = Tune::kMaxDepth;
     constexpr int UW = WIDE ? Tune::kWideBatch : 0;
     constexpr bool EARLY = Tune::kEarlyBatch;
+    constexpr bool QUADS = Tune::kScaleQuads;
     constexpr int units1 = kSlabBlocks / Fmt::kBlocks;   // units of a part per slab, S = 1
     // K-slab buffers of the token tile, double-buffered, followed (scaled
     // formats) by the slabs' scale tables.  Both are filled by direct
@@ -1273,13 +1268,13 @@ void expert_gemm_kernel(const ExpertGemm g) {
     const int G = busy_grid(rounds_for(n_act, g.N / 16, S));
     if ((int)blockIdx.x >= G) return;
     if (S == 1)
-        gemm_rounds<Fmt, NMAT, 1, cmin(U, units1), FMAX, cmin(UW, units1 / 2), PAIR, EARLY>(
+        gemm_rounds<Fmt, NMAT, 1, cmin(U, units1), FMAX, cmin(UW, units1 / 2), PAIR, EARLY, QUADS>(
             g, ix, n_act, G, xs, sc);
     else if (S == 2)
-        gemm_rounds<Fmt, NMAT, 2, cmin(U, units1 / 2), FMAX, cmin(UW, units1 / 4), PAIR, EARLY>(
+        gemm_rounds<Fmt, NMAT, 2, cmin(U, units1 / 2), FMAX, cmin(UW, units1 / 4), PAIR, EARLY, QUADS>(
             g, ix, n_act, G, xs, sc);
     else
-        gemm_rounds<Fmt, NMAT, 4, cmin(U, units1 / 4), FMAX, cmin(UW, units1 / 8), PAIR, EARLY>(
+        gemm_rounds<Fmt, NMAT, 4, cmin(U, units1 / 4), FMAX, cmin(UW, units1 / 8), PAIR, EARLY, QUADS>(
             g, ix, n_act, G, xs, sc);
 }
 
